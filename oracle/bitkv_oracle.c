@@ -1,0 +1,393 @@
+/*
+ * bitkv_oracle.c -- plain CPU oracle.  TEST INFRASTRUCTURE ONLY (see the
+ * header).  Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off -fPIC -shared
+ * (no -ffast-math: the codec needs IEEE fp32 with a correctly rounded divide).
+ *
+ * Step names follow the method as the pages describe it:
+ *   O1 quantise   asymmetric per-group uniform quantiser, x ~= s*x' + m with
+ *                 m the group minimum (HACK review, Eq. (4) and "What carries
+ *                 the argument"; TailorKV review, fp16 zero point and scale).
+ *   O2 pack       this library's bit layouts (a storage convention, not from
+ *                 the pages): K rows are an LSB-first bitstream, so 3-bit
+ *                 codes straddle 32-bit words; V codes are token-tiled.
+ *   O3 score      approximate logit per query head against the dequantised
+ *                 keys; selection score = max over the query heads of a KV
+ *                 head's group.
+ *   O4 select     the top-k tokens per KV head by that score (JetFire README,
+ *                 introduction: correction for top-k tokens).
+ *   O5 correct    softmax attention where the selected tokens use exact fp16
+ *                 keys/values from the shadow copy and every other token uses
+ *                 the dequantised ones (JetFire README, introduction;
+ *                 standard softmax attention per the TailorKV review's
+ *                 "Assumptions" list).
+ */
+#include "bitkv_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ fp16 */
+
+float orc_f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 31;
+  int m = h & 1023;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp(1.0 + m / 1024.0, e - 15);
+  }
+  return (float)(sign ? -v : v);
+}
+
+uint16_t orc_f32_to_f16(float f) {
+  uint16_t sign = signbit(f) ? 0x8000 : 0;
+  double a = fabs((double)f);
+  if (isnan(f)) return 0x7E00;
+  if (isinf(f)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: the value in units of 2^-24, rounded to nearest even
+     * (rint uses the default rounding mode, round-half-even).  A result of
+     * 1024 is exactly the smallest normal, whose bit pattern is also 1024. */
+    double q = rint(a * ldexp(1.0, 24));
+    return sign | (uint16_t)q;
+  }
+  int e2;
+  double fr = frexp(a, &e2); /* a = fr * 2^e2, fr in [0.5, 1) */
+  int e = e2 - 1;            /* a = (2*fr) * 2^e, 2*fr in [1, 2) */
+  double mant = rint((2.0 * fr - 1.0) * 1024.0);
+  if (mant == 1024.0) {
+    mant = 0.0;
+    e += 1;
+  }
+  if (e > 15) return sign | 0x7C00; /* overflow to infinity */
+  return sign | (uint16_t)(((e + 15) << 10) | (int)mant);
+}
+
+/* -------------------------------------------------------------- O1 codec */
+
+void orc_quantize_group(const uint16_t* x, int g, int bits, uint8_t* codes,
+                        uint16_t* scale16, uint16_t* zero16) {
+  float mn = INFINITY, mx = -INFINITY;
+  for (int i = 0; i < g; ++i) {
+    float v = orc_f16_to_f32(x[i]);
+    if (v < mn) mn = v;
+    if (v > mx) mx = v;
+  }
+  const float qmax = (float)((1 << bits) - 1);
+  const float s32 = (mx - mn) / qmax; /* fp32 subtract, correctly rounded divide */
+  const uint16_t s16 = orc_f32_to_f16(s32);
+  const uint16_t z16 = orc_f32_to_f16(mn); /* mn is an fp16 value: exact */
+  const float s = orc_f16_to_f32(s16);
+  const float z = orc_f16_to_f32(z16);
+  for (int i = 0; i < g; ++i) {
+    int code = 0;
+    if (s != 0.0f) {
+      const float v = orc_f16_to_f32(x[i]);
+      const float r = rintf((v - z) / s); /* nearest, ties to even */
+      code = r < 0.0f ? 0 : (r > qmax ? (int)qmax : (int)r);
+    }
+    codes[i] = (uint8_t)code;
+  }
+  *scale16 = s16;
+  *zero16 = z16;
+}
+
+void orc_quantize_rows(const uint16_t* x, int n, int D, int g, int bits,
+                       uint8_t* codes, uint32_t* meta) {
+  const int ng = D / g;
+  for (int r = 0; r < n; ++r) {
+    for (int j = 0; j < ng; ++j) {
+      uint16_t s16, z16;
+      orc_quantize_group(x + (size_t)r * D + (size_t)j * g, g, bits,
+                         codes + (size_t)r * D + (size_t)j * g, &s16, &z16);
+      meta[(size_t)r * ng + j] = (uint32_t)s16 | ((uint32_t)z16 << 16);
+    }
+  }
+}
+
+/* -------------------------------------------------------------- O2 layout */
+
+/* K: token-major rows of D*bits bits; channel c at bits [c*bits, c*bits+bits)
+ * of the row, counted LSB-first through little-endian bytes. */
+uint64_t orc_k_bitpos(int t, int c, int D, int bits) {
+  return (uint64_t)t * (uint64_t)D * bits + (uint64_t)c * bits;
+}
+
+/* V: tiles of 32 tokens.  Inside a tile, for each channel c there are four
+ * 8-code words (q = 0..3), word (c, q) at index 4*c + q.  Token r of the tile
+ * (r = t mod 32) sits in word q = (r mod 16) / 4, slot j = 4*(r / 16) + r mod 4,
+ * at bits [j*bits, j*bits+bits) of that word. */
+uint64_t orc_v_bitpos(int t, int c, int D, int bits) {
+  const int tile = t / 32;
+  const int r = t % 32;
+  const int q = (r % 16) / 4;
+  const int j = 4 * (r / 16) + (r % 4);
+  const uint64_t word_bits = 8u * (uint64_t)bits;
+  return (uint64_t)tile * 32u * (uint64_t)D * bits +
+         ((uint64_t)c * 4u + (uint64_t)q) * word_bits + (uint64_t)j * bits;
+}
+
+uint32_t orc_get_bits(const uint8_t* buf, uint64_t bitpos, int nbits) {
+  uint32_t v = 0;
+  for (int i = 0; i < nbits; ++i) {
+    const uint64_t p = bitpos + (uint64_t)i;
+    const uint32_t bit = (buf[p / 8] >> (p % 8)) & 1u;
+    v |= bit << i;
+  }
+  return v;
+}
+
+void orc_set_bits(uint8_t* buf, uint64_t bitpos, int nbits, uint32_t value) {
+  for (int i = 0; i < nbits; ++i) {
+    const uint64_t p = bitpos + (uint64_t)i;
+    const uint8_t mask = (uint8_t)(1u << (p % 8));
+    if ((value >> i) & 1u)
+      buf[p / 8] |= mask;
+    else
+      buf[p / 8] &= (uint8_t)~mask;
+  }
+}
+
+static size_t units_of(const orc_shape* s) { return (size_t)s->B * s->Hkv; }
+static size_t k_unit_bytes(const orc_shape* s) {
+  return (size_t)s->cap * s->D * s->kbits / 8;
+}
+static size_t v_unit_bytes(const orc_shape* s) {
+  return (size_t)s->cap * s->D * s->vbits / 8;
+}
+size_t orc_k_codes_bytes(const orc_shape* s) { return units_of(s) * k_unit_bytes(s); }
+size_t orc_v_codes_bytes(const orc_shape* s) { return units_of(s) * v_unit_bytes(s); }
+size_t orc_meta_bytes(const orc_shape* s) {
+  return units_of(s) * (size_t)(s->D / s->group) * s->cap * sizeof(uint32_t);
+}
+size_t orc_shadow_bytes(const orc_shape* s) {
+  return units_of(s) * (size_t)s->cap * s->D * sizeof(uint16_t);
+}
+
+static size_t meta_index(const orc_shape* s, int u, int grp, int t) {
+  return ((size_t)u * (s->D / s->group) + grp) * (size_t)s->cap + t;
+}
+
+void orc_pack_append(const orc_shape* s, uint8_t* k_codes, uint8_t* v_codes,
+                     uint32_t* k_meta, uint32_t* v_meta, uint16_t* k_shadow,
+                     uint16_t* v_shadow, const uint16_t* k_new,
+                     const uint16_t* v_new, int n_new, const int32_t* pos) {
+  const int D = s->D, g = s->group, ng = s->D / s->group;
+  uint8_t* codes = (uint8_t*)malloc((size_t)D);
+  uint32_t* meta = (uint32_t*)malloc((size_t)ng * sizeof(uint32_t));
+  for (int b = 0; b < s->B; ++b) {
+    for (int kvh = 0; kvh < s->Hkv; ++kvh) {
+      const int u = b * s->Hkv + kvh;
+      for (int j = 0; j < n_new; ++j) {
+        const int t = pos[b] + j;
+        const size_t src = (((size_t)u * n_new) + j) * D;
+        /* keys */
+        orc_quantize_rows(k_new + src, 1, D, g, s->kbits, codes, meta);
+        for (int c = 0; c < D; ++c)
+          orc_set_bits(k_codes + (size_t)u * k_unit_bytes(s),
+                       orc_k_bitpos(t, c, D, s->kbits), s->kbits, codes[c]);
+        for (int grp = 0; grp < ng; ++grp) k_meta[meta_index(s, u, grp, t)] = meta[grp];
+        memcpy(k_shadow + ((size_t)u * s->cap + t) * D, k_new + src, (size_t)D * 2);
+        /* values */
+        orc_quantize_rows(v_new + src, 1, D, g, s->vbits, codes, meta);
+        for (int c = 0; c < D; ++c)
+          orc_set_bits(v_codes + (size_t)u * v_unit_bytes(s),
+                       orc_v_bitpos(t, c, D, s->vbits), s->vbits, codes[c]);
+        for (int grp = 0; grp < ng; ++grp) v_meta[meta_index(s, u, grp, t)] = meta[grp];
+        memcpy(v_shadow + ((size_t)u * s->cap + t) * D, v_new + src, (size_t)D * 2);
+      }
+    }
+  }
+  free(codes);
+  free(meta);
+}
+
+/* x_hat = s * code + z, evaluated in fp64 (exact for fp16 s, z and small
+ * integer codes). */
+static double dequant(uint32_t meta, uint32_t code) {
+  const double sc = orc_f16_to_f32((uint16_t)(meta & 0xFFFFu));
+  const double z = orc_f16_to_f32((uint16_t)(meta >> 16));
+  return sc * (double)code + z;
+}
+
+double orc_k_hat(const orc_shape* s, const uint8_t* k_codes,
+                 const uint32_t* k_meta, int u, int t, int c) {
+  const uint32_t code = orc_get_bits(k_codes + (size_t)u * k_unit_bytes(s),
+                                     orc_k_bitpos(t, c, s->D, s->kbits), s->kbits);
+  return dequant(k_meta[meta_index(s, u, c / s->group, t)], code);
+}
+
+double orc_v_hat(const orc_shape* s, const uint8_t* v_codes,
+                 const uint32_t* v_meta, int u, int t, int c) {
+  const uint32_t code = orc_get_bits(v_codes + (size_t)u * v_unit_bytes(s),
+                                     orc_v_bitpos(t, c, s->D, s->vbits), s->vbits);
+  return dequant(v_meta[meta_index(s, u, c / s->group, t)], code);
+}
+
+/* -------------------------------------------------------------- O4 top-k */
+
+typedef struct {
+  double v;
+  int32_t t;
+} scored;
+
+static int by_score_desc(const void* a, const void* b) {
+  const scored* x = (const scored*)a;
+  const scored* y = (const scored*)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return (x->t > y->t) - (x->t < y->t); /* equal scores: lower index first */
+}
+
+static int by_int_asc(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+void orc_topk(const double* sigma, int n, int k, int32_t* idx) {
+  const int kk = k < n ? k : n;
+  scored* all = (scored*)malloc((size_t)(n > 0 ? n : 1) * sizeof(scored));
+  for (int t = 0; t < n; ++t) {
+    all[t].v = sigma[t];
+    all[t].t = t;
+  }
+  qsort(all, (size_t)n, sizeof(scored), by_score_desc);
+  for (int i = 0; i < kk; ++i) idx[i] = all[i].t;
+  qsort(idx, (size_t)kk, sizeof(int32_t), by_int_asc);
+  for (int i = kk; i < k; ++i) idx[i] = -1;
+  free(all);
+}
+
+/* ------------------------------------------------------- O3 + O5 (fp64) */
+
+/* out[h][0..D) = sum_t e^{lambda_t - m} nu_t / sum_t e^{lambda_t - m} for one
+ * query head, where token t uses the exact logit/value if in_s[t] and the
+ * approximate ones otherwise.  shat: approximate logits of this head. */
+static void attend_head(const orc_shape* s, int u, int n, const double* shat,
+                        const double* sexact, const uint8_t* in_s,
+                        const uint8_t* v_codes, const uint32_t* v_meta,
+                        const uint16_t* v_shadow, double* out) {
+  const int D = s->D;
+  if (n == 0) {
+    for (int c = 0; c < D; ++c) out[c] = 0.0;
+    return;
+  }
+  double m = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    const double lam = in_s[t] ? sexact[t] : shat[t];
+    if (lam > m) m = lam;
+  }
+  double den = 0.0;
+  for (int c = 0; c < D; ++c) out[c] = 0.0;
+  for (int t = 0; t < n; ++t) {
+    const double lam = in_s[t] ? sexact[t] : shat[t];
+    const double p = exp(lam - m);
+    den += p;
+    for (int c = 0; c < D; ++c) {
+      const double nu =
+          in_s[t] ? (double)orc_f16_to_f32(v_shadow[((size_t)u * s->cap + t) * D + c])
+                  : orc_v_hat(s, v_codes, v_meta, u, t, c);
+      out[c] += p * nu;
+    }
+  }
+  for (int c = 0; c < D; ++c) out[c] /= den;
+}
+
+void orc_decode(const orc_shape* s, const uint8_t* k_codes,
+                const uint8_t* v_codes, const uint32_t* k_meta,
+                const uint32_t* v_meta, const uint16_t* k_shadow,
+                const uint16_t* v_shadow, const uint16_t* q,
+                const int32_t* len, int k, const int32_t* sel_in,
+                double* sigma, int32_t* idx, double* out, double* out_approx,
+                double* out_exact) {
+  const int G = s->Hq / s->Hkv;
+  const int D = s->D;
+  const double sm = 1.0 / sqrt((double)D);
+  const int U = s->B * s->Hkv;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int u = 0; u < U; ++u) {
+    const int b = u / s->Hkv;
+    const int kvh = u % s->Hkv;
+    const int n = len[b];
+    const int nn = n > 0 ? n : 1;
+    double* shat = (double*)malloc((size_t)G * nn * sizeof(double));
+    double* sexact = (double*)malloc((size_t)G * nn * sizeof(double));
+    uint8_t* in_s = (uint8_t*)calloc((size_t)nn, 1);
+    uint8_t* none = (uint8_t*)calloc((size_t)nn, 1);
+    uint8_t* all = (uint8_t*)malloc((size_t)nn);
+    memset(all, 1, (size_t)nn);
+    double* sig = sigma + (size_t)u * s->cap;
+
+    /* O3: approximate logits and the selection score. */
+    for (int t = 0; t < n; ++t) {
+      double best = -INFINITY;
+      for (int i = 0; i < G; ++i) {
+        const uint16_t* qh = q + ((size_t)b * s->Hq + (size_t)kvh * G + i) * D;
+        double acc = 0.0, ex = 0.0;
+        for (int c = 0; c < D; ++c) {
+          const double qc = orc_f16_to_f32(qh[c]);
+          acc += qc * orc_k_hat(s, k_codes, k_meta, u, t, c);
+          ex += qc * (double)orc_f16_to_f32(k_shadow[((size_t)u * s->cap + t) * D + c]);
+        }
+        shat[(size_t)i * nn + t] = sm * acc;
+        sexact[(size_t)i * nn + t] = sm * ex;
+        if (sm * acc > best) best = sm * acc;
+      }
+      sig[t] = best;
+    }
+
+    /* O4: the selected set. */
+    int32_t* my_idx = idx + (size_t)u * (k > 0 ? k : 0);
+    if (sel_in) {
+      const int32_t* si = sel_in + (size_t)u * (k > 0 ? k : 0);
+      for (int i = 0; i < k; ++i)
+        if (si[i] >= 0 && si[i] < n) in_s[si[i]] = 1;
+    } else if (k > 0) {
+      orc_topk(sig, n, k, my_idx);
+      for (int i = 0; i < k; ++i)
+        if (my_idx[i] >= 0) in_s[my_idx[i]] = 1;
+    }
+
+    /* O5: per query head of the group. */
+    for (int i = 0; i < G; ++i) {
+      const size_t h = (size_t)b * s->Hq + (size_t)kvh * G + i;
+      const double* sh = shat + (size_t)i * nn;
+      const double* se = sexact + (size_t)i * nn;
+      attend_head(s, u, n, sh, se, in_s, v_codes, v_meta, v_shadow, out + h * D);
+      if (out_approx)
+        attend_head(s, u, n, sh, se, none, v_codes, v_meta, v_shadow, out_approx + h * D);
+      if (out_exact)
+        attend_head(s, u, n, sh, se, all, v_codes, v_meta, v_shadow, out_exact + h * D);
+    }
+    free(shat);
+    free(sexact);
+    free(in_s);
+    free(none);
+    free(all);
+  }
+}
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
