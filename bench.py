@@ -1,0 +1,206 @@
+"""Benchmark of one approximate-then-correct decode-attention step on one GPU.
+
+A step is one pass of the whole hot path for one attention layer, all heads:
+kv_pack_append (one new token per sequence) -> qattn_decode_approx ->
+topk_select -> qattn_correct, over the workload's context length.  Inputs are
+seeded synthetic tensors (bit_kv_attention_amd.synth), resident in HBM before
+timing starts.  The timed steps rotate over several independent cache copies
+(as separate layers would) so that the packed bytes read per rotation exceed
+the 256 MB Infinity Cache.
+
+Output: one JSON line (rank 0) with tokens/s = batch / step time, the packed-KV
+bandwidth, per-kernel times, the roofline of the dominant kernel and the CPU
+oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32) -> int:
+    meta = (D // group) * 4
+    return D * kbits // 8 + meta + D * vbits // 8 + meta
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama8b_k4v4_L32768",
+                    help="workload name from bit_kv_attention_amd.synth.WORKLOADS, or 'all'")
+    ap.add_argument("--shadow", choices=["hbm", "host"], default="hbm")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the method shards by "
+              "KV head or by context length without changing the kernels); run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    from bit_kv_attention_amd.synth import BY_NAME, WORKLOADS, make_inputs, make_new_tokens
+
+    names = [w.name for w in WORKLOADS] if args.config == "all" else [args.config]
+    for name in names:
+        w = BY_NAME[name]
+        res = bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens)
+        print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
+    dev = torch.device("cuda:0")
+    L = w.L
+    cap = ((L + 31) // 32) * 32
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits)
+    units = w.B * w.Hkv
+    ppt = packed_bytes_per_token(w.kbits, w.vbits)
+    packed = units * L * ppt
+    copies = args.copies or max(1, min(8, -(-600_000_000 // packed)))
+
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(w, L=L - 1)
+    knew, vnew = make_new_tokens(w, 1, inp.outlier_ch)
+    Kd = torch.from_numpy(inp.K).to(dev)
+    Vd = torch.from_numpy(inp.V).to(dev)
+    q = torch.from_numpy(inp.q).to(dev)
+    kn = torch.from_numpy(knew[0]).to(dev)
+    vn = torch.from_numpy(vnew[0]).to(dev)
+    caches = []
+    for c in range(copies):
+        cache = bk.allocate_cache(lay, device=dev, shadow_on_host=(args.shadow == "host"))
+        bk.kv_pack_append(lay, cache, Kd, Vd, L - 1, [0] * w.B)
+        caches.append(cache)
+    del Kd, Vd
+    torch.cuda.synchronize()
+    st = DecodeStep(lay, w.k, L, device=dev)
+    pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
+    lens = [L] * w.B
+
+    def step(i):
+        cache = caches[i % copies]
+        bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
+        st.attend(cache, q, lens)
+
+    print(f"[bench] {w.name}: warmup {args.warmup}, timing {args.steps} steps over {copies} copies",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # Per-kernel averages: the same steps again with events around each call.
+    names = ("kv_pack_append", "qattn_decode_approx", "topk_select", "qattn_correct")
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(args.steps)]
+    for i in range(args.steps):
+        cache = caches[i % copies]
+        e = ev[i]
+        e[0][0].record(); bk.kv_pack_append(lay, cache, kn, vn, 1, pos); e[0][1].record()
+        e[1][0].record(); bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws); e[1][1].record()
+        e[2][0].record(); bk.topk_select(lay, st.sigma, lens, w.k, st.idx); e[2][1].record()
+        e[3][0].record()
+        bk.qattn_correct(lay, cache, q, lens, st.idx, w.k, st.ws, st.out)
+        e[3][1].record()
+    torch.cuda.synchronize()
+    kus = {n: 1000.0 * float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+           for j, n in enumerate(names)}
+
+    tokens_per_s = w.B / (ms / 1000.0)
+    packed_gbps = packed / (ms / 1000.0) / 1e9
+    # dominant kernel: the approximate scan.  Algorithmic bytes per launch =
+    # packed codes + meta of K and V for every token of every unit, the fp32
+    # selection score written per token, and the split partial states written.
+    nsplit_bytes = bk.bkv_workspace_bytes(lay, L)
+    scan_bytes = units * L * (ppt + 4) + nsplit_bytes
+    scan_s = kus["qattn_decode_approx"] / 1e6
+    achieved = scan_bytes / scan_s / 1e9
+    res = {
+        "metric": "decode attention tokens/s + packed-KV HBM GB/s (% of peak), 32K & 128K ctx",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
+                   "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
+                   "group": w.group, "top_k": w.k, "shadow": args.shadow, "cache_copies": copies,
+                   "parallelism": "single GPU"},
+        "packed_kv_GBps": round(packed_gbps, 1),
+        "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
+        "kernel_us": {n: round(v, 2) for n, v in kus.items()},
+        "wall_s_timed_region": round(t_wall, 3),
+        "roofline": {"kernel": "qattn_decode_approx", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": scan_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, inp, knew, vnew, args.cpu_threads)
+    del caches
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, inp, knew, vnew, threads):
+    """The oracle, as it stands, on a bounded sample of the same step: `threads`
+    (batch, KV head) units, one thread each; the full step would take
+    units/threads times as long."""
+    import oracle
+    oracle.build(force=False)
+    threads = threads or min(16, os.cpu_count() or 1)
+    units = w.B * w.Hkv
+    sample = min(threads, units)
+    oracle.set_threads(sample)
+    L = w.L
+    cap = ((L + 31) // 32) * 32
+    sel = [(u // w.Hkv, u % w.Hkv) for u in range(sample)]
+    s = oracle.Shape(1, w.G * sample, sample, 128, w.kbits, w.vbits, 32, cap)
+    # fold the sampled units into one batch row of `sample` KV heads
+    K = np.stack([inp.K[b, h] for b, h in sel])[None]
+    V = np.stack([inp.V[b, h] for b, h in sel])[None]
+    q = np.concatenate([inp.q[b, h * w.G:(h + 1) * w.G] for b, h in sel])[None]
+    kn = np.stack([knew[0][b, h] for b, h in sel])[None]
+    vn = np.stack([vnew[0][b, h] for b, h in sel])[None]
+    cache = oracle.Cache(s)
+    cache.append(K, V, np.zeros(1, np.int32))
+    t = time.perf_counter()
+    cache.append(kn, vn, np.array([L - 1], np.int32))
+    cache.decode(q, np.array([L], np.int32), w.k)
+    dt = time.perf_counter() - t
+    t_step = dt * units / sample
+    return {"value": round(w.B / t_step, 4), "unit": "tokens/s", "cores": sample, "kind": "oracle",
+            "sample": f"{sample} of {units} (batch, KV head) units of one step at context {L} "
+                      f"(append + approximate scores + top-{w.k} + corrected output), one thread "
+                      f"per unit; {dt:.2f} s measured, scaled by {units}/{sample}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,178 @@
+"""ctypes binding of libbitkv.so (include/bitkv.h), same names as the C ABI.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind these calls.  torch is used for device memory and streams.
+Importing this module without the built library raises immediately: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbitkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python bit_kv_attention_amd/build.py`; there is no non-HIP fallback.")
+
+# torch ships its own HIP runtime (same soname as ROCm's).  Loading torch first
+# makes libbitkv.so bind to that runtime, which owns the tensors' memory and
+# streams; loading the library first would put a second runtime in the process.
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+STATUS = {0: "BKV_OK", 1: "BKV_E_NULL", 2: "BKV_E_SHAPE", 3: "BKV_E_UNSUPPORTED",
+          4: "BKV_E_CAPACITY", 5: "BKV_E_WORKSPACE", 6: "BKV_E_HIP", 7: "BKV_E_ARG"}
+
+
+class BitKVError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.bkv_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+class Layout(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("batch", "n_q_heads", "n_kv_heads", "head_dim", "k_bits",
+                                         "v_bits", "group", "capacity")]
+
+
+class CacheView(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("k_codes", "v_codes", "k_meta", "v_meta", "k_shadow", "v_shadow")]
+
+
+_P = C.c_void_p
+_LP = C.POINTER(Layout)
+_CP = C.POINTER(CacheView)
+_SZ = C.POINTER(C.c_size_t)
+_lib.bkv_status_string.argtypes = [C.c_int]
+_lib.bkv_status_string.restype = C.c_char_p
+_lib.bkv_cache_bytes.argtypes = [_LP, _SZ, _SZ, _SZ, _SZ]
+_lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, _SZ]
+_lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
+_lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
+_lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P]
+_lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
+for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
+           "topk_select", "qattn_correct"):
+    getattr(_lib, _f).restype = C.c_int
+
+EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append",
+            "qattn_decode_approx", "topk_select", "qattn_correct")
+
+
+def _check(fn: str, st: int) -> None:
+    if st != 0:
+        raise BitKVError(fn, st)
+
+
+def _ptr(t) -> int | None:
+    """Device/host address of a torch tensor (or None / an int address)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _host_i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_layout(batch, n_q_heads, n_kv_heads, capacity, k_bits, v_bits, head_dim=128, group=32) -> Layout:
+    return Layout(batch, n_q_heads, n_kv_heads, head_dim, k_bits, v_bits, group, capacity)
+
+
+def bkv_cache_bytes(layout: Layout):
+    a, b, c, d = C.c_size_t(), C.c_size_t(), C.c_size_t(), C.c_size_t()
+    _check("bkv_cache_bytes", _lib.bkv_cache_bytes(C.byref(layout), C.byref(a), C.byref(b), C.byref(c), C.byref(d)))
+    return a.value, b.value, c.value, d.value
+
+
+def bkv_workspace_bytes(layout: Layout, max_len: int) -> int:
+    out = C.c_size_t()
+    _check("bkv_workspace_bytes", _lib.bkv_workspace_bytes(C.byref(layout), int(max_len), C.byref(out)))
+    return out.value
+
+
+@dataclass
+class Cache:
+    """torch-allocated buffers of one layer's cache plus the C view of them."""
+    layout: Layout
+    k_codes: object
+    v_codes: object
+    k_meta: object
+    v_meta: object
+    k_shadow: object
+    v_shadow: object
+
+    def view(self) -> CacheView:
+        return CacheView(*(_ptr(getattr(self, n)) for n in ("k_codes", "v_codes", "k_meta", "v_meta",
+                                                            "k_shadow", "v_shadow")))
+
+
+def allocate_cache(layout: Layout, device="cuda", shadow_on_host: bool = False) -> Cache:
+    """Zero-filled cache buffers (torch).  With shadow_on_host the fp16 shadow
+    rows live in pinned host memory that the GPU reads across PCIe."""
+    import torch
+    kb, vb, mb, sb = bkv_cache_bytes(layout)
+    z8 = lambda n: torch.zeros(n, dtype=torch.uint8, device=device)
+    z32 = lambda n: torch.zeros(n // 4, dtype=torch.int32, device=device)
+    if shadow_on_host:
+        sh = lambda n: torch.zeros(n // 2, dtype=torch.float16, pin_memory=True)
+    else:
+        sh = lambda n: torch.zeros(n // 2, dtype=torch.float16, device=device)
+    return Cache(layout, z8(kb), z8(vb), z32(mb), z32(mb), sh(sb), sh(sb))
+
+
+def kv_pack_append(layout: Layout, cache: Cache, k_new, v_new, n_new: int, pos_host, stream=None) -> None:
+    pos = _host_i32(pos_host)
+    view = cache.view()
+    _check("kv_pack_append", _lib.kv_pack_append(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new),
+                                                 int(n_new), pos.ctypes.data, _stream(stream)))
+
+
+def qattn_decode_approx(layout: Layout, cache: Cache, q, len_host, sigma, ws, stream=None) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_decode_approx", _lib.qattn_decode_approx(C.byref(layout), C.byref(view), _ptr(q),
+                                                           lens.ctypes.data, _ptr(sigma), _ptr(ws),
+                                                           ws_bytes, _stream(stream)))
+
+
+def topk_select(layout: Layout, sigma, len_host, k: int, idx, stream=None) -> None:
+    lens = _host_i32(len_host)
+    _check("topk_select", _lib.topk_select(C.byref(layout), _ptr(sigma), lens.ctypes.data, int(k), _ptr(idx),
+                                           _stream(stream)))
+
+
+def qattn_correct(layout: Layout, cache: Cache, q, len_host, idx, k: int, ws, out, stream=None) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_correct", _lib.qattn_correct(C.byref(layout), C.byref(view), _ptr(q), lens.ctypes.data,
+                                               _ptr(idx), int(k), _ptr(ws), ws_bytes, _ptr(out),
+                                               _stream(stream)))
+
+
+def raw_status(fn: str, *args) -> int:
+    """Call an entry point with raw ctypes arguments and return its status
+    (used to exercise the host-side error paths)."""
+    return int(getattr(_lib, fn)(*args))

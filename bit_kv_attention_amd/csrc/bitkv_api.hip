@@ -1,0 +1,203 @@
+// bitkv_api.hip -- the C ABI of libbitkv.so (declared in include/bitkv.h):
+// host-side argument validation, workspace sizing and kernel launches.
+// Nothing here allocates, frees or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include "bkv_internal.h"
+
+namespace bkv {
+
+int split_tokens(int units, int max_len) {
+  // Work per workgroup: a multiple of 4 waves x 32 tokens, sized so the grid
+  // has about 1024 workgroups (4 per CU on 256 CUs) when the context allows.
+  const long long total = (long long)units * (max_len > 0 ? max_len : 1);
+  long long per = (total + 1023) / 1024;
+  per = ((per + 127) / 128) * 128;
+  if (per < 128) per = 128;
+  return (int)per;
+}
+
+int num_splits(int units, int max_len) {
+  const int chunk = split_tokens(units, max_len);
+  const int ns = (max_len + chunk - 1) / chunk;
+  return ns > 0 ? ns : 1;
+}
+
+// An upper bound of num_splits(units, m) over every m <= max_len (the split
+// count is not monotone in m): chunk >= 128 gives ceil(m/128), and
+// chunk >= units*m/1024 gives ceil(1024/units).
+static int max_splits(int units, int max_len) {
+  const int a = (max_len + 127) / 128;
+  const int b = (1024 + units - 1) / units;
+  const int m = a < b ? a : b;
+  return m > 0 ? m : 1;
+}
+
+size_t partials_bytes(int B, int Hq, int nsplit) {
+  return (size_t)B * Hq * nsplit * (2 + kHeadDim) * sizeof(float);
+}
+
+Partials partials_in(void* ws, int B, int Hq, int nsplit) {
+  float* f = static_cast<float*>(ws);
+  const size_t recs = (size_t)B * Hq * nsplit;
+  Partials p;
+  p.acc = f;
+  p.m = f + recs * kHeadDim;
+  p.l = p.m + recs;
+  return p;
+}
+
+}  // namespace bkv
+
+using namespace bkv;
+
+static bkv_status check_layout(const bkv_layout* L) {
+  if (!L) return BKV_E_NULL;
+  if (L->batch <= 0 || L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->head_dim <= 0 ||
+      L->group <= 0 || L->capacity <= 0)
+    return BKV_E_SHAPE;
+  if (L->n_q_heads % L->n_kv_heads != 0) return BKV_E_SHAPE;
+  if (L->head_dim % L->group != 0) return BKV_E_SHAPE;
+  if (L->capacity % kTile != 0) return BKV_E_SHAPE;
+  if (L->head_dim != kHeadDim || L->group != kGroup) return BKV_E_UNSUPPORTED;
+  if (L->k_bits != 3 && L->k_bits != 4) return BKV_E_UNSUPPORTED;
+  if (L->v_bits != 2 && L->v_bits != 4) return BKV_E_UNSUPPORTED;
+  const int G = L->n_q_heads / L->n_kv_heads;
+  if (G != 4 && G != 8) return BKV_E_UNSUPPORTED;
+  if (L->batch > kMaxBatch) return BKV_E_UNSUPPORTED;
+  return BKV_OK;
+}
+
+static bkv_status check_cache(const bkv_cache* c) {
+  if (!c || !c->k_codes || !c->v_codes || !c->k_meta || !c->v_meta || !c->k_shadow || !c->v_shadow)
+    return BKV_E_NULL;
+  return BKV_OK;
+}
+
+static bkv_status read_lens(const bkv_layout* L, const int32_t* len_host, SeqArg* out, int* max_len) {
+  if (!len_host) return BKV_E_NULL;
+  int mx = 0;
+  for (int b = 0; b < L->batch; ++b) {
+    const int v = len_host[b];
+    if (v < 0 || v > L->capacity) return BKV_E_CAPACITY;
+    out->v[b] = v;
+    mx = v > mx ? v : mx;
+  }
+  *max_len = mx;
+  return BKV_OK;
+}
+
+extern "C" {
+
+const char* bkv_status_string(bkv_status s) {
+  switch (s) {
+    case BKV_OK: return "ok";
+    case BKV_E_NULL: return "a required pointer is NULL";
+    case BKV_E_SHAPE: return "inconsistent shape";
+    case BKV_E_UNSUPPORTED: return "unsupported configuration";
+    case BKV_E_CAPACITY: return "position or length outside the cache capacity";
+    case BKV_E_WORKSPACE: return "workspace too small";
+    case BKV_E_HIP: return "HIP kernel launch failed";
+    case BKV_E_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+bkv_status bkv_cache_bytes(const bkv_layout* L, size_t* k_codes_bytes, size_t* v_codes_bytes,
+                           size_t* meta_bytes_each, size_t* shadow_bytes_each) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!k_codes_bytes || !v_codes_bytes || !meta_bytes_each || !shadow_bytes_each) return BKV_E_NULL;
+  const size_t units = (size_t)L->batch * L->n_kv_heads;
+  *k_codes_bytes = units * k_unit_bytes(L->k_bits, L->capacity);
+  *v_codes_bytes = units * v_unit_bytes(L->v_bits, L->capacity);
+  *meta_bytes_each = units * kGroups * (size_t)L->capacity * sizeof(uint32_t);
+  *shadow_bytes_each = units * (size_t)L->capacity * kHeadDim * sizeof(uint16_t);
+  return BKV_OK;
+}
+
+bkv_status bkv_workspace_bytes(const bkv_layout* L, int32_t max_len, size_t* bytes) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!bytes) return BKV_E_NULL;
+  if (max_len < 0 || max_len > L->capacity) return BKV_E_CAPACITY;
+  const int units = L->batch * L->n_kv_heads;
+  *bytes = partials_bytes(L->batch, L->n_q_heads, max_splits(units, max_len));
+  return BKV_OK;
+}
+
+bkv_status kv_pack_append(const bkv_layout* L, const bkv_cache* c, const uint16_t* k_new,
+                          const uint16_t* v_new, int32_t n_new, const int32_t* pos_host,
+                          void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (!k_new || !v_new || !pos_host) return BKV_E_NULL;
+  if (n_new < 0) return BKV_E_ARG;
+  SeqArg pos;
+  for (int b = 0; b < L->batch; ++b) {
+    const int p = pos_host[b];
+    if (p < 0 || (long long)p + n_new > L->capacity) return BKV_E_CAPACITY;
+    pos.v[b] = p;
+  }
+  if (n_new == 0) return BKV_OK;
+  return launch_pack_append(*L, *c, k_new, v_new, n_new, pos, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
+bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                               const int32_t* len_host, float* sigma, void* ws, size_t ws_bytes,
+                               void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (!q || !sigma || !ws) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const int units = L->batch * L->n_kv_heads;
+  const int nsplit = num_splits(units, max_len);
+  if (ws_bytes < partials_bytes(L->batch, L->n_q_heads, nsplit)) return BKV_E_WORKSPACE;
+  const Partials p = partials_in(ws, L->batch, L->n_q_heads, nsplit);
+  return launch_decode_approx(*L, *c, q, len, max_len, sigma, p, nsplit, split_tokens(units, max_len),
+                              (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
+bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
+                       int32_t* idx, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if (!sigma || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  if (k == 0) return BKV_OK;
+  return launch_topk(*L, sigma, len, k, idx, (hipStream_t)stream) == hipSuccess ? BKV_OK : BKV_E_HIP;
+}
+
+bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                         const int32_t* len_host, const int32_t* idx, int32_t k, const void* ws,
+                         size_t ws_bytes, float* out, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if (!q || !ws || !out || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const int units = L->batch * L->n_kv_heads;
+  const int nsplit = num_splits(units, max_len);
+  if (ws_bytes < partials_bytes(L->batch, L->n_q_heads, nsplit)) return BKV_E_WORKSPACE;
+  const Partials p = partials_in(const_cast<void*>(ws), L->batch, L->n_q_heads, nsplit);
+  return launch_correct(*L, *c, q, len, idx, k, p, nsplit, out, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+"""One decode step = the four C-ABI calls on one stream, with the buffers they
+need allocated once (torch device memory).  Marshalling only."""
+from __future__ import annotations
+
+from . import binding as bk
+
+
+class DecodeStep:
+    """Buffers for steps of one layer shape: sigma, workspace, idx, out."""
+
+    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda"):
+        import torch
+        self.layout = layout
+        self.k = int(k)
+        L = layout
+        self.sigma = torch.empty(L.batch * L.n_kv_heads * L.capacity, dtype=torch.float32, device=device)
+        ws_bytes = bk.bkv_workspace_bytes(L, max_len)
+        self.ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
+        self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.k, 1), dtype=torch.int32, device=device)
+        self.out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32, device=device)
+
+    def attend(self, cache: bk.Cache, q, lens, stream=None):
+        """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
+        bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
+        if self.k > 0:
+            bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, stream)
+        bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
+                         self.out, stream)
+        return self.out
+
+    def step(self, cache: bk.Cache, q, k_new, v_new, pos, stream=None):
+        """Append one token per sequence at pos[b], then attend over pos[b] + 1 tokens."""
+        bk.kv_pack_append(self.layout, cache, k_new, v_new, 1, pos, stream)
+        lens = [int(p) + 1 for p in pos]
+        return self.attend(cache, q, lens, stream)

@@ -1,0 +1,188 @@
+/*
+ * bitkv.h -- C ABI of libbitkv.so: approximate-then-correct low-bit KV decode
+ * attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method (JetFire README, introduction; title "Approximate-then-Correct
+ * Attention on Hybrid Memory"): keep the KV cache in low-bit form, compute
+ * attention approximately over it, pick the top-k tokens, and correct those
+ * tokens with exact high-precision keys and values.  The quantiser is the
+ * asymmetric per-group one of the HACK review on Pith (Eq. (4), "What carries
+ * the argument": x ~= s*x' + m, m the group minimum) with an fp16 scale and
+ * zero point per group (TailorKV review on Pith, "Assumptions & free
+ * parameters").  Top-k is taken per KV head (Jet-QSparse abstract: the
+ * selection budget is per KV head).
+ *
+ * One decode step is four calls on one stream:
+ *   kv_pack_append       quantise + pack the new token(s), write the shadow
+ *   qattn_decode_approx  approximate scores, selection score, split softmax.V
+ *   topk_select          top-k tokens per KV head by the selection score
+ *   qattn_correct        merge the splits, replace the top-k tokens' logits
+ *                        and values by exact ones, renormalise
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers unless the name ends in _host.
+ *    Shadow pointers may also be device-visible pinned host memory (see
+ *    bkv_cache).  The caller owns every buffer; the library never allocates,
+ *    frees or synchronises, and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work; results are ready when the stream is.
+ *  - Errors: every call validates its arguments on the host before any launch
+ *    and returns a status; it never aborts, throws or prints.  On any status
+ *    other than BKV_OK nothing was enqueued, except BKV_E_HIP, which reports
+ *    a failed launch (hipGetLastError) of one of the call's kernels.
+ *  - Supported shapes: head_dim 128, group 32, k_bits in {3, 4},
+ *    v_bits in {2, 4}, n_q_heads / n_kv_heads in {4, 8}, capacity a positive
+ *    multiple of 32, batch in [1, 256].  Others return BKV_E_UNSUPPORTED or
+ *    BKV_E_SHAPE.
+ *  - Query head h attends with KV head h / (n_q_heads / n_kv_heads).
+ *  - Softmax scale 1/sqrt(head_dim); no mask inside the cached tokens.
+ *  - Inputs must be finite fp16 values.
+ */
+#ifndef BITKV_H
+#define BITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BKV_OK = 0,
+  BKV_E_NULL = 1,        /* a required pointer is NULL                       */
+  BKV_E_SHAPE = 2,       /* inconsistent sizes (e.g. Hq % Hkv, capacity % 32) */
+  BKV_E_UNSUPPORTED = 3, /* valid but not built (bits, head_dim, group, G)     */
+  BKV_E_CAPACITY = 4,    /* a position or length outside [0, capacity]         */
+  BKV_E_WORKSPACE = 5,   /* workspace smaller than bkv_workspace_bytes         */
+  BKV_E_HIP = 6,         /* a kernel launch failed                             */
+  BKV_E_ARG = 7          /* other invalid scalar argument (k < 0, n_new < 0)   */
+} bkv_status;
+
+/* Shape of one attention layer's cache. */
+typedef struct {
+  int32_t batch;      /* B                                                  */
+  int32_t n_q_heads;  /* Hq                                                 */
+  int32_t n_kv_heads; /* Hkv; units are the B*Hkv (batch, KV head) pairs    */
+  int32_t head_dim;   /* D (128)                                            */
+  int32_t k_bits;     /* bits per key code (3 or 4)                         */
+  int32_t v_bits;     /* bits per value code (2 or 4)                       */
+  int32_t group;      /* channels per quantisation group along D (32)       */
+  int32_t capacity;   /* token slots per unit, multiple of 32               */
+} bkv_layout;
+
+/*
+ * The cache of one layer.  Unit u = b * Hkv + kvh is the outermost index of
+ * every buffer.  Sizes come from bkv_cache_bytes.  Zero-fill the code buffers
+ * before the first append: appends read-modify-write the shared V words.
+ *
+ *  k_codes  [B][Hkv][capacity][D*k_bits/8] bytes.  Token t's row is an
+ *           LSB-first little-endian bitstream; channel c occupies bits
+ *           [c*k_bits, (c+1)*k_bits), so with 3 bits channels 10 and 21 of
+ *           every 32-channel group straddle 32-bit words.  16-byte aligned.
+ *  v_codes  [B][Hkv][capacity/32][D][4] words of 8*v_bits bits.  In each
+ *           32-token tile, word (c, q) holds 8 codes of channel c: token r of
+ *           the tile (r = t mod 32) is in word q = (r mod 16)/4, slot
+ *           j = 4*(r/16) + r mod 4, at bits [j*v_bits, (j+1)*v_bits).
+ *           16-byte aligned.
+ *  k_meta,  [B][Hkv][D/group][capacity] uint32: fp16 scale in the low half,
+ *  v_meta   fp16 zero point (group minimum) in the high half.
+ *  k_shadow,[B][Hkv][capacity][D] fp16: the exact input rows.  Device memory,
+ *  v_shadow or pinned host memory the device can address (e.g. hipHostMalloc
+ *           with default flags): qattn_correct then gathers the selected
+ *           rows across PCIe.
+ */
+typedef struct {
+  void* k_codes;
+  void* v_codes;
+  uint32_t* k_meta;
+  uint32_t* v_meta;
+  uint16_t* k_shadow;
+  uint16_t* v_shadow;
+} bkv_cache;
+
+/* Byte sizes of the cache buffers for `layout`.  Host only. */
+bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
+                           size_t* v_codes_bytes, size_t* meta_bytes_each,
+                           size_t* shadow_bytes_each);
+
+/* Workspace bytes that cover qattn_decode_approx / qattn_correct for every
+ * step whose longest sequence has at most max_len tokens (the split partial
+ * states).  Host only.  The same workspace is passed to both calls of one
+ * step. */
+bkv_status bkv_workspace_bytes(const bkv_layout* layout, int32_t max_len,
+                               size_t* bytes);
+
+/*
+ * kv_pack_append -- quantise and store n_new tokens per sequence.
+ * For each (b, kvh) and j < n_new the token k_new/v_new[b][kvh][j][0..D)
+ * (fp16, device) goes to slot t = pos_host[b] + j: per group of 32 channels
+ * the fp16 zero z = min, scale s = fp16((max - min) / (2^bits - 1)) computed
+ * in fp32 with a correctly rounded divide, and codes
+ * clamp(rint((x - z) / s), 0, 2^bits - 1) from the stored fp16 s and z (0 when
+ * s is 0), round to nearest even throughout; then the bits, the meta words and
+ * the verbatim shadow row.
+ * Errors: BKV_E_CAPACITY unless 0 <= pos_host[b] and pos_host[b] + n_new <=
+ * capacity; BKV_E_ARG if n_new < 0 (n_new == 0 enqueues nothing).
+ */
+bkv_status kv_pack_append(const bkv_layout* layout, const bkv_cache* cache,
+                          const uint16_t* k_new, const uint16_t* v_new,
+                          int32_t n_new, const int32_t* pos_host, void* stream);
+
+/*
+ * qattn_decode_approx -- the approximate pass over the packed cache.
+ * q [B][Hq][D] fp16 (device).  Sequence b attends to its first len_host[b]
+ * tokens.  For every query head h and token t the approximate logit is
+ *   s_hat[h][t] = (1/sqrt(D)) * sum_c q[h][c] * (s * code + z),
+ * evaluated as sum over groups of s * (q . codes) + z * sum(q) (HACK review,
+ * Eq. (4), with an unquantised query).  Writes
+ *   sigma [B][Hkv][capacity] fp32: sigma[t] = max over the KV head's query
+ *         heads of s_hat[h][t] for t < len (slots up to the next multiple of
+ *         32 get -inf; others untouched);
+ *   ws:   per (b, h, split) the softmax state (running max in log2 units,
+ *         denominator, unnormalised sum of p * V_hat) of its token range.
+ * Errors: BKV_E_CAPACITY if some len_host[b] is outside [0, capacity];
+ * BKV_E_WORKSPACE if ws_bytes < bkv_workspace_bytes(layout, max len).
+ */
+bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
+                               const uint16_t* q, const int32_t* len_host,
+                               float* sigma, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * topk_select -- per (b, kvh): the min(k, len) tokens with the largest sigma,
+ * ties broken towards the lower index (JetFire README, introduction: top-k
+ * tokens get the high-precision correction).  idx [B][Hkv][k] int32 (device)
+ * receives the selected token indices in ascending order, -1 after the
+ * min(k, len)-th entry.  k == 0 enqueues nothing.
+ * Errors: BKV_E_ARG if k < 0; BKV_E_CAPACITY for a bad length.
+ */
+bkv_status topk_select(const bkv_layout* layout, const float* sigma,
+                       const int32_t* len_host, int32_t k, int32_t* idx,
+                       void* stream);
+
+/*
+ * qattn_correct -- merge the splits written by qattn_decode_approx and apply
+ * the exact correction: for the selected tokens S (idx, as written by
+ * topk_select; negative entries are skipped) the approximate logit and value
+ * are replaced by the exact ones from the shadow rows,
+ *   lambda_t = (1/sqrt(D)) q . K_t,  nu_t = V_t        (t in S)
+ *   lambda_t = s_hat[t],             nu_t = V_hat_t     (t not in S)
+ *   out[b][h] = sum_t e^{lambda_t - m} nu_t / sum_t e^{lambda_t - m}  (fp32).
+ * k == 0 gives the approximate output; idx may then be NULL.  A sequence with
+ * len 0 gives zeros.  Every idx entry must be < len of its sequence.
+ * Errors: BKV_E_ARG if k < 0; BKV_E_WORKSPACE / BKV_E_CAPACITY as above.
+ */
+bkv_status qattn_correct(const bkv_layout* layout, const bkv_cache* cache,
+                         const uint16_t* q, const int32_t* len_host,
+                         const int32_t* idx, int32_t k, const void* ws,
+                         size_t ws_bytes, float* out, void* stream);
+
+/* Static text for a status code. */
+const char* bkv_status_string(bkv_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITKV_H */

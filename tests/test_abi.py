@@ -1,0 +1,124 @@
+"""The C-ABI library loads, exports every entry point include/bitkv.h declares,
+and rejects bad arguments on the host before any launch (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bk():
+    lib = os.path.join(ROOT, "bit_kv_attention_amd", "libbitkv.so")
+    if not os.path.exists(lib):
+        from bit_kv_attention_amd import build as b
+        b.build()
+    import bit_kv_attention_amd.binding as bk
+    return bk
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "bitkv.h")) as f:
+        txt = f.read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(bk):
+    names = declared_functions()
+    assert set(names) == set(bk.EXPORTED), names
+    for n in names:
+        assert hasattr(bk._lib, n), n
+
+
+def L(bk, **kw):
+    a = dict(batch=4, n_q_heads=32, n_kv_heads=8, capacity=1024, k_bits=4, v_bits=4)
+    a.update(kw)
+    return bk.make_layout(**a)
+
+
+def test_cache_and_workspace_sizes(bk):
+    kb, vb, mb, sb = bk.bkv_cache_bytes(L(bk, k_bits=3, v_bits=2))
+    units = 32
+    assert kb == units * 1024 * 48
+    assert vb == units * 1024 * 32
+    assert mb == units * 4 * 1024 * 4
+    assert sb == units * 1024 * 128 * 2
+    w1 = bk.bkv_workspace_bytes(L(bk), 1024)
+    w0 = bk.bkv_workspace_bytes(L(bk), 0)
+    assert w1 >= 4 * 32 * 130 * 4 and w0 > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_bits=5), 3), (dict(v_bits=3), 3), (dict(n_q_heads=30), 2), (dict(n_q_heads=16, n_kv_heads=16), 3),
+    (dict(capacity=1000), 2), (dict(capacity=0), 2), (dict(batch=257), 3), (dict(batch=0), 2),
+])
+def test_bad_layouts_rejected(bk, kw, status):
+    a, b, c, d = C.c_size_t(), C.c_size_t(), C.c_size_t(), C.c_size_t()
+    lay = L(bk, **kw)
+    assert bk.raw_status("bkv_cache_bytes", C.byref(lay), C.byref(a), C.byref(b), C.byref(c), C.byref(d)) == status
+
+
+def test_unsupported_head_dim_and_group(bk):
+    out = C.c_size_t()
+    lay = bk.Layout(4, 32, 8, 64, 4, 4, 32, 1024)
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, C.byref(out)) == 3
+    lay = bk.Layout(4, 32, 8, 128, 4, 4, 64, 1024)
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, C.byref(out)) == 3
+    assert bk.raw_status("bkv_workspace_bytes", None, 10, C.byref(out)) == 1
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def fake_cache(bk):
+    return bk.CacheView(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_host_error_paths(bk):
+    import numpy as np
+    lay = L(bk)
+    cv = fake_cache(bk)
+    pos = np.zeros(4, np.int32)
+    lens = np.full(4, 100, np.int32)
+    P = lambda a: a.ctypes.data
+    # NULL cache member
+    bad = bk.CacheView(FAKE, None, FAKE, FAKE, FAKE, FAKE)
+    assert bk.raw_status("kv_pack_append", C.byref(lay), C.byref(bad), FAKE, FAKE, 1, P(pos), None) == 1
+    # capacity: pos + n_new > capacity, negative pos
+    p2 = np.array([0, 0, 1024, 0], np.int32)
+    assert bk.raw_status("kv_pack_append", C.byref(lay), C.byref(cv), FAKE, FAKE, 1, P(p2), None) == 4
+    p3 = np.array([0, -1, 0, 0], np.int32)
+    assert bk.raw_status("kv_pack_append", C.byref(lay), C.byref(cv), FAKE, FAKE, 1, P(p3), None) == 4
+    assert bk.raw_status("kv_pack_append", C.byref(lay), C.byref(cv), FAKE, FAKE, -1, P(pos), None) == 7
+    # n_new == 0 enqueues nothing and succeeds
+    assert bk.raw_status("kv_pack_append", C.byref(lay), C.byref(cv), FAKE, FAKE, 0, P(pos), None) == 0
+    # lengths beyond capacity
+    l2 = np.array([100, 2000, 5, 5], np.int32)
+    assert bk.raw_status("qattn_decode_approx", C.byref(lay), C.byref(cv), FAKE, P(l2), FAKE, FAKE,
+                         1 << 30, None) == 4
+    # workspace too small
+    need = bk.bkv_workspace_bytes(lay, 100)
+    assert bk.raw_status("qattn_decode_approx", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, FAKE,
+                         need - 1, None) == 5
+    assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, 8, FAKE,
+                         need - 1, FAKE, None) == 5
+    # k < 0, NULL idx with k > 0, k == 0 is a no-op for top-k
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), -1, FAKE, None) == 7
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 4, None, None) == 1
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 0, None, None) == 0
+    assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), None, 4, FAKE,
+                         need, FAKE, None) == 1
+    assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, -2, FAKE,
+                         need, FAKE, None) == 7
+    # NULL length array
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, None, 4, FAKE, None) == 1
+
+
+def test_status_strings(bk):
+    for s in range(8):
+        assert bk._lib.bkv_status_string(s)
+    with pytest.raises(bk.BitKVError):
+        bk.bkv_workspace_bytes(L(bk, k_bits=7), 5)
