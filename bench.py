@@ -30,6 +30,17 @@ def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32
     return D * kbits // 8 + meta + D * vbits // 8 + meta
 
 
+def scan_partial_bytes(lay, L: int) -> int:
+    """Bytes of split states the scan writes: per (b, query head, split) the
+    max, the denominator and D accumulators (fp32); splits as the library
+    chooses them (about 512 workgroups, 128-token multiples)."""
+    units = lay.batch * lay.n_kv_heads
+    per = -(-units * L // 512)
+    per = max(128, -(-per // 128) * 128)
+    nsplit = -(-L // per)
+    return lay.batch * lay.n_q_heads * nsplit * (2 + lay.head_dim) * 4
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,7 +131,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         e = ev[i]
         e[0][0].record(); bk.kv_pack_append(lay, cache, kn, vn, 1, pos); e[0][1].record()
         e[1][0].record(); bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws); e[1][1].record()
-        e[2][0].record(); bk.topk_select(lay, st.sigma, lens, w.k, st.idx); e[2][1].record()
+        e[2][0].record(); bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws); e[2][1].record()
         e[3][0].record()
         bk.qattn_correct(lay, cache, q, lens, st.idx, w.k, st.ws, st.out)
         e[3][1].record()
@@ -133,8 +144,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     # dominant kernel: the approximate scan.  Algorithmic bytes per launch =
     # packed codes + meta of K and V for every token of every unit, the fp32
     # selection score written per token, and the split partial states written.
-    nsplit_bytes = bk.bkv_workspace_bytes(lay, L)
-    scan_bytes = units * L * (ppt + 4) + nsplit_bytes
+    scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L)
     scan_s = kus["qattn_decode_approx"] / 1e6
     achieved = scan_bytes / scan_s / 1e9
     res = {

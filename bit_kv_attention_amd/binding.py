@@ -55,10 +55,10 @@ _SZ = C.POINTER(C.c_size_t)
 _lib.bkv_status_string.argtypes = [C.c_int]
 _lib.bkv_status_string.restype = C.c_char_p
 _lib.bkv_cache_bytes.argtypes = [_LP, _SZ, _SZ, _SZ, _SZ]
-_lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, _SZ]
+_lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, C.c_int32, _SZ]
 _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
-_lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P]
+_lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
            "topk_select", "qattn_correct"):
@@ -105,9 +105,9 @@ def bkv_cache_bytes(layout: Layout):
     return a.value, b.value, c.value, d.value
 
 
-def bkv_workspace_bytes(layout: Layout, max_len: int) -> int:
+def bkv_workspace_bytes(layout: Layout, max_len: int, k: int) -> int:
     out = C.c_size_t()
-    _check("bkv_workspace_bytes", _lib.bkv_workspace_bytes(C.byref(layout), int(max_len), C.byref(out)))
+    _check("bkv_workspace_bytes", _lib.bkv_workspace_bytes(C.byref(layout), int(max_len), int(k), C.byref(out)))
     return out.value
 
 
@@ -157,10 +157,11 @@ def qattn_decode_approx(layout: Layout, cache: Cache, q, len_host, sigma, ws, st
                                                            ws_bytes, _stream(stream)))
 
 
-def topk_select(layout: Layout, sigma, len_host, k: int, idx, stream=None) -> None:
+def topk_select(layout: Layout, sigma, len_host, k: int, idx, ws, stream=None) -> None:
     lens = _host_i32(len_host)
+    ws_bytes = ws.numel() * ws.element_size()
     _check("topk_select", _lib.topk_select(C.byref(layout), _ptr(sigma), lens.ctypes.data, int(k), _ptr(idx),
-                                           _stream(stream)))
+                                           _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def qattn_correct(layout: Layout, cache: Cache, q, len_host, idx, k: int, ws, out, stream=None) -> None:

@@ -10,9 +10,10 @@ namespace bkv {
 
 int split_tokens(int units, int max_len) {
   // Work per workgroup: a multiple of 4 waves x 32 tokens, sized so the grid
-  // has about 1024 workgroups (4 per CU on 256 CUs) when the context allows.
+  // has about kScanWorkgroups workgroups when the context allows (long runs
+  // per wave amortise the per-workgroup setup and merge).
   const long long total = (long long)units * (max_len > 0 ? max_len : 1);
-  long long per = (total + 1023) / 1024;
+  long long per = (total + kScanWorkgroups - 1) / kScanWorkgroups;
   per = ((per + 127) / 128) * 128;
   if (per < 128) per = 128;
   return (int)per;
@@ -26,26 +27,40 @@ int num_splits(int units, int max_len) {
 
 // An upper bound of num_splits(units, m) over every m <= max_len (the split
 // count is not monotone in m): chunk >= 128 gives ceil(m/128), and
-// chunk >= units*m/1024 gives ceil(1024/units).
+// chunk >= units*m/kScanWorkgroups gives ceil(kScanWorkgroups/units).
 static int max_splits(int units, int max_len) {
   const int a = (max_len + 127) / 128;
-  const int b = (1024 + units - 1) / units;
+  const int b = (kScanWorkgroups + units - 1) / units;
   const int m = a < b ? a : b;
   return m > 0 ? m : 1;
 }
 
-size_t partials_bytes(int B, int Hq, int nsplit) {
-  return (size_t)B * Hq * nsplit * (2 + kHeadDim) * sizeof(float);
-}
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Partials partials_in(void* ws, int B, int Hq, int nsplit) {
-  float* f = static_cast<float*>(ws);
-  const size_t recs = (size_t)B * Hq * nsplit;
-  Partials p;
-  p.acc = f;
-  p.m = f + recs * kHeadDim;
-  p.l = p.m + recs;
-  return p;
+Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bool bound) {
+  const int units = L.batch * L.n_kv_heads;
+  Workspace w;
+  w.nsplit = bound ? max_splits(units, max_len) : num_splits(units, max_len);
+  const int kmax = k < max_len ? k : max_len;
+  w.nchunk = kmax > 0 ? (kmax + kCorrChunk - 1) / kCorrChunk : 0;
+  char* base = static_cast<char*>(ws);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off = align256(off + bytes);
+    return p;
+  };
+  w.tk.hist = reinterpret_cast<uint32_t*>(take((size_t)units * kHistBins * 4));
+  w.tk.ctrl = reinterpret_cast<uint32_t*>(take((size_t)units * kCtrlWords * 4));
+  w.tk.cand = reinterpret_cast<uint64_t*>(take((size_t)units * kCandCap * 8));
+  w.tk.bitmap = reinterpret_cast<uint32_t*>(take((size_t)units * (L.capacity / 32) * 4));
+  const size_t recs = (size_t)L.batch * L.n_q_heads * w.nsplit;
+  w.part.acc = reinterpret_cast<float*>(take(recs * kHeadDim * 4));
+  w.part.m = reinterpret_cast<float*>(take(recs * 4));
+  w.part.l = reinterpret_cast<float*>(take(recs * 4));
+  w.cs = reinterpret_cast<float*>(take((size_t)L.batch * L.n_q_heads * w.nchunk * kCsStride * 4));
+  w.bytes = off;
+  return w;
 }
 
 }  // namespace bkv
@@ -117,13 +132,13 @@ bkv_status bkv_cache_bytes(const bkv_layout* L, size_t* k_codes_bytes, size_t* v
   return BKV_OK;
 }
 
-bkv_status bkv_workspace_bytes(const bkv_layout* L, int32_t max_len, size_t* bytes) {
+bkv_status bkv_workspace_bytes(const bkv_layout* L, int32_t max_len, int32_t k, size_t* bytes) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
   if (!bytes) return BKV_E_NULL;
   if (max_len < 0 || max_len > L->capacity) return BKV_E_CAPACITY;
-  const int units = L->batch * L->n_kv_heads;
-  *bytes = partials_bytes(L->batch, L->n_q_heads, max_splits(units, max_len));
+  if (k < 0) return BKV_E_ARG;
+  *bytes = workspace_layout(nullptr, *L, max_len, k, true).bytes;
   return BKV_OK;
 }
 
@@ -158,30 +173,32 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   const int units = L->batch * L->n_kv_heads;
-  const int nsplit = num_splits(units, max_len);
-  if (ws_bytes < partials_bytes(L->batch, L->n_q_heads, nsplit)) return BKV_E_WORKSPACE;
-  const Partials p = partials_in(ws, L->batch, L->n_q_heads, nsplit);
-  return launch_decode_approx(*L, *c, q, len, max_len, sigma, p, nsplit, split_tokens(units, max_len),
-                              (hipStream_t)stream) == hipSuccess
+  const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), (hipStream_t)stream) ==
+                 hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
 }
 
 bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
-                       int32_t* idx, void* stream) {
+                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
   if (k < 0) return BKV_E_ARG;
-  if (!sigma || (!idx && k > 0)) return BKV_E_NULL;
+  if (!sigma || (!idx && k > 0) || (!ws && k > 0)) return BKV_E_NULL;
   SeqArg len;
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   if (k == 0) return BKV_OK;
-  return launch_topk(*L, sigma, len, k, idx, (hipStream_t)stream) == hipSuccess ? BKV_OK : BKV_E_HIP;
+  const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_topk(*L, sigma, len, max_len, k, idx, w.tk, (hipStream_t)stream) == hipSuccess ? BKV_OK
+                                                                                               : BKV_E_HIP;
 }
 
 bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
-                         const int32_t* len_host, const int32_t* idx, int32_t k, const void* ws,
+                         const int32_t* len_host, const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
@@ -191,13 +208,10 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
   SeqArg len;
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
-  const int units = L->batch * L->n_kv_heads;
-  const int nsplit = num_splits(units, max_len);
-  if (ws_bytes < partials_bytes(L->batch, L->n_q_heads, nsplit)) return BKV_E_WORKSPACE;
-  const Partials p = partials_in(const_cast<void*>(ws), L->batch, L->n_q_heads, nsplit);
-  return launch_correct(*L, *c, q, len, idx, k, p, nsplit, out, (hipStream_t)stream) == hipSuccess
-             ? BKV_OK
-             : BKV_E_HIP;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_correct(*L, *c, q, len, idx, k, w, out, (hipStream_t)stream) == hipSuccess ? BKV_OK
+                                                                                          : BKV_E_HIP;
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ constexpr int kGroup = 32;
 constexpr int kGroups = kHeadDim / kGroup;  // 4
 constexpr int kTile = 32;                   // tokens per V tile and per scan step
 constexpr int kMaxBatch = 256;
+constexpr int kScanWorkgroups = 512;        // target grid of the approximate scan
 
 // Per-sequence lengths / positions travel by value in the kernel arguments.
 struct SeqArg {
@@ -37,30 +38,65 @@ __device__ inline uint32_t float_key(float f) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Split-L partial states inside the workspace.
+// ---- workspace ------------------------------------------------------------
+// One buffer, three regions: the top-k scratch (fixed per layout), the split
+// partial states of the scan and the states of the correction chunks.  The
+// region sizes depend on the step's longest length and k, so every call of a
+// step recomputes the same offsets from the same (lens, k).
+
+// Split-L partial states of the approximate scan.
 struct Partials {
   float* m;    // [B][Hq][nsplit]  running max, log2 units
   float* l;    // [B][Hq][nsplit]  softmax denominator
   float* acc;  // [B][Hq][nsplit][D] unnormalised sum of p * V_hat
 };
 
-// Tokens per split for a step whose longest sequence has max_len tokens:
-// a multiple of 4 waves * 32 tokens, sized for about 1024 workgroups.
+constexpr int kHistBins = 4096;  // first radix digit of the top-k: 12 key bits
+constexpr int kCandCap = 4096;   // threshold-bucket candidates resolved in LDS
+constexpr int kCtrlWords = 16;
+enum { kCtlArrive1 = 0, kCtlArrive2 = 1, kCtlDigit1 = 2, kCtlAbove1 = 3, kCtlCandCount = 4 };
+
+struct TopkScratch {
+  uint32_t* hist;    // [U][kHistBins]
+  uint32_t* ctrl;    // [U][kCtrlWords]
+  uint64_t* cand;    // [U][kCandCap] (key << 32) | token
+  uint32_t* bitmap;  // [U][capacity / 32] selected tokens
+};
+
+constexpr int kCorrChunk = 32;  // selected tokens per correction workgroup
+// Per (b, h, chunk): m_exact, l_exact, m_approx, l_approx, then the exact and
+// the approximate value sums (D each), 16-byte aligned.
+constexpr int kCsStride = 4 + 2 * kHeadDim;
+
+struct Workspace {
+  TopkScratch tk;
+  Partials part;
+  float* cs;  // [B][Hq][nchunk][kCsStride]
+  int nsplit;
+  int nchunk;
+  size_t bytes;  // total bytes this step needs
+};
+
+// Tokens per split of the scan for a step whose longest sequence has max_len
+// tokens: a multiple of 4 waves * 32 tokens, sized for about kScanWorkgroups.
 int split_tokens(int units, int max_len);
 int num_splits(int units, int max_len);
-Partials partials_in(void* ws, int B, int Hq, int nsplit);
-size_t partials_bytes(int B, int Hq, int nsplit);
+int topk_slice(int units, int max_len);
+// Offsets of the regions for a step (ws may be null to size only).  With
+// bound = true the split and chunk counts are upper bounds valid for every
+// step whose longest sequence is at most max_len.
+Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bool bound);
 
 // Launchers (return hipGetLastError of their launches).
 hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_new,
                               const uint16_t* v_new, int n_new, const SeqArg& pos, hipStream_t s);
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
-                                const SeqArg& len, int max_len, float* sigma, const Partials& p,
-                                int nsplit, int chunk, hipStream_t s);
-hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int k,
-                       int32_t* idx, hipStream_t s);
+                                const SeqArg& len, float* sigma, const Workspace& w, int chunk,
+                                hipStream_t s);
+hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
+                       int32_t* idx, const TopkScratch& tk, hipStream_t s);
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
-                          const SeqArg& len, const int32_t* idx, int k, const Partials& p,
-                          int nsplit, float* out, hipStream_t s);
+                          const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
+                          float* out, hipStream_t s);
 
 }  // namespace bkv

@@ -26,8 +26,9 @@
 //  * P.V: v_mfma_f32_16x16x32_f16 with A = 16 channels x 32 tokens of V codes
 //    and B = columns (g, h) holding fp16(p * s_g,t); channel tile nt only keeps
 //    the columns of its own group.  sum p*z is accumulated on the VALU.
-//  * Codes become fp16 integers with one AND-OR against 0x6400 (1024 + code)
-//    and one packed fp16 subtract of 1024, both exact.
+//  * Key codes become exact fp16 integers (OR into 1024 + c, subtract 1024);
+//    value codes enter as fp16 subnormals (the masked bit pattern c is the
+//    value c * 2^-24), one shift and one AND per pair, no conversion.
 #include "bkv_internal.h"
 
 namespace bkv {
@@ -48,24 +49,29 @@ constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
-// Two codes (one per 16-bit half, already masked) -> exact fp16 integers.
-__device__ inline uint32_t codes_to_half2(uint32_t two_codes) {
-  const uint32_t biased = two_codes | 0x64006400u;  // fp16 1024 + code in each half
-  half2_t h = __builtin_bit_cast(half2_t, biased);
-  h = h - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
-  return __builtin_bit_cast(uint32_t, h);
-}
-
 // y holds 4 codes of `BITS` bits in its low half and 4 in its high half; item
 // pair r of the operand is (code r, code r+4).
-template <int BITS>
+//  EXACT (keys, whose scores decide the top-k): each code becomes the fp16
+//    integer c via 1024 + c (OR into 0x6400) minus 1024, both exact; the MFMA
+//    then sums the products with fp32 rounding only.
+//  otherwise (values): the masked bits are used as fp16 bit patterns directly,
+//    i.e. the subnormal c * 2^-24, which the MFMA multiplies without flushing
+//    but sums a little less precisely (about 1e-6 relative); the 2^24 is folded
+//    into the result.
+template <int BITS, bool EXACT>
 __device__ inline half8 unpack8(uint32_t y) {
   constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : (BITS == 3) ? 0x00070007u : 0x00030003u;
   u32x4 r;
-  r.x = codes_to_half2(y & M);
-  r.y = codes_to_half2((y >> BITS) & M);
-  r.z = codes_to_half2((y >> (2 * BITS)) & M);
-  r.w = codes_to_half2((y >> (3 * BITS)) & M);
+  r.x = y & M;
+  r.y = (y >> BITS) & M;
+  r.z = (y >> (2 * BITS)) & M;
+  r.w = (y >> (3 * BITS)) & M;
+  if constexpr (EXACT) {
+    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, r[i] | 0x64006400u) - k1024);
+  }
   return __builtin_bit_cast(half8, r);
 }
 
@@ -83,7 +89,7 @@ struct Step {
   static constexpr int KW = (KB == 4) ? 1 : 2;
   uint32_t kc[2][kGroups][KW];  // key code dwords: [token tile][group][dword]
   u32x4 km[2][NT];              // key meta, tokens 4kb..4kb+3 of token tile tt
-  uint32_t vc[8];               // value word (channel 16*nt + n, quarter kb)
+  uint32_t vc[8];               // value word (quarter kb, channel 16*nt + n)
   u32x4 vm[NT][2];              // value meta: [N-tile][token tile]
 };
 
@@ -120,7 +126,7 @@ __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__
   const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB);
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    const int w = (16 * nt + n) * 4 + kb;
+    const int w = kb * kHeadDim + 16 * nt + n;  // word (quarter kb, channel 16nt + n)
     if constexpr (VB == 4)
       S.vc[nt] = reinterpret_cast<const uint32_t*>(vt)[w];
     else
@@ -128,13 +134,140 @@ __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__
   }
 }
 
+// Running softmax state of one wave (see the kernel comment).
+template <int NT>
+struct WaveState {
+  float m_run;       // running max, log2 units (same in every lane of a head)
+  float l_part;      // this lane's share of the denominator
+  float z_part[NT];  // this lane's share of sum p * z for its column (g, h)
+  floatx4 acc[8];    // P.V accumulators (x 2^-24: codes enter as fp16 subnormals)
+};
+
+// One 32-token step.  MASK: the step straddles the sequence end.
+template <int KB, int VB, int G, bool MASK>
+__device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half8 (&bq)[kGroups],
+                                          const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT>& ws,
+                                          float* __restrict__ sig, int t0, int len, int n, int kb,
+                                          float c_sig, float c_s2) {
+  constexpr int NT = Step<KB, VB, G>::NT;
+  // -- scores: D[T][tt] rows = tokens 4kb+i of token tile tt, column n --------
+  floatx4 d[NT][2];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) d[T][tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      uint32_t y;
+      if constexpr (KB == 4) {
+        y = cur.kc[tt][g][0];
+      } else {
+        const int shift = (24 * kb) & 31;
+        const uint32_t x = __builtin_amdgcn_alignbit(cur.kc[tt][g][1], cur.kc[tt][g][0], shift);
+        y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);
+      }
+      const int T = (G == 8) ? (g >> 1) : 0;
+      d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack8<KB, true>(y), bq[g], d[T][tt], 0, 0, 0);
+    }
+  }
+
+  // -- per-(token, group) scale and zero, reduce over groups ------------------
+  float s2[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    float sg4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float part = 0.f;
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        const uint32_t mw = cur.km[tt][T][i];
+        part = fmaf(d[T][tt][i], lo_half(mw), fmaf(hi_half(mw), qs[T], part));
+      }
+      if constexpr (G == 8) {
+        part += dpp<kRowRor8>(part);
+      } else {
+        part += dpp<kRowRor4>(part);
+        part += dpp<kRowRor8>(part);
+      }
+      // selection score: max over the query heads of the group
+      float sg = part * c_sig;
+      sg = fmaxf(sg, dpp<kQuadXor1>(sg));
+      sg = fmaxf(sg, dpp<kQuadXor2>(sg));
+      if constexpr (G == 8) sg = fmaxf(sg, dpp<kRowRor4>(sg));
+      float v2 = part * c_s2;
+      if constexpr (MASK) {
+        const bool valid = (t0 + 16 * tt + 4 * kb + i) < len;
+        sg = valid ? sg : -INFINITY;
+        v2 = valid ? v2 : -INFINITY;
+      }
+      sg4[i] = sg;
+      s2[tt][i] = v2;
+    }
+    if (n == 0)
+      *reinterpret_cast<floatx4*>(sig + t0 + 16 * tt + 4 * kb) = (floatx4){sg4[0], sg4[1], sg4[2], sg4[3]};
+  }
+
+  // -- online softmax (log2 units) --------------------------------------------
+  float mloc = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
+                     fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  const float m_new = fmaxf(ws.m_run, mloc);
+  if (__ballot(m_new != ws.m_run)) {  // rare after the first steps
+    const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
+    ws.l_part *= alpha;
+#pragma unroll
+    for (int T = 0; T < NT; ++T) ws.z_part[T] *= alpha;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) ws.acc[nt] *= alpha;
+    ws.m_run = m_new;
+  }
+
+  float p[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[tt][i] = __builtin_amdgcn_exp2f(s2[tt][i] - m_new);
+      ws.l_part += p[tt][i];
+    }
+
+  // -- P.V operand: column (g, h) gets fp16(p * s_g,t); sum p*z on the VALU ---
+  half8 bp[NT];
+#pragma unroll
+  for (int T = 0; T < NT; ++T) {
+    u32x4 w;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t m0 = cur.vm[T][0][r], m1 = cur.vm[T][1][r];
+      if constexpr (MASK) {  // meta past the end may hold anything
+        m0 = (t0 + 4 * kb + r) < len ? m0 : 0u;
+        m1 = (t0 + 16 + 4 * kb + r) < len ? m1 : 0u;
+      }
+      ws.z_part[T] = fmaf(p[0][r], hi_half(m0), fmaf(p[1][r], hi_half(m1), ws.z_part[T]));
+      w[r] = pack_half2(p[0][r] * lo_half(m0), p[1][r] * lo_half(m1));
+    }
+    bp[T] = __builtin_bit_cast(half8, w);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    uint32_t y = cur.vc[nt];
+    if constexpr (VB == 2) y = (y & 0xFFu) | ((y & 0xFF00u) << 8);
+    const int T = (G == 8) ? (nt >> 2) : 0;
+    ws.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack8<VB, false>(y), bp[T], ws.acc[nt], 0, 0, 0);
+  }
+}
+
 template <int KB, int VB, int G>
-__global__ __launch_bounds__(256) void decode_approx_kernel(
+__global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap,
-    int nsplit, int chunk) {
+    float* __restrict__ pl, float* __restrict__ pacc, uint32_t* __restrict__ tk_hist,
+    uint32_t* __restrict__ tk_ctrl, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk) {
   constexpr int NT = Step<KB, VB, G>::NT;
   const int u = blockIdx.y;
   const int b = u / Hkv;
@@ -143,8 +276,9 @@ __global__ __launch_bounds__(256) void decode_approx_kernel(
   const int len = lens.v[b];
   const int t_begin = split * chunk;
   const int t_end = min(len, t_begin + chunk);
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
   const int n = lane & 15;
   const int kb = lane >> 4;
 
@@ -152,181 +286,88 @@ __global__ __launch_bounds__(256) void decode_approx_kernel(
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
   const uint32_t* kmeta = k_meta + (size_t)u * kGroups * cap;
   const uint32_t* vmeta = v_meta + (size_t)u * kGroups * cap;
-  const uint16_t* qg = q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim;
 
-  // ---- query operands: column (g', h) of N-tile T --------------------------
+  // The top-k selection that follows in the step accumulates into a per-unit
+  // histogram and control words: clear them here (nothing else touches them
+  // while this kernel runs).
+  if (split == 0) {
+    for (int i = tid; i < kHistBins; i += 256) tk_hist[(size_t)u * kHistBins + i] = 0u;
+    if (tid < kCtrlWords) tk_ctrl[(size_t)u * kCtrlWords + tid] = 0u;
+  }
+
+  // ---- query operands, staged through LDS ------------------------------------
+  __shared__ uint16_t s_q[G][kHeadDim];
+  __shared__ float s_qsum[G][kGroups];
+  {
+    const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
+    if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
+    __syncthreads();
+    if (tid < G * kGroups) {
+      const int hh = tid / kGroups, g = tid % kGroups;
+      float s = 0.f;
+      for (int c = 0; c < kGroup; ++c) s += (float)__builtin_bit_cast(_Float16, s_q[hh][g * kGroup + c]);
+      s_qsum[hh][g] = s;
+    }
+    __syncthreads();
+  }
+  // column (g', h) of N-tile T: g' = n/4 (G = 4) or 2T + n/8 (G = 8)
   const int h = (G == 8) ? (n & 7) : (n & 3);
   half8 bq[kGroups];
   float qs[NT];
-  {
-    const uint16_t* qh = qg + (size_t)h * kHeadDim;
 #pragma unroll
-    for (int T = 0; T < NT; ++T) {
-      const int gq = (G == 8) ? (2 * T + (n >> 3)) : (n >> 2);
-      float s = 0.f;
-      for (int c = 0; c < kGroup; ++c) s += (float)__builtin_bit_cast(_Float16, qh[gq * kGroup + c]);
-      qs[T] = s;
+  for (int T = 0; T < NT; ++T) qs[T] = s_qsum[h][(G == 8) ? (2 * T + (n >> 3)) : (n >> 2)];
+#pragma unroll
+  for (int g = 0; g < kGroups; ++g) {
+    const int gq = (G == 8) ? (2 * (g >> 1) + (n >> 3)) : (n >> 2);
+    half8 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[2 * r] = (gq == g) ? __builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + r]) : (_Float16)0.0f;
+      v[2 * r + 1] = (gq == g) ? __builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + 4 + r]) : (_Float16)0.0f;
     }
-#pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      const int gq = (G == 8) ? (2 * (g >> 1) + (n >> 3)) : (n >> 2);
-      half8 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t a = qh[g * kGroup + 8 * kb + r];
-        const uint16_t c = qh[g * kGroup + 8 * kb + 4 + r];
-        v[2 * r] = (gq == g) ? __builtin_bit_cast(_Float16, a) : (_Float16)0.0f;
-        v[2 * r + 1] = (gq == g) ? __builtin_bit_cast(_Float16, c) : (_Float16)0.0f;
-      }
-      bq[g] = v;
-    }
+    bq[g] = v;
   }
 
   const float sm = 1.0f / sqrtf((float)kHeadDim);
-  const float sm2 = sm * kLog2e;
+  const float c_sig = sm;
+  const float c_s2 = sm * kLog2e;
+  float* sig = sigma + (size_t)u * cap;
 
-  // ---- running state --------------------------------------------------------
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-  float z_part[NT];
-  floatx4 acc[8];
+  WaveState<NT> ws;
+  ws.m_run = -INFINITY;
+  ws.l_part = 0.f;
 #pragma unroll
-  for (int T = 0; T < NT; ++T) z_part[T] = 0.f;
+  for (int T = 0; T < NT; ++T) ws.z_part[T] = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 8; ++nt) ws.acc[nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
   Step<KB, VB, G> cur, nxt;
   int t0 = t_begin + kTile * wv;
   if (t0 < t_end) load_step<KB, VB, G>(cur, kbase, vbase, kmeta, vmeta, cap, t0, n, kb);
-
   for (; t0 < t_end; t0 += 4 * kTile) {
     const bool more = (t0 + 4 * kTile) < t_end;
     if (more) load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, t0 + 4 * kTile, n, kb);
-
-    // -- scores: D[T][tt] rows = tokens 4kb+i of token tile tt, column n ------
-    floatx4 d[NT][2];
-#pragma unroll
-    for (int T = 0; T < NT; ++T)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) d[T][tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int g = 0; g < kGroups; ++g) {
-        uint32_t y;
-        if constexpr (KB == 4) {
-          y = cur.kc[tt][g][0];
-        } else {
-          const int shift = (24 * kb) & 31;
-          const uint32_t x = __builtin_amdgcn_alignbit(cur.kc[tt][g][1], cur.kc[tt][g][0], shift);
-          y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);
-        }
-        const half8 a = unpack8<KB>(y);
-        const int T = (G == 8) ? (g >> 1) : 0;
-        d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[g], d[T][tt], 0, 0, 0);
-      }
-    }
-
-    // -- per-(token, group) scale and zero, reduce over groups ----------------
-    float s2[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float part = 0.f;
-#pragma unroll
-        for (int T = 0; T < NT; ++T) {
-          const uint32_t mw = cur.km[tt][T][i];
-          part += d[T][tt][i] * lo_half(mw) + hi_half(mw) * qs[T];
-        }
-        if constexpr (G == 8) {
-          part += dpp<kRowRor8>(part);
-        } else {
-          part += dpp<kRowRor4>(part);
-          part += dpp<kRowRor8>(part);
-        }
-        const int t = t0 + 16 * tt + 4 * kb + i;
-        const bool valid = t < len;
-        // selection score: max over the query heads of the group
-        float sg = part * sm;
-        sg = fmaxf(sg, dpp<kQuadXor1>(sg));
-        sg = fmaxf(sg, dpp<kQuadXor2>(sg));
-        if constexpr (G == 8) sg = fmaxf(sg, dpp<kRowRor4>(sg));
-        if (n == 0) sigma[(size_t)u * cap + t] = valid ? sg : -INFINITY;
-        s2[tt][i] = valid ? part * sm2 : -INFINITY;
-      }
-    }
-
-    // -- online softmax (log2 units) ------------------------------------------
-    float mloc = s2[0][0];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, s2[tt][i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    if (__ballot(alpha != 1.0f)) {
-      l_part *= alpha;
-#pragma unroll
-      for (int T = 0; T < NT; ++T) z_part[T] *= alpha;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) acc[nt] *= alpha;
-    }
-    m_run = m_new;
-
-    float p[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[tt][i] = __builtin_amdgcn_exp2f(s2[tt][i] - m_new);
-        l_part += p[tt][i];
-      }
-
-    // -- P.V operand: column (g, h) gets fp16(p * s_g,t); sum p*z on the VALU --
-    half8 bp[NT];
-#pragma unroll
-    for (int T = 0; T < NT; ++T) {
-      u32x4 w;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool v0 = (t0 + 4 * kb + r) < len;
-        const bool v1 = (t0 + 16 + 4 * kb + r) < len;
-        const uint32_t m0 = cur.vm[T][0][r], m1 = cur.vm[T][1][r];
-        const float ps0 = v0 ? p[0][r] * lo_half(m0) : 0.f;
-        const float ps1 = v1 ? p[1][r] * lo_half(m1) : 0.f;
-        z_part[T] += (v0 ? p[0][r] * hi_half(m0) : 0.f) + (v1 ? p[1][r] * hi_half(m1) : 0.f);
-        w[r] = pack_half2(ps0, ps1);
-      }
-      bp[T] = __builtin_bit_cast(half8, w);
-    }
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      uint32_t y = cur.vc[nt];
-      if constexpr (VB == 2) y = (y & 0xFFu) | ((y & 0xFF00u) << 8);
-      const half8 a = unpack8<VB>(y);
-      const int T = (G == 8) ? (nt >> 2) : 0;
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bp[T], acc[nt], 0, 0, 0);
-    }
+    if (t0 + kTile <= len)
+      scan_step<KB, VB, G, false>(cur, bq, qs, ws, sig, t0, len, n, kb, c_sig, c_s2);
+    else
+      scan_step<KB, VB, G, true>(cur, bq, qs, ws, sig, t0, len, n, kb, c_sig, c_s2);
     if (more) cur = nxt;
   }
 
   // ---- combine the 4 waves of the workgroup -----------------------------------
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
+  ws.l_part += __shfl_xor(ws.l_part, 16);
+  ws.l_part += __shfl_xor(ws.l_part, 32);
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
-    z_part[T] += __shfl_xor(z_part[T], 16);
-    z_part[T] += __shfl_xor(z_part[T], 32);
+    ws.z_part[T] += __shfl_xor(ws.z_part[T], 16);
+    ws.z_part[T] += __shfl_xor(ws.z_part[T], 32);
   }
   __shared__ float s_m[4][G];
   __shared__ float s_l[4][G];
   __shared__ float s_acc[4][G][kHeadDim];
   if (kb == 0 && n < G) {
-    s_m[wv][h] = m_run;
-    s_l[wv][h] = l_part;
+    s_m[wv][h] = ws.m_run;
+    s_l[wv][h] = ws.l_part;
   }
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
@@ -335,17 +376,17 @@ __global__ __launch_bounds__(256) void decode_approx_kernel(
     for (int j = 0; j < 2; ++j) {
       const int nt = 2 * g + j;
       // nt is lane dependent; select the accumulator without dynamic indexing
-      floatx4 a = acc[0];
+      floatx4 a = ws.acc[0];
 #pragma unroll
       for (int x = 1; x < 8; ++x)
-        if (x == nt) a = acc[x];
+        if (x == nt) a = ws.acc[x];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[wv][h][16 * nt + 4 * kb + i] = a[i] + z_part[T];
+      for (int i = 0; i < 4; ++i) s_acc[wv][h][16 * nt + 4 * kb + i] = fmaf(a[i], 0x1p24f, ws.z_part[T]);
     }
   }
   __syncthreads();
 
-  for (int e = threadIdx.x; e < G * kHeadDim; e += 256) {
+  for (int e = tid; e < G * kHeadDim; e += 256) {
     const int hh = e / kHeadDim;
     const int c = e - hh * kHeadDim;
     float M = s_m[0][hh];
@@ -371,33 +412,33 @@ __global__ __launch_bounds__(256) void decode_approx_kernel(
 
 template <int KB, int VB, int G>
 hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Partials& p, int nsplit, int chunk, hipStream_t s) {
-  dim3 grid(nsplit, L.batch * L.n_kv_heads);
+                    float* sigma, const Workspace& w, int chunk, hipStream_t s) {
+  dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
   (void)hipGetLastError();  // report only this launch's status
   decode_approx_kernel<KB, VB, G><<<grid, 256, 0, s>>>(
       static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
-      c.v_meta, q, sigma, p.m, p.l, p.acc, len, L.n_q_heads, L.n_kv_heads, L.capacity, nsplit, chunk);
+      c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, w.tk.hist, w.tk.ctrl, len, L.n_q_heads,
+      L.n_kv_heads, L.capacity, w.nsplit, chunk);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
 hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Partials& p, int nsplit, int chunk, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, hipStream_t s) {
   const int G = L.n_q_heads / L.n_kv_heads;
-  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, p, nsplit, chunk, s);
-  return launch_t<KB, VB, 8>(L, c, q, len, sigma, p, nsplit, chunk, s);
+  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, s);
+  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
-                                const SeqArg& len, int max_len, float* sigma, const Partials& p,
-                                int nsplit, int chunk, hipStream_t s) {
-  (void)max_len;
-  if (L.k_bits == 4 && L.v_bits == 4) return launch_g<4, 4>(L, c, q, len, sigma, p, nsplit, chunk, s);
-  if (L.k_bits == 4 && L.v_bits == 2) return launch_g<4, 2>(L, c, q, len, sigma, p, nsplit, chunk, s);
-  if (L.k_bits == 3 && L.v_bits == 4) return launch_g<3, 4>(L, c, q, len, sigma, p, nsplit, chunk, s);
-  return launch_g<3, 2>(L, c, q, len, sigma, p, nsplit, chunk, s);
+                                const SeqArg& len, float* sigma, const Workspace& w, int chunk,
+                                hipStream_t s) {
+  if (L.k_bits == 4 && L.v_bits == 4) return launch_g<4, 4>(L, c, q, len, sigma, w, chunk, s);
+  if (L.k_bits == 4 && L.v_bits == 2) return launch_g<4, 2>(L, c, q, len, sigma, w, chunk, s);
+  if (L.k_bits == 3 && L.v_bits == 4) return launch_g<3, 4>(L, c, q, len, sigma, w, chunk, s);
+  return launch_g<3, 2>(L, c, q, len, sigma, w, chunk, s);
 }
 
 }  // namespace bkv

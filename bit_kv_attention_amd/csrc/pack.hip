@@ -106,10 +106,10 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     }
   }
   __syncthreads();
-  // value words: (channel c, quarter q) -> 8 slots of VB bits
+  // value words: word (quarter q, channel c) at q*D + c -> 8 slots of VB bits
   uint8_t* vt = v_codes + (size_t)u * v_unit_bytes(VB, cap) + (size_t)tile * v_tile_bytes(VB);
   for (int w = tid; w < kHeadDim * 4; w += 256) {
-    const int c = w >> 2, qq = w & 3;
+    const int c = w & (kHeadDim - 1), qq = w / kHeadDim;
     uint32_t word = (VB == 4) ? reinterpret_cast<uint32_t*>(vt)[w] : reinterpret_cast<uint16_t*>(vt)[w];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

@@ -14,7 +14,7 @@ class DecodeStep:
         self.k = int(k)
         L = layout
         self.sigma = torch.empty(L.batch * L.n_kv_heads * L.capacity, dtype=torch.float32, device=device)
-        ws_bytes = bk.bkv_workspace_bytes(L, max_len)
+        ws_bytes = bk.bkv_workspace_bytes(L, max_len, self.k)
         self.ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
         self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.k, 1), dtype=torch.int32, device=device)
         self.out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32, device=device)
@@ -23,7 +23,7 @@ class DecodeStep:
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
         bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
         if self.k > 0:
-            bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, stream)
+            bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, self.ws, stream)
         bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
                          self.out, stream)
         return self.out

@@ -81,11 +81,11 @@ typedef struct {
  *           LSB-first little-endian bitstream; channel c occupies bits
  *           [c*k_bits, (c+1)*k_bits), so with 3 bits channels 10 and 21 of
  *           every 32-channel group straddle 32-bit words.  16-byte aligned.
- *  v_codes  [B][Hkv][capacity/32][D][4] words of 8*v_bits bits.  In each
- *           32-token tile, word (c, q) holds 8 codes of channel c: token r of
- *           the tile (r = t mod 32) is in word q = (r mod 16)/4, slot
- *           j = 4*(r/16) + r mod 4, at bits [j*v_bits, (j+1)*v_bits).
- *           16-byte aligned.
+ *  v_codes  [B][Hkv][capacity/32][4][D] words of 8*v_bits bits.  In each
+ *           32-token tile, word (q, c) holds channel c of the 8 tokens of
+ *           quarter q: token r of the tile (r = t mod 32) is in quarter
+ *           q = (r mod 16)/4, slot j = 4*(r/16) + r mod 4, at bits
+ *           [j*v_bits, (j+1)*v_bits) of the word.  16-byte aligned.
  *  k_meta,  [B][Hkv][D/group][capacity] uint32: fp16 scale in the low half,
  *  v_meta   fp16 zero point (group minimum) in the high half.
  *  k_shadow,[B][Hkv][capacity][D] fp16: the exact input rows.  Device memory,
@@ -107,12 +107,14 @@ bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
                            size_t* v_codes_bytes, size_t* meta_bytes_each,
                            size_t* shadow_bytes_each);
 
-/* Workspace bytes that cover qattn_decode_approx / qattn_correct for every
- * step whose longest sequence has at most max_len tokens (the split partial
- * states).  Host only.  The same workspace is passed to both calls of one
- * step. */
+/* Workspace bytes that cover qattn_decode_approx, topk_select and
+ * qattn_correct for every step whose longest sequence has at most max_len
+ * tokens and whose top-k budget is k.  Host only.  One workspace serves the
+ * three calls of a step (the scan's split states, the top-k scratch and the
+ * correction's chunk states live in it); it needs no initialisation.  Calls
+ * that may run concurrently (on different streams) need separate workspaces. */
 bkv_status bkv_workspace_bytes(const bkv_layout* layout, int32_t max_len,
-                               size_t* bytes);
+                               int32_t k, size_t* bytes);
 
 /*
  * kv_pack_append -- quantise and store n_new tokens per sequence.
@@ -143,7 +145,7 @@ bkv_status kv_pack_append(const bkv_layout* layout, const bkv_cache* cache,
  *   ws:   per (b, h, split) the softmax state (running max in log2 units,
  *         denominator, unnormalised sum of p * V_hat) of its token range.
  * Errors: BKV_E_CAPACITY if some len_host[b] is outside [0, capacity];
- * BKV_E_WORKSPACE if ws_bytes < bkv_workspace_bytes(layout, max len).
+ * BKV_E_WORKSPACE if ws_bytes is too small (bkv_workspace_bytes).
  */
 bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
                                const uint16_t* q, const int32_t* len_host,
@@ -153,14 +155,16 @@ bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
 /*
  * topk_select -- per (b, kvh): the min(k, len) tokens with the largest sigma,
  * ties broken towards the lower index (JetFire README, introduction: top-k
- * tokens get the high-precision correction).  idx [B][Hkv][k] int32 (device)
- * receives the selected token indices in ascending order, -1 after the
- * min(k, len)-th entry.  k == 0 enqueues nothing.
- * Errors: BKV_E_ARG if k < 0; BKV_E_CAPACITY for a bad length.
+ * tokens get the high-precision correction; Jet-QSparse abstract: the budget
+ * is per KV head).  idx [B][Hkv][k] int32 (device) receives the selected token
+ * indices in ascending order, -1 after the min(k, len)-th entry.  Uses the
+ * top-k scratch region of ws.  k == 0 enqueues nothing.
+ * Errors: BKV_E_ARG if k < 0; BKV_E_CAPACITY for a bad length;
+ * BKV_E_WORKSPACE if ws is too small.
  */
 bkv_status topk_select(const bkv_layout* layout, const float* sigma,
                        const int32_t* len_host, int32_t k, int32_t* idx,
-                       void* stream);
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply
@@ -171,12 +175,14 @@ bkv_status topk_select(const bkv_layout* layout, const float* sigma,
  *   lambda_t = s_hat[t],             nu_t = V_hat_t     (t not in S)
  *   out[b][h] = sum_t e^{lambda_t - m} nu_t / sum_t e^{lambda_t - m}  (fp32).
  * k == 0 gives the approximate output; idx may then be NULL.  A sequence with
- * len 0 gives zeros.  Every idx entry must be < len of its sequence.
+ * len 0 gives zeros.  Entries outside [0, len) are skipped.  ws must hold the
+ * split states written by qattn_decode_approx for the same lengths; the call
+ * writes its chunk states into ws.
  * Errors: BKV_E_ARG if k < 0; BKV_E_WORKSPACE / BKV_E_CAPACITY as above.
  */
 bkv_status qattn_correct(const bkv_layout* layout, const bkv_cache* cache,
                          const uint16_t* q, const int32_t* len_host,
-                         const int32_t* idx, int32_t k, const void* ws,
+                         const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream);
 
 /* Static text for a status code. */

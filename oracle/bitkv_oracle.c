@@ -121,10 +121,10 @@ uint64_t orc_k_bitpos(int t, int c, int D, int bits) {
   return (uint64_t)t * (uint64_t)D * bits + (uint64_t)c * bits;
 }
 
-/* V: tiles of 32 tokens.  Inside a tile, for each channel c there are four
- * 8-code words (q = 0..3), word (c, q) at index 4*c + q.  Token r of the tile
- * (r = t mod 32) sits in word q = (r mod 16) / 4, slot j = 4*(r / 16) + r mod 4,
- * at bits [j*bits, j*bits+bits) of that word. */
+/* V: tiles of 32 tokens.  Inside a tile there are 4*D words of 8 codes:
+ * word (q, c) at index q*D + c holds channel c of the 8 tokens of quarter q.
+ * Token r of the tile (r = t mod 32) sits in quarter q = (r mod 16) / 4,
+ * slot j = 4*(r / 16) + r mod 4, at bits [j*bits, j*bits+bits) of the word. */
 uint64_t orc_v_bitpos(int t, int c, int D, int bits) {
   const int tile = t / 32;
   const int r = t % 32;
@@ -132,7 +132,7 @@ uint64_t orc_v_bitpos(int t, int c, int D, int bits) {
   const int j = 4 * (r / 16) + (r % 4);
   const uint64_t word_bits = 8u * (uint64_t)bits;
   return (uint64_t)tile * 32u * (uint64_t)D * bits +
-         ((uint64_t)c * 4u + (uint64_t)q) * word_bits + (uint64_t)j * bits;
+         ((uint64_t)q * (uint64_t)D + (uint64_t)c) * word_bits + (uint64_t)j * bits;
 }
 
 uint32_t orc_get_bits(const uint8_t* buf, uint64_t bitpos, int nbits) {

@@ -46,9 +46,12 @@ def test_cache_and_workspace_sizes(bk):
     assert vb == units * 1024 * 32
     assert mb == units * 4 * 1024 * 4
     assert sb == units * 1024 * 128 * 2
-    w1 = bk.bkv_workspace_bytes(L(bk), 1024)
-    w0 = bk.bkv_workspace_bytes(L(bk), 0)
-    assert w1 >= 4 * 32 * 130 * 4 and w0 > 0
+    w1 = bk.bkv_workspace_bytes(L(bk), 1024, 64)
+    w0 = bk.bkv_workspace_bytes(L(bk), 0, 0)
+    assert w1 >= 4 * 32 * 130 * 4 + 4 * 32 * 2 * 260 * 4 and w0 > 0
+    # the bound covers every shorter step
+    for m in range(0, 1025, 37):
+        assert bk.bkv_workspace_bytes(L(bk), m, 64) <= w1
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -64,10 +67,12 @@ def test_bad_layouts_rejected(bk, kw, status):
 def test_unsupported_head_dim_and_group(bk):
     out = C.c_size_t()
     lay = bk.Layout(4, 32, 8, 64, 4, 4, 32, 1024)
-    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, C.byref(out)) == 3
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
     lay = bk.Layout(4, 32, 8, 128, 4, 4, 64, 1024)
-    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, C.byref(out)) == 3
-    assert bk.raw_status("bkv_workspace_bytes", None, 10, C.byref(out)) == 1
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
+    assert bk.raw_status("bkv_workspace_bytes", None, 10, 4, C.byref(out)) == 1
+    lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024)
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, -1, C.byref(out)) == 7
 
 
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
@@ -99,26 +104,29 @@ def test_host_error_paths(bk):
     l2 = np.array([100, 2000, 5, 5], np.int32)
     assert bk.raw_status("qattn_decode_approx", C.byref(lay), C.byref(cv), FAKE, P(l2), FAKE, FAKE,
                          1 << 30, None) == 4
-    # workspace too small
-    need = bk.bkv_workspace_bytes(lay, 100)
+    # workspace too small (64 bytes is below every region: no call below may
+    # reach a launch, the pointers are fake)
+    need = bk.bkv_workspace_bytes(lay, 100, 8)
     assert bk.raw_status("qattn_decode_approx", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, FAKE,
-                         need - 1, None) == 5
+                         64, None) == 5
     assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, 8, FAKE,
-                         need - 1, FAKE, None) == 5
+                         64, FAKE, None) == 5
     # k < 0, NULL idx with k > 0, k == 0 is a no-op for top-k
-    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), -1, FAKE, None) == 7
-    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 4, None, None) == 1
-    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 0, None, None) == 0
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), -1, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 4, None, FAKE, need, None) == 1
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 4, FAKE, None, need, None) == 1
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 4, FAKE, FAKE, 100, None) == 5
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, P(lens), 0, None, None, 0, None) == 0
     assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), None, 4, FAKE,
                          need, FAKE, None) == 1
     assert bk.raw_status("qattn_correct", C.byref(lay), C.byref(cv), FAKE, P(lens), FAKE, -2, FAKE,
                          need, FAKE, None) == 7
     # NULL length array
-    assert bk.raw_status("topk_select", C.byref(lay), FAKE, None, 4, FAKE, None) == 1
+    assert bk.raw_status("topk_select", C.byref(lay), FAKE, None, 4, FAKE, FAKE, need, None) == 1
 
 
 def test_status_strings(bk):
     for s in range(8):
         assert bk._lib.bkv_status_string(s)
     with pytest.raises(bk.BitKVError):
-        bk.bkv_workspace_bytes(L(bk, k_bits=7), 5)
+        bk.bkv_workspace_bytes(L(bk, k_bits=7), 5, 1)

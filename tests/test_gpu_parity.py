@@ -141,3 +141,69 @@ def test_ties_take_lower_index(P):
     assert np.all(sig[others] == sig[0])
     want = sorted([250] + others[:9]) if sig[250] > sig[0] else others[:10]
     assert idx == want
+
+
+@pytest.mark.parametrize("L,k", [(10000, 50), (5000, 4999), (4100, 1)])
+def test_topk_bucket_overflow_fallback(P, L, k):
+    """All keys equal: every score lands in the threshold bucket, more
+    candidates than the in-LDS list holds, so the selection falls back to
+    re-reading the scores; ties must resolve to the lowest indices."""
+    banner(f"top-k overflow L={L} k={k}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    rng = np.random.default_rng(5)
+    cap = ((L + 31) // 32) * 32
+    row = rng.standard_normal(128).astype(np.float16)
+    K = np.tile(row, (1, 1, L, 1))
+    V = rng.standard_normal((1, 1, L, 128)).astype(np.float16)
+    q = rng.standard_normal((1, 8, 128)).astype(np.float16)
+    lay = bk.make_layout(1, 8, 1, cap, 3, 2)
+    gc = bk.allocate_cache(lay)
+    bk.kv_pack_append(lay, gc, P.to_dev(K), P.to_dev(V), L, [0])
+    st = DecodeStep(lay, k, L)
+    out = st.attend(gc, P.to_dev(q), [L])
+    torch.cuda.synchronize()
+    sig = st.sigma.cpu().numpy()[:L]
+    assert np.all(sig == sig[0])
+    assert st.idx.cpu().numpy()[:k].tolist() == list(range(k))
+    # equal keys: the output is the weighted mean with exact values for the
+    # first k tokens and dequantised ones for the rest
+    import oracle
+    oc = oracle.Cache(oracle.Shape(1, 8, 1, 128, 3, 2, 32, cap))
+    oc.append(K, V, np.zeros(1, np.int32))
+    ref = oc.decode(q, np.array([L], np.int32), k, sel=st.idx.cpu().numpy()[:k].reshape(1, 1, k))
+    P.assert_close(out.cpu().numpy().reshape(1, 8, 128), ref["out"], "equal keys")
+
+
+def test_many_correction_chunks(P):
+    """k >= len at 17000 tokens: 532 correction chunks per head (more than one
+    LDS batch in the merge), the output is exact attention."""
+    banner("k=L at 17000 tokens")
+    w = P.Workload("bigk", 1, 4, 1, 128, 17000, 3, 2, 32, 17000, 4, 21)
+    pair = P.build_pair(w, L=17000, cap=17024)
+    lens = np.array([17000])
+    r = P.run_step(pair, lens, 17000)
+    orc = pair["oc"].decode(pair["q"], lens, 0, want_exact=True)
+    P.assert_close(r["out"], orc["out_exact"], "k=L")
+    assert r["idx"][0, 0].tolist() == list(range(17000))
+
+
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
+def test_step_parity_multi_slice(P, kb, vb, G):
+    """Few units and a long context: several top-k slices and scan splits per
+    unit, so the cross-workgroup paths (histogram, candidates, bitmap) run."""
+    banner(f"multi-slice kb={kb} vb={vb} G={G}")
+    w = P.Workload("ms", 1, 2 * G, 2, 128, 6000, kb, vb, 32, 40, 8, 300 + G)
+    pair = P.build_pair(w, L=6000, cap=6016)
+    lens = np.array([6000])
+    r = P.run_step(pair, lens, 40)
+    orc = pair["oc"].decode(pair["q"], lens, 40)
+    import oracle
+    for h in range(w.Hkv):
+        want = oracle.topk(r["sigma"][0, h, :6000].astype(np.float64), 40)
+        assert np.array_equal(r["idx"][0, h], want)
+        P.assert_topk_near_tie(r["idx"][0, h], orc["idx"][0, h], orc["sigma"][0, h], 6000, f"h{h}")
+    orc_s = pair["oc"].decode(pair["q"], lens, 40, sel=r["idx"])
+    P.assert_close(r["out"], orc_s["out"], "out vs oracle(S_gpu)")
+    P.assert_close(r["out"], orc["out"], "out vs oracle(S_oracle)")
