@@ -52,6 +52,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes (3 times), the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -61,6 +64,16 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
+        return 0
     from bit_kv_attention_amd import binding as bk
     from bit_kv_attention_amd.step import DecodeStep
     from bit_kv_attention_amd.synth import BY_NAME, WORKLOADS, make_inputs, make_new_tokens

@@ -40,9 +40,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 
 // DPP helpers (row = 16 lanes).
+// The patterns used (quad_perm, row_ror) read a valid lane for every lane, so
+// `old` is irrelevant; leaving it undefined lets the compiler fold the move
+// into the consuming add/max.
 template <int CTRL>
 __device__ inline float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
@@ -62,15 +65,21 @@ template <int BITS, bool EXACT>
 __device__ inline half8 unpack8(uint32_t y) {
   constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : (BITS == 3) ? 0x00070007u : 0x00030003u;
   u32x4 r;
-  r.x = y & M;
-  r.y = (y >> BITS) & M;
-  r.z = (y >> (2 * BITS)) & M;
-  r.w = (y >> (3 * BITS)) & M;
   if constexpr (EXACT) {
+    // gfx9 VOP3 takes no literal: with the mask in an SGPR and the bias in a
+    // VGPR the AND and OR become one v_and_or_b32.
+    uint32_t mask = M, bias;
+    asm("s_mov_b32 %0, %1" : "=s"(mask) : "i"(M));
+    asm("v_mov_b32 %0, 0x64006400" : "=v"(bias));
     const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, r[i] | 0x64006400u) - k1024);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t biased = ((y >> (BITS * i)) & mask) | bias;
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) - k1024);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (y >> (BITS * i)) & M;
   }
   return __builtin_bit_cast(half8, r);
 }
