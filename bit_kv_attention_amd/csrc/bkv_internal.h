@@ -24,11 +24,41 @@ struct SeqArg {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-// Byte sizes per unit (b, kvh).
-__host__ __device__ inline size_t k_row_bytes(int kbits) { return (size_t)kHeadDim * kbits / 8; }
-__host__ __device__ inline size_t k_unit_bytes(int kbits, int cap) { return (size_t)cap * k_row_bytes(kbits); }
+// ---- packed layouts --------------------------------------------------------
+// Keys: blocks of kKBlock tokens.  Channel c = 32g + 8e + j (group g, eighth
+// e, offset j).  A block is 64 chunks in the order (e, token mod 16); chunk
+// (e, r) holds the 32 codes of channels 32g + 8e + j of token r in the order
+// (g, j), KB bits each (4*KB bytes).  So the 16 tokens x 4 eighths of a block
+// are exactly the 64 lanes' A operands of a 16x16x32 MFMA tile, in lane order.
+// Values: tiles of kTile tokens.  Token r of the tile is in quarter
+// q = (r mod 16)/4 at slot j = 4(r/16) + r mod 4; channel c belongs to lane
+// l = 16q + c mod 16 as its column n = c/16.  A dword holds 4/VB columns of
+// one lane: column n in dword d = n/(4/VB) at sub-position s = n mod (4/VB),
+// slot j at bit 16(j/4) + 4*VB*s + VB(j mod 4) -- so a right shift by 8s
+// leaves the column in the layout the P.V MFMA unpack expects.  Dword d of
+// lane l is dword 256(d/4) + 4l + d mod 4 of the tile (16-byte pieces,
+// piece-major: each piece is one coalesced 1 KB load of a wave).
+constexpr int kKBlock = 16;
+
+__host__ __device__ inline size_t k_chunk_bytes(int kbits) { return (size_t)4 * kbits; }
+__host__ __device__ inline size_t k_block_bytes(int kbits) { return (size_t)kKBlock * kHeadDim * kbits / 8; }
+__host__ __device__ inline size_t k_unit_bytes(int kbits, int cap) { return (size_t)(cap / kKBlock) * k_block_bytes(kbits); }
 __host__ __device__ inline size_t v_tile_bytes(int vbits) { return (size_t)kTile * kHeadDim * vbits / 8; }
 __host__ __device__ inline size_t v_unit_bytes(int vbits, int cap) { return (size_t)(cap / kTile) * v_tile_bytes(vbits); }
+
+// Byte offset, inside a unit's key codes, of the chunk (eighth e) of token t.
+__host__ __device__ inline size_t k_chunk_offset(int kbits, int t, int e) {
+  return (size_t)(t / kKBlock) * k_block_bytes(kbits) + (size_t)(e * kKBlock + t % kKBlock) * k_chunk_bytes(kbits);
+}
+// Dword index inside a value tile, and bit inside that dword, of the code of
+// (token r of the tile, channel c).
+__host__ __device__ inline void v_code_pos(int vbits, int r, int c, int& dw, int& bit) {
+  const int q = (r & 15) >> 2, j = 4 * (r >> 4) + (r & 3);
+  const int l = 16 * q + (c & 15), n = c >> 4;
+  const int cpd = 4 / vbits, d = n / cpd, sub = n % cpd;
+  dw = 256 * (d >> 2) + 4 * l + (d & 3);
+  bit = 16 * (j >> 2) + 4 * vbits * sub + vbits * (j & 3);
+}
 
 // Order-preserving map of a float onto uint32 (larger float -> larger key);
 // -0 is folded onto +0 so that equal values compare equal.

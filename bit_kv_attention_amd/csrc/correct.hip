@@ -91,9 +91,18 @@ __global__ __launch_bounds__(256) void corr_chunk_kernel(
       const uint4* kr = reinterpret_cast<const uint4*>(ksh + (size_t)t * kHeadDim + c0);
       const uint4 k0 = kr[0], k1 = kr[1];
       const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      const uint32_t* row = reinterpret_cast<const uint32_t*>(kbase + (size_t)t * k_row_bytes(KB));
-      const int bit0 = c0 * KB;
-      const uint64_t bits = ((uint64_t)row[bit0 >> 5] | ((uint64_t)row[(bit0 >> 5) + 1] << 32)) >> (bit0 & 31);
+      // channels c0..c0+15 are the group-(part/2) fields of the chunks of
+      // eighths 2*(part%2) and 2*(part%2)+1 (8*KB bits each)
+      uint32_t fld[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const uint32_t* ch =
+            reinterpret_cast<const uint32_t*>(kbase + k_chunk_offset(KB, t, 2 * (part & 1) + x));
+        const int b0 = 8 * KB * (part >> 1);
+        const int d0 = b0 >> 5, d1 = min(d0 + 1, KB - 1);
+        fld[x] = (uint32_t)((((uint64_t)ch[d1] << 32) | ch[d0]) >> (b0 & 31));
+      }
+      const uint64_t bits = ((uint64_t)fld[0] & ((1ull << (8 * KB)) - 1)) | ((uint64_t)fld[1] << (8 * KB));
       const uint32_t mw = kmeta[(size_t)(c0 / kGroup) * cap + t];
       const float s = h2f((uint16_t)(mw & 0xFFFFu)), z = h2f((uint16_t)(mw >> 16));
 #pragma unroll
@@ -155,15 +164,10 @@ __global__ __launch_bounds__(256) void corr_chunk_kernel(
     vx[j] = 0.f;
     vq[j] = 0.f;
     if (t >= 0) {
-      const int r = t % kTile;
-      const int qq = (r & 15) >> 2;
-      const int slot = 4 * (r >> 4) + (r & 3);
-      const uint8_t* vt = vbase + (size_t)(t / kTile) * v_tile_bytes(VB);
-      uint32_t code;
-      if constexpr (VB == 4)
-        code = (reinterpret_cast<const uint32_t*>(vt)[qq * kHeadDim + c] >> (4 * slot)) & 15u;
-      else
-        code = (reinterpret_cast<const uint16_t*>(vt)[qq * kHeadDim + c] >> (2 * slot)) & 3u;
+      int dw, bit;
+      v_code_pos(VB, t % kTile, c, dw, bit);
+      const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + (size_t)(t / kTile) * v_tile_bytes(VB));
+      const uint32_t code = (vt[dw] >> bit) & ((1u << VB) - 1);
       const uint32_t mw = vmeta[(size_t)(c / kGroup) * cap + t];
       vx[j] = h2f(vsh[(size_t)t * kHeadDim + c]);
       vq[j] = fmaf(h2f((uint16_t)(mw & 0xFFFFu)), (float)code, h2f((uint16_t)(mw >> 16)));

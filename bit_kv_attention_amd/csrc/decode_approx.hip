@@ -29,6 +29,13 @@
 //  * Key codes become exact fp16 integers (OR into 1024 + c, subtract 1024);
 //    value codes enter as fp16 subnormals (the masked bit pattern c is the
 //    value c * 2^-24), one shift and one AND per pair, no conversion.
+//  * Memory: the packed layouts put each lane's operands at byte 16*lane (key
+//    chunks: 12*lane for 3 bits) of contiguous 1 KB runs, so a wave's step is
+//    4-6 fully coalesced 16-byte-per-lane loads, prefetched one step ahead
+//    into a second register set.  The scale/zero words, which several lanes
+//    share, are loaded once (one 16-byte load per lane covers the step's K
+//    and V meta) and handed out through a per-wave LDS slot.  Selection scores
+//    are staged in LDS and stored every 8 steps as one coalesced store.
 #include "bkv_internal.h"
 
 namespace bkv {
@@ -92,56 +99,58 @@ __device__ inline uint32_t pack_half2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3), aligned(4)));
+
+// The bytes of one 32-token step of one wave, as loaded: every load is a
+// whole 1 KB (or 768 B) run of the unit's buffers, lane i taking bytes
+// 16i..16i+15 (12i..12i+11 for 3-bit keys), which the layouts make the
+// lane's own MFMA operand.
 template <int KB, int VB, int G>
 struct Step {
   static constexpr int NT = (G == 8) ? 2 : 1;
-  static constexpr int KW = (KB == 4) ? 1 : 2;
-  uint32_t kc[2][kGroups][KW];  // key code dwords: [token tile][group][dword]
-  u32x4 km[2][NT];              // key meta, tokens 4kb..4kb+3 of token tile tt
-  uint32_t vc[8];               // value word (quarter kb, channel 16*nt + n)
-  u32x4 vm[NT][2];              // value meta: [N-tile][token tile]
+  uint32_t kc[2][KB];   // key chunk (eighth kb, token 16tt + n): 4 groups x 8 codes
+  u32x4 vd[VB / 2];     // value dwords of lane (kb, n), piece-major
+  u32x4 meta;           // lane < 32: key meta, else value meta (group, 4 tokens)
 };
 
 template <int KB, int VB, int G>
 __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__ kbase,
                                  const uint8_t* __restrict__ vbase, const uint32_t* __restrict__ kmeta,
-                                 const uint32_t* __restrict__ vmeta, int cap, int t0, int n, int kb) {
-  constexpr int NT = Step<KB, VB, G>::NT;
-  constexpr int RB = kHeadDim * KB / 8;  // bytes per key row
+                                 const uint32_t* __restrict__ vmeta, int cap, int t0, int lane) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(kbase + (size_t)(t0 + 16 * tt + n) * RB);
+    const uint8_t* blk = kbase + (size_t)(t0 / kKBlock + tt) * k_block_bytes(KB) + (size_t)lane * k_chunk_bytes(KB);
+    if constexpr (KB == 4) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(blk);
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) {
-      if constexpr (KB == 4) {
-        S.kc[tt][g][0] = row[4 * g + kb];
-      } else {
-        const int d0 = 3 * g + ((24 * kb) >> 5);
-        const int d1 = min(d0 + 1, 3 * g + 2);
-        S.kc[tt][g][0] = row[d0];
-        S.kc[tt][g][1] = row[d1];
-      }
+      for (int i = 0; i < 4; ++i) S.kc[tt][i] = x[i];
+    } else {
+      const u32x3 x = *reinterpret_cast<const u32x3*>(blk);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) S.kc[tt][i] = x[i];
     }
   }
+  const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB) + (size_t)lane * 16;
 #pragma unroll
-  for (int T = 0; T < NT; ++T) {
-    const int gq = (G == 8) ? (2 * T + (n >> 3)) : (n >> 2);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      S.km[tt][T] = *reinterpret_cast<const u32x4*>(kmeta + (size_t)gq * cap + t0 + 16 * tt + 4 * kb);
-      S.vm[T][tt] = *reinterpret_cast<const u32x4*>(vmeta + (size_t)gq * cap + t0 + 16 * tt + 4 * kb);
-    }
-  }
-  const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB);
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int w = kb * kHeadDim + 16 * nt + n;  // word (quarter kb, channel 16nt + n)
-    if constexpr (VB == 4)
-      S.vc[nt] = reinterpret_cast<const uint32_t*>(vt)[w];
-    else
-      S.vc[nt] = reinterpret_cast<const uint16_t*>(vt)[w];
-  }
+  for (int pc = 0; pc < VB / 2; ++pc) S.vd[pc] = *reinterpret_cast<const u32x4*>(vt + 1024 * pc);
+  const uint32_t* mp = (lane < 32 ? kmeta : vmeta) + (size_t)((lane & 31) >> 3) * cap + t0 + 4 * (lane & 7);
+  S.meta = *reinterpret_cast<const u32x4*>(mp);
 }
+
+// Meta of a step in the wave's LDS slot: 16-byte cells
+// [K/V][token tile tt][quarter kb][group g] = the 4 tokens 16tt + 4kb + i.
+__device__ inline int meta_cell(int kv, int tt, int kb, int g) { return kv * 32 + tt * 16 + kb * 4 + g; }
+
+// Orders a wave's LDS accesses across its lanes: what some lanes wrote before
+// is what other lanes read after (a wave's LDS operations execute in order;
+// this keeps the compiler from moving them across each other).
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+constexpr int kSigBatch = 8;  // steps of selection scores staged per wave before a store
 
 // Running softmax state of one wave (see the kernel comment).
 template <int NT>
@@ -154,9 +163,10 @@ struct WaveState {
 
 // One 32-token step.  MASK: the step straddles the sequence end.
 template <int KB, int VB, int G, bool MASK>
-__device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half8 (&bq)[kGroups],
+__device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
+                                          const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const half8 (&bq)[kGroups],
                                           const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT>& ws,
-                                          float* __restrict__ sig, int t0, int len, int n, int kb,
+                                          floatx4* __restrict__ sig_row, int t0, int len, int n, int kb,
                                           float c_sig, float c_s2) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // -- scores: D[T][tt] rows = tokens 4kb+i of token tile tt, column n --------
@@ -171,10 +181,10 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half
     for (int g = 0; g < kGroups; ++g) {
       uint32_t y;
       if constexpr (KB == 4) {
-        y = cur.kc[tt][g][0];
-      } else {
-        const int shift = (24 * kb) & 31;
-        const uint32_t x = __builtin_amdgcn_alignbit(cur.kc[tt][g][1], cur.kc[tt][g][0], shift);
+        y = cur.kc[tt][g];
+      } else {  // 24-bit field g at bit 24g of the 96-bit chunk; codes 4..7 to the high half
+        const int d0 = (24 * g) >> 5, d1 = (d0 + 1 < 3) ? d0 + 1 : 2;
+        const uint32_t x = __builtin_amdgcn_alignbit(cur.kc[tt][d1], cur.kc[tt][d0], (24 * g) & 31);
         y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);
       }
       const int T = (G == 8) ? (g >> 1) : 0;
@@ -192,7 +202,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half
       float part = 0.f;
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
-        const uint32_t mw = cur.km[tt][T][i];
+        const uint32_t mw = km[tt][T][i];
         part = fmaf(d[T][tt][i], lo_half(mw), fmaf(hi_half(mw), qs[T], part));
       }
       if constexpr (G == 8) {
@@ -216,7 +226,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half
       s2[tt][i] = v2;
     }
     if (n == 0)
-      *reinterpret_cast<floatx4*>(sig + t0 + 16 * tt + 4 * kb) = (floatx4){sg4[0], sg4[1], sg4[2], sg4[3]};
+      sig_row[4 * tt + kb] = (floatx4){sg4[0], sg4[1], sg4[2], sg4[3]};
   }
 
   // -- online softmax (log2 units) --------------------------------------------
@@ -251,7 +261,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half
     u32x4 w;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      uint32_t m0 = cur.vm[T][0][r], m1 = cur.vm[T][1][r];
+      uint32_t m0 = vm[T][0][r], m1 = vm[T][1][r];
       if constexpr (MASK) {  // meta past the end may hold anything
         m0 = (t0 + 4 * kb + r) < len ? m0 : 0u;
         m1 = (t0 + 16 + 4 * kb + r) < len ? m1 : 0u;
@@ -263,8 +273,8 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const half
   }
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
-    uint32_t y = cur.vc[nt];
-    if constexpr (VB == 2) y = (y & 0xFFu) | ((y & 0xFF00u) << 8);
+    // column nt: V4 dword nt; V2 dword nt/2 shifted by 8 for odd nt
+    const uint32_t y = (VB == 4) ? cur.vd[nt >> 2][nt & 3] : (cur.vd[0][nt >> 1] >> (8 * (nt & 1)));
     const int T = (G == 8) ? (nt >> 2) : 0;
     ws.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack8<VB, false>(y), bp[T], ws.acc[nt], 0, 0, 0);
   }
@@ -278,16 +288,18 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     float* __restrict__ pl, float* __restrict__ pacc, uint32_t* __restrict__ tk_hist,
     uint32_t* __restrict__ tk_ctrl, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk) {
   constexpr int NT = Step<KB, VB, G>::NT;
-  const int u = blockIdx.y;
+  // (workgroup and lane ids via the builtins: this file is built without IEEE
+  // mode, so the device library's id functions would not be inlined)
+  const int u = __builtin_amdgcn_workgroup_id_y();
   const int b = u / Hkv;
   const int kvh = u - b * Hkv;
-  const int split = blockIdx.x;
+  const int split = __builtin_amdgcn_workgroup_id_x();
   const int len = lens.v[b];
   const int t_begin = split * chunk;
   const int t_end = min(len, t_begin + chunk);
-  const int tid = threadIdx.x;
+  const int tid = __builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int n = lane & 15;
   const int kb = lane >> 4;
 
@@ -350,18 +362,82 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) ws.acc[nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
-  Step<KB, VB, G> cur, nxt;
+  // per-wave LDS slot for the step's meta (each wave only touches its own)
+  __shared__ u32x4 s_meta[4][64];
+  u32x4* slot = s_meta[wv];
+  const int wcell = meta_cell(lane >> 5, (lane & 7) >> 2, lane & 3, (lane & 31) >> 3);
+
+  // Selection scores go through a per-wave LDS buffer of kSigBatch steps and
+  // leave as one coalesced 16-byte-per-lane store (no stores in the steps).
+  __shared__ floatx4 s_sig[4][kSigBatch][8];
+  int sig_count = 0;   // steps staged
+  int sig_first = 0;   // t0 of the first staged step
+  auto flush_sig = [&]() {
+    wave_lds_order();
+    const int i = lane >> 3;
+    if (i < sig_count)
+      *reinterpret_cast<floatx4*>(sig + sig_first + 4 * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7];
+    wave_lds_order();
+    sig_count = 0;
+  };
+
+  // Meta of the step -> this lane's cells: lane (n, kb) needs its column's
+  // group for tokens 16tt + 4kb + i.
+  auto meta_cells = [&](const u32x4& meta, u32x4 (&km)[2][NT], u32x4 (&vm)[NT][2]) {
+    wave_lds_order();  // the previous step's reads of the slot come first
+    slot[wcell] = meta;
+    wave_lds_order();
+#pragma unroll
+    for (int T = 0; T < NT; ++T) {
+      const int gq = (G == 8) ? (2 * T + (n >> 3)) : (n >> 2);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        km[tt][T] = slot[meta_cell(0, tt, kb, gq)];
+        vm[T][tt] = slot[meta_cell(1, tt, kb, gq)];
+      }
+    }
+  };
+
+  // One whole step: prefetch the wave's next step into `nxt` (unconditionally
+  // -- the last step re-reads its own bytes -- so that the compiler's wait for
+  // this step's data counts those loads), then score and accumulate `cur`.
+  // The loop is unrolled twice so the two register sets alternate without
+  // copies (a copy of registers with loads in flight would wait for them).
+  auto full_step = [&](Step<KB, VB, G>& cur, Step<KB, VB, G>& nxt, int t0) {
+    const int tn = (t0 + 4 * kTile) < t_end ? t0 + 4 * kTile : t0;
+    load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane);
+    u32x4 km[2][NT], vm[NT][2];
+    meta_cells(cur.meta, km, vm);
+    if (sig_count == 0) sig_first = t0;
+    scan_step<KB, VB, G, false>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_sig, c_s2);
+    if (++sig_count == kSigBatch) flush_sig();
+  };
+  // The step that straddles the end of the split (at most one per wave).
+  auto last_step = [&](Step<KB, VB, G>& cur, int t0) {
+    u32x4 km[2][NT], vm[NT][2];
+    meta_cells(cur.meta, km, vm);
+    if (sig_count == 0) sig_first = t0;
+    scan_step<KB, VB, G, true>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_sig, c_s2);
+    ++sig_count;
+  };
+  Step<KB, VB, G> sa, sb;
   int t0 = t_begin + kTile * wv;
-  if (t0 < t_end) load_step<KB, VB, G>(cur, kbase, vbase, kmeta, vmeta, cap, t0, n, kb);
-  for (; t0 < t_end; t0 += 4 * kTile) {
-    const bool more = (t0 + 4 * kTile) < t_end;
-    if (more) load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, t0 + 4 * kTile, n, kb);
-    if (t0 + kTile <= len)
-      scan_step<KB, VB, G, false>(cur, bq, qs, ws, sig, t0, len, n, kb, c_sig, c_s2);
-    else
-      scan_step<KB, VB, G, true>(cur, bq, qs, ws, sig, t0, len, n, kb, c_sig, c_s2);
-    if (more) cur = nxt;
+  if (t0 < t_end) load_step<KB, VB, G>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane);
+  for (;;) {
+    if (t0 + kTile > t_end) {
+      if (t0 < t_end) last_step(sa, t0);
+      break;
+    }
+    full_step(sa, sb, t0);
+    t0 += 4 * kTile;
+    if (t0 + kTile > t_end) {
+      if (t0 < t_end) last_step(sb, t0);
+      break;
+    }
+    full_step(sb, sa, t0);
+    t0 += 4 * kTile;
   }
+  if (sig_count > 0) flush_sig();
 
   // ---- combine the 4 waves of the workgroup -----------------------------------
   ws.l_part += __shfl_xor(ws.l_part, 16);

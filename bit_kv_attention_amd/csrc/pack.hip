@@ -11,9 +11,11 @@
 // group in channel order (same tie behaviour for +-0 as a plain loop).
 //
 // One workgroup per (32-token tile, unit): thread (token r, K/V, group)
-// quantises one group; key bits are whole dwords per group (3*32 or 4*32 bits)
-// so each thread stores its own; value words mix 8 tokens, so they are
-// assembled from LDS afterwards with a read-modify-write of the tile's words.
+// quantises one group and leaves its codes in LDS; then one thread per key
+// chunk (one token's codes of one eighth of every group) writes that chunk
+// whole, and value words, which mix 8 tokens, are assembled with a
+// read-modify-write of the tile's words (tokens outside the append keep
+// their bits).
 #include "bkv_internal.h"
 
 // The codec must match a plain IEEE evaluation operation for operation.
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
   const int t_hi = min(p0 + n_new, tile * kTile + kTile);
   if (t_lo >= t_hi) return;
 
-  __shared__ uint8_t s_vcode[kTile][kHeadDim];
+  __shared__ uint8_t s_code[2][kTile][kHeadDim];  // [K/V][token][channel]
   const int tid = threadIdx.x;
   const int r = tid >> 3;
   const int kv = (tid >> 2) & 1;
@@ -86,44 +88,58 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
 #pragma unroll
     for (int i = 0; i < kGroup; i += 8)
       *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
-    if (kv == 0) {
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) s_code[kv][r][grp * kGroup + i] = code[i];
+  }
+  __syncthreads();
+  // key chunks: chunk (eighth e, token r) of the 16-token block holds the
+  // codes of channels 32g + 8e + j, packed in the order (g, j) at KB bits
+  // each -- 4*KB bytes, written whole by one thread.
+  if (tid < 4 * kTile) {
+    const int rr = tid & (kTile - 1), e = tid >> 5;
+    const int tt = tile * kTile + rr;
+    if (tt >= t_lo && tt < t_hi) {
       uint32_t w[KB];
 #pragma unroll
       for (int j = 0; j < KB; ++j) w[j] = 0;
 #pragma unroll
-      for (int i = 0; i < kGroup; ++i) {
-        const int bp = i * KB;
-        w[bp >> 5] |= (uint32_t)code[i] << (bp & 31);
-        if ((bp & 31) + KB > 32) w[(bp >> 5) + 1] |= (uint32_t)code[i] >> (32 - (bp & 31));
+      for (int m = 0; m < 32; ++m) {
+        const uint32_t cd = s_code[0][rr][32 * (m >> 3) + 8 * e + (m & 7)];
+        const int bp = m * KB;
+        w[bp >> 5] |= cd << (bp & 31);
+        if ((bp & 31) + KB > 32) w[(bp >> 5) + 1] |= cd >> (32 - (bp & 31));
       }
-      uint32_t* row = reinterpret_cast<uint32_t*>(k_codes + (size_t)u * k_unit_bytes(KB, cap) +
-                                                  (size_t)t * k_row_bytes(KB));
+      uint32_t* chunk = reinterpret_cast<uint32_t*>(
+          k_codes + (size_t)u * k_unit_bytes(KB, cap) + (size_t)(tt / kKBlock) * k_block_bytes(KB) +
+          (size_t)(e * kKBlock + (tt % kKBlock)) * k_chunk_bytes(KB));
 #pragma unroll
-      for (int j = 0; j < KB; ++j) row[grp * KB + j] = w[j];
-    } else {
-#pragma unroll
-      for (int i = 0; i < kGroup; ++i) s_vcode[r][grp * kGroup + i] = code[i];
+      for (int j = 0; j < KB; ++j) chunk[j] = w[j];
     }
   }
-  __syncthreads();
-  // value words: word (quarter q, channel c) at q*D + c -> 8 slots of VB bits
-  uint8_t* vt = v_codes + (size_t)u * v_unit_bytes(VB, cap) + (size_t)tile * v_tile_bytes(VB);
-  for (int w = tid; w < kHeadDim * 4; w += 256) {
-    const int c = w & (kHeadDim - 1), qq = w / kHeadDim;
-    uint32_t word = (VB == 4) ? reinterpret_cast<uint32_t*>(vt)[w] : reinterpret_cast<uint16_t*>(vt)[w];
+  // value dwords: dword w of the tile belongs to lane l = (w/4) mod 64 as its
+  // dword d = 4(w/256) + w mod 4, i.e. columns n = d*cpd + s (s < cpd) of
+  // quarter l/16; only the slots of appended tokens are replaced
+  constexpr int kCpd = 4 / VB;
+  uint32_t* vt = reinterpret_cast<uint32_t*>(v_codes + (size_t)u * v_unit_bytes(VB, cap) +
+                                             (size_t)tile * v_tile_bytes(VB));
+  for (int w = tid; w < kHeadDim * VB; w += 256) {
+    const int l = (w >> 2) & 63, d = 4 * (w >> 8) + (w & 3), qq = l >> 4;
+    uint32_t word = vt[w];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = (j < 4) ? (4 * qq + j) : (16 + 4 * qq + (j - 4));
-      const int tt = tile * kTile + rr;
-      if (tt >= t_lo && tt < t_hi) {
-        const uint32_t m = ((1u << VB) - 1) << (j * VB);
-        word = (word & ~m) | ((uint32_t)s_vcode[rr][c] << (j * VB));
+    for (int sub = 0; sub < kCpd; ++sub) {
+      const int c = 16 * (d * kCpd + sub) + (l & 15);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int rr = (j < 4) ? (4 * qq + j) : (16 + 4 * qq + (j - 4));
+        const int tt = tile * kTile + rr;
+        if (tt >= t_lo && tt < t_hi) {
+          const int bit = 16 * (j >> 2) + 4 * VB * sub + VB * (j & 3);
+          const uint32_t m = ((1u << VB) - 1) << bit;
+          word = (word & ~m) | ((uint32_t)s_code[1][rr][c] << bit);
+        }
       }
     }
-    if (VB == 4)
-      reinterpret_cast<uint32_t*>(vt)[w] = word;
-    else
-      reinterpret_cast<uint16_t*>(vt)[w] = (uint16_t)word;
+    vt[w] = word;
   }
 }
 

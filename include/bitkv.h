@@ -77,15 +77,20 @@ typedef struct {
  * every buffer.  Sizes come from bkv_cache_bytes.  Zero-fill the code buffers
  * before the first append: appends read-modify-write the shared V words.
  *
- *  k_codes  [B][Hkv][capacity][D*k_bits/8] bytes.  Token t's row is an
- *           LSB-first little-endian bitstream; channel c occupies bits
- *           [c*k_bits, (c+1)*k_bits), so with 3 bits channels 10 and 21 of
- *           every 32-channel group straddle 32-bit words.  16-byte aligned.
- *  v_codes  [B][Hkv][capacity/32][4][D] words of 8*v_bits bits.  In each
- *           32-token tile, word (q, c) holds channel c of the 8 tokens of
- *           quarter q: token r of the tile (r = t mod 32) is in quarter
- *           q = (r mod 16)/4, slot j = 4*(r/16) + r mod 4, at bits
- *           [j*v_bits, (j+1)*v_bits) of the word.  16-byte aligned.
+ *  k_codes  [B][Hkv][capacity/16][64][4*k_bits] bytes: blocks of 16 tokens.
+ *           Channel c = 32g + 8e + j (group g, eighth e, offset j).  Chunk
+ *           (e, r) of a block, at index 16e + r, holds the codes of token r
+ *           of the block for channels 32g + 8e + j in the order (g, j),
+ *           k_bits each, LSB-first little-endian (with 3 bits a code can
+ *           straddle a 32-bit word).  16-byte aligned.
+ *  v_codes  [B][Hkv][capacity/32][128*v_bits] uint32: tiles of 32 tokens.
+ *           Token r of the tile is in quarter q = (r mod 16)/4 at slot
+ *           j = 4*(r/16) + r mod 4; channel c has owner l = 16q + c mod 16
+ *           and column n = c/16.  With m = 4/v_bits columns per dword,
+ *           column n is in dword d = n/m at sub-position s = n mod m, and
+ *           slot j is at bit 16*(j/4) + 4*v_bits*s + v_bits*(j mod 4) of it.
+ *           Dword d of owner l is dword 256*(d/4) + 4l + d mod 4 of the
+ *           tile.  16-byte aligned.
  *  k_meta,  [B][Hkv][D/group][capacity] uint32: fp16 scale in the low half,
  *  v_meta   fp16 zero point (group minimum) in the high half.
  *  k_shadow,[B][Hkv][capacity][D] fp16: the exact input rows.  Device memory,

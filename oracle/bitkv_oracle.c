@@ -8,8 +8,10 @@
  *                 m the group minimum (HACK review, Eq. (4) and "What carries
  *                 the argument"; TailorKV review, fp16 zero point and scale).
  *   O2 pack       this library's bit layouts (a storage convention, not from
- *                 the pages): K rows are an LSB-first bitstream, so 3-bit
- *                 codes straddle 32-bit words; V codes are token-tiled.
+ *                 the pages): K codes in 16-token blocks of (run of 8
+ *                 channels, token) chunks, V codes in 32-token tiles of
+ *                 dwords that each hold 8 tokens of 1 or 2 channels; both
+ *                 LSB-first little-endian.
  *   O3 score      approximate logit per query head against the dequantised
  *                 keys; selection score = max over the query heads of a KV
  *                 head's group.
@@ -115,24 +117,43 @@ void orc_quantize_rows(const uint16_t* x, int n, int D, int g, int bits,
 
 /* -------------------------------------------------------------- O2 layout */
 
-/* K: token-major rows of D*bits bits; channel c at bits [c*bits, c*bits+bits)
- * of the row, counted LSB-first through little-endian bytes. */
+/* K: blocks of 16 tokens.  Channel c has group g = c / 32, eighth
+ * e = (c mod 32) / 8 (which 8-channel run of its group) and offset j = c mod 8.
+ * A block is 64 chunks in the order (e, token mod 16); a chunk is the D/32
+ * group fields of one (token, e) in group order, and a field is the 8 codes
+ * of that run, code j at bits [j*bits, j*bits+bits).  Bits are counted
+ * LSB-first through little-endian bytes, so with 3 bits a 24-bit field may
+ * straddle 32-bit words. */
 uint64_t orc_k_bitpos(int t, int c, int D, int bits) {
-  return (uint64_t)t * (uint64_t)D * bits + (uint64_t)c * bits;
+  const int ng = D / 32;
+  const int g = c / 32, e = (c % 32) / 8, j = c % 8;
+  const uint64_t field_bits = 8u * (uint64_t)bits;
+  const uint64_t chunk_bits = (uint64_t)ng * field_bits;
+  const uint64_t chunk = (uint64_t)e * 16u + (uint64_t)(t % 16);
+  return (uint64_t)(t / 16) * 16u * (uint64_t)D * bits + chunk * chunk_bits +
+         (uint64_t)g * field_bits + (uint64_t)j * bits;
 }
 
-/* V: tiles of 32 tokens.  Inside a tile there are 4*D words of 8 codes:
- * word (q, c) at index q*D + c holds channel c of the 8 tokens of quarter q.
- * Token r of the tile (r = t mod 32) sits in quarter q = (r mod 16) / 4,
- * slot j = 4*(r / 16) + r mod 4, at bits [j*bits, j*bits+bits) of the word. */
+/* V (bits 2 or 4): tiles of 32 tokens.  Token r of the tile (r = t mod 32)
+ * lies in quarter q = (r mod 16) / 4 at slot j = 4*(r / 16) + r mod 4.
+ * Channel c belongs to owner l = 16*q + c mod 16 as column n = c / 16.  A
+ * 32-bit dword holds 4/bits columns of one owner: column n is in dword
+ * d = n / (4/bits) at sub-position s = n mod (4/bits), and its slot j sits at
+ * bit 16*(j / 4) + 4*bits*s + bits*(j mod 4) of that dword (slots 0..3 in the
+ * low half, 4..7 in the high half).  The tile stores dword d of owner l at
+ * index 256*(d / 4) + 4*l + d mod 4: 16-byte pieces, piece-major. */
 uint64_t orc_v_bitpos(int t, int c, int D, int bits) {
   const int tile = t / 32;
   const int r = t % 32;
   const int q = (r % 16) / 4;
   const int j = 4 * (r / 16) + (r % 4);
-  const uint64_t word_bits = 8u * (uint64_t)bits;
-  return (uint64_t)tile * 32u * (uint64_t)D * bits +
-         ((uint64_t)q * (uint64_t)D + (uint64_t)c) * word_bits + (uint64_t)j * bits;
+  const int l = 16 * q + c % 16;
+  const int n = c / 16;
+  const int cpd = 4 / bits;
+  const int d = n / cpd, sub = n % cpd;
+  const uint64_t dw = 256u * (uint64_t)(d / 4) + 4u * (uint64_t)l + (uint64_t)(d % 4);
+  const uint64_t bit = 16u * (uint64_t)(j / 4) + 4u * (uint64_t)bits * sub + (uint64_t)bits * (j % 4);
+  return (uint64_t)tile * 32u * (uint64_t)D * bits + dw * 32u + bit;
 }
 
 uint32_t orc_get_bits(const uint8_t* buf, uint64_t bitpos, int nbits) {

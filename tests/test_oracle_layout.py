@@ -23,7 +23,7 @@ def test_golden_bit_positions(orc):
         assert orc.v_bitpos(e["t"], e["c"], 128, e["bits"]) == e["bitpos"], e
 
 
-@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("bits", [2, 4])
 def test_v_tile_is_a_partition(orc, bits):
     D = 128
     owner = np.full(32 * D * bits, -1, dtype=np.int64)
@@ -38,28 +38,62 @@ def test_v_tile_is_a_partition(orc, bits):
 
 
 @pytest.mark.parametrize("bits", [3, 4])
-def test_k_rows_closed_form(orc, bits):
-    """Packed K rows equal an independently built little-endian integer
-    sum_c code_c << (bits*c)."""
+def test_k_block_is_a_partition(orc, bits):
+    D = 128
+    owner = np.full(16 * D * bits, -1, dtype=np.int64)
+    for r in range(16):
+        for c in range(D):
+            p = orc.k_bitpos(r, c, D, bits)
+            assert np.all(owner[p:p + bits] == -1)
+            owner[p:p + bits] = r * D + c
+    assert np.all(owner >= 0)
+    assert orc.k_bitpos(16, 0, D, bits) == 16 * D * bits
+
+
+def k_block_closed_form(codes16, bits):
+    """The bytes of one 16-token K block built as one little-endian integer:
+    chunk (e, r) at chunk index 16*e + r holds, for g = 0..3, the field
+    sum_j code[r][32g + 8e + j] << (bits*j) at bit offset 8*bits*g."""
+    fb = 8 * bits
+    val = 0
+    for e in range(4):
+        for r in range(16):
+            chunk = 0
+            for g in range(4):
+                field = 0
+                for j in range(8):
+                    field |= int(codes16[r, 32 * g + 8 * e + j]) << (bits * j)
+                chunk |= field << (fb * g)
+            val |= chunk << (4 * fb * (16 * e + r))
+    nbytes = 16 * 128 * bits // 8
+    return np.frombuffer(val.to_bytes(nbytes, "little"), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_k_blocks_closed_form(orc, bits):
+    """Packed K blocks equal an independently built integer (see
+    k_block_closed_form); the last block is partly filled and the rows past
+    the appended tokens stay zero."""
     rng = np.random.default_rng(bits)
     s = orc.Shape(B=1, Hq=1, Hkv=1, D=128, kbits=bits, vbits=2, group=32, cap=64)
     cache = orc.Cache(s)
-    K = rng.standard_normal((1, 1, 40, 128)).astype(np.float16)
-    V = rng.standard_normal((1, 1, 40, 128)).astype(np.float16)
+    n = 40
+    K = rng.standard_normal((1, 1, n, 128)).astype(np.float16)
+    V = rng.standard_normal((1, 1, n, 128)).astype(np.float16)
     cache.append(K, V, [0])
     codes, _, _ = orc.quantize_rows(K[0, 0], 32, bits)
-    rb = 128 * bits // 8
-    for t in range(40):
-        val = 0
-        for c in range(128):
-            val |= int(codes[t, c]) << (bits * c)
-        want = np.frombuffer(val.to_bytes(rb, "little"), dtype=np.uint8)
-        assert np.array_equal(cache.k_codes[t * rb:(t + 1) * rb], want)
-    if bits == 4:  # nibble closed form
-        row = cache.k_codes[:rb]
-        assert np.array_equal(row, (codes[0, 0::2] | (codes[0, 1::2] << 4)).astype(np.uint8))
-    # unwritten rows stay zero
-    assert not cache.k_codes[40 * rb:].any()
+    full = np.zeros((48, 128), dtype=np.int64)
+    full[:n] = codes
+    bb = 16 * 128 * bits // 8
+    for blk in range(3):
+        want = k_block_closed_form(full[16 * blk:16 * blk + 16], bits)
+        assert np.array_equal(cache.k_codes[blk * bb:(blk + 1) * bb], want), blk
+    if bits == 4:  # nibble form of chunk (e=0, r=0): bytes 4g+i = channels 32g+2i, 32g+2i+1
+        chunk = cache.k_codes[:16]
+        want = np.array([codes[0, 32 * g + 2 * i] | (codes[0, 32 * g + 2 * i + 1] << 4)
+                         for g in range(4) for i in range(4)], dtype=np.uint8)
+        assert np.array_equal(chunk, want)
+    assert not cache.k_codes[3 * bb:].any()
 
 
 @pytest.mark.parametrize("bits", [2, 4])
