@@ -37,6 +37,21 @@ static int max_splits(int units, int max_len) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int topk_slice(int max_len, int k) {
+  if (k <= 0) return 0;
+  const long long slots = (long long)((max_len + kTopkSliceMax - 1) / kTopkSliceMax) * k;
+  return slots <= kTopkMergeMax ? kTopkSliceMax : 0;
+}
+
+// Candidate slots per unit: ceil(max_len/S)*k, at most kTopkMergeMax when the
+// two-kernel path runs -- a bound for every shorter step too (the region is
+// sized even when this max_len itself takes the single-workgroup kernel).
+static size_t topk_slots(int max_len, int k) {
+  if (k <= 0) return 0;
+  const long long a = (long long)((max_len + kTopkSliceMax - 1) / kTopkSliceMax) * k;
+  return (size_t)(a < kTopkMergeMax ? a : kTopkMergeMax);
+}
+
 Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bool bound) {
   const int units = L.batch * L.n_kv_heads;
   Workspace w;
@@ -50,15 +65,12 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
     off = align256(off + bytes);
     return p;
   };
-  w.tk.hist = reinterpret_cast<uint32_t*>(take((size_t)units * kHistBins * 4));
-  w.tk.ctrl = reinterpret_cast<uint32_t*>(take((size_t)units * kCtrlWords * 4));
-  w.tk.cand = reinterpret_cast<uint64_t*>(take((size_t)units * kCandCap * 8));
-  w.tk.bitmap = reinterpret_cast<uint32_t*>(take((size_t)units * (L.capacity / 32) * 4));
   const size_t recs = (size_t)L.batch * L.n_q_heads * w.nsplit;
   w.part.acc = reinterpret_cast<float*>(take(recs * kHeadDim * 4));
   w.part.m = reinterpret_cast<float*>(take(recs * 4));
   w.part.l = reinterpret_cast<float*>(take(recs * 4));
   w.cs = reinterpret_cast<float*>(take((size_t)L.batch * L.n_q_heads * w.nchunk * kCsStride * 4));
+  w.tkc = reinterpret_cast<uint64_t*>(take((size_t)units * topk_slots(max_len, k) * 8));
   w.bytes = off;
   return w;
 }
@@ -191,9 +203,9 @@ bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* l
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   if (k == 0) return BKV_OK;
-  const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_topk(*L, sigma, len, max_len, k, idx, w.tk, (hipStream_t)stream) == hipSuccess ? BKV_OK
+  return launch_topk(*L, sigma, len, max_len, k, idx, w.tkc, (hipStream_t)stream) == hipSuccess ? BKV_OK
                                                                                                : BKV_E_HIP;
 }
 

@@ -69,8 +69,8 @@ __device__ inline uint32_t float_key(float f) {
 }
 
 // ---- workspace ------------------------------------------------------------
-// One buffer, three regions: the top-k scratch (fixed per layout), the split
-// partial states of the scan and the states of the correction chunks.  The
+// One buffer: the split partial states of the scan, the states of the
+// correction chunks and the top-k candidate slots.  The
 // region sizes depend on the step's longest length and k, so every call of a
 // step recomputes the same offsets from the same (lens, k).
 
@@ -81,27 +81,22 @@ struct Partials {
   float* acc;  // [B][Hq][nsplit][D] unnormalised sum of p * V_hat
 };
 
-constexpr int kHistBins = 4096;  // first radix digit of the top-k: 12 key bits
-constexpr int kCandCap = 4096;   // threshold-bucket candidates resolved in LDS
-constexpr int kCtrlWords = 16;
-enum { kCtlArrive1 = 0, kCtlArrive2 = 1, kCtlDigit1 = 2, kCtlAbove1 = 3, kCtlCandCount = 4 };
-
-struct TopkScratch {
-  uint32_t* hist;    // [U][kHistBins]
-  uint32_t* ctrl;    // [U][kCtrlWords]
-  uint64_t* cand;    // [U][kCandCap] (key << 32) | token
-  uint32_t* bitmap;  // [U][capacity / 32] selected tokens
-};
-
 constexpr int kCorrChunk = 32;  // selected tokens per correction workgroup
 // Per (b, h, chunk): m_exact, l_exact, m_approx, l_approx, then the exact and
 // the approximate value sums (D each), 16-byte aligned.
 constexpr int kCsStride = 4 + 2 * kHeadDim;
 
+// Top-k: slices of S = kTopkSliceMax tokens whose local top-k candidates,
+// ceil(max_len/S)*k slots per unit, must fit the merge's kTopkMergeMax;
+// otherwise S = 0 selects the single-workgroup kernel.
+constexpr int kTopkSliceMax = 8192;
+constexpr int kTopkMergeMax = 16384;
+int topk_slice(int max_len, int k);
+
 struct Workspace {
-  TopkScratch tk;
   Partials part;
   float* cs;  // [B][Hq][nchunk][kCsStride]
+  uint64_t* tkc;  // [U][top-k candidate slots] (composite keys)
   int nsplit;
   int nchunk;
   size_t bytes;  // total bytes this step needs
@@ -111,7 +106,6 @@ struct Workspace {
 // tokens: a multiple of 4 waves * 32 tokens, sized for about kScanWorkgroups.
 int split_tokens(int units, int max_len);
 int num_splits(int units, int max_len);
-int topk_slice(int units, int max_len);
 // Offsets of the regions for a step (ws may be null to size only).  With
 // bound = true the split and chunk counts are upper bounds valid for every
 // step whose longest sequence is at most max_len.
@@ -124,7 +118,7 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 hipStream_t s);
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
-                       int32_t* idx, const TopkScratch& tk, hipStream_t s);
+                       int32_t* idx, uint64_t* cand, hipStream_t s);
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
                           float* out, hipStream_t s);

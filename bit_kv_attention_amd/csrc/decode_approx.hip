@@ -285,8 +285,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc, uint32_t* __restrict__ tk_hist,
-    uint32_t* __restrict__ tk_ctrl, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk) {
+    float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -307,14 +306,6 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
   const uint32_t* kmeta = k_meta + (size_t)u * kGroups * cap;
   const uint32_t* vmeta = v_meta + (size_t)u * kGroups * cap;
-
-  // The top-k selection that follows in the step accumulates into a per-unit
-  // histogram and control words: clear them here (nothing else touches them
-  // while this kernel runs).
-  if (split == 0) {
-    for (int i = tid; i < kHistBins; i += 256) tk_hist[(size_t)u * kHistBins + i] = 0u;
-    if (tid < kCtrlWords) tk_ctrl[(size_t)u * kCtrlWords + tid] = 0u;
-  }
 
   // ---- query operands, staged through LDS ------------------------------------
   __shared__ uint16_t s_q[G][kHeadDim];
@@ -502,7 +493,7 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
   (void)hipGetLastError();  // report only this launch's status
   decode_approx_kernel<KB, VB, G><<<grid, 256, 0, s>>>(
       static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
-      c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, w.tk.hist, w.tk.ctrl, len, L.n_q_heads,
+      c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
       L.n_kv_heads, L.capacity, w.nsplit, chunk);
   return hipGetLastError();
 }

@@ -3,389 +3,414 @@
 // (JetFire README, introduction: only the top-k tokens get the high-precision
 // correction; Jet-QSparse abstract: the budget is per KV head.)
 //
-// Scores map to order-preserving 32-bit keys.  Two launches, each spread over
-// `nslice` workgroups per unit so that the whole GPU reads the scores (the
-// unit's histogram and control words were cleared by the scan that wrote the
-// scores, earlier in the same step):
-//   pass 1 histogram of the top 12 key bits (LDS per slice, then global
-//          atomics); the last workgroup to finish finds the 12-bit digit d1
-//          that holds the k-th largest key and the count above it;
-//   pass 2 every slice writes a bitmap of the tokens whose digit is > d1 and
-//          appends the tokens whose digit is == d1 (the candidates) to a list;
-//          the last workgroup resolves the candidates exactly (a radix select
-//          over the remaining 20 bits, then the lowest indices among the keys
-//          equal to the k-th), sets their bits, and turns the bitmap into the
-//          sorted index list.  If the candidates overflow the list (degenerate
-//          score distributions) the last workgroup re-reads the unit's scores
-//          for the remaining radix passes.
+// One workgroup of 1024 threads per unit; nothing leaves the workgroup until
+// the answer is known, so there is no cross-workgroup protocol at all.
+//
+// Every token gets the composite key c(t) = (ordered bits of sigma_t) << 32 |
+// ~t: larger c means a larger score, or an equal score and a lower index, and
+// no two tokens share a c.  The selected set is {t : c(t) >= T} with T the
+// kk-th largest composite, found by a radix select, most significant digit
+// first (digit widths 12, 10, 10 over the score bits, 11, 11, 10 over the
+// index bits):
+//   a pass histograms the next digit of the entries that match the prefix so
+//   far (LDS atomics), and the digit holding the kk-th largest is appended to
+//   the prefix.  The first passes read the scores from memory; as soon as the
+//   prefix matches at most kCandMax tokens those are copied into LDS and the
+//   remaining passes run there.  It stops when every entry under the prefix
+//   is needed; T is then the smallest composite with that prefix.
+// Last, c(t) >= T becomes ascending indices: each wave owns a contiguous run
+// of the tokens, counts its selected ones with ballots, a prefix sum over the
+// 16 wave counts places the runs, and a second pass writes them in order.
 #include "bkv_internal.h"
 
 namespace bkv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
+constexpr int kCandMax = 4096;
+constexpr int kLevels = 6;
+constexpr int kBatch = 16;  // scores per thread loaded together (independent loads in flight)
+__constant__ const int kDigitBits[kLevels] = {12, 10, 10, 11, 11, 10};
 
-// Cross-workgroup data of one launch moves only through agent-scope atomics,
-// which are performed at the device's coherence point: no cache maintenance
-// (a device-wide fence writes back and invalidates the L2 of every XCD) is
-// needed.  A workgroup publishes by finishing all its memory operations
-// (s_waitcnt 0 in every wave, then a barrier) before its arrival atomic.
-__device__ inline uint32_t ld_dev(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_dev64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_dev(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void st_dev64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Every memory operation this wave issued has completed.
-__device__ inline void wait_mem() { __builtin_amdgcn_s_waitcnt(0); }
-
-// Arrival at a per-unit counter after publishing; true in the last of `count`.
-__device__ inline bool arrive_last(uint32_t* counter, uint32_t count, int* s_flag) {
-  wait_mem();
-  __syncthreads();
-  if (threadIdx.x == 0) *s_flag = (atomicAdd(counter, 1u) == count - 1);
-  __syncthreads();
-  return *s_flag != 0;
+__device__ inline uint64_t composite(float s, int t) {
+  return ((uint64_t)float_key(s) << 32) | (uint64_t)(~(uint32_t)t);
 }
 
-// Exclusive prefix sum over the workgroup; `total` gets the sum of all.
-__device__ inline int block_excl_scan(int v, int* s_tmp, int& total) {
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+// Exclusive prefix sum over a workgroup of NW waves (wave shuffles, then the
+// wave totals through LDS); `total` gets the sum of all.
+template <int NW>
+__device__ inline int block_excl_scan(int v, int* s_wsum, int& total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) s_tmp[wv] = x;
   __syncthreads();
-  int before = 0, tot = 0;
+  if (lane == 63) s_wsum[wv] = x;
+  __syncthreads();
+  int before = 0;
+  total = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = s_tmp[w];
-    before += (w < wv) ? c : 0;
-    tot += c;
+  for (int w = 0; w < NW; ++w) {
+    const int s = s_wsum[w];
+    before += (w < wv) ? s : 0;
+    total += s;
   }
-  __syncthreads();
-  total = tot;
   return before + x - v;
 }
 
-// Given an LDS histogram of nb bins, find the digit d holding the need-th
-// largest element (counting from the top): count(digit > d) < need <=
-// count(digit >= d).  Returns d and, through `above`, count(digit > d).
-__device__ inline int find_digit(const uint32_t* hist, int nb, int need, int* s_tmp, int* s_res, int& above) {
-  const int per = nb / kThreads;
-  if (threadIdx.x == 0) {
-    s_res[0] = 0;
-    s_res[1] = 0;
-  }
-  int mine = 0;
-  for (int j = 0; j < per; ++j) mine += (int)hist[nb - 1 - (threadIdx.x * per + j)];
-  int total;
-  const int before = block_excl_scan(mine, s_tmp, total);  // also orders the s_res reset
-  if (before < need && before + mine >= need) {
-    int run = before;
-    for (int j = 0; j < per; ++j) {
-      const int d = nb - 1 - (threadIdx.x * per + j);
-      const int c = (int)hist[d];
-      if (run + c >= need) {
-        s_res[0] = d;
-        s_res[1] = run;
-        break;
-      }
-      run += c;
-    }
-  }
-  __syncthreads();
-  above = s_res[1];
-  const int d = s_res[0];
-  __syncthreads();
-  return d;
-}
-
-__global__ __launch_bounds__(kThreads) void topk_pass1_kernel(const float* __restrict__ sigma, TopkScratch tk,
-                                                              SeqArg lens, int Hkv, int cap, int k, int slice) {
-  const int u = blockIdx.y;
-  const int n = lens.v[u / Hkv];
-  const int kk = min(k, n);
-  const int t_lo = blockIdx.x * slice;
-  const int t_hi = min(n, t_lo + slice);
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int s_tmp[kWaves];
-  __shared__ int s_res[2];
-  __shared__ int s_last;
-  const bool work = kk > 0 && kk < n;  // otherwise the selection is trivial
-  if (work) {
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads) s_hist[i] = 0;
+// The need-th largest of `count` composites that LDS holds (get(i) gives
+// entry i; entries equal to 0 are empty slots and never selected), by the
+// radix select described above, entirely in LDS.  Returns T with exactly
+// `need` entries >= T.  NT threads.
+template <int NT, typename Get>
+__device__ uint64_t lds_threshold(Get get, int count, int need, uint32_t* s_hist, int* s_wsum, int* s_res) {
+  const int tid = threadIdx.x;
+  uint64_t P = 0;
+  int plen = 0;
+  for (int lv = 0; lv < kLevels; ++lv) {
+    const int d = kDigitBits[lv];
+    const int nb = 1 << d;
+    const int shift = 64 - plen - d;
+    for (int i = tid; i < nb; i += NT) s_hist[i] = 0u;
     __syncthreads();
-    const float* sg = sigma + (size_t)u * cap;
-    for (int base = t_lo; base < t_hi; base += 8 * kThreads) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = base + j * kThreads + threadIdx.x;
-        v[j] = (t < t_hi) ? sg[t] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = base + j * kThreads + threadIdx.x;
-        if (t < t_hi) atomicAdd(&s_hist[float_key(v[j]) >> 20], 1u);
-      }
+    for (int i = tid; i < count; i += NT) {
+      const uint64_t c = get(i);
+      if (plen == 0 || (c >> (64 - plen)) == P) atomicAdd(&s_hist[(uint32_t)(c >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    uint32_t* gh = tk.hist + (size_t)u * kHistBins;
-    for (int i = threadIdx.x; i < kHistBins; i += kThreads)
-      if (s_hist[i]) atomicAdd(&gh[i], s_hist[i]);
-  }
-  uint32_t* ctrl = tk.ctrl + (size_t)u * kCtrlWords;
-  if (!arrive_last(&ctrl[kCtlArrive1], gridDim.x, &s_last) || !work) return;
-  const uint32_t* gh = tk.hist + (size_t)u * kHistBins;
-  {
-    uint32_t v[kHistBins / kThreads];
-#pragma unroll
-    for (int j = 0; j < kHistBins / kThreads; ++j) v[j] = ld_dev(&gh[j * kThreads + threadIdx.x]);
-#pragma unroll
-    for (int j = 0; j < kHistBins / kThreads; ++j) s_hist[j * kThreads + threadIdx.x] = v[j];
-  }
-  __syncthreads();
-  int above;
-  const int d1 = find_digit(s_hist, kHistBins, kk, s_tmp, s_res, above);
-  if (threadIdx.x == 0) {
-    st_dev(&ctrl[kCtlDigit1], (uint32_t)d1);
-    st_dev(&ctrl[kCtlAbove1], (uint32_t)above);
-  }
-}
-
-// The last workgroup's exact resolution of the threshold bucket.  On return
-// every selected candidate's bit is set in the unit's bitmap (global).
-__device__ void resolve_candidates(const float* __restrict__ sg, uint32_t* __restrict__ bm, const uint32_t* ctrl,
-                                   const uint64_t* __restrict__ cand, int n, int kk, uint32_t* s_key,
-                                   uint32_t* s_idx, uint32_t* s_hist, int* s_tmp, int* s_res) {
-  const uint32_t d1 = ld_dev(&ctrl[kCtlDigit1]);
-  const int need1 = kk - (int)ld_dev(&ctrl[kCtlAbove1]);
-  const int cc = (int)ld_dev(&ctrl[kCtlCandCount]);
-  const bool in_lds = cc <= kCandCap;
-  if (in_lds) {
-    for (int i0 = 0; i0 < cc; i0 += 4 * kThreads) {
-      uint64_t e[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + j * kThreads + threadIdx.x;
-        e[j] = i < cc ? ld_dev64(&cand[i]) : 0ull;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + j * kThreads + threadIdx.x;
-        if (i < cc) {
-          s_key[i] = (uint32_t)(e[j] >> 32);
-          s_idx[i] = (uint32_t)e[j];
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // two more radix digits (bits 19..10 and 9..0) among the bucket's keys
-  uint32_t prefix = d1 << 20, pmask = 0xFFF00000u;
-  int need = need1;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 10 : 0;
-    for (int i = threadIdx.x; i < 1024; i += kThreads) s_hist[i] = 0;
-    __syncthreads();
-    if (in_lds) {
-      for (int i = threadIdx.x; i < cc; i += kThreads)
-        if ((s_key[i] & pmask) == prefix) atomicAdd(&s_hist[(s_key[i] >> shift) & 1023u], 1u);
-    } else {
-      for (int t = threadIdx.x; t < n; t += kThreads) {
-        const uint32_t key = float_key(sg[t]);
-        if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 1023u], 1u);
-      }
-    }
-    __syncthreads();
-    int above;
-    const int d = find_digit(s_hist, 1024, need, s_tmp, s_res, above);
-    need -= above;
-    prefix |= (uint32_t)d << shift;
-    pmask |= 1023u << shift;
-  }
-  const uint32_t T = prefix;  // the k-th largest key; `need` keys equal to T are taken
-  int te = 0;
-  {
+    const int per = nb / NT;
+    const int top = nb - 1 - tid * per;
     int mine = 0;
-    if (in_lds) {
-      for (int i = threadIdx.x; i < cc; i += kThreads) mine += (s_key[i] == T);
-    } else {
-      for (int t = threadIdx.x; t < n; t += kThreads) mine += (float_key(sg[t]) == T);
-    }
-    block_excl_scan(mine, s_tmp, te);
-  }
-  // Among the keys equal to T the `need` lowest indices are taken: a radix
-  // select of the need-th largest ~index (11 + 11 + 10 bits).
-  uint32_t tie_lim = 0xFFFFFFFFu;  // ties with index <= tie_lim are taken
-  if (te > need) {
-    uint32_t tp = 0, tm = 0;
-    int nd = need;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const int nb = pass == 2 ? 1024 : 2048;
-      for (int i = threadIdx.x; i < nb; i += kThreads) s_hist[i] = 0;
-      __syncthreads();
-      if (in_lds) {
-        for (int i = threadIdx.x; i < cc; i += kThreads)
-          if (s_key[i] == T) {
-            const uint32_t r = ~s_idx[i];
-            if ((r & tm) == tp) atomicAdd(&s_hist[(r >> shift) & (uint32_t)(nb - 1)], 1u);
-          }
-      } else {
-        for (int t = threadIdx.x; t < n; t += kThreads)
-          if (float_key(sg[t]) == T) {
-            const uint32_t r = ~(uint32_t)t;
-            if ((r & tm) == tp) atomicAdd(&s_hist[(r >> shift) & (uint32_t)(nb - 1)], 1u);
-          }
+    for (int i = 0; i < per; ++i) mine += (int)s_hist[top - i];
+    int total;
+    int above = block_excl_scan<NT / 64>(mine, s_wsum, total);
+    if (above < need && above + mine >= need) {
+      for (int i = 0; i < per; ++i) {
+        const int h = (int)s_hist[top - i];
+        if (above + h >= need) {
+          s_res[0] = top - i;
+          s_res[1] = above;
+          break;
+        }
+        above += h;
       }
-      __syncthreads();
-      int above;
-      const int d = find_digit(s_hist, nb, nd, s_tmp, s_res, above);
-      nd -= above;
-      tp |= (uint32_t)d << shift;
-      tm |= (uint32_t)(nb - 1) << shift;
     }
-    tie_lim = ~tp;
+    __syncthreads();
+    const int D = s_res[0];
+    need -= s_res[1];
+    P = (P << d) | (uint64_t)D;
+    plen += d;
+    const int m = (int)s_hist[D];
+    __syncthreads();
+    if (m == need) break;
   }
-  if (in_lds) {
-    for (int i = threadIdx.x; i < cc; i += kThreads) {
-      const uint32_t key = s_key[i], t = s_idx[i];
-      if (key > T || (key == T && t <= tie_lim)) atomicOr(&bm[t >> 5], 1u << (t & 31));
-    }
-  } else {
-    for (int t = threadIdx.x; t < n; t += kThreads) {
-      const uint32_t key = float_key(sg[t]);
-      if ((key >> 20) == d1 && (key > T || (key == T && (uint32_t)t <= tie_lim)))
-        atomicOr(&bm[t >> 5], 1u << (t & 31));
-    }
-  }
-  wait_mem();
-  __syncthreads();
+  return (plen >= 64) ? P : (P << (64 - plen));
 }
 
-__global__ __launch_bounds__(kThreads) void topk_pass2_kernel(const float* __restrict__ sigma, TopkScratch tk,
-                                                              int32_t* __restrict__ idx, SeqArg lens, int Hkv,
-                                                              int cap, int k, int slice) {
-  const int u = blockIdx.y;
-  const int n = lens.v[u / Hkv];
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ sigma, int32_t* __restrict__ idx,
+                                                        SeqArg lens, int Hkv, int cap, int k) {
+  const int u = blockIdx.x;
+  const int b = u / Hkv;
+  const int n = lens.v[b];
   const int kk = min(k, n);
-  const int t_lo = blockIdx.x * slice;
-  const int t_hi = min(n, t_lo + slice);
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const float* sg = sigma + (size_t)u * cap;
-  uint32_t* ctrl = tk.ctrl + (size_t)u * kCtrlWords;
-  uint32_t* bm = tk.bitmap + (size_t)u * (cap / 32);
-  uint64_t* cand = tk.cand + (size_t)u * kCandCap;
-  const bool resolve = kk > 0 && kk < n;
-  const uint32_t d1 = resolve ? ctrl[kCtlDigit1] : 0u;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const float* __restrict__ sg = sigma + (size_t)u * cap;
+  int32_t* __restrict__ out = idx + (size_t)u * k;
 
-  // bitmap words of this slice (slices are multiples of 1024 tokens)
-  for (int base0 = t_lo; base0 < t_hi; base0 += 8 * kThreads) {
-    float v[8];
+  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
+  if (kk == n) {  // every token (or none) is selected
+    for (int i = tid; i < n; i += kThreads) out[i] = i;
+    return;
+  }
+
+  __shared__ uint32_t s_hist[1 << 12];
+  __shared__ uint64_t s_cand[kCandMax];
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_ncand;
+  __shared__ int s_digit, s_above;
+
+  uint64_t P = 0;  // prefix of T, plen bits
+  int plen = 0;
+  int need = kk;   // entries still to take under the prefix
+  bool in_lds = false;
+  int ncand = 0;
+
+  for (int lv = 0; lv < kLevels; ++lv) {
+    const int d = kDigitBits[lv];
+    const int nb = 1 << d;
+    const int shift = 64 - plen - d;
+    for (int i = tid; i < nb; i += kThreads) s_hist[i] = 0u;
+    __syncthreads();
+    auto count = [&](uint64_t c) {
+      if (plen == 0 || (c >> (64 - plen)) == P) atomicAdd(&s_hist[(uint32_t)(c >> shift) & (nb - 1)], 1u);
+    };
+    if (in_lds) {
+      for (int i = tid; i < ncand; i += kThreads) count(s_cand[i]);
+    } else {
+      for (int t0 = 0; t0 < n; t0 += kBatch * kThreads) {
+        float v[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = base0 + j * kThreads + threadIdx.x;
-      v[j] = (resolve && t < t_hi) ? sg[t] : 0.f;
+        for (int i = 0; i < kBatch; ++i) {
+          const int t = t0 + i * kThreads + tid;
+          v[i] = sg[min(t, n - 1)];  // clamped: every load unconditional
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int t = t0 + i * kThreads + tid;
+          if (t < n) count(composite(v[i], t));
+        }
+      }
     }
+    __syncthreads();
+    // the digit D with  sum_{x > D} hist[x] < need <= sum_{x >= D} hist[x]:
+    // thread j owns the bins from nb-1-j*per downwards, per = nb / 1024
+    const int per = nb / kThreads;
+    const int top = nb - 1 - tid * per;
+    int mine = 0;
+    for (int i = 0; i < per; ++i) mine += (int)s_hist[top - i];
+    int total;
+    int above = block_excl_scan<kWaves>(mine, s_wsum, total);  // count in the bins above this thread's
+    if (above < need && above + mine >= need) {
+      for (int i = 0; i < per; ++i) {
+        const int h = (int)s_hist[top - i];
+        if (above + h >= need) {
+          s_digit = top - i;
+          s_above = above;
+          break;
+        }
+        above += h;
+      }
+    }
+    __syncthreads();
+    const int D = s_digit;
+    need -= s_above;
+    P = (P << d) | (uint64_t)D;
+    plen += d;
+    const int m = (int)s_hist[D];
+    __syncthreads();  // everyone has read s_digit, s_above and s_hist
+    if (m == need) break;
+    if (!in_lds && m <= kCandMax) {
+      // copy the tokens under the prefix into LDS (one LDS atomic per wave)
+      if (tid == 0) s_ncand = 0;
+      __syncthreads();
+      for (int t0 = 0; t0 < n; t0 += kBatch * kThreads) {
+        float v[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int base = base0 + j * kThreads;
-      if (base >= t_hi) break;  // uniform
-      const int t = base + threadIdx.x;
-      bool bit = false;
-      if (t < t_hi) {
-        if (kk == n) {
-          bit = true;
-        } else if (resolve) {
-          const uint32_t key = float_key(v[j]);
-          bit = (key >> 20) > d1;
-          if ((key >> 20) == d1) {
-            // wave-aggregated append to the candidate list
-            const uint64_t m = __ballot(true);
-            const int nlead = __popcll(m & ((1ull << lane) - 1));
-            uint32_t slot0 = 0;
-            if (nlead == 0) slot0 = atomicAdd(&ctrl[kCtlCandCount], (uint32_t)__popcll(m));
-            slot0 = __shfl(slot0, __ffsll((unsigned long long)m) - 1);
-            const uint32_t slot = slot0 + nlead;
-            if (slot < (uint32_t)kCandCap) st_dev64(&cand[slot], ((uint64_t)key << 32) | (uint32_t)t);
+        for (int i = 0; i < kBatch; ++i) {
+          const int t = t0 + i * kThreads + tid;
+          v[i] = sg[min(t, n - 1)];  // clamped: every load unconditional
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+          const int t = t0 + i * kThreads + tid;
+          uint64_t c = 0;
+          bool hit = false;
+          if (t < n) {
+            c = composite(v[i], t);
+            hit = (c >> (64 - plen)) == P;
+          }
+          const uint64_t mask = __ballot(hit);
+          if (mask) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&s_ncand, __popcll(mask));
+            base = __shfl(base, 0);
+            if (hit) s_cand[base + __popcll(mask & ((1ull << lane) - 1))] = c;
           }
         }
       }
-      const uint64_t word = __ballot(bit);
-      const int w0 = (base + wv * 64) >> 5;
-      if (lane == 0 && base + wv * 64 < t_hi) st_dev(&bm[w0], (uint32_t)word);
-      if (lane == 0 && base + wv * 64 + 32 < t_hi) st_dev(&bm[w0 + 1], (uint32_t)(word >> 32));
+      __syncthreads();
+      in_lds = true;
+      ncand = m;
     }
   }
-  __shared__ int s_last;
-  if (!arrive_last(&ctrl[kCtlArrive2], gridDim.x, &s_last)) return;
+  const uint64_t T = (plen >= 64) ? P : (P << (64 - plen));
 
-  __shared__ uint32_t s_key[kCandCap];
-  __shared__ uint32_t s_idx[kCandCap];
-  __shared__ uint32_t s_hist[kHistBins];
-  __shared__ int s_tmp[kWaves];
-  __shared__ int s_res[2];
-  if (resolve) resolve_candidates(sg, bm, ctrl, cand, n, kk, s_key, s_idx, s_hist, s_tmp, s_res);
-
-  // bitmap -> ascending index list: thread j owns words [j*per, j*per+per)
-  int32_t* out = idx + (size_t)u * k;
-  const int nw = (n + 31) / 32;
-  const int per = (nw + kThreads - 1) / kThreads;
-  const int w_lo = threadIdx.x * per;
+  // ascending indices of {t : c(t) >= T}: wave w owns the contiguous range
+  // [w*R, w*R + R) of 64-token blocks; it counts its selected tokens (ballot
+  // popcounts), one prefix sum over the 16 wave counts places the ranges, and
+  // the wave writes its tokens in order in a second pass.
+  const int wv = tid >> 6;
+  const int nblk = (n + 63) / 64;
+  const int R = (nblk + kWaves - 1) / kWaves;  // blocks per wave
+  const int b_lo = wv * R, b_hi = min(nblk, b_lo + R);
+  auto sel_mask = [&](int blk, float v) -> uint64_t {
+    const int t = blk * 64 + lane;
+    return __ballot(t < n && composite(v, t) >= T);
+  };
   int mine = 0;
-  for (int w0 = 0; w0 < per; w0 += 8) {
-    uint32_t b8[8];
+  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+    float v[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b8[j] = (w0 + j < per && w_lo + w0 + j < nw) ? ld_dev(&bm[w_lo + w0 + j]) : 0u;
+    for (int i = 0; i < kBatch; ++i) {
+      const int t = (b0 + i) * 64 + lane;
+      v[i] = sg[min(t, n - 1)];
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mine += __popc(b8[j]);
+    for (int i = 0; i < kBatch; ++i)
+      if (b0 + i < b_hi) mine += __popcll(sel_mask(b0 + i, v[i]));
   }
   int total;
-  int pos = block_excl_scan(mine, s_tmp, total);
-  for (int w = w_lo; w < min(nw, w_lo + per); ++w) {
-    uint32_t bits = ld_dev(&bm[w]);
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (pos < kk) out[pos] = w * 32 + b;
-      ++pos;
+  int pos = __shfl(block_excl_scan<kWaves>(lane == 0 ? mine : 0, s_wsum, total), 0);
+  for (int b0 = b_lo; b0 < b_hi; b0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int t = (b0 + i) * 64 + lane;
+      v[i] = sg[min(t, n - 1)];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (b0 + i < b_hi) {
+        const uint64_t mask = sel_mask(b0 + i, v[i]);
+        if ((mask >> lane) & 1ull) out[pos + __popcll(mask & ((1ull << lane) - 1))] = (b0 + i) * 64 + lane;
+        pos += __popcll(mask);
+      }
     }
   }
-  for (int i = kk + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+}
+
+// ---- two-kernel path: slice-local top-k, then the merge ----------------------
+// Local: workgroup (slice s, unit) keeps the scores of tokens [s*S, s*S + S)
+// (S = kTopkSliceMax) in LDS, finds the exact top min(kk, slice length) of the slice and writes
+// their composites in index order to cand[u][s*k + j].  Every token of the
+// unit's top-kk is in its slice's top-kk, so the union holds the answer.
+// Merge: one workgroup per unit loads the nslice*k candidate slots into LDS
+// (empty slots as 0), finds the kk-th largest composite T there and writes
+// the candidates >= T in slot order, which is ascending token order.
+constexpr int kLocalThreads = 1024;
+constexpr int kLocalMax = kTopkSliceMax;   // slice tokens in LDS
+constexpr int kMergeMax = kTopkMergeMax;   // candidate slots in LDS per unit
+
+__global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(const float* __restrict__ sigma,
+                                                                   uint64_t* __restrict__ cand, SeqArg lens, int Hkv,
+                                                                   int cap, int k, int S, int cstride) {
+  const int s = blockIdx.x, u = blockIdx.y;
+  const int n = lens.v[u / Hkv];
+  const int kk = min(k, n);
+  const int t0 = s * S;
+  const int len = min(S, n - t0);
+  if (kk == n || len <= 0) return;  // nothing to choose / empty slice
+  const int cnt = min(kk, len);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ float s_v[kLocalMax];
+  __shared__ uint32_t s_hist[1 << 12];
+  __shared__ int s_wsum[kLocalThreads / 64];
+  __shared__ int s_res[2];
+  const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
+  for (int i0 = 0; i0 < len; i0 += kBatch * kLocalThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kLocalThreads + tid;
+      v[j] = sg[min(i, len - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j * kLocalThreads + tid;
+      if (i < len) s_v[i] = v[j];
+    }
+  }
+  __syncthreads();
+  auto get = [&](int i) { return composite(s_v[i], t0 + i); };
+  const uint64_t T = (cnt == len) ? 0 : lds_threshold<kLocalThreads>(get, len, cnt, s_hist, s_wsum, s_res);
+  // write the slice's top entries in index order (per-wave runs of 64-token
+  // blocks, as in the single-workgroup kernel)
+  const int nblk = (len + 63) / 64;
+  const int R = (nblk + kLocalThreads / 64 - 1) / (kLocalThreads / 64);
+  const int b_lo = wv * R, b_hi = min(nblk, b_lo + R);
+  int mine = 0;
+  for (int bk = b_lo; bk < b_hi; ++bk) {
+    const int i = bk * 64 + lane;
+    mine += __popcll(__ballot(i < len && get(i) >= T));
+  }
+  int total;
+  int pos = __shfl(block_excl_scan<kLocalThreads / 64>(lane == 0 ? mine : 0, s_wsum, total), 0);
+  uint64_t* __restrict__ dst = cand + (size_t)u * cstride + (size_t)s * k;
+  for (int bk = b_lo; bk < b_hi; ++bk) {
+    const int i = bk * 64 + lane;
+    const uint64_t c = i < len ? get(i) : 0;
+    const uint64_t mask = __ballot(i < len && c >= T);
+    if ((mask >> lane) & 1ull) dst[pos + __popcll(mask & ((1ull << lane) - 1))] = c;
+    pos += __popcll(mask);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ cand,
+                                                              int32_t* __restrict__ idx, SeqArg lens, int Hkv,
+                                                              int k, int S, int cstride) {
+  const int u = blockIdx.x;
+  const int n = lens.v[u / Hkv];
+  const int kk = min(k, n);
+  const int tid = threadIdx.x;
+  int32_t* __restrict__ out = idx + (size_t)u * k;
+  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
+  if (kk == n) {
+    for (int i = tid; i < n; i += kThreads) out[i] = i;
+    return;
+  }
+  const int ns = (n + S - 1) / S;  // slices holding tokens
+  const int slots = ns * k;
+  __shared__ uint64_t s_c[kMergeMax];
+  __shared__ uint32_t s_hist[1 << 12];
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_res[2];
+  const uint64_t* __restrict__ src = cand + (size_t)u * cstride;
+  for (int p0 = 0; p0 < slots; p0 += kBatch * kThreads) {
+    uint64_t v[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {  // clamped, unconditional loads first
+      const int p = p0 + j * kThreads + tid;
+      const int pc = min(p, slots - 1);
+      const int s = pc / k, jj = pc - s * k;
+      const int cnt = min(kk, min(S, n - s * S));
+      ok[j] = p < slots && jj < cnt;
+      v[j] = src[s * k + min(jj, cnt - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = ok[j] ? v[j] : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int p = p0 + j * kThreads + tid;
+      if (p < slots) s_c[p] = v[j];
+    }
+  }
+  __syncthreads();
+  auto get = [&](int i) { return s_c[i]; };
+  const uint64_t T = lds_threshold<kThreads>(get, slots, kk, s_hist, s_wsum, s_res);
+  // slots in order: thread j owns the contiguous slots [j*per, j*per + per)
+  const int per = (slots + kThreads - 1) / kThreads;
+  const int p_lo = tid * per, p_hi = min(slots, p_lo + per);
+  int mine = 0;
+  for (int p = p_lo; p < p_hi; ++p) mine += (s_c[p] >= T) ? 1 : 0;
+  int total;
+  int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
+  for (int p = p_lo; p < p_hi; ++p) {
+    const uint64_t c = s_c[p];
+    if (c >= T) out[pos++] = (int32_t)~(uint32_t)(c & 0xFFFFFFFFu);
+  }
 }
 
 }  // namespace
 
-int topk_slice(int units, int max_len) {
-  // slices of whole 1024-token blocks, about 512 workgroups in all
-  long long per = ((long long)units * (max_len > 0 ? max_len : 1) + 511) / 512;
-  per = ((per + 1023) / 1024) * 1024;
-  return per < 1024 ? 1024 : (int)per;
-}
-
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
-                       int32_t* idx, const TopkScratch& tk, hipStream_t s) {
+                       int32_t* idx, uint64_t* cand, hipStream_t s) {
   const int units = L.batch * L.n_kv_heads;
-  const int slice = topk_slice(units, max_len);
-  const int nslice = max(1, (max_len + slice - 1) / slice);
+  const int S = topk_slice(max_len, k);
   (void)hipGetLastError();  // report only this call's launches
-  topk_pass1_kernel<<<dim3(nslice, units), kThreads, 0, s>>>(sigma, tk, len, L.n_kv_heads, L.capacity, k, slice);
-  topk_pass2_kernel<<<dim3(nslice, units), kThreads, 0, s>>>(sigma, tk, idx, len, L.n_kv_heads, L.capacity, k,
-                                                             slice);
+  if (S == 0) {
+    topk_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, k);
+  } else {
+    const int ns = (max_len + S - 1) / S;
+    topk_local_kernel<<<dim3(ns > 0 ? ns : 1, units), kLocalThreads, 0, s>>>(sigma, cand, len, L.n_kv_heads,
+                                                                           L.capacity, k, S, ns * k);
+    topk_merge_kernel<<<units, kThreads, 0, s>>>(cand, idx, len, L.n_kv_heads, k, S, ns * k);
+  }
   return hipGetLastError();
 }
 
