@@ -49,25 +49,33 @@ struct Online {
 
 constexpr int kRecBatch = 16;
 
-// Merge of `cnt` records j: max m[j*sm], denominator l[j*sl], value v[j*sv]
-// (each load independent of the others, kRecBatch at a time).
-__device__ inline void merge_records(Online& st, const float* __restrict__ m, const float* __restrict__ l,
-                                     const float* __restrict__ v, size_t sm, size_t sv, int cnt) {
-  for (int j0 = 0; j0 < cnt; j0 += kRecBatch) {
-    float mm[kRecBatch], ll[kRecBatch], vv[kRecBatch];
+// Records j0..j0+kRecBatch-1 of a set (max m[j*sm], denominator l[j*sm],
+// value v[j*sv]); past cnt they are empty.  Loads are clamped and
+// unconditional so that a whole batch is in flight at once.
+struct RecBatch {
+  float m[kRecBatch], l[kRecBatch], v[kRecBatch];
+  __device__ void load(const float* __restrict__ pm_, const float* __restrict__ pl_, const float* __restrict__ pv,
+                       size_t sm, size_t sv, int cnt, int j0) {
 #pragma unroll
-    for (int i = 0; i < kRecBatch; ++i) {  // unconditional (clamped) loads, then select
-      const bool ok = j0 + i < cnt;
-      const size_t j = (size_t)min(j0 + i, cnt - 1);
-      const float a = m[j * sm], b = l[j * sm], x = v[j * sv];
-      mm[i] = ok ? a : -INFINITY;
-      ll[i] = ok ? b : 0.f;
-      vv[i] = ok ? x : 0.f;
+    for (int i = 0; i < kRecBatch; ++i) {
+      const size_t j = (size_t)max(min(j0 + i, cnt - 1), 0);
+      m[i] = pm_[j * sm];
+      l[i] = pl_[j * sm];
+      v[i] = pv[j * sv];
     }
 #pragma unroll
-    for (int i = 0; i < kRecBatch; ++i) st.add(mm[i], ll[i], vv[i]);
+    for (int i = 0; i < kRecBatch; ++i) {
+      const bool ok = j0 + i < cnt;
+      m[i] = ok ? m[i] : -INFINITY;
+      l[i] = ok ? l[i] : 0.f;
+      v[i] = ok ? v[i] : 0.f;
+    }
   }
-}
+  __device__ void into(Online& st) const {
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) st.add(m[i], l[i], v[i]);
+  }
+};
 
 // One workgroup per (b, query head), one thread per channel.
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
@@ -85,20 +93,29 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   const int kk = min(k, n);
   const int nc = (kk + kCorrChunk - 1) / kCorrChunk;
   const float* ps = cs + rec * (size_t)nchunk * kCsStride;
-  Online ex;  // exact state of the selected tokens
-  merge_records(ex, ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nc);
+  // exact state of the selected tokens, approximate state of every token and
+  // approximate terms of the selected tokens; a batch's loads of all three
+  // are issued before any is used
+  const int nap = (kk < n) ? nsplit : 0;  // every token selected: the scan state is not needed
+  const int nsel = (kk < n) ? nc : 0;
+  Online ex, ap, sel;
+  for (int j0 = 0; j0 < max(nc, nap); j0 += kRecBatch) {
+    RecBatch be, ba, bs;
+    be.load(ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nc, j0);
+    ba.load(pm + rec * nsplit, pl + rec * nsplit, pacc + rec * nsplit * kHeadDim + c, 1, kHeadDim, nap, j0);
+    bs.load(ps + 2, ps + 3, ps + 4 + kHeadDim + c, kCsStride, kCsStride, nsel, j0);
+    be.into(ex);
+    ba.into(ap);
+    bs.into(sel);
+  }
   if (kk == n) {
     o[c] = ex.a / ex.l;
     return;
   }
-  Online ap;  // approximate state of every token
-  merge_records(ap, pm + rec * nsplit, pl + rec * nsplit, pacc + rec * nsplit * kHeadDim + c, 1, kHeadDim, nsplit);
   if (kk == 0) {
     o[c] = ap.a / ap.l;
     return;
   }
-  Online sel;  // approximate terms of the selected tokens
-  merge_records(sel, ps + 2, ps + 3, ps + 4 + kHeadDim + c, kCsStride, kCsStride, nc);
   const float M = ap.m;
   const float fs = sel.scale_to(M);
   const float A = ap.a - fs * sel.a, L = fmaxf(ap.l - fs * sel.l, 0.f);
