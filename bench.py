@@ -125,17 +125,27 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Timed region: the steps, with events on the library's stream (torch's
+    # current stream) around every scan launch for the roofline figure.
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record()
     for i in range(args.steps):
-        step(i)
+        cache = caches[i % copies]
+        bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
+        sev[i][0].record()
+        bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws)
+        sev[i][1].record()
+        bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws)
+        bk.qattn_correct(lay, cache, q, lens, st.idx, w.k, st.ws, st.out)
     e1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1) / args.steps
+    scan_us_timed = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in sev]))
 
-    # Per-kernel averages: the same steps again with events around each call.
+    # Per-call breakdown: the same steps again with events around each call.
     names = ("kv_pack_append", "qattn_decode_approx", "topk_select", "qattn_correct")
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(args.steps)]
@@ -158,8 +168,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     # packed codes + meta of K and V for every token of every unit, the fp32
     # selection score written per token, and the split partial states written.
     scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L)
-    scan_s = kus["qattn_decode_approx"] / 1e6
+    scan_s = scan_us_timed / 1e6
     achieved = scan_bytes / scan_s / 1e9
+    traffic = measured_traffic(w.name)
     res = {
         "metric": "decode attention tokens/s + packed-KV HBM GB/s (% of peak), 32K & 128K ctx",
         "value": round(tokens_per_s, 1),
@@ -183,13 +194,42 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "wall_s_timed_region": round(t_wall, 3),
         "roofline": {"kernel": "qattn_decode_approx", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": scan_bytes},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
+                     "kernel_us_per_launch": round(scan_us_timed, 2)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, inp, knew, vnew, args.cpu_threads)
     del caches
     torch.cuda.empty_cache()
     return res
+
+
+SCAN_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_kv_attention_amd", "csrc",
+                           "decode_approx.hip")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the scan kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE per dispatch, each scaled by what the same
+    counter reads for a plain copy of known size), or None when there is no
+    summary for this workload or the kernel source has changed since the
+    counters were taken."""
+    import hashlib
+    path = os.path.join(PROFILES, f"decode_approx_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    with open(SCAN_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if vals.get("source_sha256") != sha or "hbm_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["hbm_bytes_per_launch"]))
 
 
 def cpu_baseline(w, inp, knew, vnew, threads):
