@@ -65,6 +65,7 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
     off = align256(off + bytes);
     return p;
   };
+  w.tkctr = reinterpret_cast<uint32_t*>(take((size_t)units * 4));
   const size_t recs = (size_t)L.batch * L.n_q_heads * w.nsplit;
   w.part.acc = reinterpret_cast<float*>(take(recs * kHeadDim * 4));
   w.part.m = reinterpret_cast<float*>(take(recs * 4));
@@ -205,7 +206,7 @@ bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* l
   if (k == 0) return BKV_OK;
   const Workspace w = workspace_layout(ws, *L, max_len, k, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_topk(*L, sigma, len, max_len, k, idx, w.tkc, (hipStream_t)stream) == hipSuccess ? BKV_OK
+  return launch_topk(*L, sigma, len, max_len, k, idx, w.tkc, w.tkctr, (hipStream_t)stream) == hipSuccess ? BKV_OK
                                                                                                : BKV_E_HIP;
 }
 

@@ -69,8 +69,9 @@ __device__ inline uint32_t float_key(float f) {
 }
 
 // ---- workspace ------------------------------------------------------------
-// One buffer: the split partial states of the scan, the states of the
-// correction chunks and the top-k candidate slots.  The
+// One buffer: the top-k arrival counters (zero-filled once by the caller,
+// left at zero by every call), the split partial states of the scan, the
+// states of the correction chunks and the top-k candidate slots.  The
 // region sizes depend on the step's longest length and k, so every call of a
 // step recomputes the same offsets from the same (lens, k).
 
@@ -97,6 +98,7 @@ struct Workspace {
   Partials part;
   float* cs;  // [B][Hq][nchunk][kCsStride]
   uint64_t* tkc;  // [U][top-k candidate slots] (composite keys)
+  uint32_t* tkctr;  // [U] arrivals of the top-k slice workgroups (zero between calls)
   int nsplit;
   int nchunk;
   size_t bytes;  // total bytes this step needs
@@ -118,7 +120,7 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 hipStream_t s);
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
-                       int32_t* idx, uint64_t* cand, hipStream_t s);
+                       int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
                           float* out, hipStream_t s);

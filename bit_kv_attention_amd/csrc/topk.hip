@@ -195,132 +195,170 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   }
 }
 
-// ---- two-kernel path: slice-local top-k, then the merge ----------------------
-// Local: workgroup (slice s, unit) keeps the scores of tokens [s*S, s*S + S)
-// (S = kTopkSliceMax) in LDS, finds the exact top min(kk, slice length) of the slice and writes
-// their composites in index order to cand[u][s*k + j].  Every token of the
-// unit's top-kk is in its slice's top-kk, so the union holds the answer.
-// Merge: one workgroup per unit loads the nslice*k candidate slots into LDS
-// (empty slots as 0), finds the kk-th largest composite T there and writes
-// the candidates >= T in slot order, which is ascending token order.
-constexpr int kLocalThreads = 1024;
+// ---- slice-local top-k, then the merge by the unit's last workgroup ---------
+// Workgroup (slice s, unit) keeps the scores of tokens [s*S, s*S + S)
+// (S = kTopkSliceMax) in LDS, finds the exact top min(kk, slice length) of the
+// slice and writes their composites in index order to cand[u][s*k + j].
+// Every token of the unit's top-kk is in its slice's top-kk, so the union
+// holds the answer.  Then it arrives at the unit's counter; the last of the
+// unit's workgroups loads the nslice*k candidate slots into LDS (empty slots
+// as 0), finds the kk-th largest composite T there and writes the candidates
+// >= T in slot order, which is ascending token order, then clears the counter.
+// Candidates cross workgroups through agent-scope atomic stores and loads,
+// which the device performs at its coherence point (no cache maintenance);
+// a workgroup has finished all its memory operations before it arrives.
+constexpr int kLocalThreads = kThreads;
 constexpr int kLocalMax = kTopkSliceMax;   // slice tokens in LDS
 constexpr int kMergeMax = kTopkMergeMax;   // candidate slots in LDS per unit
 
-__global__ __launch_bounds__(kLocalThreads) void topk_local_kernel(const float* __restrict__ sigma,
-                                                                   uint64_t* __restrict__ cand, SeqArg lens, int Hkv,
-                                                                   int cap, int k, int S, int cstride) {
+__device__ inline void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merge of one unit's candidate slots (see above); all kThreads threads.
+// AGENT: the slots were written by other workgroups of this launch.
+template <bool AGENT>
+__device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int k, int S,
+                           uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res) {
+  const int tid = threadIdx.x;
+  const int kk = min(k, n);
+  int32_t* __restrict__ out = idx + (size_t)u * k;
+  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
+  if (kk == n) {  // every token (or none) is selected
+    for (int i = tid; i < n; i += kThreads) out[i] = i;
+  } else {
+    const int ns = (n + S - 1) / S;  // slices holding tokens
+    const int slots = ns * k;
+    for (int p0 = 0; p0 < slots; p0 += kBatch * kThreads) {
+      uint64_t v[kBatch];
+      bool ok[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {  // clamped, unconditional loads first
+        const int p = p0 + j * kThreads + tid;
+        const int pc = min(p, slots - 1);
+        const int sl = pc / k, jj = pc - sl * k;
+        const int cnt = min(kk, min(S, n - sl * S));
+        ok[j] = p < slots && jj < cnt;
+        const uint64_t* src = &ucand[sl * k + min(jj, cnt - 1)];
+        v[j] = AGENT ? ld_dev64(src) : *src;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int p = p0 + j * kThreads + tid;
+        if (p < slots) s_c[p] = ok[j] ? v[j] : 0;
+      }
+    }
+    __syncthreads();
+    auto get = [&](int i) { return s_c[i]; };
+    const uint64_t T = lds_threshold<kThreads>(get, slots, kk, s_hist, s_wsum, s_res);
+    // slots in order: thread j owns the contiguous slots [j*per, j*per + per)
+    const int per = (slots + kThreads - 1) / kThreads;
+    const int p_lo = tid * per, p_hi = min(slots, p_lo + per);
+    int mine = 0;
+    for (int p = p_lo; p < p_hi; ++p) mine += (s_c[p] >= T) ? 1 : 0;
+    int total;
+    int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
+    for (int p = p_lo; p < p_hi; ++p) {
+      const uint64_t c = s_c[p];
+      if (c >= T) out[pos++] = (int32_t)~(uint32_t)(c & 0xFFFFFFFFu);
+    }
+  }
+}
+
+template <bool FUSED>
+__global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float* __restrict__ sigma,
+                                                                    uint64_t* __restrict__ cand,
+                                                                    uint32_t* __restrict__ counter,
+                                                                    int32_t* __restrict__ idx, SeqArg lens, int Hkv,
+                                                                    int cap, int k, int S, int cstride) {
+  __shared__ __attribute__((aligned(16))) float s_v[kLocalMax];  // the slice's scores; then (fused) the slots
+  __shared__ uint32_t s_hist[1 << 12];
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_res[2];
+  __shared__ int s_last;
   const int s = blockIdx.x, u = blockIdx.y;
   const int n = lens.v[u / Hkv];
   const int kk = min(k, n);
   const int t0 = s * S;
   const int len = min(S, n - t0);
-  if (kk == n || len <= 0) return;  // nothing to choose / empty slice
-  const int cnt = min(kk, len);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  __shared__ float s_v[kLocalMax];
-  __shared__ uint32_t s_hist[1 << 12];
-  __shared__ int s_wsum[kLocalThreads / 64];
-  __shared__ int s_res[2];
-  const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
-  for (int i0 = 0; i0 < len; i0 += kBatch * kLocalThreads) {
-    float v[kBatch];
+  uint64_t* __restrict__ ucand = cand + (size_t)u * cstride;
+
+  if (kk < n && len > 0) {  // a slice with tokens to choose from
+    const int cnt = min(kk, len);
+    const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
+    for (int i0 = 0; i0 < len; i0 += kBatch * kLocalThreads) {
+      float v[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = i0 + j * kLocalThreads + tid;
-      v[j] = sg[min(i, len - 1)];
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kLocalThreads + tid;
+        v[j] = sg[min(i, len - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = i0 + j * kLocalThreads + tid;
+        if (i < len) s_v[i] = v[j];
+      }
     }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = i0 + j * kLocalThreads + tid;
-      if (i < len) s_v[i] = v[j];
+    __syncthreads();
+    auto get = [&](int i) { return composite(s_v[i], t0 + i); };
+    const uint64_t T = (cnt == len) ? 0 : lds_threshold<kLocalThreads>(get, len, cnt, s_hist, s_wsum, s_res);
+    // the slice's top entries in index order (per-wave runs of 64-token blocks)
+    const int nblk = (len + 63) / 64;
+    const int R = (nblk + kWaves - 1) / kWaves;
+    const int b_lo = wv * R, b_hi = min(nblk, b_lo + R);
+    int mine = 0;
+    for (int bk = b_lo; bk < b_hi; ++bk) {
+      const int i = bk * 64 + lane;
+      mine += __popcll(__ballot(i < len && get(i) >= T));
+    }
+    int total;
+    int pos = __shfl(block_excl_scan<kWaves>(lane == 0 ? mine : 0, s_wsum, total), 0);
+    uint64_t* __restrict__ dst = ucand + (size_t)s * k;
+    for (int bk = b_lo; bk < b_hi; ++bk) {
+      const int i = bk * 64 + lane;
+      const uint64_t c = i < len ? get(i) : 0;
+      const uint64_t mask = __ballot(i < len && c >= T);
+      if ((mask >> lane) & 1ull) {
+        uint64_t* p = &dst[pos + __popcll(mask & ((1ull << lane) - 1))];
+        if (FUSED) st_dev64(p, c); else *p = c;
+      }
+      pos += __popcll(mask);
     }
   }
+
+  if (!FUSED) return;
+  // ---- arrival; the unit's last workgroup merges ------------------------------
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's candidates are written
   __syncthreads();
-  auto get = [&](int i) { return composite(s_v[i], t0 + i); };
-  const uint64_t T = (cnt == len) ? 0 : lds_threshold<kLocalThreads>(get, len, cnt, s_hist, s_wsum, s_res);
-  // write the slice's top entries in index order (per-wave runs of 64-token
-  // blocks, as in the single-workgroup kernel)
-  const int nblk = (len + 63) / 64;
-  const int R = (nblk + kLocalThreads / 64 - 1) / (kLocalThreads / 64);
-  const int b_lo = wv * R, b_hi = min(nblk, b_lo + R);
-  int mine = 0;
-  for (int bk = b_lo; bk < b_hi; ++bk) {
-    const int i = bk * 64 + lane;
-    mine += __popcll(__ballot(i < len && get(i) >= T));
-  }
-  int total;
-  int pos = __shfl(block_excl_scan<kLocalThreads / 64>(lane == 0 ? mine : 0, s_wsum, total), 0);
-  uint64_t* __restrict__ dst = cand + (size_t)u * cstride + (size_t)s * k;
-  for (int bk = b_lo; bk < b_hi; ++bk) {
-    const int i = bk * 64 + lane;
-    const uint64_t c = i < len ? get(i) : 0;
-    const uint64_t mask = __ballot(i < len && c >= T);
-    if ((mask >> lane) & 1ull) dst[pos + __popcll(mask & ((1ull << lane) - 1))] = c;
-    pos += __popcll(mask);
-  }
+  if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  merge_unit<true>(ucand, idx, u, n, k, S, reinterpret_cast<uint64_t*>(s_v), s_hist, s_wsum, s_res);
+  if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
 }
 
+// The merge as a launch of its own (candidate slots beyond the slice stage's
+// LDS footprint): one workgroup per unit.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ cand,
-                                                              int32_t* __restrict__ idx, SeqArg lens, int Hkv,
-                                                              int k, int S, int cstride) {
-  const int u = blockIdx.x;
-  const int n = lens.v[u / Hkv];
-  const int kk = min(k, n);
-  const int tid = threadIdx.x;
-  int32_t* __restrict__ out = idx + (size_t)u * k;
-  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
-  if (kk == n) {
-    for (int i = tid; i < n; i += kThreads) out[i] = i;
-    return;
-  }
-  const int ns = (n + S - 1) / S;  // slices holding tokens
-  const int slots = ns * k;
+                                                              int32_t* __restrict__ idx, SeqArg lens, int Hkv, int k,
+                                                              int S, int cstride) {
   __shared__ uint64_t s_c[kMergeMax];
   __shared__ uint32_t s_hist[1 << 12];
   __shared__ int s_wsum[kWaves];
   __shared__ int s_res[2];
-  const uint64_t* __restrict__ src = cand + (size_t)u * cstride;
-  for (int p0 = 0; p0 < slots; p0 += kBatch * kThreads) {
-    uint64_t v[kBatch];
-    bool ok[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {  // clamped, unconditional loads first
-      const int p = p0 + j * kThreads + tid;
-      const int pc = min(p, slots - 1);
-      const int s = pc / k, jj = pc - s * k;
-      const int cnt = min(kk, min(S, n - s * S));
-      ok[j] = p < slots && jj < cnt;
-      v[j] = src[s * k + min(jj, cnt - 1)];
-    }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) v[j] = ok[j] ? v[j] : 0;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int p = p0 + j * kThreads + tid;
-      if (p < slots) s_c[p] = v[j];
-    }
-  }
-  __syncthreads();
-  auto get = [&](int i) { return s_c[i]; };
-  const uint64_t T = lds_threshold<kThreads>(get, slots, kk, s_hist, s_wsum, s_res);
-  // slots in order: thread j owns the contiguous slots [j*per, j*per + per)
-  const int per = (slots + kThreads - 1) / kThreads;
-  const int p_lo = tid * per, p_hi = min(slots, p_lo + per);
-  int mine = 0;
-  for (int p = p_lo; p < p_hi; ++p) mine += (s_c[p] >= T) ? 1 : 0;
-  int total;
-  int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
-  for (int p = p_lo; p < p_hi; ++p) {
-    const uint64_t c = s_c[p];
-    if (c >= T) out[pos++] = (int32_t)~(uint32_t)(c & 0xFFFFFFFFu);
-  }
+  const int u = blockIdx.x;
+  merge_unit<false>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv], k, S, s_c, s_hist, s_wsum, s_res);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
-                       int32_t* idx, uint64_t* cand, hipStream_t s) {
+                       int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s) {
   const int units = L.batch * L.n_kv_heads;
   const int S = topk_slice(max_len, k);
   (void)hipGetLastError();  // report only this call's launches
@@ -328,9 +366,16 @@ hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& le
     topk_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, k);
   } else {
     const int ns = (max_len + S - 1) / S;
-    topk_local_kernel<<<dim3(ns > 0 ? ns : 1, units), kLocalThreads, 0, s>>>(sigma, cand, len, L.n_kv_heads,
-                                                                           L.capacity, k, S, ns * k);
-    topk_merge_kernel<<<units, kThreads, 0, s>>>(cand, idx, len, L.n_kv_heads, k, S, ns * k);
+    const int slots = ns * k;
+    const dim3 grid(ns > 0 ? ns : 1, units);
+    if ((size_t)slots * 8 <= (size_t)kLocalMax * 4) {  // the merge fits the slice stage's LDS: fused
+      topk_slices_kernel<true><<<grid, kLocalThreads, 0, s>>>(sigma, cand, counter, idx, len, L.n_kv_heads,
+                                                              L.capacity, k, S, slots);
+    } else {
+      topk_slices_kernel<false><<<grid, kLocalThreads, 0, s>>>(sigma, cand, counter, idx, len, L.n_kv_heads,
+                                                               L.capacity, k, S, slots);
+      topk_merge_kernel<<<units, kThreads, 0, s>>>(cand, idx, len, L.n_kv_heads, k, S, slots);
+    }
   }
   return hipGetLastError();
 }

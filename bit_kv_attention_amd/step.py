@@ -15,7 +15,8 @@ class DecodeStep:
         L = layout
         self.sigma = torch.empty(L.batch * L.n_kv_heads * L.capacity, dtype=torch.float32, device=device)
         ws_bytes = bk.bkv_workspace_bytes(L, max_len, self.k)
-        self.ws = torch.empty(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
+        # zero-filled once: the calls keep their arrival counters in it at zero
+        self.ws = torch.zeros(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
         self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.k, 1), dtype=torch.int32, device=device)
         self.out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32, device=device)
 

@@ -115,9 +115,11 @@ bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
 /* Workspace bytes that cover qattn_decode_approx, topk_select and
  * qattn_correct for every step whose longest sequence has at most max_len
  * tokens and whose top-k budget is k.  Host only.  One workspace serves the
- * three calls of a step (the scan's split states, the top-k scratch and the
- * correction's chunk states live in it); it needs no initialisation.  Calls
- * that may run concurrently (on different streams) need separate workspaces. */
+ * three calls of a step (the scan's split states, the top-k candidates and
+ * arrival counters and the correction's chunk states live in it).  Zero-fill
+ * it once after allocating it; every call leaves the counters at zero again.
+ * Calls that may run concurrently (on different streams) need separate
+ * workspaces. */
 bkv_status bkv_workspace_bytes(const bkv_layout* layout, int32_t max_len,
                                int32_t k, size_t* bytes);
 

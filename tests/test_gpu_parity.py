@@ -207,3 +207,35 @@ def test_step_parity_multi_slice(P, kb, vb, G):
     orc_s = pair["oc"].decode(pair["q"], lens, 40, sel=r["idx"])
     P.assert_close(r["out"], orc_s["out"], "out vs oracle(S_gpu)")
     P.assert_close(r["out"], orc["out"], "out vs oracle(S_oracle)")
+
+
+@pytest.mark.parametrize("L,k", [(32768, 256), (20000, 3000), (40000, 4000), (9000, 1)])
+def test_topk_paths_on_given_scores(P, L, k):
+    """topk_select on given scores with many exact ties, ragged lengths and two
+    calls in a row on one workspace: the fused slice+merge launch (few
+    candidate slots), the separate merge launch (many) and the
+    single-workgroup kernel (too many for the merge), against the oracle's
+    full sort."""
+    banner(f"top-k paths L={L} k={k}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    B, Hkv = 2, 2
+    cap = ((L + 31) // 32) * 32
+    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, 4, 4)
+    rng = np.random.default_rng(L + k)
+    sig = (np.round(rng.standard_normal((B, Hkv, cap)) * 64) / 64).astype(np.float32)  # many ties
+    sig[:, :, ::97] = 3.5  # a tied block above the rest
+    lens = [L, L // 3 + 5]
+    st = DecodeStep(lay, k, L)
+    st.sigma.copy_(torch.from_numpy(sig.reshape(-1)))
+    for rep in range(2):
+        st.idx.fill_(-7)
+        bk.topk_select(lay, st.sigma, lens, k, st.idx, st.ws)
+        torch.cuda.synchronize()
+        idx = st.idx.cpu().numpy().reshape(B, Hkv, k)
+        for b in range(B):
+            for h in range(Hkv):
+                want = oracle.topk(sig[b, h, :lens[b]].astype(np.float64), k)
+                assert np.array_equal(idx[b, h], want), (rep, b, h)
