@@ -7,15 +7,17 @@
 //   z = min x,  s = fp16((max - min) / (2^b - 1))   [fp32 subtract, IEEE divide]
 //   code = clamp(rint((x - z) / s), 0, 2^b - 1)     [stored fp16 s and z; 0 if s == 0]
 // then the codes go into the packed layouts, (s, z) into the meta planes and
-// the fp16 row verbatim into the shadow.  Min/max run sequentially over the
-// group in channel order (same tie behaviour for +-0 as a plain loop).
+// the fp16 row verbatim into the shadow.
 //
-// One workgroup per (32-token tile, unit): thread (token r, K/V, group)
-// quantises one group and leaves its codes in LDS; then one thread per key
-// chunk (one token's codes of one eighth of every group) writes that chunk
-// whole, and value words, which mix 8 tokens, are assembled with a
-// read-modify-write of the tile's words (tokens outside the append keep
-// their bits).
+// One workgroup per (32-token tile, unit).  Four lanes share one group of
+// one token (8 channels each): partial min/max per lane, merged across the
+// four lanes with ties resolved toward the lower channels, so the result --
+// including the sign of a zero minimum -- is that of one sequential pass in
+// channel order.  A lane's 8 key codes are exactly one group's share of one
+// key chunk (4*KB bytes: its eighth of each of the 4 groups), so keys go
+// straight to HBM.  Value dwords mix 8 tokens and are rebuilt from codes in
+// LDS with a read-modify-write (slots of tokens outside the append keep
+// their bits); their loads are issued before the quantiser runs.
 #include "bkv_internal.h"
 
 // The codec must match a plain IEEE evaluation operation for operation.
@@ -30,116 +32,117 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     uint32_t* __restrict__ v_meta, uint16_t* __restrict__ k_shadow, uint16_t* __restrict__ v_shadow,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n_new, SeqArg pos,
     int Hkv, int cap) {
-  const int u = blockIdx.y;
+  const int u = __builtin_amdgcn_workgroup_id_y();
   const int b = u / Hkv;
   const int p0 = pos.v[b];
-  const int tile = p0 / kTile + blockIdx.x;
-  const int t_lo = max(p0, tile * kTile);
-  const int t_hi = min(p0 + n_new, tile * kTile + kTile);
+  const int tile = p0 / kTile + (int)__builtin_amdgcn_workgroup_id_x();
+  const int t0 = tile * kTile;
+  const int t_lo = max(p0, t0);
+  const int t_hi = min(p0 + n_new, t0 + kTile);
   if (t_lo >= t_hi) return;
+  const int tid = __builtin_amdgcn_workitem_id_x();
 
-  __shared__ uint8_t s_code[2][kTile][kHeadDim];  // [K/V][token][channel]
-  const int tid = threadIdx.x;
-  const int r = tid >> 3;
-  const int kv = (tid >> 2) & 1;
-  const int grp = tid & 3;
-  const int t = tile * kTile + r;
-  if (t >= t_lo && t < t_hi) {
-    const int bits = kv ? VB : KB;
-    const uint16_t* src = (kv ? v_new : k_new) + ((size_t)u * n_new + (t - p0)) * kHeadDim + grp * kGroup;
-    uint16_t x[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 8) {
-      const uint4 w = *reinterpret_cast<const uint4*>(src + i);
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[i + 2 * j] = (uint16_t)(ww[j] & 0xFFFFu);
-        x[i + 2 * j + 1] = (uint16_t)(ww[j] >> 16);
-      }
-    }
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      const float v = (float)__builtin_bit_cast(_Float16, x[i]);
-      if (v < mn) mn = v;
-      if (v > mx) mx = v;
-    }
-    const float qmax = (float)((1 << bits) - 1);
-    const float s32 = (mx - mn) / qmax;
-    const _Float16 s16 = (_Float16)s32;
-    const _Float16 z16 = (_Float16)mn;
-    const float s = (float)s16, z = (float)z16;
-    uint8_t code[kGroup];
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) {
-      int cd = 0;
-      if (s != 0.0f) {
-        const float v = (float)__builtin_bit_cast(_Float16, x[i]);
-        const float rr = __builtin_rintf((v - z) / s);
-        cd = rr < 0.0f ? 0 : (rr > qmax ? (int)qmax : (int)rr);
-      }
-      code[i] = (uint8_t)cd;
-    }
-    const uint32_t meta = (uint32_t)__builtin_bit_cast(uint16_t, s16) |
-                          ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
-    (kv ? v_meta : k_meta)[((size_t)u * kGroups + grp) * cap + t] = meta;
-    uint16_t* dst = (kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + grp * kGroup;
-#pragma unroll
-    for (int i = 0; i < kGroup; i += 8)
-      *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
-#pragma unroll
-    for (int i = 0; i < kGroup; ++i) s_code[kv][r][grp * kGroup + i] = code[i];
-  }
-  __syncthreads();
-  // key chunks: chunk (eighth e, token r) of the 16-token block holds the
-  // codes of channels 32g + 8e + j, packed in the order (g, j) at KB bits
-  // each -- 4*KB bytes, written whole by one thread.
-  if (tid < 4 * kTile) {
-    const int rr = tid & (kTile - 1), e = tid >> 5;
-    const int tt = tile * kTile + rr;
-    if (tt >= t_lo && tt < t_hi) {
-      uint32_t w[KB];
-#pragma unroll
-      for (int j = 0; j < KB; ++j) w[j] = 0;
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        const uint32_t cd = s_code[0][rr][32 * (m >> 3) + 8 * e + (m & 7)];
-        const int bp = m * KB;
-        w[bp >> 5] |= cd << (bp & 31);
-        if ((bp & 31) + KB > 32) w[(bp >> 5) + 1] |= cd >> (32 - (bp & 31));
-      }
-      uint32_t* chunk = reinterpret_cast<uint32_t*>(
-          k_codes + (size_t)u * k_unit_bytes(KB, cap) + (size_t)(tt / kKBlock) * k_block_bytes(KB) +
-          (size_t)(e * kKBlock + (tt % kKBlock)) * k_chunk_bytes(KB));
-#pragma unroll
-      for (int j = 0; j < KB; ++j) chunk[j] = w[j];
-    }
-  }
-  // value dwords: dword w of the tile belongs to lane l = (w/4) mod 64 as its
-  // dword d = 4(w/256) + w mod 4, i.e. columns n = d*cpd + s (s < cpd) of
-  // quarter l/16; only the slots of appended tokens are replaced
+  // value dwords this thread rebuilds: dword w of the tile is dword
+  // d = 4(w/256) + w mod 4 of lane l = (w/4) mod 64, which holds the slots of
+  // tokens 4q..4q+3 and 16+4q..16+4q+3 (q = l/16) for 4/VB columns
+  constexpr int kWords = kHeadDim * VB / 256;  // per thread
   constexpr int kCpd = 4 / VB;
   uint32_t* vt = reinterpret_cast<uint32_t*>(v_codes + (size_t)u * v_unit_bytes(VB, cap) +
                                              (size_t)tile * v_tile_bytes(VB));
-  for (int w = tid; w < kHeadDim * VB; w += 256) {
+  uint32_t word[kWords];
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) word[i] = vt[tid + 256 * i];
+
+  __shared__ uint8_t s_vcode[kTile][kHeadDim];  // value codes [token][channel]
+  const int sub = tid & 3, grp = (tid >> 2) & 3, kv = (tid >> 4) & 1;
+  const int c0 = grp * kGroup + sub * 8;  // first channel of this lane
+  const float qmax = (float)((1 << (kv ? VB : KB)) - 1);
+  for (int r = (t_lo - t0) & ~7; r < t_hi - t0; r += 8) {
+    const int t = t0 + r + (tid >> 5);
+    if (t < t_lo || t >= t_hi) continue;
+    const uint16_t* src = (kv ? v_new : k_new) + ((size_t)u * n_new + (t - p0)) * kHeadDim + c0;
+    const uint4 w4 = *reinterpret_cast<const uint4*>(src);
+    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] & 0xFFFFu));
+      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] >> 16));
+    }
+    float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (x[j] < mn) mn = x[j];
+      if (x[j] > mx) mx = x[j];
+    }
+    // merge with the neighbouring lanes, lower channels first on ties
+#pragma unroll
+    for (int m = 1; m < 4; m <<= 1) {
+      const float omn = __shfl_xor(mn, m), omx = __shfl_xor(mx, m);
+      const bool hi = (sub & m) != 0;  // partner holds the lower channels
+      const float lmn = hi ? omn : mn, umn = hi ? mn : omn;
+      const float lmx = hi ? omx : mx, umx = hi ? mx : omx;
+      mn = (umn < lmn) ? umn : lmn;
+      mx = (umx > lmx) ? umx : lmx;
+    }
+    const _Float16 s16 = (_Float16)((mx - mn) / qmax);
+    const _Float16 z16 = (_Float16)mn;
+    const float s = (float)s16, z = (float)z16;
+    uint32_t code[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int cd = 0;
+      if (s != 0.0f) {
+        const float rr = __builtin_rintf((x[j] - z) / s);
+        cd = rr < 0.0f ? 0 : (rr > qmax ? (int)qmax : (int)rr);
+      }
+      code[j] = (uint32_t)cd;
+    }
+    if (sub == 0)
+      (kv ? v_meta : k_meta)[((size_t)u * kGroups + grp) * cap + t] =
+          (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+    *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + c0) = w4;
+    if (kv == 0) {
+      // chunk (eighth sub) of token t: codes (g, j) at bit KB(8g + j), so this
+      // group's 8 codes fill bytes KB*grp .. KB*grp + KB - 1
+      uint32_t f = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f |= code[j] << (KB * j);
+      uint8_t* chunk = k_codes + (size_t)u * k_unit_bytes(KB, cap) + k_chunk_offset(KB, t, sub) + KB * grp;
+      if (KB == 4) {
+        *reinterpret_cast<uint32_t*>(chunk) = f;
+      } else {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) chunk[i] = (uint8_t)(f >> (8 * i));
+      }
+    } else {
+      uint2 cw;
+      cw.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+      cw.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+      *reinterpret_cast<uint2*>(&s_vcode[r + (tid >> 5)][c0]) = cw;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kWords; ++i) {
+    const int w = tid + 256 * i;
     const int l = (w >> 2) & 63, d = 4 * (w >> 8) + (w & 3), qq = l >> 4;
-    uint32_t word = vt[w];
+    bool touched = false;
 #pragma unroll
-    for (int sub = 0; sub < kCpd; ++sub) {
-      const int c = 16 * (d * kCpd + sub) + (l & 15);
+    for (int j = 0; j < 8; ++j) {
+      const int rr = (j < 4) ? (4 * qq + j) : (16 + 4 * qq + (j - 4));
+      const int tt = t0 + rr;
+      if (tt < t_lo || tt >= t_hi) continue;
+      touched = true;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int rr = (j < 4) ? (4 * qq + j) : (16 + 4 * qq + (j - 4));
-        const int tt = tile * kTile + rr;
-        if (tt >= t_lo && tt < t_hi) {
-          const int bit = 16 * (j >> 2) + 4 * VB * sub + VB * (j & 3);
-          const uint32_t m = ((1u << VB) - 1) << bit;
-          word = (word & ~m) | ((uint32_t)s_code[1][rr][c] << bit);
-        }
+      for (int sb = 0; sb < kCpd; ++sb) {
+        const int c = 16 * (d * kCpd + sb) + (l & 15);
+        const int bit = 16 * (j >> 2) + 4 * VB * sb + VB * (j & 3);
+        const uint32_t m = ((1u << VB) - 1) << bit;
+        word[i] = (word[i] & ~m) | ((uint32_t)s_vcode[rr][c] << bit);
       }
     }
-    vt[w] = word;
+    if (touched) vt[w] = word[i];
   }
 }
 

@@ -48,6 +48,64 @@ def test_pack_bit_exact(P, kb, vb):
         assert np.array_equal(g[name], o[name]), name
 
 
+def special_rows(rng, n):
+    """fp16 rows [n, 128] whose groups hit the quantiser's edge cases:
+    constant groups (step 0), a zero minimum met as -0 before +0 and as +0
+    before -0 (the stored zero point keeps the first one's sign), the fp16
+    extremes, a range so small that the fp16 step underflows to 0, and one
+    value apart from an otherwise constant group."""
+    x = rng.standard_normal((n, 128)).astype(np.float16)
+    for t in range(n):
+        case = t % 6
+        g = (t // 6) % 4
+        sl = slice(32 * g, 32 * g + 32)
+        if case == 0:
+            x[t, sl] = np.float16(1.5)
+        elif case == 1:
+            x[t, sl] = np.abs(x[t, sl]) + np.float16(0.5)
+            x[t, 32 * g + 3] = np.float16(-0.0)
+            x[t, 32 * g + 20] = np.float16(0.0)
+        elif case == 2:
+            x[t, sl] = np.abs(x[t, sl]) + np.float16(0.5)
+            x[t, 32 * g + 9] = np.float16(0.0)
+            x[t, 32 * g + 30] = np.float16(-0.0)
+        elif case == 3:
+            x[t, 32 * g] = np.float16(65504.0)
+            x[t, 32 * g + 31] = np.float16(-65504.0)
+        elif case == 4:
+            x[t, sl] = np.float16(2.0 ** -14)
+            x[t, 32 * g + 17] = np.float16(2.0 ** -14 + 2.0 ** -24)
+        else:
+            x[t, sl] = np.float16(-3.0)
+            x[t, 32 * g + (t % 32)] = np.float16(7.25)
+    return x
+
+
+@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2)])
+def test_pack_special_values(P, kb, vb):
+    """Edge-value groups, bulk then one token at a time, bit-exact."""
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    import oracle
+    banner(f"pack special values kb={kb} vb={vb}")
+    rng = np.random.default_rng(7)
+    B, Hkv, n, cap = 2, 2, 48, 64
+    K = special_rows(rng, B * Hkv * n).reshape(B, Hkv, n, 128)
+    V = special_rows(rng, B * Hkv * n)[::-1].copy().reshape(B, Hkv, n, 128)
+    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, kb, vb)
+    gc = bk.allocate_cache(lay)
+    oc = oracle.Cache(oracle.Shape(B, 4 * Hkv, Hkv, 128, kb, vb, 32, cap))
+    steps = [(0, 40)] + [(t, t + 1) for t in range(40, n)]
+    for a, e in steps:
+        Kn, Vn = K[:, :, a:e], V[:, :, a:e]
+        bk.kv_pack_append(lay, gc, P.to_dev(Kn), P.to_dev(Vn), e - a, [a, a])
+        oc.append(Kn, Vn, np.array([a, a], np.int32))
+    torch.cuda.synchronize()
+    g, o = P.gpu_buffers(gc), P.orc_buffers(oc)
+    for name in g:
+        assert np.array_equal(g[name], o[name]), name
+
+
 @pytest.mark.parametrize("kb,vb,G", COMBOS)
 def test_step_parity_small(P, kb, vb, G):
     banner(f"step kb={kb} vb={vb} G={G}")
