@@ -27,7 +27,9 @@
 //    and B = columns (g, h) holding fp16(p * s_g,t); channel tile nt only keeps
 //    the columns of its own group.  sum p*z is accumulated on the VALU.
 //  * Key codes become exact fp16 integers (OR into 1024 + c, subtract 1024);
-//    value codes enter as fp16 subnormals (the masked bit pattern c is the
+//    pairs 1 and 3 are masked in place at bit KB, i.e. as 2^KB * c, and the
+//    query operand carries 2^-KB on those slots (one shift per two pairs).
+//    Value codes enter as fp16 subnormals (the masked bit pattern c is the
 //    value c * 2^-24), one shift and one AND per pair, no conversion.
 //  * Memory: the packed layouts put each lane's operands at byte 16*lane (key
 //    chunks: 12*lane for 3 bits) of contiguous 1 KB runs, so a wave's step is
@@ -54,45 +56,75 @@ template <int CTRL>
 __device__ inline float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
+// Max with the lane 16 (32) apart, by the gfx950 row swaps: with both operands
+// x, permlane16_swap returns (x of the even row of each row pair in both, x of
+// the odd row in both) -- i.e. own and partner values in some order (likewise
+// for the halves with permlane32_swap); no LDS round trip.
+__device__ inline float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;
 constexpr int kRowRor8 = 0x128;
 
-// y holds 4 codes of `BITS` bits in its low half and 4 in its high half; item
-// pair r of the operand is (code r, code r+4).
-//  EXACT (keys, whose scores decide the top-k): each code becomes the fp16
-//    integer c via 1024 + c (OR into 0x6400) minus 1024, both exact; the MFMA
-//    then sums the products with fp32 rounding only.
-//  otherwise (values): the masked bits are used as fp16 bit patterns directly,
-//    i.e. the subnormal c * 2^-24, which the MFMA multiplies without flushing
-//    but sums a little less precisely (about 1e-6 relative); the 2^24 is folded
-//    into the result.
-template <int BITS, bool EXACT>
-__device__ inline half8 unpack8(uint32_t y) {
-  constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : (BITS == 3) ? 0x00070007u : 0x00030003u;
+// y holds 4 codes of `BITS` bits in its low half and 4 in its high half (code
+// r + 4 at bit 16 + BITS*r); item pair r of the operand is (code r, code r+4).
+//
+// Keys, whose scores decide the top-k: each pair becomes exact fp16 integers
+// through 1024 + x (OR into 0x6400) minus 1024.  Pairs 0 and 2 are masked at
+// bit 0 (x = c); pairs 1 and 3 in place at bit BITS (x = 2^BITS * c, still
+// below 1024), so one shift serves two pairs.  The query operand carries
+// 2^-BITS on the slots of pairs 1 and 3: every product is then exactly
+// c * q, except that a query entry below 2^(BITS-14) in magnitude is rounded
+// there (to within 2^(BITS-25)).  The MFMA sums with fp32 rounding only.
+template <int BITS>
+__device__ inline half8 unpack_keys(uint32_t y) {
+  constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : 0x00070007u;
+  // gfx9 VOP3 takes no literal: with the masks in SGPRs and the bias in a
+  // VGPR each AND and OR becomes one v_and_or_b32.
+  uint32_t m0, m1, bias;
+  asm("s_mov_b32 %0, %1" : "=s"(m0) : "i"(M));
+  asm("s_mov_b32 %0, %1" : "=s"(m1) : "i"(M << BITS));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(bias));
+  const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const uint32_t t = y >> (2 * BITS);
+  const uint32_t x[4] = {(y & m0) | bias, (y & m1) | bias, (t & m0) | bias, (t & m1) | bias};
   u32x4 r;
-  if constexpr (EXACT) {
-    // gfx9 VOP3 takes no literal: with the mask in an SGPR and the bias in a
-    // VGPR the AND and OR become one v_and_or_b32.
-    uint32_t mask = M, bias;
-    asm("s_mov_b32 %0, %1" : "=s"(mask) : "i"(M));
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(bias));
-    const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t biased = ((y >> (BITS * i)) & mask) | bias;
-      r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, biased) - k1024);
-    }
-  } else {
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x[i]) - k1024);
+  return __builtin_bit_cast(half8, r);
+}
+
+// Values: every pair masked at bit 0, used as fp16 bit patterns directly,
+// i.e. the subnormals c * 2^-24, which the MFMA multiplies without flushing
+// but sums a little less precisely (about 1e-6 of the sum of |products|);
+// the 2^24 is folded into the result.
+template <int BITS>
+__device__ inline half8 unpack_values(uint32_t y) {
+  constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : 0x00030003u;
+  u32x4 r;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (y >> (BITS * i)) & M;
-  }
+  for (int i = 0; i < 4; ++i) r[i] = (y >> (BITS * i)) & M;
   return __builtin_bit_cast(half8, r);
 }
 
 __device__ inline float lo_half(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
 __device__ inline float hi_half(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// a * (fp16 low half of w) as a fused multiply-add with +0: the compiler
+// makes it one v_fma_mix (with the fp16 conversion that follows, one
+// v_fma_mixlo/mixhi_f16), rounded like the plain product; here a >= 0 and
+// the half is a scale >= 0, so the sign of a zero result cannot differ.  A
+// plain product would convert the half first and then multiply.  (Not inline
+// asm: the compiler does not check hazards inside asm, and this operand comes
+// straight from v_exp, whose result needs a wait state before use.)
+__device__ inline float mul_lo_half(float a, uint32_t w) { return fmaf(a, lo_half(w), 0.0f); }
 
 __device__ inline uint32_t pack_half2(float lo, float hi) {
   half2_t h = {(_Float16)lo, (_Float16)hi};
@@ -188,7 +220,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);
       }
       const int T = (G == 8) ? (g >> 1) : 0;
-      d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack8<KB, true>(y), bq[g], d[T][tt], 0, 0, 0);
+      d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys<KB>(y), bq[g], d[T][tt], 0, 0, 0);
     }
   }
 
@@ -232,8 +264,8 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
   // -- online softmax (log2 units) --------------------------------------------
   float mloc = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
                      fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  mloc = max_xor16(mloc);
+  mloc = max_xor32(mloc);
   const float m_new = fmaxf(ws.m_run, mloc);
   if (__ballot(m_new != ws.m_run)) {  // rare after the first steps
     const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
@@ -267,7 +299,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         m1 = (t0 + 16 + 4 * kb + r) < len ? m1 : 0u;
       }
       ws.z_part[T] = fmaf(p[0][r], hi_half(m0), fmaf(p[1][r], hi_half(m1), ws.z_part[T]));
-      w[r] = pack_half2(p[0][r] * lo_half(m0), p[1][r] * lo_half(m1));
+      w[r] = pack_half2(mul_lo_half(p[0][r], m0), mul_lo_half(p[1][r], m1));
     }
     bp[T] = __builtin_bit_cast(half8, w);
   }
@@ -276,7 +308,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
     // column nt: V4 dword nt; V2 dword nt/2 shifted by 8 for odd nt
     const uint32_t y = (VB == 4) ? cur.vd[nt >> 2][nt & 3] : (cur.vd[0][nt >> 1] >> (8 * (nt & 1)));
     const int T = (G == 8) ? (nt >> 2) : 0;
-    ws.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack8<VB, false>(y), bp[T], ws.acc[nt], 0, 0, 0);
+    ws.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_values<VB>(y), bp[T], ws.acc[nt], 0, 0, 0);
   }
 }
 
@@ -333,9 +365,12 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     const int gq = (G == 8) ? (2 * (g >> 1) + (n >> 3)) : (n >> 2);
     half8 v;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v[2 * r] = (gq == g) ? __builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + r]) : (_Float16)0.0f;
-      v[2 * r + 1] = (gq == g) ? __builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + 4 + r]) : (_Float16)0.0f;
+    for (int r = 0; r < 4; ++r) {  // slots of pairs 1 and 3 carry 2^-KB (see unpack_keys)
+      const float sc = (r & 1) ? 1.0f / (float)(1 << KB) : 1.0f;
+      const float q0 = (float)__builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + r]);
+      const float q1 = (float)__builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + 4 + r]);
+      v[2 * r] = (gq == g) ? (_Float16)(q0 * sc) : (_Float16)0.0f;
+      v[2 * r + 1] = (gq == g) ? (_Float16)(q1 * sc) : (_Float16)0.0f;
     }
     bq[g] = v;
   }
