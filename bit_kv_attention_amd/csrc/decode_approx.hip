@@ -101,16 +101,29 @@ __device__ inline half8 unpack_keys(uint32_t y) {
   return __builtin_bit_cast(half8, r);
 }
 
-// Values: every pair masked at bit 0, used as fp16 bit patterns directly,
-// i.e. the subnormals c * 2^-24, which the MFMA multiplies without flushing
-// but sums a little less precisely (about 1e-6 of the sum of |products|);
+// Values: the masked bits are used as fp16 bit patterns directly, i.e. the
+// subnormals c * 2^(o-24) for a code masked at bit o (patterns below 0x800 are
+// linear in their value), which the MFMA multiplies without flushing but sums
+// a little less precisely (about 1e-6 of the sum of |products|).  V4: pairs 0
+// and 2 at o = 0, pairs 1 and 3 at o = 4 (one shift per two pairs); V2: pair r
+// at o = 2r (no shift).  The P operand carries 2^-o on the matching slots and
 // the 2^24 is folded into the result.
+template <int BITS>
+__device__ constexpr int value_slot_exp(int r) { return (BITS == 4) ? 4 * (r & 1) : 2 * r; }
 template <int BITS>
 __device__ inline half8 unpack_values(uint32_t y) {
   constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : 0x00030003u;
   u32x4 r;
+  if constexpr (BITS == 4) {
+    const uint32_t t = y >> 8;
+    r[0] = y & M;
+    r[1] = y & (M << 4);
+    r[2] = t & M;
+    r[3] = t & (M << 4);
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (y >> (BITS * i)) & M;
+    for (int i = 0; i < 4; ++i) r[i] = y & (M << (2 * i));
+  }
   return __builtin_bit_cast(half8, r);
 }
 
@@ -184,22 +197,25 @@ __device__ inline void wave_lds_order() {
 
 constexpr int kSigBatch = 8;  // steps of selection scores staged per wave before a store
 
-// Running softmax state of one wave (see the kernel comment).
-template <int NT>
+// Running softmax state of one wave (see the kernel comment).  ZS distinct
+// value-slot scales 2^-o: the sum p * z is kept per scale, x 2^-o.
+template <int NT, int ZS>
 struct WaveState {
-  float m_run;       // running max, log2 units (same in every lane of a head)
-  float l_part;      // this lane's share of the denominator
-  float z_part[NT];  // this lane's share of sum p * z for its column (g, h)
-  floatx4 acc[8];    // P.V accumulators (x 2^-24: codes enter as fp16 subnormals)
+  float m_run;           // running max, log2 units (same in every lane of a head)
+  float l_part;          // this lane's share of the denominator
+  float z_part[NT][ZS];  // this lane's share of sum p * z for its column (g, h)
+  floatx4 acc[8];        // P.V accumulators (x 2^-24: codes enter as fp16 subnormals)
 };
+template <int VB>
+constexpr int kZS = (VB == 4) ? 2 : 4;
 
 // One 32-token step.  MASK: the step straddles the sequence end.
 template <int KB, int VB, int G, bool MASK>
 __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
                                           const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const half8 (&bq)[kGroups],
-                                          const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT>& ws,
+                                          const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
                                           floatx4* __restrict__ sig_row, int t0, int len, int n, int kb,
-                                          float c_sig, float c_s2) {
+                                          float c_s2) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // -- scores: D[T][tt] rows = tokens 4kb+i of token tile tt, column n --------
   floatx4 d[NT][2];
@@ -243,48 +259,51 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         part += dpp<kRowRor4>(part);
         part += dpp<kRowRor8>(part);
       }
-      // selection score: max over the query heads of the group
-      float sg = part * c_sig;
+      if constexpr (MASK) part = ((t0 + 16 * tt + 4 * kb + i) < len) ? part : -INFINITY;
+      // selection score: max over the query heads of the group (the positive
+      // factor 1/sqrt(D) commutes with the max and is applied when stored)
+      float sg = part;
       sg = fmaxf(sg, dpp<kQuadXor1>(sg));
       sg = fmaxf(sg, dpp<kQuadXor2>(sg));
       if constexpr (G == 8) sg = fmaxf(sg, dpp<kRowRor4>(sg));
-      float v2 = part * c_s2;
-      if constexpr (MASK) {
-        const bool valid = (t0 + 16 * tt + 4 * kb + i) < len;
-        sg = valid ? sg : -INFINITY;
-        v2 = valid ? v2 : -INFINITY;
-      }
       sg4[i] = sg;
-      s2[tt][i] = v2;
+      s2[tt][i] = part;  // logit x sqrt(D); x c_s2 gives log2 units
     }
     if (n == 0)
       sig_row[4 * tt + kb] = (floatx4){sg4[0], sg4[1], sg4[2], sg4[3]};
   }
 
   // -- online softmax (log2 units) --------------------------------------------
+  // (max(x) * c == max(x * c) for c > 0, rounding included)
   float mloc = fmaxf(fmaxf(fmaxf(s2[0][0], s2[0][1]), fmaxf(s2[0][2], s2[0][3])),
                      fmaxf(fmaxf(s2[1][0], s2[1][1]), fmaxf(s2[1][2], s2[1][3])));
   mloc = max_xor16(mloc);
   mloc = max_xor32(mloc);
-  const float m_new = fmaxf(ws.m_run, mloc);
+  const float m_new = fmaxf(ws.m_run, mloc * c_s2);
   if (__ballot(m_new != ws.m_run)) {  // rare after the first steps
     const float alpha = __builtin_amdgcn_exp2f(ws.m_run - m_new);
     ws.l_part *= alpha;
 #pragma unroll
-    for (int T = 0; T < NT; ++T) ws.z_part[T] *= alpha;
+    for (int T = 0; T < NT; ++T)
+#pragma unroll
+      for (int e = 0; e < kZS<VB>; ++e) ws.z_part[T][e] *= alpha;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) ws.acc[nt] *= alpha;
     ws.m_run = m_new;
   }
 
+  // p[tt][r] is the weight x 2^-o of slot r's value scale (see unpack_values)
   float p[2][4];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
+  for (int i = 0; i < 4; ++i) {
+    const int o = value_slot_exp<VB>(i);
+    const float nm = -m_new - (float)o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p[tt][i] = __builtin_amdgcn_exp2f(s2[tt][i] - m_new);
-      ws.l_part += p[tt][i];
+    for (int tt = 0; tt < 2; ++tt) {
+      p[tt][i] = __builtin_amdgcn_exp2f(fmaf(s2[tt][i], c_s2, nm));
+      ws.l_part = (o == 0) ? ws.l_part + p[tt][i] : fmaf(p[tt][i], (float)(1 << o), ws.l_part);
     }
+  }
 
   // -- P.V operand: column (g, h) gets fp16(p * s_g,t); sum p*z on the VALU ---
   half8 bp[NT];
@@ -298,7 +317,8 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         m0 = (t0 + 4 * kb + r) < len ? m0 : 0u;
         m1 = (t0 + 16 + 4 * kb + r) < len ? m1 : 0u;
       }
-      ws.z_part[T] = fmaf(p[0][r], hi_half(m0), fmaf(p[1][r], hi_half(m1), ws.z_part[T]));
+      float& zr = ws.z_part[T][(VB == 4) ? (r & 1) : r];
+      zr = fmaf(p[0][r], hi_half(m0), fmaf(p[1][r], hi_half(m1), zr));
       w[r] = pack_half2(mul_lo_half(p[0][r], m0), mul_lo_half(p[1][r], m1));
     }
     bp[T] = __builtin_bit_cast(half8, w);
@@ -380,11 +400,13 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   const float c_s2 = sm * kLog2e;
   float* sig = sigma + (size_t)u * cap;
 
-  WaveState<NT> ws;
+  WaveState<NT, kZS<VB>> ws;
   ws.m_run = -INFINITY;
   ws.l_part = 0.f;
 #pragma unroll
-  for (int T = 0; T < NT; ++T) ws.z_part[T] = 0.f;
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int e = 0; e < kZS<VB>; ++e) ws.z_part[T][e] = 0.f;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) ws.acc[nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
@@ -402,7 +424,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     wave_lds_order();
     const int i = lane >> 3;
     if (i < sig_count)
-      *reinterpret_cast<floatx4*>(sig + sig_first + 4 * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7];
+      *reinterpret_cast<floatx4*>(sig + sig_first + 4 * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7] * c_sig;
     wave_lds_order();
     sig_count = 0;
   };
@@ -435,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, false>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_sig, c_s2);
+    scan_step<KB, VB, G, false>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2);
     if (++sig_count == kSigBatch) flush_sig();
   };
   // The step that straddles the end of the split (at most one per wave).
@@ -443,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, true>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_sig, c_s2);
+    scan_step<KB, VB, G, true>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2);
     ++sig_count;
   };
   Step<KB, VB, G> sa, sb;
@@ -468,10 +490,15 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   // ---- combine the 4 waves of the workgroup -----------------------------------
   ws.l_part += __shfl_xor(ws.l_part, 16);
   ws.l_part += __shfl_xor(ws.l_part, 32);
+  float z_tot[NT];
 #pragma unroll
   for (int T = 0; T < NT; ++T) {
-    ws.z_part[T] += __shfl_xor(ws.z_part[T], 16);
-    ws.z_part[T] += __shfl_xor(ws.z_part[T], 32);
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < kZS<VB>; ++e) z = fmaf(ws.z_part[T][e], (float)(1 << value_slot_exp<VB>(e)), z);
+    z += __shfl_xor(z, 16);
+    z += __shfl_xor(z, 32);
+    z_tot[T] = z;
   }
   __shared__ float s_m[4][G];
   __shared__ float s_l[4][G];
@@ -492,7 +519,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
       for (int x = 1; x < 8; ++x)
         if (x == nt) a = ws.acc[x];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s_acc[wv][h][16 * nt + 4 * kb + i] = fmaf(a[i], 0x1p24f, ws.z_part[T]);
+      for (int i = 0; i < 4; ++i) s_acc[wv][h][16 * nt + 4 * kb + i] = fmaf(a[i], 0x1p24f, z_tot[T]);
     }
   }
   __syncthreads();
