@@ -118,8 +118,10 @@ bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
  * three calls of a step (the scan's split states, the top-k candidates and
  * arrival counters and the correction's chunk states live in it).  Zero-fill
  * it once after allocating it; every call leaves the counters at zero again.
- * Calls that may run concurrently (on different streams) need separate
- * workspaces. */
+ * They sit at the start, one per (batch, KV head): zero-fill again before a
+ * call whose layout has more batch * n_kv_heads than the calls before it on
+ * this workspace.  Calls that may run concurrently (on different streams)
+ * need separate workspaces. */
 bkv_status bkv_workspace_bytes(const bkv_layout* layout, int32_t max_len,
                                int32_t k, size_t* bytes);
 
