@@ -37,18 +37,25 @@ static int max_splits(int units, int max_len) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int topk_slice(int max_len, int k) {
+int topk_slice(int units, int max_len, int k) {
   if (k <= 0) return 0;
-  const long long slots = (long long)((max_len + kTopkSliceMax - 1) / kTopkSliceMax) * k;
-  return slots <= kTopkMergeMax ? kTopkSliceMax : 0;
+  auto slots_for = [&](int S) { return (long long)((max_len + S - 1) / S) * k; };
+  if (slots_for(kTopkSliceMax) > kTopkMergeMax) return 0;
+  // halve the slices while the grid would leave compute units idle
+  int S = kTopkSliceMax;
+  while (S > kTopkSliceMin && (long long)units * ((max_len + S - 1) / S) < kTopkGridMin &&
+         slots_for(S / 2) <= kTopkMergeMax)
+    S /= 2;
+  return S;
 }
 
-// Candidate slots per unit: ceil(max_len/S)*k, at most kTopkMergeMax when the
-// two-kernel path runs -- a bound for every shorter step too (the region is
-// sized even when this max_len itself takes the single-workgroup kernel).
+// Candidate slots per unit: ceil(max_len/S)*k <= ceil(max_len/kTopkSliceMin)*k,
+// at most kTopkMergeMax when the two-kernel path runs -- a bound for every
+// shorter step too (the region is sized even when this max_len itself takes
+// the single-workgroup kernel).
 static size_t topk_slots(int max_len, int k) {
   if (k <= 0) return 0;
-  const long long a = (long long)((max_len + kTopkSliceMax - 1) / kTopkSliceMax) * k;
+  const long long a = (long long)((max_len + kTopkSliceMin - 1) / kTopkSliceMin) * k;
   return (size_t)(a < kTopkMergeMax ? a : kTopkMergeMax);
 }
 

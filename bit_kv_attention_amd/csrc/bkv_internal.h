@@ -87,12 +87,15 @@ constexpr int kCorrChunk = 32;  // selected tokens per correction workgroup
 // the approximate value sums (D each), 16-byte aligned.
 constexpr int kCsStride = 4 + 2 * kHeadDim;
 
-// Top-k: slices of S = kTopkSliceMax tokens whose local top-k candidates,
-// ceil(max_len/S)*k slots per unit, must fit the merge's kTopkMergeMax;
-// otherwise S = 0 selects the single-workgroup kernel.
+// Top-k: slices of S tokens (kTopkSliceMax, halved down to kTopkSliceMin
+// while fewer than kTopkGridMin slice workgroups would run) whose local top-k
+// candidates, ceil(max_len/S)*k slots per unit, must fit the merge's
+// kTopkMergeMax; otherwise S = 0 selects the single-workgroup kernel.
 constexpr int kTopkSliceMax = 8192;
+constexpr int kTopkSliceMin = 2048;
+constexpr int kTopkGridMin = 256;
 constexpr int kTopkMergeMax = 16384;
-int topk_slice(int max_len, int k);
+int topk_slice(int units, int max_len, int k);
 
 struct Workspace {
   Partials part;

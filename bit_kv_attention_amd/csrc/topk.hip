@@ -197,8 +197,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
 // ---- slice-local top-k, then the merge by the unit's last workgroup ---------
 // Workgroup (slice s, unit) keeps the scores of tokens [s*S, s*S + S)
-// (S = kTopkSliceMax) in LDS, finds the exact top min(kk, slice length) of the
-// slice and writes their composites in index order to cand[u][s*k + j].
+// (S <= kTopkSliceMax, chosen on the host) in LDS, finds the exact top
+// min(kk, slice length) of the slice and writes their composites in index
+// order to cand[u][s*k + j].
 // Every token of the unit's top-kk is in its slice's top-kk, so the union
 // holds the answer.  Then it arrives at the unit's counter; the last of the
 // unit's workgroups loads the nslice*k candidate slots into LDS (empty slots
@@ -360,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s) {
   const int units = L.batch * L.n_kv_heads;
-  const int S = topk_slice(max_len, k);
+  const int S = topk_slice(units, max_len, k);
   (void)hipGetLastError();  // report only this call's launches
   if (S == 0) {
     topk_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, k);
