@@ -97,3 +97,109 @@ __device__ inline uint64_t lds_threshold(Get get, int count, int need, uint32_t*
 }
 
 }  // namespace bkv
+
+namespace bkv {
+
+// Value of a float_key (-0 comes back as +0).
+__device__ inline float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+constexpr int kHistBins = 4096;
+
+// The need-th largest of the composites spread over the workgroup (thread
+// tid holds entry j*NT + tid in c[j]; 0 = empty slot; get(i) reads entry i
+// for the fallback), with few barriers: one histogram of the score values
+// over kHistBins equal bins between the smallest and largest score, which
+// is monotone in the score, so every entry of a higher bin beats every entry
+// of a lower one; the bin D holding the need-th largest is found with one
+// scan, and the entries of bin D are ranked exactly -- by one wave when at
+// most 64 (the usual case: the bins are narrow), else by the radix select
+// restricted to bin D.  s_hist: kHistBins words; s_mm: 2*NT/64 floats;
+// s_small: 65 words; s_res: 4 ints.
+template <int NT, int PER, typename Get>
+__device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int need, Get get, uint32_t* s_hist,
+                                       int* s_wsum, int* s_res, float* s_mm, uint64_t* s_small) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const float x = key_value((uint32_t)(c[j] >> 32));
+    lo = c[j] ? fminf(lo, x) : lo;
+    hi = c[j] ? fmaxf(hi, x) : hi;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = fminf(lo, __shfl_xor(lo, o));
+    hi = fmaxf(hi, __shfl_xor(hi, o));
+  }
+  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+  if (lane == 0) {
+    s_mm[wv] = lo;
+    s_mm[NW + wv] = hi;
+  }
+  if (tid == 0) s_res[2] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = fminf(lo, s_mm[w]);
+    hi = fmaxf(hi, s_mm[NW + w]);
+  }
+  // bin(x) = clamp(floor((x - lo) * scale)): monotone in x (each step is);
+  // an empty or infinite range puts everything in one bin (fmaxf drops NaN)
+  const float scale = (float)kHistBins / (hi - lo);
+  auto bin = [&](uint64_t cc) {
+    const float f = (key_value((uint32_t)(cc >> 32)) - lo) * scale;
+    return (int)fminf(fmaxf(f, 0.0f), (float)(kHistBins - 1));
+  };
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (c[j]) atomicAdd(&s_hist[bin(c[j])], 1u);
+  __syncthreads();
+  // the bin D with  sum_{x > D} hist[x] < need <= sum_{x >= D} hist[x]
+  constexpr int per = kHistBins / NT;
+  const int top = kHistBins - 1 - tid * per;
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) mine += (int)s_hist[top - i];
+  int total;
+  int above = block_excl_scan<NW>(mine, s_wsum, total);
+  if (above < need && above + mine >= need) {
+    for (int i = 0; i < per; ++i) {
+      const int h = (int)s_hist[top - i];
+      if (above + h >= need) {
+        s_res[0] = top - i;
+        s_res[1] = above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+  const int D = s_res[0];
+  const int need2 = need - s_res[1];
+  const int mD = (int)s_hist[D];
+  if (mD > 64) {  // many entries share bin D: radix select among them
+    __syncthreads();  // s_hist is reused
+    auto getD = [&](int i) {
+      const uint64_t cc = get(i);
+      return (cc && bin(cc) == D) ? cc : 0ull;
+    };
+    return lds_threshold<NT>(getD, count, need2, s_hist, s_wsum, s_res);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (c[j] && bin(c[j]) == D) s_small[atomicAdd(&s_res[2], 1)] = c[j];
+  __syncthreads();
+  if (wv == 0) {  // rank the (distinct) entries of bin D
+    const uint64_t x = lane < mD ? s_small[lane] : 0ull;
+    int rank = 0;
+    for (int i = 0; i < mD; ++i) rank += s_small[i] > x ? 1 : 0;
+    if (lane < mD && rank == need2 - 1) s_small[64] = x;
+  }
+  __syncthreads();
+  return s_small[64];
+}
+
+}  // namespace bkv

@@ -221,9 +221,11 @@ __device__ inline uint64_t ld_dev64(const uint64_t* p) {
 
 // The merge of one unit's candidate slots (see above); all kThreads threads.
 // AGENT: the slots were written by other workgroups of this launch.
-template <bool AGENT>
+// At most MAXSLOTS slots.
+template <bool AGENT, int MAXSLOTS>
 __device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int k, int S,
-                           uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res) {
+                           uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm,
+                           uint64_t* s_small) {
   const int tid = threadIdx.x;
   const int kk = min(k, n);
   int32_t* __restrict__ out = idx + (size_t)u * k;
@@ -233,28 +235,28 @@ __device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restri
   } else {
     const int ns = (n + S - 1) / S;  // slices holding tokens
     const int slots = ns * k;
-    for (int p0 = 0; p0 < slots; p0 += kBatch * kThreads) {
-      uint64_t v[kBatch];
-      bool ok[kBatch];
+    constexpr int kPer = MAXSLOTS / kThreads;
+    uint64_t v[kPer];  // slot j*kThreads + tid (0: empty)
+    bool ok[kPer];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {  // clamped, unconditional loads first
-        const int p = p0 + j * kThreads + tid;
-        const int pc = min(p, slots - 1);
-        const int sl = pc / k, jj = pc - sl * k;
-        const int cnt = min(kk, min(S, n - sl * S));
-        ok[j] = p < slots && jj < cnt;
-        const uint64_t* src = &ucand[sl * k + min(jj, cnt - 1)];
-        v[j] = AGENT ? ld_dev64(src) : *src;
-      }
+    for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first
+      const int p = j * kThreads + tid;
+      const int pc = min(p, slots - 1);
+      const int sl = pc / k, jj = pc - sl * k;
+      const int cnt = min(kk, min(S, n - sl * S));
+      ok[j] = p < slots && jj < cnt;
+      const uint64_t* src = &ucand[sl * k + min(jj, cnt - 1)];
+      v[j] = AGENT ? ld_dev64(src) : *src;
+    }
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int p = p0 + j * kThreads + tid;
-        if (p < slots) s_c[p] = ok[j] ? v[j] : 0;
-      }
+    for (int j = 0; j < kPer; ++j) {
+      const int p = j * kThreads + tid;
+      v[j] = ok[j] ? v[j] : 0;
+      if (p < slots) s_c[p] = v[j];
     }
     __syncthreads();
     auto get = [&](int i) { return s_c[i]; };
-    const uint64_t T = lds_threshold<kThreads>(get, slots, kk, s_hist, s_wsum, s_res);
+    const uint64_t T = hist_select<kThreads>(v, slots, kk, get, s_hist, s_wsum, s_res, s_mm, s_small);
     // slots in order: thread j owns the contiguous slots [j*per, j*per + per)
     const int per = (slots + kThreads - 1) / kThreads;
     const int p_lo = tid * per, p_hi = min(slots, p_lo + per);
@@ -278,8 +280,10 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   __shared__ __attribute__((aligned(16))) float s_v[kLocalMax];  // the slice's scores; then (fused) the slots
   __shared__ uint32_t s_hist[1 << 12];
   __shared__ int s_wsum[kWaves];
-  __shared__ int s_res[2];
+  __shared__ int s_res[4];
   __shared__ int s_last;
+  __shared__ float s_mm[2 * kWaves];
+  __shared__ uint64_t s_small[65];
   const int s = blockIdx.x, u = blockIdx.y;
   const int n = lens.v[u / Hkv];
   const int kk = min(k, n);
@@ -291,22 +295,24 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   if (kk < n && len > 0) {  // a slice with tokens to choose from
     const int cnt = min(kk, len);
     const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
-    for (int i0 = 0; i0 < len; i0 += kBatch * kLocalThreads) {
-      float v[kBatch];
+    constexpr int kPer = kLocalMax / kLocalThreads;
+    float v[kPer];  // token t0 + j*kLocalThreads + tid
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = i0 + j * kLocalThreads + tid;
-        v[j] = sg[min(i, len - 1)];
-      }
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kLocalThreads + tid;
+      v[j] = sg[min(i, len - 1)];  // clamped: every load unconditional
+    }
+    uint64_t c[kPer];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = i0 + j * kLocalThreads + tid;
-        if (i < len) s_v[i] = v[j];
-      }
+    for (int j = 0; j < kPer; ++j) {
+      const int i = j * kLocalThreads + tid;
+      if (i < len) s_v[i] = v[j];
+      c[j] = i < len ? composite(v[j], t0 + i) : 0ull;
     }
     __syncthreads();
     auto get = [&](int i) { return composite(s_v[i], t0 + i); };
-    const uint64_t T = (cnt == len) ? 0 : lds_threshold<kLocalThreads>(get, len, cnt, s_hist, s_wsum, s_res);
+    const uint64_t T = (cnt == len) ? 0
+                                    : hist_select<kLocalThreads>(c, len, cnt, get, s_hist, s_wsum, s_res, s_mm, s_small);
     // the slice's top entries in index order (per-wave runs of 64-token blocks)
     const int nblk = (len + 63) / 64;
     const int R = (nblk + kWaves - 1) / kWaves;
@@ -339,7 +345,8 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   __syncthreads();
   if (!s_last) return;
 
-  merge_unit<true>(ucand, idx, u, n, k, S, reinterpret_cast<uint64_t*>(s_v), s_hist, s_wsum, s_res);
+  merge_unit<true, kLocalMax * 4 / 8>(ucand, idx, u, n, k, S, reinterpret_cast<uint64_t*>(s_v), s_hist, s_wsum,
+                                      s_res, s_mm, s_small);
   if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
 }
 
@@ -351,9 +358,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
   __shared__ uint64_t s_c[kMergeMax];
   __shared__ uint32_t s_hist[1 << 12];
   __shared__ int s_wsum[kWaves];
-  __shared__ int s_res[2];
+  __shared__ int s_res[4];
+  __shared__ float s_mm[2 * kWaves];
+  __shared__ uint64_t s_small[65];
   const int u = blockIdx.x;
-  merge_unit<false>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv], k, S, s_c, s_hist, s_wsum, s_res);
+  merge_unit<false, kMergeMax>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv], k, S, s_c, s_hist, s_wsum, s_res,
+                               s_mm, s_small);
 }
 
 }  // namespace
