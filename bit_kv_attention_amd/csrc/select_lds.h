@@ -1,11 +1,13 @@
-// select_lds.h -- the radix select on composite (score, index) keys shared by
-// the top-k kernels and the fused select-and-correct kernel.
+// select_lds.h -- workgroup-wide selection of the need-th largest composite
+// (score, index) key, shared by the top-k kernels.
 //
 // A token's composite key is (order-preserving bits of its score) << 32 | ~t:
 // larger means a larger score, or an equal score and a lower index, and no
-// two tokens share one.  The need-th largest composite T is found most
+// two tokens share one.  hist_select (below) finds the need-th largest T with
+// one histogram of score values and an exact ranking of the threshold bin.
+// lds_threshold is the general radix select it falls back on: most
 // significant digit first (widths 12, 10, 10 over the score bits, 11, 11, 10
-// over the index bits): a pass histograms the next digit of the entries under
+// over the index bits), a pass histograms the next digit of the entries under
 // the prefix so far (LDS atomics), the digit holding the need-th largest is
 // appended, and it stops once every entry under the prefix is needed; T is
 // then the smallest composite with that prefix.
@@ -22,17 +24,41 @@ __device__ inline uint64_t composite(float s, int t) {
   return ((uint64_t)float_key(s) << 32) | (uint64_t)(~(uint32_t)t);
 }
 
-// Exclusive prefix sum over a workgroup of NW waves (wave shuffles, then the
-// wave totals through LDS); `total` gets the sum of all.
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within
+// each row of 16 lanes, then lane 15 of rows 0 and 2 is added into rows 1 and
+// 3 and lane 31 into rows 2 and 3 (row broadcasts).  Lanes without a source
+// add 0.
+__device__ inline int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Minimum / maximum over the 64 lanes of a wave, in every lane: DPP within a
+// row, then the gfx950 row swaps (each returns own and partner value).
+template <bool MAX>
+__device__ inline float wave_minmax(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true)));  // row_ror:4
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)));  // row_ror:8
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+// Exclusive prefix sum over a workgroup of NW waves (wave scan, then the wave
+// totals through LDS); `total` gets the sum of all.
 template <int NW>
 __device__ inline int block_excl_scan(int v, int* s_wsum, int& total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) s_wsum[wv] = x;
   __syncthreads();
@@ -107,19 +133,20 @@ __device__ inline float key_value(uint32_t key) {
 
 constexpr int kHistBins = 4096;
 
-// The need-th largest of the composites spread over the workgroup (thread
-// tid holds entry j*NT + tid in c[j]; 0 = empty slot; get(i) reads entry i
-// for the fallback), with few barriers: one histogram of the score values
-// over kHistBins equal bins between the smallest and largest score, which
-// is monotone in the score, so every entry of a higher bin beats every entry
-// of a lower one; the bin D holding the need-th largest is found with one
-// scan, and the entries of bin D are ranked exactly -- by one wave when at
-// most 64 (the usual case: the bins are narrow), else by the radix select
-// restricted to bin D.  s_hist: kHistBins words; s_mm: 2*NT/64 floats;
-// s_small: 65 words; s_res: 4 ints.
-template <int NT, int PER, typename Get>
-__device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int need, Get get, uint32_t* s_hist,
-                                       int* s_wsum, int* s_res, float* s_mm, uint64_t* s_small) {
+// The need-th largest of the composites spread over the workgroup, with few
+// barriers.  Each thread holds PER entries in c[] (0 = empty slot; which
+// entries, does not matter here).  One histogram of the score values over
+// kHistBins equal bins between the smallest and largest score -- the bin is
+// monotone in the score, so every entry of a higher bin beats every entry of
+// a lower one; one scan finds the bin D holding the need-th largest, and the
+// entries of bin D are ranked exactly: by one wave when at most 64 (the
+// usual case: the bins are narrow), else by the radix select restricted to
+// bin D, for which fill() first puts every entry i of [0, count) where get(i)
+// reads it.  s_hist: kHistBins words; s_mm: 2*NT/64 floats; s_small: 65
+// words; s_res: 4 ints.
+template <int NT, int PER, typename Get, typename Fill>
+__device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int need, Get get, Fill fill,
+                                       uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm, uint64_t* s_small) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   float lo = INFINITY, hi = -INFINITY;
@@ -129,11 +156,8 @@ __device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int 
     lo = c[j] ? fminf(lo, x) : lo;
     hi = c[j] ? fmaxf(hi, x) : hi;
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    lo = fminf(lo, __shfl_xor(lo, o));
-    hi = fmaxf(hi, __shfl_xor(hi, o));
-  }
+  lo = wave_minmax<false>(lo);
+  hi = wave_minmax<true>(hi);
   for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
   if (lane == 0) {
     s_mm[wv] = lo;
@@ -181,7 +205,8 @@ __device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int 
   const int need2 = need - s_res[1];
   const int mD = (int)s_hist[D];
   if (mD > 64) {  // many entries share bin D: radix select among them
-    __syncthreads();  // s_hist is reused
+    fill();
+    __syncthreads();  // s_hist is reused; the entries are in place
     auto getD = [&](int i) {
       const uint64_t cc = get(i);
       return (cc && bin(cc) == D) ? cc : 0ull;

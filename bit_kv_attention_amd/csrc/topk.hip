@@ -235,39 +235,40 @@ __device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restri
   } else {
     const int ns = (n + S - 1) / S;  // slices holding tokens
     const int slots = ns * k;
+    // thread tid holds the contiguous slots [tid*per, tid*per + per)
     constexpr int kPer = MAXSLOTS / kThreads;
-    uint64_t v[kPer];  // slot j*kThreads + tid (0: empty)
+    const int per = (slots + kThreads - 1) / kThreads;  // <= kPer
+    const int p_lo = tid * per;
+    uint64_t v[kPer];  // 0: empty
     bool ok[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first
-      const int p = j * kThreads + tid;
+      const int p = p_lo + j;
       const int pc = min(p, slots - 1);
       const int sl = pc / k, jj = pc - sl * k;
       const int cnt = min(kk, min(S, n - sl * S));
-      ok[j] = p < slots && jj < cnt;
+      ok[j] = j < per && p < slots && jj < cnt;
       const uint64_t* src = &ucand[sl * k + min(jj, cnt - 1)];
       v[j] = AGENT ? ld_dev64(src) : *src;
     }
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int p = j * kThreads + tid;
-      v[j] = ok[j] ? v[j] : 0;
-      if (p < slots) s_c[p] = v[j];
-    }
-    __syncthreads();
+    for (int j = 0; j < kPer; ++j) v[j] = ok[j] ? v[j] : 0;
     auto get = [&](int i) { return s_c[i]; };
-    const uint64_t T = hist_select<kThreads>(v, slots, kk, get, s_hist, s_wsum, s_res, s_mm, s_small);
-    // slots in order: thread j owns the contiguous slots [j*per, j*per + per)
-    const int per = (slots + kThreads - 1) / kThreads;
-    const int p_lo = tid * per, p_hi = min(slots, p_lo + per);
+    auto fill = [&]() {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (j < per && p_lo + j < slots) s_c[p_lo + j] = v[j];
+    };
+    const uint64_t T = hist_select<kThreads>(v, slots, kk, get, fill, s_hist, s_wsum, s_res, s_mm, s_small);
+    // the slots >= T in slot order, which is ascending token order
     int mine = 0;
-    for (int p = p_lo; p < p_hi; ++p) mine += (s_c[p] >= T) ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += (v[j] && v[j] >= T) ? 1 : 0;
     int total;
     int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
-    for (int p = p_lo; p < p_hi; ++p) {
-      const uint64_t c = s_c[p];
-      if (c >= T) out[pos++] = (int32_t)~(uint32_t)(c & 0xFFFFFFFFu);
-    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (v[j] && v[j] >= T) out[pos++] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
   }
 }
 
@@ -295,45 +296,48 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   if (kk < n && len > 0) {  // a slice with tokens to choose from
     const int cnt = min(kk, len);
     const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
+    // thread tid holds the contiguous tokens t0 + [tid*kPer, tid*kPer + kPer)
     constexpr int kPer = kLocalMax / kLocalThreads;
-    float v[kPer];  // token t0 + j*kLocalThreads + tid
+    const int i0 = tid * kPer;
+    float v[kPer];
+    if (i0 + kPer <= len) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = j * kLocalThreads + tid;
-      v[j] = sg[min(i, len - 1)];  // clamped: every load unconditional
-    }
-    uint64_t c[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int i = j * kLocalThreads + tid;
-      if (i < len) s_v[i] = v[j];
-      c[j] = i < len ? composite(v[j], t0 + i) : 0ull;
-    }
-    __syncthreads();
-    auto get = [&](int i) { return composite(s_v[i], t0 + i); };
-    const uint64_t T = (cnt == len) ? 0
-                                    : hist_select<kLocalThreads>(c, len, cnt, get, s_hist, s_wsum, s_res, s_mm, s_small);
-    // the slice's top entries in index order (per-wave runs of 64-token blocks)
-    const int nblk = (len + 63) / 64;
-    const int R = (nblk + kWaves - 1) / kWaves;
-    const int b_lo = wv * R, b_hi = min(nblk, b_lo + R);
-    int mine = 0;
-    for (int bk = b_lo; bk < b_hi; ++bk) {
-      const int i = bk * 64 + lane;
-      mine += __popcll(__ballot(i < len && get(i) >= T));
-    }
-    int total;
-    int pos = __shfl(block_excl_scan<kWaves>(lane == 0 ? mine : 0, s_wsum, total), 0);
-    uint64_t* __restrict__ dst = ucand + (size_t)s * k;
-    for (int bk = b_lo; bk < b_hi; ++bk) {
-      const int i = bk * 64 + lane;
-      const uint64_t c = i < len ? get(i) : 0;
-      const uint64_t mask = __ballot(i < len && c >= T);
-      if ((mask >> lane) & 1ull) {
-        uint64_t* p = &dst[pos + __popcll(mask & ((1ull << lane) - 1))];
-        if (FUSED) st_dev64(p, c); else *p = c;
+      for (int j = 0; j < kPer; j += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(sg + i0 + j);
+        v[j] = x.x;
+        v[j + 1] = x.y;
+        v[j + 2] = x.z;
+        v[j + 3] = x.w;
       }
-      pos += __popcll(mask);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) v[j] = sg[min(i0 + j, len - 1)];  // clamped: unconditional
+    }
+    uint64_t c[kPer];  // 0: past the slice
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) c[j] = (i0 + j < len) ? composite(v[j], t0 + i0 + j) : 0ull;
+    auto get = [&](int i) { return composite(s_v[i], t0 + i); };
+    auto fill = [&]() {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (i0 + j < len) s_v[i0 + j] = v[j];
+    };
+    const uint64_t T = (cnt == len) ? 0
+                                    : hist_select<kLocalThreads>(c, len, cnt, get, fill, s_hist, s_wsum, s_res, s_mm,
+                                                                 s_small);
+    // the slice's entries >= T in index order
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += (c[j] && c[j] >= T) ? 1 : 0;
+    int total;
+    int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
+    uint64_t* __restrict__ dst = ucand + (size_t)s * k;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (c[j] && c[j] >= T) {
+        if (FUSED) st_dev64(&dst[pos], c[j]); else dst[pos] = c[j];
+        ++pos;
+      }
     }
   }
 
