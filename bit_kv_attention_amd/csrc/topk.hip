@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 // Workgroup (slice s, unit) keeps the scores of tokens [s*S, s*S + S)
 // (S <= kTopkSliceMax, chosen on the host) in LDS, finds the exact top
 // min(kk, slice length) of the slice and writes their composites in index
-// order to cand[u][s*k + j].
+// order to cand[u][s*k + j], and 0 into its slots past them.
 // Every token of the unit's top-kk is in its slice's top-kk, so the union
 // holds the answer.  Then it arrives at the unit's counter; the last of the
 // unit's workgroups loads the nslice*k candidate slots into LDS (empty slots
@@ -219,6 +219,30 @@ __device__ inline uint64_t ld_dev64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Output positions of the selected entries held as entry j*NW*64 + 64w + lane
+// (wave w): their rank in that order among the selected ones.  Per (j, w) the
+// count comes from a ballot, one block scan over the PER*NW counts places
+// them.  s_tmp: PER*NW ints.
+template <int PER, int NW>
+__device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER], int* s_wsum, int* s_tmp) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  uint64_t mask[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    mask[j] = __ballot(sel[j]);
+    if (lane == 0) s_tmp[j * NW + wv] = __popcll(mask[j]);
+  }
+  __syncthreads();
+  const int cnt = (tid < PER * NW) ? s_tmp[tid] : 0;
+  int total;
+  const int before = block_excl_scan<NW>(cnt, s_wsum, total);  // (its barriers order the reads above)
+  if (tid < PER * NW) s_tmp[tid] = before;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) at[j] = s_tmp[j * NW + wv] + __popcll(mask[j] & below);
+}
+
 // The merge of one unit's candidate slots (see above); all kThreads threads.
 // AGENT: the slots were written by other workgroups of this launch.
 // At most MAXSLOTS slots.
@@ -235,21 +259,16 @@ __device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restri
   } else {
     const int ns = (n + S - 1) / S;  // slices holding tokens
     const int slots = ns * k;
-    // thread tid holds the contiguous slots [tid*per, tid*per + per)
+    // thread tid holds slots j*kThreads + tid (coalesced loads)
     constexpr int kPer = MAXSLOTS / kThreads;
-    const int per = (slots + kThreads - 1) / kThreads;  // <= kPer
-    const int p_lo = tid * per;
     uint64_t v[kPer];  // 0: empty
     bool ok[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first
-      const int p = p_lo + j;
-      const int pc = min(p, slots - 1);
-      const int sl = pc / k, jj = pc - sl * k;
-      const int cnt = min(kk, min(S, n - sl * S));
-      ok[j] = j < per && p < slots && jj < cnt;
-      const uint64_t* src = &ucand[sl * k + min(jj, cnt - 1)];
+    for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first (unused slots hold 0)
+      const int p = j * kThreads + tid;
+      const uint64_t* src = &ucand[min(p, slots - 1)];
       v[j] = AGENT ? ld_dev64(src) : *src;
+      ok[j] = p < slots;
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) v[j] = ok[j] ? v[j] : 0;
@@ -257,18 +276,19 @@ __device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restri
     auto fill = [&]() {
 #pragma unroll
       for (int j = 0; j < kPer; ++j)
-        if (j < per && p_lo + j < slots) s_c[p_lo + j] = v[j];
+        if (j * kThreads + tid < slots) s_c[j * kThreads + tid] = v[j];
     };
     const uint64_t T = hist_select<kThreads>(v, slots, kk, get, fill, s_hist, s_wsum, s_res, s_mm, s_small);
-    // the slots >= T in slot order, which is ascending token order
-    int mine = 0;
+    // the slots >= T in slot order (ascending token order): slot j*kThreads +
+    // 64w + lane is (j, w, lane) in that order
+    bool sel[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) mine += (v[j] && v[j] >= T) ? 1 : 0;
-    int total;
-    int pos = block_excl_scan<kWaves>(mine, s_wsum, total);
+    for (int j = 0; j < kPer; ++j) sel[j] = v[j] && v[j] >= T;
+    int at[kPer];
+    ordered_positions<kPer, kWaves>(sel, at, s_wsum, reinterpret_cast<int*>(s_hist));
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
-      if (v[j] && v[j] >= T) out[pos++] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
+      if (sel[j]) out[at[j]] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
   }
 }
 
@@ -338,6 +358,9 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
         if (FUSED) st_dev64(&dst[pos], c[j]); else dst[pos] = c[j];
         ++pos;
       }
+    }
+    for (int j = cnt + tid; j < k; j += kLocalThreads) {  // the slice's unused slots
+      if (FUSED) st_dev64(&dst[j], 0ull); else dst[j] = 0ull;
     }
   }
 
