@@ -30,6 +30,8 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
 __device__ inline float h2f(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
 
 // Running softmax state: max m (log2 units), scaled sums a and l.
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   if (ip0 >= kk) return;  // the combine reads only the chunks below kk
   const float sm2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
 
-  __shared__ float s_q[G][kHeadDim];
+  __shared__ uint4 s_qh[G][kHeadDim / 8];  // the query rows as fp16 pairs
+  __shared__ float s_qs[G][kHeadDim / 16];  // sums of 16-channel runs of the query rows
   __shared__ int s_t[kCorrChunk];
   __shared__ float s_lg[2][kCorrChunk][G];  // logits, log2 units: [exact/approx]
   __shared__ float s_w[2][kCorrChunk][G];   // weights
@@ -155,13 +158,14 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     const int ii = ip0 + (tid & (kCorrChunk - 1));
     const int tv = idx[(size_t)u * k + min(ii, kk - 1)];
     if (tid < G * kHeadDim / 8) {
+      (&s_qh[0][0])[tid] = w;
+      // 8 fp16 per thread; two neighbours make a 16-channel run
       const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-      float* dst = &s_q[0][0] + tid * 8;
+      float r = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dst[2 * j] = h2f((uint16_t)(ww[j] & 0xFFFFu));
-        dst[2 * j + 1] = h2f((uint16_t)(ww[j] >> 16));
-      }
+      for (int j = 0; j < 4; ++j) r += h2f((uint16_t)(ww[j] & 0xFFFFu)) + h2f((uint16_t)(ww[j] >> 16));
+      r += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xB1, 0xF, 0xF, true));  // + neighbour
+      if ((tid & 1) == 0) (&s_qs[0][0])[tid >> 1] = r;
     }
     if (tid < kCorrChunk) s_t[tid] = (ii < kk && tv >= 0 && tv < n) ? tv : -1;
   }
@@ -220,10 +224,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
 
   // ---- logits: 8 threads per token, 16 channels each ------------------------
+  // fp16 pairs through v_dot2_f32_f16 (exact products, fp32 sums): the exact
+  // key pairs, and for the approximate logit the codes as exact fp16
+  // integers, whose dot product with q takes the group's scale once, plus
+  // zero x (sum of q over the run) -- the scan's own form of the score.
   {
     float ex[G], ap[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) ex[h] = ap[h] = 0.f;
     {
       const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
       const int sh = (8 * KB * (part >> 1)) & 31;
@@ -231,25 +237,40 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 #pragma unroll
       for (int x = 0; x < 2; ++x) fld[x] = (uint32_t)((((uint64_t)kraw[x][1] << 32) | kraw[x][0]) >> sh);
       const uint64_t bits = ((uint64_t)fld[0] & ((1ull << (8 * KB)) - 1)) | ((uint64_t)fld[1] << (8 * KB));
+      constexpr uint32_t M = (1u << KB) - 1;
+      const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+      half2_t cp[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t lo = (uint32_t)(bits >> (KB * 2 * i)) & M, hi = (uint32_t)(bits >> (KB * (2 * i + 1))) & M;
+        cp[i] = __builtin_bit_cast(half2_t, lo | (hi << 16) | 0x64006400u) - k1024;
+      }
       const float s = h2f((uint16_t)(kmw & 0xFFFFu)), z = h2f((uint16_t)(kmw >> 16));
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float kx = h2f((uint16_t)(kw[j >> 1] >> (16 * (j & 1))));
-        const float kh = fmaf(s, (float)((bits >> (KB * j)) & ((1u << KB) - 1)), z);
+      for (int h = 0; h < G; ++h) {
+        const uint4 qa = s_qh[h][2 * part], qb = s_qh[h][2 * part + 1];
+        const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        float e = 0.f, d = 0.f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          ex[h] = fmaf(s_q[h][c0 + j], kx, ex[h]);
-          ap[h] = fmaf(s_q[h][c0 + j], kh, ap[h]);
+        for (int i = 0; i < 8; ++i) {
+          const half2_t qq = __builtin_bit_cast(half2_t, qw[i]);
+          e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
+          d = __builtin_amdgcn_fdot2(cp[i], qq, d, false);
         }
+        ex[h] = e;
+        ap[h] = fmaf(s, d, z * s_qs[h][part]);
       }
     }
+    // sum over the token's 8 threads (lanes 8m..8m+7): quads by DPP, then the
+    // other quad (row_ror:12 brings lane l+4 to lanes 0 and 8 of each row)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int off = 1; off < 8; off <<= 1) {
-        ex[h] += __shfl_xor(ex[h], off);
-        ap[h] += __shfl_xor(ap[h], off);
-      }
+      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0xB1, 0xF, 0xF, true));
+      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0xB1, 0xF, 0xF, true));
+      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0x4E, 0xF, 0xF, true));
+      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0x4E, 0xF, 0xF, true));
+      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0x12C, 0xF, 0xF, true));
+      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0x12C, 0xF, 0xF, true));
     }
     if (part == 0) {
 #pragma unroll
