@@ -33,10 +33,10 @@ def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32
 def scan_partial_bytes(lay, L: int) -> int:
     """Bytes of split states the scan writes: per (b, query head, split) the
     max, the denominator and D accumulators (fp32); splits as the library
-    chooses them (about 512 workgroups, 128-token multiples)."""
+    chooses them (about 256 workgroups, 256-token multiples)."""
     units = lay.batch * lay.n_kv_heads
-    per = -(-units * L // 512)
-    per = max(128, -(-per // 128) * 128)
+    per = -(-units * L // 256)
+    per = max(256, -(-per // 256) * 256)
     nsplit = -(-L // per)
     return lay.batch * lay.n_q_heads * nsplit * (2 + lay.head_dim) * 4
 

@@ -9,13 +9,14 @@
 namespace bkv {
 
 int split_tokens(int units, int max_len) {
-  // Work per workgroup: a multiple of 4 waves x 32 tokens, sized so the grid
-  // has about kScanWorkgroups workgroups when the context allows (long runs
-  // per wave amortise the per-workgroup setup and merge).
+  // Work per workgroup: a multiple of kScanWaves waves x 32 tokens, sized so
+  // the grid has about kScanWorkgroups workgroups when the context allows
+  // (long runs per wave amortise the per-workgroup setup and merge).
+  constexpr int q = kScanWaves * kTile;
   const long long total = (long long)units * (max_len > 0 ? max_len : 1);
   long long per = (total + kScanWorkgroups - 1) / kScanWorkgroups;
-  per = ((per + 127) / 128) * 128;
-  if (per < 128) per = 128;
+  per = ((per + q - 1) / q) * q;
+  if (per < q) per = q;
   return (int)per;
 }
 
@@ -26,10 +27,11 @@ int num_splits(int units, int max_len) {
 }
 
 // An upper bound of num_splits(units, m) over every m <= max_len (the split
-// count is not monotone in m): chunk >= 128 gives ceil(m/128), and
-// chunk >= units*m/kScanWorkgroups gives ceil(kScanWorkgroups/units).
+// count is not monotone in m): chunk >= q = kScanWaves*32 gives ceil(m/q),
+// and chunk >= units*m/kScanWorkgroups gives ceil(kScanWorkgroups/units).
 static int max_splits(int units, int max_len) {
-  const int a = (max_len + 127) / 128;
+  constexpr int q = kScanWaves * kTile;
+  const int a = (max_len + q - 1) / q;
   const int b = (kScanWorkgroups + units - 1) / units;
   const int m = a < b ? a : b;
   return m > 0 ? m : 1;

@@ -14,7 +14,8 @@ constexpr int kGroup = 32;
 constexpr int kGroups = kHeadDim / kGroup;  // 4
 constexpr int kTile = 32;                   // tokens per V tile and per scan step
 constexpr int kMaxBatch = 256;
-constexpr int kScanWorkgroups = 512;        // target grid of the approximate scan
+constexpr int kScanWaves = 8;               // waves per workgroup of the approximate scan
+constexpr int kScanWorkgroups = 256;        // target grid of the approximate scan
 
 // Per-sequence lengths / positions travel by value in the kernel arguments.
 struct SeqArg {

@@ -9,7 +9,7 @@
 // split of the token range, the online-softmax state of sum_t p_t * V_hat_t
 // with V_hat = s*code + z applied the same way (sum p*s*code + sum p*z).
 //
-// Mapping onto gfx950 (one workgroup = 4 waves = one (b, kvh) unit and one
+// Mapping onto gfx950 (one workgroup = kScanWaves waves = one (b, kvh) unit and one
 // split; each wave takes 32-token steps):
 //  * Scores: v_mfma_f32_16x16x32_f16 with A = 16 tokens x the 32 codes of one
 //    quantisation group (exact integers in fp16) and B = 16 columns that pair
@@ -333,7 +333,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 }
 
 template <int KB, int VB, int G>
-__global__ __launch_bounds__(256, 2) void decode_approx_kernel(
+__global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
@@ -411,20 +411,20 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   for (int nt = 0; nt < 8; ++nt) ws.acc[nt] = (floatx4){0.f, 0.f, 0.f, 0.f};
 
   // per-wave LDS slot for the step's meta (each wave only touches its own)
-  __shared__ u32x4 s_meta[4][64];
+  __shared__ u32x4 s_meta[kScanWaves][64];
   u32x4* slot = s_meta[wv];
   const int wcell = meta_cell(lane >> 5, (lane & 7) >> 2, lane & 3, (lane & 31) >> 3);
 
   // Selection scores go through a per-wave LDS buffer of kSigBatch steps and
   // leave as one coalesced 16-byte-per-lane store (no stores in the steps).
-  __shared__ floatx4 s_sig[4][kSigBatch][8];
+  __shared__ floatx4 s_sig[kScanWaves][kSigBatch][8];
   int sig_count = 0;   // steps staged
   int sig_first = 0;   // t0 of the first staged step
   auto flush_sig = [&]() {
     wave_lds_order();
     const int i = lane >> 3;
     if (i < sig_count)
-      *reinterpret_cast<floatx4*>(sig + sig_first + 4 * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7] * c_sig;
+      *reinterpret_cast<floatx4*>(sig + sig_first + kScanWaves * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7] * c_sig;
     wave_lds_order();
     sig_count = 0;
   };
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   // The loop is unrolled twice so the two register sets alternate without
   // copies (a copy of registers with loads in flight would wait for them).
   auto full_step = [&](Step<KB, VB, G>& cur, Step<KB, VB, G>& nxt, int t0) {
-    const int tn = (t0 + 4 * kTile) < t_end ? t0 + 4 * kTile : t0;
+    const int tn = (t0 + kScanWaves * kTile) < t_end ? t0 + kScanWaves * kTile : t0;
     load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane);
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
@@ -477,17 +477,17 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
       break;
     }
     full_step(sa, sb, t0);
-    t0 += 4 * kTile;
+    t0 += kScanWaves * kTile;
     if (t0 + kTile > t_end) {
       if (t0 < t_end) last_step(sb, t0);
       break;
     }
     full_step(sb, sa, t0);
-    t0 += 4 * kTile;
+    t0 += kScanWaves * kTile;
   }
   if (sig_count > 0) flush_sig();
 
-  // ---- combine the 4 waves of the workgroup -----------------------------------
+  // ---- combine the waves of the workgroup -----------------------------------
   ws.l_part += __shfl_xor(ws.l_part, 16);
   ws.l_part += __shfl_xor(ws.l_part, 32);
   float z_tot[NT];
@@ -500,9 +500,9 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
     z += __shfl_xor(z, 32);
     z_tot[T] = z;
   }
-  __shared__ float s_m[4][G];
-  __shared__ float s_l[4][G];
-  __shared__ float s_acc[4][G][kHeadDim];
+  __shared__ float s_m[kScanWaves][G];
+  __shared__ float s_l[kScanWaves][G];
+  __shared__ float s_acc[kScanWaves][G][kHeadDim];
   if (kb == 0 && n < G) {
     s_m[wv][h] = ws.m_run;
     s_l[wv][h] = ws.l_part;
@@ -524,16 +524,16 @@ __global__ __launch_bounds__(256, 2) void decode_approx_kernel(
   }
   __syncthreads();
 
-  for (int e = tid; e < G * kHeadDim; e += 256) {
+  for (int e = tid; e < G * kHeadDim; e += 64 * kScanWaves) {
     const int hh = e / kHeadDim;
     const int c = e - hh * kHeadDim;
     float M = s_m[0][hh];
 #pragma unroll
-    for (int x = 1; x < 4; ++x) M = fmaxf(M, s_m[x][hh]);
+    for (int x = 1; x < kScanWaves; ++x) M = fmaxf(M, s_m[x][hh]);
     float a = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < kScanWaves; ++x) {
         const float f = __builtin_amdgcn_exp2f(s_m[x][hh] - M);
         a += f * s_acc[x][hh][c];
         l += f * s_l[x][hh];
@@ -553,7 +553,7 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
                     float* sigma, const Workspace& w, int chunk, hipStream_t s) {
   dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
   (void)hipGetLastError();  // report only this launch's status
-  decode_approx_kernel<KB, VB, G><<<grid, 256, 0, s>>>(
+  decode_approx_kernel<KB, VB, G><<<grid, 64 * kScanWaves, 0, s>>>(
       static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
       c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
       L.n_kv_heads, L.capacity, w.nsplit, chunk);
