@@ -75,16 +75,18 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
       if (x[j] < mn) mn = x[j];
       if (x[j] > mx) mx = x[j];
     }
-    // merge with the neighbouring lanes, lower channels first on ties
-#pragma unroll
-    for (int m = 1; m < 4; m <<= 1) {
-      const float omn = __shfl_xor(mn, m), omx = __shfl_xor(mx, m);
-      const bool hi = (sub & m) != 0;  // partner holds the lower channels
+    // merge with the neighbouring lanes of the quad (tid ^ 1, then tid ^ 2, by
+    // DPP), lower channels first on ties
+    auto merge = [&](float omn, float omx, bool hi) {  // hi: the partner holds the lower channels
       const float lmn = hi ? omn : mn, umn = hi ? mn : omn;
       const float lmx = hi ? omx : mx, umx = hi ? mx : omx;
       mn = (umn < lmn) ? umn : lmn;
       mx = (umx > lmx) ? umx : lmx;
-    }
+    };
+    merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, true)),
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)), (sub & 1) != 0);
+    merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)),
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)), (sub & 2) != 0);
     const _Float16 s16 = (_Float16)((mx - mn) / qmax);
     const _Float16 z16 = (_Float16)mn;
     const float s = (float)s16, z = (float)z16;
