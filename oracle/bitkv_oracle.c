@@ -16,7 +16,10 @@
  *                 keys; selection score = max over the query heads of a KV
  *                 head's group.
  *   O4 select     the top-k tokens per KV head by that score (JetFire README,
- *                 introduction: correction for top-k tokens).
+ *                 introduction: correction for top-k tokens); optionally the
+ *                 newest w tokens as well, always (a recent window kept at
+ *                 full precision, as the HACK review, the Jet-QSparse abstract
+ *                 and the TailorKV review do).
  *   O5 correct    softmax attention where the selected tokens use exact fp16
  *                 keys/values from the shadow copy and every other token uses
  *                 the dequantised ones (JetFire README, introduction;
@@ -285,6 +288,19 @@ void orc_topk(const double* sigma, int n, int k, int32_t* idx) {
   qsort(idx, (size_t)kk, sizeof(int32_t), by_int_asc);
   for (int i = kk; i < k; ++i) idx[i] = -1;
   free(all);
+}
+
+/* O4 with an exact recent window (the HACK review keeps the newest block in
+ * fp16, the Jet-QSparse abstract keeps recent pages in BF16, TailorKV keeps
+ * local tokens at full precision): the last min(w, n) tokens are always in
+ * the set, and O4 picks k more among the tokens before them. */
+void orc_topk_window(const double* sigma, int n, int k, int w, int32_t* idx) {
+  const int nw = w < n ? w : n;
+  const int n0 = n - nw;
+  const int kk = k < n0 ? k : n0;
+  orc_topk(sigma, n0, k, idx); /* idx[0..kk) ascending, idx[kk..k) = -1 */
+  for (int i = 0; i < nw; ++i) idx[kk + i] = n0 + i;
+  for (int i = kk + nw; i < k + w; ++i) idx[i] = -1;
 }
 
 /* ------------------------------------------------------- O3 + O5 (fp64) */

@@ -107,6 +107,11 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
  * asc), written ascending to idx[0..), rest of idx[0..k) set to -1. */
 void orc_topk(const double* sigma, int n, int k, int32_t* idx);
 
+/* O4 with a recent window of w tokens always selected: the last min(w, n)
+ * tokens plus O4's min(k, n - min(w, n)) largest of the tokens before them,
+ * ascending in idx[0..), the rest of idx[0..k+w) set to -1. */
+void orc_topk_window(const double* sigma, int n, int k, int w, int32_t* idx);
+
 void orc_set_threads(int n);
 int orc_get_threads(void);
 

@@ -202,3 +202,39 @@ def test_hack_eq4_identity_for_unquantised_query():
         q32, c32 = q.astype(np.float32), c.astype(np.float32)
         rhs32 = np.float32(s) * (q32 @ c32) + np.float32(z) * q32.sum(dtype=np.float32)
         assert abs(float(rhs32) - lhs) <= 4e-6 * (np.abs(q) @ np.abs(s * c + z) + abs(z) * np.abs(q).sum())
+
+
+def test_topk_window_brute_force(orc):
+    """O4 with a recent window: the last min(w, n) tokens always, plus the k
+    largest (ties to the lower index) of the tokens before them; ascending,
+    then -1.  w = 0 is plain O4; w >= n selects every token."""
+    rng = np.random.default_rng(11)
+    for n in (0, 1, 7, 40, 130):
+        sig = np.round(rng.standard_normal(n) * 3) / 2  # many exact ties
+        for k in (0, 1, 5, n, n + 3):
+            for w in (0, 1, 4, n, n + 2):
+                got = orc.topk_window(sig, k, w)
+                nw = min(w, n)
+                n0 = n - nw
+                order = sorted(range(n0), key=lambda t: (-sig[t], t))
+                want = sorted(order[:min(k, n0)]) + list(range(n0, n))
+                want += [-1] * (k + w - len(want))
+                assert got.tolist() == want, (n, k, w)
+                if w == 0:
+                    assert got.tolist() == orc.topk(sig, k).tolist()
+
+
+def test_window_covering_everything_equals_dense_attention(orc):
+    """A window as long as the context puts every token in the exact set: the
+    corrected output is then dense fp16 attention, even with k = 0."""
+    w = small_workload(kbits=3, vbits=2, L=120)
+    inp = make_inputs(w)
+    cache = build(orc, w, inp)
+    lens = np.full(w.B, w.L)
+    r0 = cache.decode(inp.q, lens, k=0, want_approx=True)
+    win = w.L
+    sel = np.stack([[orc.topk_window(r0["sigma"][b, h, :w.L], 0, win) for h in range(w.Hkv)]
+                    for b in range(w.B)])
+    r = cache.decode(inp.q, lens, k=win, sel=sel)
+    ref = dense(inp.q.astype(np.float64), inp.K.astype(np.float64), inp.V.astype(np.float64), w.G)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
