@@ -49,6 +49,8 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="llama8b_k4v4_L32768",
                     help="workload name from bit_kv_attention_amd.synth.WORKLOADS, or 'all'")
     ap.add_argument("--shadow", choices=["hbm", "host"], default="hbm")
+    ap.add_argument("--window", type=int, default=0,
+                    help="also correct the newest WINDOW tokens of every sequence (topk_select_window)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -111,9 +113,16 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         caches.append(cache)
     del Kd, Vd
     torch.cuda.synchronize()
-    st = DecodeStep(lay, w.k, L, device=dev)
+    W = args.window
+    st = DecodeStep(lay, w.k, L, device=dev, window=W)
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
+
+    def select():
+        if W > 0:
+            bk.topk_select_window(lay, st.sigma, lens, w.k, W, st.idx, st.ws)
+        else:
+            bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws)
 
     def step(i):
         cache = caches[i % copies]
@@ -137,8 +146,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         sev[i][0].record()
         bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws)
         sev[i][1].record()
-        bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws)
-        bk.qattn_correct(lay, cache, q, lens, st.idx, w.k, st.ws, st.out)
+        select()
+        bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
     e1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -154,9 +163,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         e = ev[i]
         e[0][0].record(); bk.kv_pack_append(lay, cache, kn, vn, 1, pos); e[0][1].record()
         e[1][0].record(); bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws); e[1][1].record()
-        e[2][0].record(); bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws); e[2][1].record()
+        e[2][0].record(); select(); e[2][1].record()
         e[3][0].record()
-        bk.qattn_correct(lay, cache, q, lens, st.idx, w.k, st.ws, st.out)
+        bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
         e[3][1].record()
     torch.cuda.synchronize()
     kus = {n: 1000.0 * float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
@@ -186,7 +195,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
-                   "group": w.group, "top_k": w.k, "shadow": args.shadow, "cache_copies": copies,
+                   "group": w.group, "top_k": w.k, "recent_window": W, "shadow": args.shadow,
+                   "cache_copies": copies,
                    "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
         "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
@@ -197,7 +207,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "kernel_us_per_launch": round(scan_us_timed, 2)},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and W == 0:  # the oracle's timed path has no window
         res["cpu_baseline"] = cpu_baseline(w, inp, knew, vnew, args.cpu_threads)
     del caches
     torch.cuda.empty_cache()

@@ -203,20 +203,32 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
              : BKV_E_HIP;
 }
 
-bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
-                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+static bkv_status topk_rows(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
+                            int32_t window, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
-  if (k < 0) return BKV_E_ARG;
-  if (!sigma || (!idx && k > 0) || (!ws && k > 0)) return BKV_E_NULL;
+  if (k < 0 || window < 0 || (long long)k + window > 0x7FFFFFFF) return BKV_E_ARG;
+  const int row = k + window;
+  if (!sigma || (!idx && row > 0) || (!ws && row > 0)) return BKV_E_NULL;
   SeqArg len;
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
-  if (k == 0) return BKV_OK;
-  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (row == 0) return BKV_OK;
+  const Workspace w = workspace_layout(ws, *L, max_len, row, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_topk(*L, sigma, len, max_len, k, idx, w.tkc, w.tkctr, (hipStream_t)stream) == hipSuccess ? BKV_OK
-                                                                                               : BKV_E_HIP;
+  return launch_topk(*L, sigma, len, max_len, k, window, idx, w.tkc, w.tkctr, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
+bkv_status topk_select(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
+                       int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return topk_rows(L, sigma, len_host, k, 0, idx, ws, ws_bytes, stream);
+}
+
+bkv_status topk_select_window(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,
+                              int32_t window, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return topk_rows(L, sigma, len_host, k, window, idx, ws, ws_bytes, stream);
 }
 
 bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,

@@ -123,7 +123,8 @@ hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uin
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 hipStream_t s);
-hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
+// Rows of k + W entries per unit (W: the recent window, 0 for none).
+hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,

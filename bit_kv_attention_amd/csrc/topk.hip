@@ -2,6 +2,11 @@
 // score, ties to the lower index, written in ascending index order.
 // (JetFire README, introduction: only the top-k tokens get the high-precision
 // correction; Jet-QSparse abstract: the budget is per KV head.)
+// With a recent window of W tokens (HACK review and TailorKV review: the
+// newest tokens are kept at full precision) the last nw = min(W, len) tokens
+// are always taken: the selection runs over the first n = len - nw tokens,
+// and a unit's row of k + W entries holds the min(k, n) selected indices,
+// then n .. n + nw - 1, then -1.
 //
 // One workgroup of 1024 threads per unit; nothing leaves the workgroup until
 // the answer is known, so there is no cross-workgroup protocol at all.
@@ -32,20 +37,27 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kCandMax = 4096;
 constexpr int kBatch = 16;  // scores per thread loaded together (independent loads in flight)
 
+// Entries [kk, stride) of a unit's row: the nw window tokens n, n+1, ...,
+// then -1.  All threads of the workgroup.
+__device__ inline void write_tail(int32_t* __restrict__ out, int kk, int n, int nw, int stride) {
+  for (int i = threadIdx.x; i < stride - kk; i += blockDim.x) out[kk + i] = (i < nw) ? n + i : -1;
+}
+
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ sigma, int32_t* __restrict__ idx,
-                                                        SeqArg lens, int Hkv, int cap, int k) {
+                                                        SeqArg lens, int Hkv, int cap, int k, int W) {
   const int u = blockIdx.x;
   const int b = u / Hkv;
-  const int n = lens.v[b];
+  const int nw = min(W, lens.v[b]);
+  const int n = lens.v[b] - nw;  // tokens to select from
   const int kk = min(k, n);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const float* __restrict__ sg = sigma + (size_t)u * cap;
-  int32_t* __restrict__ out = idx + (size_t)u * k;
+  int32_t* __restrict__ out = idx + (size_t)u * (k + W);
 
-  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
-  if (kk == n) {  // every token (or none) is selected
-    for (int i = tid; i < n; i += kThreads) out[i] = i;
+  write_tail(out, kk, n, nw, k + W);
+  if (kk == n || kk == 0) {  // every token (or none) is selected
+    for (int i = tid; i < kk; i += kThreads) out[i] = i;
     return;
   }
 
@@ -246,16 +258,17 @@ __device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER],
 // The merge of one unit's candidate slots (see above); all kThreads threads.
 // AGENT: the slots were written by other workgroups of this launch.
 // At most MAXSLOTS slots.
+// n: tokens selected from (the window's nw follow them).
 template <bool AGENT, int MAXSLOTS>
-__device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int k, int S,
-                           uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm,
+__device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int nw,
+                           int k, int W, int S, uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm,
                            uint64_t* s_small) {
   const int tid = threadIdx.x;
   const int kk = min(k, n);
-  int32_t* __restrict__ out = idx + (size_t)u * k;
-  for (int i = kk + tid; i < k; i += kThreads) out[i] = -1;
-  if (kk == n) {  // every token (or none) is selected
-    for (int i = tid; i < n; i += kThreads) out[i] = i;
+  int32_t* __restrict__ out = idx + (size_t)u * (k + W);
+  write_tail(out, kk, n, nw, k + W);
+  if (kk == n || kk == 0) {  // every token (or none) is selected
+    for (int i = tid; i < kk; i += kThreads) out[i] = i;
   } else {
     const int ns = (n + S - 1) / S;  // slices holding tokens
     const int slots = ns * k;
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
                                                                     uint64_t* __restrict__ cand,
                                                                     uint32_t* __restrict__ counter,
                                                                     int32_t* __restrict__ idx, SeqArg lens, int Hkv,
-                                                                    int cap, int k, int S, int cstride) {
+                                                                    int cap, int k, int W, int S, int cstride) {
   __shared__ __attribute__((aligned(16))) float s_v[kLocalMax];  // the slice's scores; then (fused) the slots
   __shared__ uint32_t s_hist[1 << 12];
   __shared__ int s_wsum[kWaves];
@@ -306,14 +319,15 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   __shared__ float s_mm[2 * kWaves];
   __shared__ uint64_t s_small[65];
   const int s = blockIdx.x, u = blockIdx.y;
-  const int n = lens.v[u / Hkv];
+  const int nw = min(W, lens.v[u / Hkv]);
+  const int n = lens.v[u / Hkv] - nw;  // tokens to select from
   const int kk = min(k, n);
   const int t0 = s * S;
   const int len = min(S, n - t0);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint64_t* __restrict__ ucand = cand + (size_t)u * cstride;
 
-  if (kk < n && len > 0) {  // a slice with tokens to choose from
+  if (0 < kk && kk < n && len > 0) {  // a slice with tokens to choose from
     const int cnt = min(kk, len);
     const float* __restrict__ sg = sigma + (size_t)u * cap + t0;
     // thread tid holds the contiguous tokens t0 + [tid*kPer, tid*kPer + kPer)
@@ -372,8 +386,8 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   __syncthreads();
   if (!s_last) return;
 
-  merge_unit<true, kLocalMax * 4 / 8>(ucand, idx, u, n, k, S, reinterpret_cast<uint64_t*>(s_v), s_hist, s_wsum,
-                                      s_res, s_mm, s_small);
+  merge_unit<true, kLocalMax * 4 / 8>(ucand, idx, u, n, nw, k, W, S, reinterpret_cast<uint64_t*>(s_v), s_hist,
+                                      s_wsum, s_res, s_mm, s_small);
   if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
 }
 
@@ -381,7 +395,7 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
 // LDS footprint): one workgroup per unit.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ cand,
                                                               int32_t* __restrict__ idx, SeqArg lens, int Hkv, int k,
-                                                              int S, int cstride) {
+                                                              int W, int S, int cstride) {
   __shared__ uint64_t s_c[kMergeMax];
   __shared__ uint32_t s_hist[1 << 12];
   __shared__ int s_wsum[kWaves];
@@ -389,30 +403,32 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
   __shared__ float s_mm[2 * kWaves];
   __shared__ uint64_t s_small[65];
   const int u = blockIdx.x;
-  merge_unit<false, kMergeMax>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv], k, S, s_c, s_hist, s_wsum, s_res,
-                               s_mm, s_small);
+  const int nw = min(W, lens.v[u / Hkv]);
+  merge_unit<false, kMergeMax>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv] - nw, nw, k, W, S, s_c, s_hist,
+                               s_wsum, s_res, s_mm, s_small);
 }
 
 }  // namespace
 
-hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k,
+hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s) {
   const int units = L.batch * L.n_kv_heads;
-  const int S = topk_slice(units, max_len, k);
+  const int max_sel = max_len > W ? max_len - W : 0;  // the longest range selected from
+  const int S = topk_slice(units, max_sel, k);
   (void)hipGetLastError();  // report only this call's launches
   if (S == 0) {
-    topk_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, k);
+    topk_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, k, W);
   } else {
-    const int ns = (max_len + S - 1) / S;
+    const int ns = (max_sel + S - 1) / S;
     const int slots = ns * k;
     const dim3 grid(ns > 0 ? ns : 1, units);
     if ((size_t)slots * 8 <= (size_t)kLocalMax * 4) {  // the merge fits the slice stage's LDS: fused
       topk_slices_kernel<true><<<grid, kLocalThreads, 0, s>>>(sigma, cand, counter, idx, len, L.n_kv_heads,
-                                                              L.capacity, k, S, slots);
+                                                              L.capacity, k, W, S, slots);
     } else {
       topk_slices_kernel<false><<<grid, kLocalThreads, 0, s>>>(sigma, cand, counter, idx, len, L.n_kv_heads,
-                                                               L.capacity, k, S, slots);
-      topk_merge_kernel<<<units, kThreads, 0, s>>>(cand, idx, len, L.n_kv_heads, k, S, slots);
+                                                               L.capacity, k, W, S, slots);
+      topk_merge_kernel<<<units, kThreads, 0, s>>>(cand, idx, len, L.n_kv_heads, k, W, S, slots);
     }
   }
   return hipGetLastError();

@@ -6,26 +6,32 @@ from . import binding as bk
 
 
 class DecodeStep:
-    """Buffers for steps of one layer shape: sigma, workspace, idx, out."""
+    """Buffers for steps of one layer shape: sigma, workspace, idx, out.
+    window > 0 also corrects the newest `window` tokens of every sequence
+    (topk_select_window); the rows of idx then hold k + window entries."""
 
-    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda"):
+    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0):
         import torch
         self.layout = layout
         self.k = int(k)
+        self.window = int(window)
+        self.row = self.k + self.window
         L = layout
         self.sigma = torch.empty(L.batch * L.n_kv_heads * L.capacity, dtype=torch.float32, device=device)
-        ws_bytes = bk.bkv_workspace_bytes(L, max_len, self.k)
+        ws_bytes = bk.bkv_workspace_bytes(L, max_len, self.row)
         # zero-filled once: the calls keep their arrival counters in it at zero
         self.ws = torch.zeros(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
-        self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.k, 1), dtype=torch.int32, device=device)
+        self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.row, 1), dtype=torch.int32, device=device)
         self.out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32, device=device)
 
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
         bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
-        if self.k > 0:
+        if self.window > 0:
+            bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
+        elif self.k > 0:
             bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, self.ws, stream)
-        bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
+        bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.row > 0 else None, self.row, self.ws,
                          self.out, stream)
         return self.out
 

@@ -16,6 +16,7 @@
  *   kv_pack_append       quantise + pack the new token(s), write the shadow
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
  *   topk_select          top-k tokens per KV head by the selection score
+ *   topk_select_window   the same, plus the newest tokens always selected
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
  *
@@ -174,6 +175,25 @@ bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
 bkv_status topk_select(const bkv_layout* layout, const float* sigma,
                        const int32_t* len_host, int32_t k, int32_t* idx,
                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * topk_select_window -- topk_select with a recent window: per (b, kvh) the
+ * newest nw = min(window, len) tokens are always selected (HACK review and
+ * TailorKV review: the most recent tokens stay at full precision; Jet-QSparse
+ * abstract: the top-k budget is per KV head) and the top-k runs over the
+ * first n = len - nw tokens.  idx [B][Hkv][k + window] int32 (device): the
+ * min(k, n) tokens with the largest sigma among t < n (ties to the lower
+ * index) in ascending order, then n, n + 1, ..., len - 1, then -1 -- the
+ * whole row is ascending, and qattn_correct takes it with k + window as its k.
+ * window == 0 is topk_select.  Size ws with bkv_workspace_bytes(layout,
+ * max_len, k + window).  k + window == 0 enqueues nothing.
+ * Errors: BKV_E_ARG if k < 0, window < 0 or k + window overflows int32;
+ * BKV_E_CAPACITY for a bad length; BKV_E_WORKSPACE if ws is too small.
+ */
+bkv_status topk_select_window(const bkv_layout* layout, const float* sigma,
+                              const int32_t* len_host, int32_t k,
+                              int32_t window, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply

@@ -123,6 +123,16 @@ def test_host_error_paths(bk):
                          need, FAKE, None) == 7
     # NULL length array
     assert bk.raw_status("topk_select", C.byref(lay), FAKE, None, 4, FAKE, FAKE, need, None) == 1
+    # the recent-window variant: negative or overflowing sizes, NULL idx, a
+    # workspace sized for k alone (the row is k + window), the empty row
+    tw = "topk_select_window"
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 4, -1, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), -1, 4, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 2**31 - 4, 8, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 0, 4, None, FAKE, need, None) == 1
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 4, 1000, FAKE, FAKE, need, None) == 5
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 0, 0, None, None, 0, None) == 0
+    assert bk.raw_status(tw, C.byref(lay), FAKE, P(l2), 4, 4, FAKE, FAKE, 1 << 30, None) == 4
 
 
 def test_status_strings(bk):

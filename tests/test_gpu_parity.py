@@ -297,3 +297,81 @@ def test_topk_paths_on_given_scores(P, L, k):
             for h in range(Hkv):
                 want = oracle.topk(sig[b, h, :lens[b]].astype(np.float64), k)
                 assert np.array_equal(idx[b, h], want), (rep, b, h)
+
+
+@pytest.mark.parametrize("L,k,W", [(32768, 256, 64), (20000, 3000, 128), (40000, 4000, 32), (9000, 1, 16),
+                                   (5000, 0, 100), (3000, 64, 5000), (6000, 40, 0)])
+def test_topk_window_on_given_scores(P, L, k, W):
+    """topk_select_window on given scores (many exact ties): the newest
+    min(W, len) tokens always, the top-k over the rest, ascending, -1 fill --
+    every top-k path, k = 0, a window longer than the sequence, len 0, and
+    W = 0 equal to topk_select; two calls in a row on one workspace."""
+    banner(f"top-k window L={L} k={k} W={W}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    B, Hkv = 4, 2
+    cap = ((L + 31) // 32) * 32
+    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, 4, 4)
+    rng = np.random.default_rng(L + k + W)
+    sig = (np.round(rng.standard_normal((B, Hkv, cap)) * 64) / 64).astype(np.float32)
+    sig[:, :, ::97] = 3.5
+    lens = [L, L // 3 + 5, W // 2, 0]
+    row = k + W
+    st = DecodeStep(lay, k, L, window=W)
+    st.sigma.copy_(torch.from_numpy(sig.reshape(-1)))
+    for rep in range(2):
+        st.idx.fill_(-7)
+        bk.topk_select_window(lay, st.sigma, lens, k, W, st.idx, st.ws)
+        torch.cuda.synchronize()
+        idx = st.idx.cpu().numpy().reshape(B, Hkv, max(row, 1))[:, :, :row]
+        for b in range(B):
+            for h in range(Hkv):
+                want = oracle.topk_window(sig[b, h, :lens[b]].astype(np.float64), k, W)
+                assert np.array_equal(idx[b, h], want), (rep, b, h)
+    if W == 0:
+        st.idx.fill_(-7)
+        bk.topk_select(lay, st.sigma, lens, k, st.idx, st.ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(st.idx.cpu().numpy().reshape(B, Hkv, k), idx)
+
+
+@pytest.mark.parametrize("kb,vb,G,W", [(4, 4, 4, 64), (3, 2, 8, 200)])
+def test_step_parity_window(P, kb, vb, G, W):
+    """A whole step with a recent window: the GPU's rows against the oracle's
+    selection on the GPU's scores (exact), the output against the oracle on
+    the GPU's rows and on its own."""
+    banner(f"step window kb={kb} vb={vb} G={G} W={W}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("win", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 500 + G + W)
+    pair = P.build_pair(w, L=3000, cap=3008)
+    lens = np.array([3000, 1234, W // 3])
+    k = 32
+    pos = [int(x) - 1 for x in lens]
+    from bit_kv_attention_amd import binding as bk
+    bk.kv_pack_append(pair["lay"], pair["gc"], P.to_dev(pair["k1"]), P.to_dev(pair["v1"]), 1, pos)
+    pair["oc"].append(pair["k1"], pair["v1"], np.array(pos, np.int32))
+    st = DecodeStep(pair["lay"], k, 3000, window=W)
+    out = st.attend(pair["gc"], P.to_dev(pair["q"]), lens)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    sigma = st.sigma.cpu().numpy().reshape(w.B, w.Hkv, pair["cap"])
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, k + W)
+    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True)
+    sel_o = np.full_like(idx, -1)
+    for b in range(w.B):
+        n = lens[b]
+        np.testing.assert_allclose(sigma[b, :, :n], orc["sigma"][b, :, :n], rtol=1e-5, atol=2e-5)
+        for h in range(w.Hkv):
+            want = oracle.topk_window(sigma[b, h, :n].astype(np.float64), k, W)
+            assert np.array_equal(idx[b, h], want), (b, h)
+            sel_o[b, h] = oracle.topk_window(orc["sigma"][b, h, :n], k, W)
+            kk = min(k, n - min(W, n))  # the selected part of the row
+            P.assert_topk_near_tie(idx[b, h, :kk], sel_o[b, h, :kk], orc["sigma"][b, h], n - min(W, n), f"b{b}h{h}")
+    orc_s = pair["oc"].decode(pair["q"], lens, k + W, sel=idx)
+    P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
+    orc_o = pair["oc"].decode(pair["q"], lens, k + W, sel=sel_o)
+    P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
