@@ -65,6 +65,7 @@ def lib():
         L.orc_decode.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P, P, P, P, P, P]
         L.orc_topk.argtypes = [P, C.c_int, C.c_int, P]
         L.orc_topk_window.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
+        L.orc_topk_blocks.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
         L.orc_set_threads.argtypes = [C.c_int]
         L.orc_get_threads.restype = C.c_int
         _lib = L
@@ -219,4 +220,13 @@ def topk_window(sigma: np.ndarray, k: int, w: int) -> np.ndarray:
     sigma = np.ascontiguousarray(sigma, dtype=np.float64)
     idx = np.full(max(k + w, 0), -1, dtype=np.int32)
     lib().orc_topk_window(_p(sigma), int(sigma.shape[0]), int(k), int(w), _p(idx))
+    return idx
+
+
+def topk_blocks(sigma: np.ndarray, nb: int, bs: int) -> np.ndarray:
+    """O4 by blocks of bs tokens scored by their largest sigma (nb * bs slots,
+    see the C header)."""
+    sigma = np.ascontiguousarray(sigma, dtype=np.float64)
+    idx = np.full(max(nb * bs, 0), -1, dtype=np.int32)
+    lib().orc_topk_blocks(_p(sigma), int(sigma.shape[0]), int(nb), int(bs), _p(idx))
     return idx

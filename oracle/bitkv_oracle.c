@@ -303,6 +303,28 @@ void orc_topk_window(const double* sigma, int n, int k, int w, int32_t* idx) {
   for (int i = kk + nw; i < k + w; ++i) idx[i] = -1;
 }
 
+/* O4 over blocks of bs tokens scored by their largest sigma: the top-k of the
+ * block scores, each chosen block then expanded to its tokens. */
+void orc_topk_blocks(const double* sigma, int n, int nb, int bs, int32_t* idx) {
+  const int nblk = (n + bs - 1) / bs;
+  double* score = (double*)malloc((size_t)(nblk > 0 ? nblk : 1) * sizeof(double));
+  int32_t* chosen = (int32_t*)malloc((size_t)(nb > 0 ? nb : 1) * sizeof(int32_t));
+  for (int j = 0; j < nblk; ++j) {
+    double m = -INFINITY;
+    for (int t = j * bs; t < n && t < (j + 1) * bs; ++t)
+      if (sigma[t] > m) m = sigma[t];
+    score[j] = m;
+  }
+  orc_topk(score, nblk, nb, chosen); /* ascending block indices, then -1 */
+  for (int r = 0; r < nb; ++r)
+    for (int x = 0; x < bs; ++x) {
+      const long long t = (long long)chosen[r] * bs + x;
+      idx[(size_t)r * bs + x] = (chosen[r] >= 0 && t < n) ? (int32_t)t : -1;
+    }
+  free(score);
+  free(chosen);
+}
+
 /* ------------------------------------------------------- O3 + O5 (fp64) */
 
 /* out[h][0..D) = sum_t e^{lambda_t - m} nu_t / sum_t e^{lambda_t - m} for one

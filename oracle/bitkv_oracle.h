@@ -23,7 +23,7 @@
  *  - Jet-QSparse abstract: per-KV-head selection, fp16 values with fp32
  *    accumulation in the output-forming step.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - zero point = fp16 group minimum; scale = fp16((max-min)/(2^b-1)) computed
  *    in fp32 with a correctly rounded divide; codes use the *stored* fp16
  *    scale/zero; round-to-nearest-even everywhere; a zero scale gives code 0.
@@ -111,6 +111,14 @@ void orc_topk(const double* sigma, int n, int k, int32_t* idx);
  * tokens plus O4's min(k, n - min(w, n)) largest of the tokens before them,
  * ascending in idx[0..), the rest of idx[0..k+w) set to -1. */
 void orc_topk_window(const double* sigma, int n, int k, int w, int32_t* idx);
+
+/* O4 by blocks (Jet-QSparse abstract: the scan's scores select whole
+ * 128-token blocks per KV head): block j holds tokens [j*bs, min(n, j*bs+bs))
+ * and scores the maximum sigma over them; O4 picks the min(nb, ceil(n/bs))
+ * best blocks (ties to the lower block), and idx[0..nb*bs) lists them in
+ * ascending order, block r of the list at idx[r*bs..r*bs+bs) as its tokens
+ * (-1 past n), then -1. */
+void orc_topk_blocks(const double* sigma, int n, int nb, int bs, int32_t* idx);
 
 void orc_set_threads(int n);
 int orc_get_threads(void);

@@ -238,3 +238,63 @@ def test_window_covering_everything_equals_dense_attention(orc):
     r = cache.decode(inp.q, lens, k=win, sel=sel)
     ref = dense(inp.q.astype(np.float64), inp.K.astype(np.float64), inp.V.astype(np.float64), w.G)
     np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_topk_blocks_brute_force(orc):
+    """O4 by blocks: every chosen block beats every other block by (largest
+    sigma desc, block index asc), the blocks come out ascending as their
+    tokens (the ragged last one cut at n), then -1; block size 1 is plain
+    O4, and a budget covering every block lists every token."""
+    rng = np.random.default_rng(12)
+    for n in (0, 1, 7, 40, 131):
+        sig = np.round(rng.standard_normal(n) * 3) / 2  # many exact ties
+        for bs in (1, 2, 4, 32):
+            nblk = -(-n // bs)
+            score = [max(sig[j * bs:(j + 1) * bs]) for j in range(nblk)]
+            for nb in (0, 1, 3, nblk, nblk + 2):
+                got = orc.topk_blocks(sig, nb, bs)
+                assert got.shape == (nb * bs,)
+                kb = min(nb, nblk)
+                chosen = [int(got[r * bs]) // bs for r in range(kb)]
+                assert chosen == sorted(set(chosen)) and len(chosen) == kb, (n, bs, nb)
+                for c in chosen:
+                    for j in set(range(nblk)) - set(chosen):
+                        assert score[c] > score[j] or (score[c] == score[j] and c < j), (n, bs, nb, c, j)
+                want = [t for c in chosen for t in list(range(c * bs, min(n, c * bs + bs))) +
+                        [-1] * (c * bs + bs - min(n, c * bs + bs))]
+                want += [-1] * (nb * bs - len(want))
+                assert got.tolist() == want, (n, bs, nb)
+                if bs == 1:
+                    assert got.tolist() == orc.topk(sig, nb).tolist()
+                if nb >= nblk:
+                    assert got[:n].tolist() == list(range(n))
+
+
+def test_topk_blocks_planted_token_selects_its_block(orc):
+    """One token far above the rest puts its block first; with one block of
+    budget exactly that block is listed."""
+    rng = np.random.default_rng(13)
+    sig = rng.standard_normal(1000)
+    for t in (0, 127, 128, 517, 999):
+        s = sig.copy()
+        s[t] = 50.0
+        got = orc.topk_blocks(s, 1, 128)
+        j = t // 128
+        want = list(range(j * 128, min(1000, j * 128 + 128)))
+        assert got.tolist() == want + [-1] * (128 - len(want)), t
+
+
+def test_blocks_covering_everything_equals_dense_attention(orc):
+    """A block budget covering the context corrects every token: the output
+    is dense fp16 attention."""
+    w = small_workload(kbits=4, vbits=4, L=120)
+    inp = make_inputs(w)
+    cache = build(orc, w, inp)
+    lens = np.full(w.B, w.L)
+    r0 = cache.decode(inp.q, lens, k=0, want_approx=True)
+    nb, bs = 4, 32
+    sel = np.stack([[orc.topk_blocks(r0["sigma"][b, h, :w.L], nb, bs) for h in range(w.Hkv)]
+                    for b in range(w.B)])
+    r = cache.decode(inp.q, lens, k=nb * bs, sel=sel)
+    ref = dense(inp.q.astype(np.float64), inp.K.astype(np.float64), inp.V.astype(np.float64), w.G)
+    np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
