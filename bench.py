@@ -49,6 +49,10 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="llama8b_k4v4_L32768",
                     help="workload name from bit_kv_attention_amd.synth.WORKLOADS, or 'all'")
     ap.add_argument("--shadow", choices=["hbm", "host"], default="hbm")
+    ap.add_argument("--blocks", type=int, default=0, metavar="NB",
+                    help="select NB whole blocks of --block tokens per KV head (topk_select_blocks) "
+                         "instead of the workload's top-k tokens")
+    ap.add_argument("--block", type=int, default=128)
     ap.add_argument("--window", type=int, default=0,
                     help="also correct the newest WINDOW tokens of every sequence (topk_select_window)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
@@ -114,12 +118,18 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     del Kd, Vd
     torch.cuda.synchronize()
     W = args.window
-    st = DecodeStep(lay, w.k, L, device=dev, window=W)
+    NB = args.blocks
+    if NB:
+        st = DecodeStep(lay, NB, L, device=dev, block=args.block)
+    else:
+        st = DecodeStep(lay, w.k, L, device=dev, window=W)
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
 
     def select():
-        if W > 0:
+        if NB > 0:
+            bk.topk_select_blocks(lay, st.sigma, lens, NB, args.block, st.idx)
+        elif W > 0:
             bk.topk_select_window(lay, st.sigma, lens, w.k, W, st.idx, st.ws)
         else:
             bk.topk_select(lay, st.sigma, lens, w.k, st.idx, st.ws)
@@ -195,7 +205,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
-                   "group": w.group, "top_k": w.k, "recent_window": W, "shadow": args.shadow,
+                   "group": w.group, "top_k": 0 if NB else w.k, "recent_window": W,
+                   "blocks": NB, "block": args.block if NB else 0, "shadow": args.shadow,
                    "cache_copies": copies,
                    "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
@@ -207,7 +218,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "kernel_us_per_launch": round(scan_us_timed, 2)},
     }
-    if not args.no_cpu_baseline and W == 0:  # the oracle's timed path has no window
+    if not args.no_cpu_baseline and W == 0 and NB == 0:  # the oracle's timed path has no window
         res["cpu_baseline"] = cpu_baseline(w, inp, knew, vnew, args.cpu_threads)
     del caches
     torch.cuda.empty_cache()

@@ -60,13 +60,15 @@ _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
+_lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
-           "topk_select", "topk_select_window", "qattn_correct"):
+           "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
 
 EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append",
-            "qattn_decode_approx", "topk_select", "topk_select_window", "qattn_correct")
+            "qattn_decode_approx", "topk_select", "topk_select_window", "topk_select_blocks",
+            "qattn_correct")
 
 
 def _check(fn: str, st: int) -> None:
@@ -171,6 +173,12 @@ def topk_select_window(layout: Layout, sigma, len_host, k: int, window: int, idx
     _check("topk_select_window", _lib.topk_select_window(C.byref(layout), _ptr(sigma), lens.ctypes.data, int(k),
                                                          int(window), _ptr(idx), _ptr(ws), ws_bytes,
                                                          _stream(stream)))
+
+
+def topk_select_blocks(layout: Layout, sigma, len_host, n_blocks: int, block: int, idx, stream=None) -> None:
+    lens = _host_i32(len_host)
+    _check("topk_select_blocks", _lib.topk_select_blocks(C.byref(layout), _ptr(sigma), lens.ctypes.data,
+                                                         int(n_blocks), int(block), _ptr(idx), _stream(stream)))
 
 
 def qattn_correct(layout: Layout, cache: Cache, q, len_host, idx, k: int, ws, out, stream=None) -> None:

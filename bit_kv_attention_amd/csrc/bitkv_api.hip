@@ -231,6 +231,25 @@ bkv_status topk_select_window(const bkv_layout* L, const float* sigma, const int
   return topk_rows(L, sigma, len_host, k, window, idx, ws, ws_bytes, stream);
 }
 
+bkv_status topk_select_blocks(const bkv_layout* L, const float* sigma, const int32_t* len_host,
+                              int32_t n_blocks, int32_t block, int32_t* idx, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (n_blocks < 0 || block < 32 || block > 1024 || (block & (block - 1)) != 0 ||
+      (long long)n_blocks * block > 0x7FFFFFFF)
+    return BKV_E_ARG;
+  if ((L->capacity + block - 1) / block > kTopkBlocksMax) return BKV_E_UNSUPPORTED;
+  if (!sigma || (!idx && n_blocks > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  if (n_blocks == 0) return BKV_OK;
+  int lgb = 0;
+  while ((1 << lgb) < block) ++lgb;
+  return launch_topk_blocks(*L, sigma, len, n_blocks, lgb, idx, (hipStream_t)stream) == hipSuccess ? BKV_OK
+                                                                                                 : BKV_E_HIP;
+}
+
 bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
                          const int32_t* len_host, const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream) {

@@ -96,6 +96,7 @@ constexpr int kTopkSliceMax = 8192;
 constexpr int kTopkSliceMin = 2048;
 constexpr int kTopkGridMin = 256;
 constexpr int kTopkMergeMax = 16384;
+constexpr int kTopkBlocksMax = 8192;  // blocks per unit for block selection (ceil(capacity / block))
 int topk_slice(int units, int max_len, int k);
 
 struct Workspace {
@@ -123,6 +124,9 @@ hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uin
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 hipStream_t s);
+// Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
+hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
+                              int32_t* idx, hipStream_t s);
 // Rows of k + W entries per unit (W: the recent window, 0 for none).
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);

@@ -408,7 +408,110 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
                                s_wsum, s_res, s_mm, s_small);
 }
 
+// ---- block selection -----------------------------------------------------
+// One workgroup per unit.  Block j holds tokens [j*bs, min(n, j*bs + bs)) and
+// scores the largest sigma among them (Jet-QSparse abstract: the dense scan's
+// scores choose whole 128-token blocks per KV head).  The block maxima come
+// from coalesced 16-byte loads (a wave covers 256 contiguous tokens per load,
+// bs/4 lanes per block reduce by butterfly shuffles; a block longer than 256
+// tokens takes several loads of one wave) into LDS; the select finds the
+// kb-th largest (score, block) composite as the token top-k does; the chosen
+// blocks are ranked in ascending order and the row is written as their
+// tokens, block r at [r*bs, r*bs + bs), -1 past n.
+constexpr int kBlkMax = kTopkBlocksMax;
+constexpr int kBlkPer = kBlkMax / kThreads;
+constexpr int kBlkBatch = 4;  // spans per wave with loads in flight together
+
+__global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __restrict__ sigma,
+                                                               int32_t* __restrict__ idx, SeqArg lens, int Hkv,
+                                                               int cap, int nb, int lgb) {
+  __shared__ uint32_t s_bkey[kBlkMax];  // float_key of each block's largest score; then the chosen blocks
+  __shared__ uint32_t s_hist[kHistBins];
+  __shared__ int s_wsum[kWaves];
+  __shared__ int s_res[4];
+  __shared__ float s_mm[2 * kWaves];
+  __shared__ uint64_t s_small[65];
+  const int u = blockIdx.x;
+  const int n = lens.v[u / Hkv];
+  const int bs = 1 << lgb;
+  const int nblk = (n + bs - 1) >> lgb;
+  const int kb = min(nb, nblk);
+  const int row = nb << lgb;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* __restrict__ out = idx + (size_t)u * row;
+  if (kb == nblk) {  // every block (or none): the tokens in order
+    for (int i = tid; i < row; i += kThreads) out[i] = (i < n) ? i : -1;
+    return;
+  }
+
+  // block maxima: wave wv takes spans of max(bs, 256) tokens
+  const float* __restrict__ sg = sigma + (size_t)u * cap;
+  const int span = bs > 256 ? bs : 256;
+  const int nspan = (n + span - 1) / span;
+  const int G = (bs < 256 ? bs : 256) / 4;  // lanes per block in one load
+  for (int s0 = wv; s0 < nspan; s0 += kBlkBatch * kWaves) {
+    float m[kBlkBatch];
+#pragma unroll
+    for (int i = 0; i < kBlkBatch; ++i) m[i] = -INFINITY;
+    for (int c = 0; c < span; c += 256) {
+      float4 x[kBlkBatch];
+#pragma unroll
+      for (int i = 0; i < kBlkBatch; ++i) {  // clamped: every load unconditional and inside the unit's row
+        const int t = (s0 + i * kWaves) * span + c + 4 * lane;
+        x[i] = *reinterpret_cast<const float4*>(sg + min(t, cap - 4));
+      }
+#pragma unroll
+      for (int i = 0; i < kBlkBatch; ++i) {
+        const int t = (s0 + i * kWaves) * span + c + 4 * lane;
+        const float a = fmaxf(t < n ? x[i].x : -INFINITY, t + 1 < n ? x[i].y : -INFINITY);
+        const float b = fmaxf(t + 2 < n ? x[i].z : -INFINITY, t + 3 < n ? x[i].w : -INFINITY);
+        m[i] = fmaxf(m[i], fmaxf(a, b));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBlkBatch; ++i) {
+      for (int off = 1; off < G; off <<= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], off));
+      const int j = ((s0 + i * kWaves) * span + 4 * lane) >> lgb;
+      if ((lane & (G - 1)) == 0 && j < nblk) s_bkey[j] = float_key(m[i]);
+    }
+  }
+  __syncthreads();
+
+  // the kb best blocks: entry j = i*kThreads + tid
+  uint64_t c[kBlkPer];  // 0: no block
+#pragma unroll
+  for (int i = 0; i < kBlkPer; ++i) {
+    const int j = i * kThreads + tid;
+    c[i] = (j < nblk) ? (((uint64_t)s_bkey[j] << 32) | (uint64_t)(~(uint32_t)j)) : 0ull;
+  }
+  auto get = [&](int j) { return ((uint64_t)s_bkey[j] << 32) | (uint64_t)(~(uint32_t)j); };
+  auto fill = [] {};  // the keys are in LDS already
+  const uint64_t T = hist_select<kThreads>(c, nblk, kb, get, fill, s_hist, s_wsum, s_res, s_mm, s_small);
+  bool sel[kBlkPer];
+#pragma unroll
+  for (int i = 0; i < kBlkPer; ++i) sel[i] = c[i] && c[i] >= T;
+  int at[kBlkPer];
+  ordered_positions<kBlkPer, kWaves>(sel, at, s_wsum, reinterpret_cast<int*>(s_hist));
+  // (every read of s_bkey is behind the barriers of ordered_positions)
+#pragma unroll
+  for (int i = 0; i < kBlkPer; ++i)
+    if (sel[i]) s_bkey[at[i]] = (uint32_t)(i * kThreads + tid);
+  __syncthreads();
+  for (int i = tid; i < row; i += kThreads) {
+    const int t = (int)s_bkey[i >> lgb] * bs + (i & (bs - 1));  // i >> lgb < kb = nb here
+    out[i] = (t < n) ? t : -1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
+                              int32_t* idx, hipStream_t s) {
+  const int units = L.batch * L.n_kv_heads;
+  (void)hipGetLastError();  // report only this call's launch
+  topk_blocks_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, nb, lgb);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s) {

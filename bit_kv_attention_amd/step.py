@@ -8,14 +8,19 @@ from . import binding as bk
 class DecodeStep:
     """Buffers for steps of one layer shape: sigma, workspace, idx, out.
     window > 0 also corrects the newest `window` tokens of every sequence
-    (topk_select_window); the rows of idx then hold k + window entries."""
+    (topk_select_window); the rows of idx then hold k + window entries.
+    block > 0 selects k whole blocks of `block` tokens instead
+    (topk_select_blocks); the rows then hold k * block entries."""
 
-    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0):
+    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0):
         import torch
         self.layout = layout
         self.k = int(k)
         self.window = int(window)
-        self.row = self.k + self.window
+        self.block = int(block)
+        if self.block and self.window:
+            raise ValueError("a recent window and block selection do not combine")
+        self.row = self.k * self.block if self.block else self.k + self.window
         L = layout
         self.sigma = torch.empty(L.batch * L.n_kv_heads * L.capacity, dtype=torch.float32, device=device)
         ws_bytes = bk.bkv_workspace_bytes(L, max_len, self.row)
@@ -27,7 +32,10 @@ class DecodeStep:
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
         bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
-        if self.window > 0:
+        if self.block > 0:
+            if self.k > 0:
+                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, stream)
+        elif self.window > 0:
             bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
         elif self.k > 0:
             bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, self.ws, stream)

@@ -17,6 +17,7 @@
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
  *   topk_select          top-k tokens per KV head by the selection score
  *   topk_select_window   the same, plus the newest tokens always selected
+ *   topk_select_blocks   or whole blocks of tokens by their best score
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
  *
@@ -194,6 +195,26 @@ bkv_status topk_select_window(const bkv_layout* layout, const float* sigma,
                               const int32_t* len_host, int32_t k,
                               int32_t window, int32_t* idx, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * topk_select_blocks -- block-granular selection: per (b, kvh) block j holds
+ * tokens [j*block, min(len, j*block + block)) and scores the largest sigma
+ * among them; the min(n_blocks, ceil(len/block)) best blocks are chosen, ties
+ * to the lower block (Jet-QSparse abstract: the dense scan's scores select
+ * 128-token blocks per KV head for exact fp16 value aggregation).
+ * idx [B][Hkv][n_blocks * block] int32 (device): the chosen blocks in
+ * ascending order, chosen block r as its tokens at idx[r*block ..
+ * r*block + block) (-1 past len), then -1; qattn_correct takes it with
+ * n_blocks * block as its k (size ws with bkv_workspace_bytes(layout,
+ * max_len, n_blocks * block)).  Needs no workspace.  n_blocks == 0 enqueues
+ * nothing.
+ * Errors: BKV_E_ARG unless block is a power of two in [32, 1024],
+ * n_blocks >= 0 and n_blocks * block fits int32; BKV_E_UNSUPPORTED if
+ * ceil(capacity / block) > 8192; BKV_E_CAPACITY for a bad length.
+ */
+bkv_status topk_select_blocks(const bkv_layout* layout, const float* sigma,
+                              const int32_t* len_host, int32_t n_blocks,
+                              int32_t block, int32_t* idx, void* stream);
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply

@@ -375,3 +375,82 @@ def test_step_parity_window(P, kb, vb, G, W):
     P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
     orc_o = pair["oc"].decode(pair["q"], lens, k + W, sel=sel_o)
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
+
+
+@pytest.mark.parametrize("L,nb,bs,ties", [(32768, 16, 128, False), (32768, 16, 128, True), (131072, 64, 128, True),
+                                          (40000, 3, 1024, False), (9000, 70, 32, True), (5000, 50, 128, False),
+                                          (6000, 7, 512, True)])
+def test_topk_blocks_on_given_scores(P, L, nb, bs, ties):
+    """topk_select_blocks on given scores against the oracle: distinct and
+    massively tied block scores (the select's fallback), a budget covering
+    every block, blocks longer than one load, a ragged last block, len 0;
+    two calls in a row."""
+    banner(f"block top-k L={L} nb={nb} bs={bs} ties={ties}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd import binding as bk
+    B, Hkv = 3, 2
+    cap = ((L + 31) // 32) * 32
+    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, 4, 4)
+    rng = np.random.default_rng(L + nb + bs)
+    if ties:
+        sig = (np.round(rng.standard_normal((B, Hkv, cap)) * 64) / 64).astype(np.float32)
+        sig[:, :, ::97] = 3.5  # nearly every block ties at the top
+    else:
+        sig = rng.standard_normal((B, Hkv, cap)).astype(np.float32)
+    lens = [L, L // 3 + 5, 0]
+    row = nb * bs
+    sigd = torch.from_numpy(sig.reshape(-1)).cuda()
+    idxd = torch.empty(B * Hkv * row, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        idxd.fill_(-7)
+        bk.topk_select_blocks(lay, sigd, lens, nb, bs, idxd)
+        torch.cuda.synchronize()
+        idx = idxd.cpu().numpy().reshape(B, Hkv, row)
+        for b in range(B):
+            for h in range(Hkv):
+                want = oracle.topk_blocks(sig[b, h, :lens[b]].astype(np.float64), nb, bs)
+                assert np.array_equal(idx[b, h], want), (rep, b, h)
+
+
+@pytest.mark.parametrize("kb,vb,G,nb,bs", [(4, 4, 4, 6, 128), (3, 2, 8, 20, 32)])
+def test_step_parity_blocks(P, kb, vb, G, nb, bs):
+    """A whole step with block selection: the GPU's rows against the oracle's
+    block selection on the GPU's scores (exact) and on its own (chosen blocks
+    may differ only by near-ties of the block score), the output against the
+    oracle on both rows."""
+    banner(f"step blocks kb={kb} vb={vb} G={G} nb={nb} bs={bs}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("blk", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 700 + G + nb)
+    pair = P.build_pair(w, L=3000, cap=3008)
+    lens = np.array([3000, 1234, 77])
+    pos = [int(x) - 1 for x in lens]
+    bk.kv_pack_append(pair["lay"], pair["gc"], P.to_dev(pair["k1"]), P.to_dev(pair["v1"]), 1, pos)
+    pair["oc"].append(pair["k1"], pair["v1"], np.array(pos, np.int32))
+    st = DecodeStep(pair["lay"], nb, 3000, block=bs)
+    out = st.attend(pair["gc"], P.to_dev(pair["q"]), lens)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    sigma = st.sigma.cpu().numpy().reshape(w.B, w.Hkv, pair["cap"])
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, nb * bs)
+    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True)
+    sel_o = np.full_like(idx, -1)
+    for b in range(w.B):
+        n = lens[b]
+        np.testing.assert_allclose(sigma[b, :, :n], orc["sigma"][b, :, :n], rtol=1e-5, atol=2e-5)
+        nblk = -(-n // bs)
+        for h in range(w.Hkv):
+            want = oracle.topk_blocks(sigma[b, h, :n].astype(np.float64), nb, bs)
+            assert np.array_equal(idx[b, h], want), (b, h)
+            sel_o[b, h] = oracle.topk_blocks(orc["sigma"][b, h, :n], nb, bs)
+            bscore = np.array([orc["sigma"][b, h, j * bs:min(n, j * bs + bs)].max() for j in range(nblk)])
+            kbk = min(nb, nblk)
+            P.assert_topk_near_tie(idx[b, h, ::bs][:kbk] // bs, sel_o[b, h, ::bs][:kbk] // bs, bscore, nblk,
+                                   f"b{b}h{h}")
+    orc_s = pair["oc"].decode(pair["q"], lens, nb * bs, sel=idx)
+    P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
+    orc_o = pair["oc"].decode(pair["q"], lens, nb * bs, sel=sel_o)
+    P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
