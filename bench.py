@@ -1,8 +1,10 @@
 """Benchmark of one approximate-then-correct decode-attention step on one GPU.
 
 A step is one pass of the whole hot path for one attention layer, all heads:
-kv_pack_append (one new token per sequence) -> qattn_decode_approx ->
-topk_select -> qattn_correct, over the workload's context length.  Inputs are
+kv_pack_append (one new token per sequence) -> qattn_decode_select (the
+approximate scan with the per-KV-head top-k in the same launch; or, with
+--two-launch, qattn_decode_approx -> topk_select) -> qattn_correct, over the
+workload's context length.  Inputs are
 seeded synthetic tensors (bit_kv_attention_amd.synth), resident in HBM before
 timing starts.  The timed steps rotate over several independent cache copies
 (as separate layers would) so that the packed bytes read per rotation exceed
@@ -53,6 +55,8 @@ def main(argv=None) -> int:
                     help="select NB whole blocks of --block tokens per KV head (topk_select_blocks) "
                          "instead of the workload's top-k tokens")
     ap.add_argument("--block", type=int, default=128)
+    ap.add_argument("--two-launch", action="store_true",
+                    help="run the scan and the top-k as two calls (qattn_decode_approx, topk_select)")
     ap.add_argument("--window", type=int, default=0,
                     help="also correct the newest WINDOW tokens of every sequence (topk_select_window)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
@@ -122,7 +126,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     if NB:
         st = DecodeStep(lay, NB, L, device=dev, block=args.block)
     else:
-        st = DecodeStep(lay, w.k, L, device=dev, window=W)
+        st = DecodeStep(lay, w.k, L, device=dev, window=W, fused=not args.two_launch)
+    fused = st.fused and not NB and not W
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
 
@@ -154,9 +159,13 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         cache = caches[i % copies]
         bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
         sev[i][0].record()
-        bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws)
-        sev[i][1].record()
-        select()
+        if fused:
+            bk.qattn_decode_select(lay, cache, q, lens, w.k, st.sigma, st.idx, st.ws)
+            sev[i][1].record()
+        else:
+            bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws)
+            sev[i][1].record()
+            select()
         bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
     e1.record()
     torch.cuda.synchronize()
@@ -165,18 +174,25 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     scan_us_timed = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in sev]))
 
     # Per-call breakdown: the same steps again with events around each call.
-    names = ("kv_pack_append", "qattn_decode_approx", "topk_select", "qattn_correct")
+    if fused:
+        names = ("kv_pack_append", "qattn_decode_select", "qattn_correct")
+        calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                 lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
+                 lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))
+    else:
+        names = ("kv_pack_append", "qattn_decode_approx", "topk_select", "qattn_correct")
+        calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                 lambda c: bk.qattn_decode_approx(lay, c, q, lens, st.sigma, st.ws),
+                 lambda c: select(),
+                 lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(args.steps)]
     for i in range(args.steps):
         cache = caches[i % copies]
-        e = ev[i]
-        e[0][0].record(); bk.kv_pack_append(lay, cache, kn, vn, 1, pos); e[0][1].record()
-        e[1][0].record(); bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws); e[1][1].record()
-        e[2][0].record(); select(); e[2][1].record()
-        e[3][0].record()
-        bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
-        e[3][1].record()
+        for j, call in enumerate(calls):
+            ev[i][j][0].record()
+            call(cache)
+            ev[i][j][1].record()
     torch.cuda.synchronize()
     kus = {n: 1000.0 * float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
            for j, n in enumerate(names)}
@@ -185,8 +201,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     packed_gbps = packed / (ms / 1000.0) / 1e9
     # dominant kernel: the approximate scan.  Algorithmic bytes per launch =
     # packed codes + meta of K and V for every token of every unit, the fp32
-    # selection score written per token, and the split partial states written.
-    scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L)
+    # selection score written per token, and the split partial states written
+    # (plus, with the selection in the same launch, the k indices per unit).
+    scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L) + (units * w.k * 4 if fused else 0)
     scan_s = scan_us_timed / 1e6
     achieved = scan_bytes / scan_s / 1e9
     traffic = measured_traffic(w.name)
@@ -208,12 +225,12 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                    "group": w.group, "top_k": 0 if NB else w.k, "recent_window": W,
                    "blocks": NB, "block": args.block if NB else 0, "shadow": args.shadow,
                    "cache_copies": copies,
-                   "parallelism": "single GPU"},
+                   "selection_in_scan_launch": fused, "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
         "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": {n: round(v, 2) for n, v in kus.items()},
         "wall_s_timed_region": round(t_wall, 3),
-        "roofline": {"kernel": "qattn_decode_approx", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "qattn_decode_select" if fused else "qattn_decode_approx", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "kernel_us_per_launch": round(scan_us_timed, 2)},

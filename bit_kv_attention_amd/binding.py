@@ -59,15 +59,16 @@ _lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, C.c_int32, _SZ]
 _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
+_lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
-           "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
+           "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
 
 EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append",
-            "qattn_decode_approx", "topk_select", "topk_select_window", "topk_select_blocks",
+            "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct")
 
 
@@ -158,6 +159,15 @@ def qattn_decode_approx(layout: Layout, cache: Cache, q, len_host, sigma, ws, st
     _check("qattn_decode_approx", _lib.qattn_decode_approx(C.byref(layout), C.byref(view), _ptr(q),
                                                            lens.ctypes.data, _ptr(sigma), _ptr(ws),
                                                            ws_bytes, _stream(stream)))
+
+
+def qattn_decode_select(layout: Layout, cache: Cache, q, len_host, k: int, sigma, idx, ws, stream=None) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_decode_select", _lib.qattn_decode_select(C.byref(layout), C.byref(view), _ptr(q),
+                                                           lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
+                                                           _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def topk_select(layout: Layout, sigma, len_host, k: int, idx, ws, stream=None) -> None:

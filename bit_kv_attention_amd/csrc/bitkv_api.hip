@@ -80,7 +80,15 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
   w.part.m = reinterpret_cast<float*>(take(recs * 4));
   w.part.l = reinterpret_cast<float*>(take(recs * 4));
   w.cs = reinterpret_cast<float*>(take((size_t)L.batch * L.n_q_heads * w.nchunk * kCsStride * 4));
-  w.tkc = reinterpret_cast<uint64_t*>(take((size_t)units * topk_slots(max_len, k) * 8));
+  // candidate slots: the top-k kernels', or the scan's own selection (nsplit
+  // slots of k; used only when they fit kSelSlots, so that bounds them)
+  size_t slots = topk_slots(max_len, k);
+  if (k > 0) {
+    const long long f = (long long)w.nsplit * k;
+    const size_t fs = (size_t)(bound ? (f < kSelSlots ? f : kSelSlots) : (f <= kSelSlots ? f : 0));
+    slots = fs > slots ? fs : slots;
+  }
+  w.tkc = reinterpret_cast<uint64_t*>(take((size_t)units * slots * 8));
   w.bytes = off;
   return w;
 }
@@ -197,10 +205,33 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
   const int units = L->batch * L->n_kv_heads;
   const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), (hipStream_t)stream) ==
-                 hipSuccess
+  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0,
+                              (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
+}
+
+bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                               const int32_t* len_host, int32_t k, float* sigma, int32_t* idx, void* ws,
+                               size_t ws_bytes, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if (!q || !sigma || !ws || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  const int chunk = split_tokens(units, max_len);
+  const hipStream_t s = (hipStream_t)stream;
+  if (k > 0 && chunk <= kSelStage && (long long)w.nsplit * k <= kSelSlots)  // selection inside the scan
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, s) != hipSuccess) return BKV_E_HIP;
+  if (k == 0) return BKV_OK;
+  return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
 
 static bkv_status topk_rows(const bkv_layout* L, const float* sigma, const int32_t* len_host, int32_t k,

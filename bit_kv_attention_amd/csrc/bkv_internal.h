@@ -97,6 +97,10 @@ constexpr int kTopkSliceMin = 2048;
 constexpr int kTopkGridMin = 256;
 constexpr int kTopkMergeMax = 16384;
 constexpr int kTopkBlocksMax = 8192;  // blocks per unit for block selection (ceil(capacity / block))
+// Top-k inside the approximate scan: a split's scores staged in LDS, and the
+// unit's candidate slots (nsplit * k) merged in LDS.
+constexpr int kSelStage = 16384;
+constexpr int kSelSlots = 8192;
 int topk_slice(int units, int max_len, int k);
 
 struct Workspace {
@@ -121,9 +125,11 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
 // Launchers (return hipGetLastError of their launches).
 hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_new,
                               const uint16_t* v_new, int n_new, const SeqArg& pos, hipStream_t s);
+// ksel > 0: the same launch also writes the top-ksel rows to idx (its split
+// length chunk <= kSelStage and nsplit * ksel <= kSelSlots).
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                hipStream_t s);
+                                int32_t* idx, int ksel, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
                               int32_t* idx, hipStream_t s);

@@ -39,6 +39,7 @@
 //    and V meta) and handed out through a per-wave LDS slot.  Selection scores
 //    are staged in LDS and stored every 8 steps as one coalesced store.
 #include "bkv_internal.h"
+#include "select_lds.h"
 
 namespace bkv {
 namespace {
@@ -332,12 +333,17 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
   }
 }
 
-template <int KB, int VB, int G>
+// SEL: the launch also selects the top-ksel tokens per unit (the same set
+// topk_select finds): each workgroup keeps its split's selection scores in
+// LDS, leaves the split's top-min(kk, split length) composites in index order
+// in cand, and the unit's last workgroup to finish merges them into idx.
+template <int KB, int VB, int G, bool SEL>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
-    float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk) {
+    float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
+    uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -418,13 +424,19 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
   // Selection scores go through a per-wave LDS buffer of kSigBatch steps and
   // leave as one coalesced 16-byte-per-lane store (no stores in the steps).
   __shared__ floatx4 s_sig[kScanWaves][kSigBatch][8];
+  // SEL: the split's selection scores, as stored ([t - t_begin])
+  __shared__ __attribute__((aligned(16))) float s_split[SEL ? kSelStage : 1];
   int sig_count = 0;   // steps staged
   int sig_first = 0;   // t0 of the first staged step
   auto flush_sig = [&]() {
     wave_lds_order();
     const int i = lane >> 3;
-    if (i < sig_count)
-      *reinterpret_cast<floatx4*>(sig + sig_first + kScanWaves * kTile * i + 4 * (lane & 7)) = s_sig[wv][i][lane & 7] * c_sig;
+    if (i < sig_count) {
+      const int t = sig_first + kScanWaves * kTile * i + 4 * (lane & 7);
+      const floatx4 v = s_sig[wv][i][lane & 7] * c_sig;
+      *reinterpret_cast<floatx4*>(sig + t) = v;
+      if constexpr (SEL) *reinterpret_cast<floatx4*>(&s_split[t - t_begin]) = v;
+    }
     wave_lds_order();
     sig_count = 0;
   };
@@ -546,37 +558,77 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
       pl[rec] = l;
     }
   }
+
+  if constexpr (SEL) {
+    // ---- the split's top-min(kk, split length), then the unit's merge -----------
+    // (the barrier above ordered every flush before these reads)
+    constexpr int NT = 64 * kScanWaves;
+    __shared__ uint32_t s_hist[kHistBins];
+    __shared__ int s_wsum[kScanWaves];
+    __shared__ int s_res[4];
+    __shared__ int s_last;
+    __shared__ float s_mm[2 * kScanWaves];
+    __shared__ uint64_t s_small[65];
+    const int kk = min(ksel, len);
+    const int len_s = max(0, t_end - t_begin);
+    uint64_t* __restrict__ ucand = cand + (size_t)u * nsplit * ksel;
+    if (0 < kk && kk < len && len_s > 0) {
+      const int cnt = min(kk, len_s);
+      auto get = [&](int i) { return composite(s_split[i], t_begin + i); };
+      const uint64_t T =
+          (cnt == len_s) ? 0 : hist_select_lds<NT>(get, len_s, cnt, s_hist, s_wsum, s_res, s_mm, s_small);
+      uint64_t* __restrict__ dst = ucand + (size_t)split * ksel;
+      auto keep = [&](int i) { return i < len_s && get(i) >= T; };
+      auto put = [&](int i, int r) { st_dev64(&dst[r], get(i)); };
+      ordered_put<NT>(len_s, keep, put, s_wsum, reinterpret_cast<int*>(s_hist));
+      for (int j = cnt + tid; j < ksel; j += NT) st_dev64(&dst[j], 0ull);  // the split's unused slots
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's candidates are written
+    __syncthreads();
+    if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == (uint32_t)nsplit - 1);
+    __syncthreads();
+    if (!s_last) return;
+    merge_unit<NT, true, kSelSlots>(ucand, idx, u, len, 0, ksel, 0, chunk, reinterpret_cast<uint64_t*>(s_split),
+                                    s_hist, s_wsum, s_res, s_mm, s_small);
+    if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
+  }
 }
 
 template <int KB, int VB, int G>
 hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, hipStream_t s) {
   dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
   (void)hipGetLastError();  // report only this launch's status
-  decode_approx_kernel<KB, VB, G><<<grid, 64 * kScanWaves, 0, s>>>(
-      static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
-      c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
-      L.n_kv_heads, L.capacity, w.nsplit, chunk);
+  if (ksel > 0)
+    decode_approx_kernel<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
+        c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
+        L.n_kv_heads, L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel);
+  else
+    decode_approx_kernel<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
+        static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
+        c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
+        L.n_kv_heads, L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
 hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, hipStream_t s) {
   const int G = L.n_q_heads / L.n_kv_heads;
-  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, s);
-  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, s);
+  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                hipStream_t s) {
-  if (L.k_bits == 4 && L.v_bits == 4) return launch_g<4, 4>(L, c, q, len, sigma, w, chunk, s);
-  if (L.k_bits == 4 && L.v_bits == 2) return launch_g<4, 2>(L, c, q, len, sigma, w, chunk, s);
-  if (L.k_bits == 3 && L.v_bits == 4) return launch_g<3, 4>(L, c, q, len, sigma, w, chunk, s);
-  return launch_g<3, 2>(L, c, q, len, sigma, w, chunk, s);
+                                int32_t* idx, int ksel, hipStream_t s) {
+  if (L.k_bits == 4 && L.v_bits == 4) return launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+  if (L.k_bits == 4 && L.v_bits == 2) return launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+  if (L.k_bits == 3 && L.v_bits == 4) return launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+  return launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
 }
 
 }  // namespace bkv

@@ -57,7 +57,7 @@ __device__ inline float wave_minmax(float x) {
 // totals through LDS); `total` gets the sum of all.
 template <int NW>
 __device__ inline int block_excl_scan(int v, int* s_wsum, int& total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63, wv = (int)__builtin_amdgcn_workitem_id_x() >> 6;
   const int x = wave_incl_scan(v);
   __syncthreads();
   if (lane == 63) s_wsum[wv] = x;
@@ -79,7 +79,7 @@ __device__ inline int block_excl_scan(int v, int* s_wsum, int& total) {
 // `need` entries >= T.  NT threads.
 template <int NT, typename Get>
 __device__ inline uint64_t lds_threshold(Get get, int count, int need, uint32_t* s_hist, int* s_wsum, int* s_res) {
-  const int tid = threadIdx.x;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
   uint64_t P = 0;
   int plen = 0;
   for (int lv = 0; lv < kLevels; ++lv) {
@@ -148,7 +148,7 @@ template <int NT, int PER, typename Get, typename Fill>
 __device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int need, Get get, Fill fill,
                                        uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm, uint64_t* s_small) {
   constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
   float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -225,6 +225,209 @@ __device__ inline uint64_t hist_select(const uint64_t (&c)[PER], int count, int 
   }
   __syncthreads();
   return s_small[64];
+}
+
+// Entries [kk, stride) of a unit's row: the nw window tokens n, n+1, ...,
+// then -1.  All NT threads of the workgroup.
+template <int NT>
+__device__ inline void write_tail(int32_t* __restrict__ out, int kk, int n, int nw, int stride) {
+  for (int i = (int)__builtin_amdgcn_workitem_id_x(); i < stride - kk; i += NT) out[kk + i] = (i < nw) ? n + i : -1;
+}
+
+// Candidates cross workgroups through agent-scope atomic stores and loads,
+// which the device performs at its coherence point (no cache maintenance).
+__device__ inline void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output positions of the selected entries held as entry j*NW*64 + 64w + lane
+// (wave w): their rank in that order among the selected ones.  Per (j, w) the
+// count comes from a ballot, one block scan over the PER*NW counts places
+// them.  s_tmp: PER*NW ints.
+template <int PER, int NW>
+__device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER], int* s_wsum, int* s_tmp) {
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  uint64_t mask[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    mask[j] = __ballot(sel[j]);
+    if (lane == 0) s_tmp[j * NW + wv] = __popcll(mask[j]);
+  }
+  __syncthreads();
+  const int cnt = (tid < PER * NW) ? s_tmp[tid] : 0;
+  int total;
+  const int before = block_excl_scan<NW>(cnt, s_wsum, total);  // (its barriers order the reads above)
+  if (tid < PER * NW) s_tmp[tid] = before;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) at[j] = s_tmp[j * NW + wv] + __popcll(mask[j] & below);
+}
+
+// The merge of one unit's candidate slots: slice s of S tokens left its
+// top-min(k, slice length) composites in index order at ucand[s*k ..], 0 in
+// its unused slots.  The kk = min(k, n)-th largest slot is found and the slots
+// >= it are written in slot order, which is ascending token order, to the
+// unit's row of k + W entries, then the window and -1 (write_tail).  All NT
+// threads.  AGENT: the slots were written by other workgroups of this launch.
+// At most MAXSLOTS slots.  n: tokens selected from (the window's nw follow).
+template <int NT, bool AGENT, int MAXSLOTS>
+__device__ __attribute__((always_inline)) inline void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int nw,
+                           int k, int W, int S, uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm,
+                           uint64_t* s_small) {
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int kk = min(k, n);
+  int32_t* __restrict__ out = idx + (size_t)u * (k + W);
+  write_tail<NT>(out, kk, n, nw, k + W);
+  if (kk == n || kk == 0) {  // every token (or none) is selected
+    for (int i = tid; i < kk; i += NT) out[i] = i;
+  } else {
+    const int ns = (n + S - 1) / S;  // slices holding tokens
+    const int slots = ns * k;
+    // thread tid holds slots j*NT + tid (coalesced loads)
+    constexpr int kPer = MAXSLOTS / NT;
+    uint64_t v[kPer];  // 0: empty
+    bool ok[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first (unused slots hold 0)
+      const int p = j * NT + tid;
+      const uint64_t* src = &ucand[min(p, slots - 1)];
+      v[j] = AGENT ? ld_dev64(src) : *src;
+      ok[j] = p < slots;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = ok[j] ? v[j] : 0;
+    auto get = [&](int i) { return s_c[i]; };
+    auto fill = [&]() {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (j * NT + tid < slots) s_c[j * NT + tid] = v[j];
+    };
+    const uint64_t T = hist_select<NT>(v, slots, kk, get, fill, s_hist, s_wsum, s_res, s_mm, s_small);
+    // the slots >= T in slot order (ascending token order): slot j*NT +
+    // 64w + lane is (j, w, lane) in that order
+    bool sel[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) sel[j] = v[j] && v[j] >= T;
+    int at[kPer];
+    ordered_positions<kPer, NT / 64>(sel, at, s_wsum, reinterpret_cast<int*>(s_hist));
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (sel[j]) out[at[j]] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
+  }
+}
+
+
+// hist_select over entries that live in LDS or are computed on the fly:
+// get(i) gives the composite of entry i for i < count (all nonzero); any
+// count.  Same steps and LDS arrays as hist_select; the radix fallback reads
+// get() directly.
+template <int NT, typename Get>
+__device__ inline uint64_t hist_select_lds(Get get, int count, int need, uint32_t* s_hist, int* s_wsum, int* s_res,
+                                           float* s_mm, uint64_t* s_small) {
+  constexpr int NW = NT / 64;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int i = tid; i < count; i += NT) {
+    const float x = key_value((uint32_t)(get(i) >> 32));
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  lo = wave_minmax<false>(lo);
+  hi = wave_minmax<true>(hi);
+  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
+  if (lane == 0) {
+    s_mm[wv] = lo;
+    s_mm[NW + wv] = hi;
+  }
+  if (tid == 0) s_res[2] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = fminf(lo, s_mm[w]);
+    hi = fmaxf(hi, s_mm[NW + w]);
+  }
+  const float scale = (float)kHistBins / (hi - lo);
+  auto bin = [&](uint64_t cc) {
+    const float f = (key_value((uint32_t)(cc >> 32)) - lo) * scale;
+    return (int)fminf(fmaxf(f, 0.0f), (float)(kHistBins - 1));
+  };
+  for (int i = tid; i < count; i += NT) atomicAdd(&s_hist[bin(get(i))], 1u);
+  __syncthreads();
+  constexpr int per = kHistBins / NT;
+  const int top = kHistBins - 1 - tid * per;
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < per; ++i) mine += (int)s_hist[top - i];
+  int total;
+  int above = block_excl_scan<NW>(mine, s_wsum, total);
+  if (above < need && above + mine >= need) {
+    for (int i = 0; i < per; ++i) {
+      const int h = (int)s_hist[top - i];
+      if (above + h >= need) {
+        s_res[0] = top - i;
+        s_res[1] = above;
+        break;
+      }
+      above += h;
+    }
+  }
+  __syncthreads();
+  const int D = s_res[0];
+  const int need2 = need - s_res[1];
+  const int mD = (int)s_hist[D];
+  if (mD > 64) {  // many entries share bin D: radix select among them
+    __syncthreads();  // s_hist is reused
+    auto getD = [&](int i) {
+      const uint64_t cc = get(i);
+      return (bin(cc) == D) ? cc : 0ull;
+    };
+    return lds_threshold<NT>(getD, count, need2, s_hist, s_wsum, s_res);
+  }
+  for (int i = tid; i < count; i += NT) {
+    const uint64_t cc = get(i);
+    if (bin(cc) == D) s_small[atomicAdd(&s_res[2], 1)] = cc;
+  }
+  __syncthreads();
+  if (wv == 0) {  // rank the (distinct) entries of bin D
+    const uint64_t x = lane < mD ? s_small[lane] : 0ull;
+    int rank = 0;
+    for (int i = 0; i < mD; ++i) rank += s_small[i] > x ? 1 : 0;
+    if (lane < mD && rank == need2 - 1) s_small[64] = x;
+  }
+  __syncthreads();
+  return s_small[64];
+}
+
+// Entries i < count with keep(i) true, in ascending i, get their rank among
+// the kept ones: put(i, rank).  Entry i = j*NT + tid; per (j, wave) one
+// ballot count, one block scan over them (at most NT counts: count <= NT*NT/64
+// entries).  s_tmp: ceil(count/NT)*NT/64 ints.
+template <int NT, typename Keep, typename Put>
+__device__ inline void ordered_put(int count, Keep keep, Put put, int* s_wsum, int* s_tmp) {
+  constexpr int NW = NT / 64;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+  const int per = (count + NT - 1) / NT;
+  for (int j = 0; j < per; ++j) {
+    const uint64_t mask = __ballot(keep(j * NT + tid));
+    if (lane == 0) s_tmp[j * NW + wv] = __popcll(mask);
+  }
+  __syncthreads();
+  const int cnt = (tid < per * NW) ? s_tmp[tid] : 0;
+  int total;
+  const int before = block_excl_scan<NW>(cnt, s_wsum, total);
+  if (tid < per * NW) s_tmp[tid] = before;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1;
+  for (int j = 0; j < per; ++j) {
+    const int i = j * NT + tid;
+    const bool k = keep(i);
+    const uint64_t mask = __ballot(k);
+    if (k) put(i, s_tmp[j * NW + wv] + __popcll(mask & below));
+  }
 }
 
 }  // namespace bkv

@@ -37,12 +37,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kCandMax = 4096;
 constexpr int kBatch = 16;  // scores per thread loaded together (independent loads in flight)
 
-// Entries [kk, stride) of a unit's row: the nw window tokens n, n+1, ...,
-// then -1.  All threads of the workgroup.
-__device__ inline void write_tail(int32_t* __restrict__ out, int kk, int n, int nw, int stride) {
-  for (int i = threadIdx.x; i < stride - kk; i += blockDim.x) out[kk + i] = (i < nw) ? n + i : -1;
-}
-
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ sigma, int32_t* __restrict__ idx,
                                                         SeqArg lens, int Hkv, int cap, int k, int W) {
   const int u = blockIdx.x;
@@ -55,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const float* __restrict__ sg = sigma + (size_t)u * cap;
   int32_t* __restrict__ out = idx + (size_t)u * (k + W);
 
-  write_tail(out, kk, n, nw, k + W);
+  write_tail<kThreads>(out, kk, n, nw, k + W);
   if (kk == n || kk == 0) {  // every token (or none) is selected
     for (int i = tid; i < kk; i += kThreads) out[i] = i;
     return;
@@ -224,87 +218,6 @@ constexpr int kLocalThreads = kThreads;
 constexpr int kLocalMax = kTopkSliceMax;   // slice tokens in LDS
 constexpr int kMergeMax = kTopkMergeMax;   // candidate slots in LDS per unit
 
-__device__ inline void st_dev64(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint64_t ld_dev64(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Output positions of the selected entries held as entry j*NW*64 + 64w + lane
-// (wave w): their rank in that order among the selected ones.  Per (j, w) the
-// count comes from a ballot, one block scan over the PER*NW counts places
-// them.  s_tmp: PER*NW ints.
-template <int PER, int NW>
-__device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER], int* s_wsum, int* s_tmp) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint64_t below = (1ull << lane) - 1;
-  uint64_t mask[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    mask[j] = __ballot(sel[j]);
-    if (lane == 0) s_tmp[j * NW + wv] = __popcll(mask[j]);
-  }
-  __syncthreads();
-  const int cnt = (tid < PER * NW) ? s_tmp[tid] : 0;
-  int total;
-  const int before = block_excl_scan<NW>(cnt, s_wsum, total);  // (its barriers order the reads above)
-  if (tid < PER * NW) s_tmp[tid] = before;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < PER; ++j) at[j] = s_tmp[j * NW + wv] + __popcll(mask[j] & below);
-}
-
-// The merge of one unit's candidate slots (see above); all kThreads threads.
-// AGENT: the slots were written by other workgroups of this launch.
-// At most MAXSLOTS slots.
-// n: tokens selected from (the window's nw follow them).
-template <bool AGENT, int MAXSLOTS>
-__device__ void merge_unit(const uint64_t* __restrict__ ucand, int32_t* __restrict__ idx, int u, int n, int nw,
-                           int k, int W, int S, uint64_t* s_c, uint32_t* s_hist, int* s_wsum, int* s_res, float* s_mm,
-                           uint64_t* s_small) {
-  const int tid = threadIdx.x;
-  const int kk = min(k, n);
-  int32_t* __restrict__ out = idx + (size_t)u * (k + W);
-  write_tail(out, kk, n, nw, k + W);
-  if (kk == n || kk == 0) {  // every token (or none) is selected
-    for (int i = tid; i < kk; i += kThreads) out[i] = i;
-  } else {
-    const int ns = (n + S - 1) / S;  // slices holding tokens
-    const int slots = ns * k;
-    // thread tid holds slots j*kThreads + tid (coalesced loads)
-    constexpr int kPer = MAXSLOTS / kThreads;
-    uint64_t v[kPer];  // 0: empty
-    bool ok[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {  // clamped, unconditional loads first (unused slots hold 0)
-      const int p = j * kThreads + tid;
-      const uint64_t* src = &ucand[min(p, slots - 1)];
-      v[j] = AGENT ? ld_dev64(src) : *src;
-      ok[j] = p < slots;
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = ok[j] ? v[j] : 0;
-    auto get = [&](int i) { return s_c[i]; };
-    auto fill = [&]() {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (j * kThreads + tid < slots) s_c[j * kThreads + tid] = v[j];
-    };
-    const uint64_t T = hist_select<kThreads>(v, slots, kk, get, fill, s_hist, s_wsum, s_res, s_mm, s_small);
-    // the slots >= T in slot order (ascending token order): slot j*kThreads +
-    // 64w + lane is (j, w, lane) in that order
-    bool sel[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) sel[j] = v[j] && v[j] >= T;
-    int at[kPer];
-    ordered_positions<kPer, kWaves>(sel, at, s_wsum, reinterpret_cast<int*>(s_hist));
-#pragma unroll
-    for (int j = 0; j < kPer; ++j)
-      if (sel[j]) out[at[j]] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
-  }
-}
-
 template <bool FUSED>
 __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float* __restrict__ sigma,
                                                                     uint64_t* __restrict__ cand,
@@ -386,7 +299,7 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
   __syncthreads();
   if (!s_last) return;
 
-  merge_unit<true, kLocalMax * 4 / 8>(ucand, idx, u, n, nw, k, W, S, reinterpret_cast<uint64_t*>(s_v), s_hist,
+  merge_unit<kThreads, true, kLocalMax * 4 / 8>(ucand, idx, u, n, nw, k, W, S, reinterpret_cast<uint64_t*>(s_v), s_hist,
                                       s_wsum, s_res, s_mm, s_small);
   if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
 }
@@ -404,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
   __shared__ uint64_t s_small[65];
   const int u = blockIdx.x;
   const int nw = min(W, lens.v[u / Hkv]);
-  merge_unit<false, kMergeMax>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv] - nw, nw, k, W, S, s_c, s_hist,
+  merge_unit<kThreads, false, kMergeMax>(cand + (size_t)u * cstride, idx, u, lens.v[u / Hkv] - nw, nw, k, W, S, s_c, s_hist,
                                s_wsum, s_res, s_mm, s_small);
 }
 

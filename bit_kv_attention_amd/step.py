@@ -10,10 +10,14 @@ class DecodeStep:
     window > 0 also corrects the newest `window` tokens of every sequence
     (topk_select_window); the rows of idx then hold k + window entries.
     block > 0 selects k whole blocks of `block` tokens instead
-    (topk_select_blocks); the rows then hold k * block entries."""
+    (topk_select_blocks); the rows then hold k * block entries.  Plain top-k
+    runs as qattn_decode_select (scan and selection in one launch where it
+    fits) unless fused is False."""
 
-    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0):
+    def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0,
+                 fused: bool = True):
         import torch
+        self.fused = bool(fused)
         self.layout = layout
         self.k = int(k)
         self.window = int(window)
@@ -31,6 +35,11 @@ class DecodeStep:
 
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
+        if self.fused and self.block == 0 and self.window == 0:
+            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream)
+            bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
+                             self.out, stream)
+            return self.out
         bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
         if self.block > 0:
             if self.k > 0:

@@ -15,6 +15,7 @@
  * One decode step is four calls on one stream:
  *   kv_pack_append       quantise + pack the new token(s), write the shadow
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
+ *   qattn_decode_select  the same and topk_select, in one launch where it fits
  *   topk_select          top-k tokens per KV head by the selection score
  *   topk_select_window   the same, plus the newest tokens always selected
  *   topk_select_blocks   or whole blocks of tokens by their best score
@@ -162,6 +163,24 @@ bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
                                const uint16_t* q, const int32_t* len_host,
                                float* sigma, void* ws, size_t ws_bytes,
                                void* stream);
+
+/*
+ * qattn_decode_select -- qattn_decode_approx followed by topk_select with the
+ * same layout, cache, q, lengths, k and workspace, with identical results
+ * (sigma, the split states in ws and idx [B][Hkv][k]).  Where the workspace
+ * layout allows (each scan workgroup's token range at most 16384 tokens and
+ * its number of ranges per (b, kvh) times k at most 8192) the selection runs
+ * inside the scan's launch: every workgroup keeps its range's sigma on chip,
+ * leaves its range's top-min(k, len) candidates in ws, and the last
+ * workgroup of each (b, kvh) to finish merges them; otherwise the two
+ * launches run.  k == 0 is qattn_decode_approx (idx may then be NULL).  Size
+ * ws with bkv_workspace_bytes(layout, max_len, k).
+ * Errors: as qattn_decode_approx and topk_select.
+ */
+bkv_status qattn_decode_select(const bkv_layout* layout, const bkv_cache* cache,
+                               const uint16_t* q, const int32_t* len_host,
+                               int32_t k, float* sigma, int32_t* idx, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /*
  * topk_select -- per (b, kvh): the min(k, len) tokens with the largest sigma,

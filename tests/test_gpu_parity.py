@@ -454,3 +454,40 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs):
     P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
     orc_o = pair["oc"].decode(pair["q"], lens, nb * bs, sel=sel_o)
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
+
+
+@pytest.mark.parametrize("kb,vb,G", COMBOS)
+def test_decode_select_equals_two_calls(P, kb, vb, G):
+    """qattn_decode_select (selection inside the scan's launch) against
+    qattn_decode_approx + topk_select on the same inputs: identical sigma, rows
+    and output, rows exact against the oracle's top-k of that sigma; ragged and
+    empty sequences, k = 1, k >= len, and a budget past the in-launch limit
+    (two launches)."""
+    banner(f"decode_select kb={kb} vb={vb} G={G}")
+    import torch
+    import oracle
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("sel", 4, 2 * G, 2, 128, 4000, kb, vb, 32, 32, 6, 900 + 10 * kb + vb + G)
+    pair = P.build_pair(w, L=4000, cap=4000)
+    lens = np.array([3999, 2500, 1, 0])  # (the prefill filled 3999 slots)
+    q = P.to_dev(pair["q"])
+    for k in (1, 37, 300, 500, 2600, 5000):  # 16 ranges per unit: 500 is the last in-launch budget
+        runs = []
+        for fused in (True, False):
+            st = DecodeStep(pair["lay"], k, 3999, fused=fused)
+            for _ in range(2):  # twice on one workspace
+                st.sigma.fill_(float("nan"))
+                st.idx.fill_(-7)
+                out = st.attend(pair["gc"], q, lens)
+            torch.cuda.synchronize()
+            runs.append((st.sigma.cpu().numpy().reshape(w.B, w.Hkv, -1), st.idx.cpu().numpy().reshape(w.B, w.Hkv, k),
+                         out.cpu().numpy()))
+        (s1, i1, o1), (s0, i0, o0) = runs
+        for b in range(w.B):
+            n = lens[b]
+            assert np.array_equal(s1[b, :, :n], s0[b, :, :n]), (k, b)
+            for h in range(w.Hkv):
+                want = oracle.topk(s1[b, h, :n].astype(np.float64), k)
+                assert np.array_equal(i1[b, h], want), (k, b, h)
+        assert np.array_equal(i1, i0), k
+        assert np.array_equal(o1, o0), k
