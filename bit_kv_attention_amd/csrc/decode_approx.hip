@@ -574,13 +574,29 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     uint64_t* __restrict__ ucand = cand + (size_t)u * nsplit * ksel;
     if (0 < kk && kk < len && len_s > 0) {
       const int cnt = min(kk, len_s);
+      // thread tid holds entries j*NT + tid in registers (0: past the range)
+      constexpr int PER = kSelStage / NT;
+      uint64_t c[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = j * NT + tid;
+        c[j] = (i < len_s) ? composite(s_split[i], t_begin + i) : 0ull;
+      }
       auto get = [&](int i) { return composite(s_split[i], t_begin + i); };
-      const uint64_t T =
-          (cnt == len_s) ? 0 : hist_select_lds<NT>(get, len_s, cnt, s_hist, s_wsum, s_res, s_mm, s_small);
+      auto fill = [] {};  // the scores are in LDS already
+      const uint64_t T = (cnt == len_s) ? 0
+                                        : hist_select<NT>(c, len_s, cnt, get, fill, s_hist, s_wsum, s_res, s_mm,
+                                                          s_small);
+      // the entries >= T in index order (entry j*NT + 64w + lane is (j, w, lane))
+      bool sel[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) sel[j] = c[j] && c[j] >= T;
+      int at[PER];
+      ordered_positions<PER, kScanWaves>(sel, at, s_wsum, reinterpret_cast<int*>(s_hist));
       uint64_t* __restrict__ dst = ucand + (size_t)split * ksel;
-      auto keep = [&](int i) { return i < len_s && get(i) >= T; };
-      auto put = [&](int i, int r) { st_dev64(&dst[r], get(i)); };
-      ordered_put<NT>(len_s, keep, put, s_wsum, reinterpret_cast<int*>(s_hist));
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if (sel[j]) st_dev64(&dst[at[j]], c[j]);
       for (int j = cnt + tid; j < ksel; j += NT) st_dev64(&dst[j], 0ull);  // the split's unused slots
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's candidates are written
