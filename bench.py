@@ -55,6 +55,9 @@ def main(argv=None) -> int:
                     help="select NB whole blocks of --block tokens per KV head (topk_select_blocks) "
                          "instead of the workload's top-k tokens")
     ap.add_argument("--block", type=int, default=128)
+    ap.add_argument("--exact", choices=["gpu", "host"], default="gpu",
+                    help="host: the exact half of the correction on the host's cores from a pinned host "
+                         "shadow (qattn_exact_host + qattn_correct_hybrid)")
     ap.add_argument("--two-launch", action="store_true",
                     help="run the scan and the top-k as two calls (qattn_decode_approx, topk_select)")
     ap.add_argument("--window", type=int, default=0,
@@ -116,7 +119,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     vn = torch.from_numpy(vnew[0]).to(dev)
     caches = []
     for c in range(copies):
-        cache = bk.allocate_cache(lay, device=dev, shadow_on_host=(args.shadow == "host"))
+        cache = bk.allocate_cache(lay, device=dev, shadow_on_host=(args.shadow == "host" or args.exact == "host"))
         bk.kv_pack_append(lay, cache, Kd, Vd, L - 1, [0] * w.B)
         caches.append(cache)
     del Kd, Vd
@@ -128,6 +131,10 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     else:
         st = DecodeStep(lay, w.k, L, device=dev, window=W, fused=not args.two_launch)
     fused = st.fused and not NB and not W
+    hybrid = args.exact == "host"
+    if hybrid and not fused:
+        raise SystemExit("--exact host runs with the plain top-k step (no --blocks, --window, --two-launch)")
+    nthr = args.cpu_threads or 16
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
 
@@ -142,7 +149,10 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     def step(i):
         cache = caches[i % copies]
         bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
-        st.attend(cache, q, lens)
+        if hybrid:
+            st.attend_hybrid(cache, q, lens, nthr)
+        else:
+            st.attend(cache, q, lens)
 
     print(f"[bench] {w.name}: warmup {args.warmup}, timing {args.steps} steps over {copies} copies",
           file=sys.stderr, flush=True)
@@ -172,7 +182,10 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
             ev_i[1].record()
         if not fused:
             select()
-        bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
+        if hybrid:
+            st.attend_hybrid(cache, q, lens, nthr, select=False)
+        else:
+            bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
     e1.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
@@ -180,7 +193,12 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     scan_us_timed = 1000.0 * float(np.mean([a.elapsed_time(b) for a, b in sev]))
 
     # Per-call breakdown: the same steps again with events around each call.
-    if fused:
+    if hybrid:
+        names = ("kv_pack_append", "qattn_decode_select", "exact_host_and_copies+qattn_correct_hybrid")
+        calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                 lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
+                 lambda c: st.attend_hybrid(c, q, lens, nthr, select=False))
+    elif fused:
         names = ("kv_pack_append", "qattn_decode_select", "qattn_correct")
         calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
                  lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
@@ -229,7 +247,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
                    "group": w.group, "top_k": 0 if NB else w.k, "recent_window": W,
-                   "blocks": NB, "block": args.block if NB else 0, "shadow": args.shadow,
+                   "blocks": NB, "block": args.block if NB else 0,
+                   "shadow": "host" if hybrid else args.shadow, "exact": args.exact,
                    "cache_copies": copies,
                    "selection_in_scan_launch": fused, "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
@@ -241,7 +260,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "kernel_us_per_launch": round(scan_us_timed, 2), "launches_timed": len(sev)},
     }
-    if not args.no_cpu_baseline and W == 0 and NB == 0:  # the oracle's timed path has no window
+    if not args.no_cpu_baseline and W == 0 and NB == 0 and not hybrid:  # the oracle's timed path has no window
         res["cpu_baseline"] = cpu_baseline(w, inp, knew, vnew, args.cpu_threads)
     del caches
     torch.cuda.empty_cache()

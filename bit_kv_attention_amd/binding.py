@@ -63,13 +63,15 @@ _lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
+_lib.qattn_correct_hybrid.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P, _P]
+_lib.qattn_exact_host.argtypes = [_LP, _P, _P, _P, _P, _P, C.c_int32, _P, C.c_int32]
 for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
            "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
 
 EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append",
             "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
-            "qattn_correct")
+            "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host")
 
 
 def _check(fn: str, st: int) -> None:
@@ -198,6 +200,36 @@ def qattn_correct(layout: Layout, cache: Cache, q, len_host, idx, k: int, ws, ou
     _check("qattn_correct", _lib.qattn_correct(C.byref(layout), C.byref(view), _ptr(q), lens.ctypes.data,
                                                _ptr(idx), int(k), _ptr(ws), ws_bytes, _ptr(out),
                                                _stream(stream)))
+
+
+def qattn_correct_hybrid(layout: Layout, cache: Cache, q, len_host, idx, k: int, exact_state, ws, out,
+                         stream=None) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_correct_hybrid", _lib.qattn_correct_hybrid(C.byref(layout), C.byref(view), _ptr(q),
+                                                             lens.ctypes.data, _ptr(idx), int(k), _ptr(exact_state),
+                                                             _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def qattn_exact_host(layout: Layout, k_shadow_host, v_shadow_host, q_host, len_host, idx_host, k: int, state_host,
+                     n_threads: int = 0) -> None:
+    """Host computation: every array argument is host memory (CPU tensors or
+    numpy arrays)."""
+    lens = _host_i32(len_host)
+    _check("qattn_exact_host", _lib.qattn_exact_host(C.byref(layout), _hptr(k_shadow_host), _hptr(v_shadow_host),
+                                                     _hptr(q_host), lens.ctypes.data, _hptr(idx_host), int(k),
+                                                     _hptr(state_host), int(n_threads)))
+
+
+def _hptr(a):
+    """Address of a host array (torch CPU tensor or numpy array)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    assert not a.is_cuda, "host array expected"
+    return a.data_ptr()
 
 
 def raw_status(fn: str, *args) -> int:

@@ -18,7 +18,10 @@ LIB = os.path.join(HERE, "libbitkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "topk.hip", "correct.hip"]
+SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "topk.hip", "correct.hip", "host_correct.cpp"]
+# host-only source (the host-side exact correction), OpenMP over host threads
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-fopenmp", "-I", os.path.join(ROOT, "include")]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
@@ -38,12 +41,15 @@ EXTRA = {"decode_approx.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed on {src}")
+        raise RuntimeError(f"compile failed on {src}")
     return obj
 
 
@@ -52,7 +58,7 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-lgomp", "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=not verbose)
     os.replace(tmp, LIB)
     return LIB

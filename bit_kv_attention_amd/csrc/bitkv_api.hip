@@ -294,8 +294,26 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   const Workspace w = workspace_layout(ws, *L, max_len, k, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_correct(*L, *c, q, len, idx, k, w, out, (hipStream_t)stream) == hipSuccess ? BKV_OK
-                                                                                          : BKV_E_HIP;
+  return launch_correct(*L, *c, q, len, idx, k, w, nullptr, out, (hipStream_t)stream) == hipSuccess ? BKV_OK
+                                                                                                   : BKV_E_HIP;
+}
+
+bkv_status qattn_correct_hybrid(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                                const int32_t* len_host, const int32_t* idx, int32_t k, const float* exact_state,
+                                void* ws, size_t ws_bytes, float* out, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!c || !c->k_codes || !c->v_codes || !c->k_meta || !c->v_meta) return BKV_E_NULL;
+  if (k < 0) return BKV_E_ARG;
+  if (!q || !ws || !out || !exact_state || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_correct(*L, *c, q, len, idx, k, w, exact_state, out, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
 }
 
 }  // extern "C"

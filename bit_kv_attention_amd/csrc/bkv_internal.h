@@ -87,6 +87,7 @@ constexpr int kCorrChunk = 32;  // selected tokens per correction workgroup
 // Per (b, h, chunk): m_exact, l_exact, m_approx, l_approx, then the exact and
 // the approximate value sums (D each), 16-byte aligned.
 constexpr int kCsStride = 4 + 2 * kHeadDim;
+constexpr int kStateFloats = 2 + kHeadDim;  // one exact state {m, l, a[0..D)}
 
 // Top-k: slices of S tokens (kTopkSliceMax, halved down to kTopkSliceMin
 // while fewer than kTopkGridMin slice workgroups would run) whose local top-k
@@ -136,8 +137,9 @@ hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const Seq
 // Rows of k + W entries per unit (W: the recent window, 0 for none).
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);
+// hx: exact states from elsewhere ([B][Hq][kStateFloats]), or null.
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
-                          float* out, hipStream_t s);
+                          const float* hx, float* out, hipStream_t s);
 
 }  // namespace bkv

@@ -79,11 +79,13 @@ struct RecBatch {
   }
 };
 
-// One workgroup per (b, query head), one thread per channel.
+// One workgroup per (b, query head), one thread per channel.  hx (may be
+// null): the exact state of the selected tokens per (b, query head),
+// {m, l, a[0..D)}, in place of the chunk records' exact parts.
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                            const float* __restrict__ pacc, const float* __restrict__ cs,
-                                                           float* __restrict__ out, SeqArg lens, int Hq, int nsplit,
-                                                           int nchunk, int k) {
+                                                           const float* __restrict__ hx, float* __restrict__ out,
+                                                           SeqArg lens, int Hq, int nsplit, int nchunk, int k) {
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int n = lens.v[b];
   const size_t rec = (size_t)b * Hq + h;
@@ -101,9 +103,14 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   const int nap = (kk < n) ? nsplit : 0;  // every token selected: the scan state is not needed
   const int nsel = (kk < n) ? nc : 0;
   Online ex, ap, sel;
+  const int nex = hx ? 0 : nc;  // exact records from the chunks
+  if (hx) {
+    const float* x = hx + rec * kStateFloats;
+    ex.add(x[0], x[1], x[2 + c]);
+  }
   for (int j0 = 0; j0 < max(nc, nap); j0 += kRecBatch) {
     RecBatch be, ba, bs;
-    be.load(ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nc, j0);
+    be.load(ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nex, j0);
     ba.load(pm + rec * nsplit, pl + rec * nsplit, pacc + rec * nsplit * kHeadDim + c, 1, kHeadDim, nap, j0);
     bs.load(ps + 2, ps + 3, ps + 4 + kHeadDim + c, kCsStride, kCsStride, nsel, j0);
     be.into(ex);
@@ -126,7 +133,9 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   o[c] = (fa * A + fe * ex.a) / (fa * L + fe * ex.l);
 }
 
-template <int KB, int VB, int G>
+// EX = false: only the approximate terms (the exact state comes from
+// elsewhere, see qattn_correct_hybrid); the shadow rows are not read.
+template <int KB, int VB, int G, bool EX>
 __global__ __launch_bounds__(256) void chunk_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
@@ -190,9 +199,13 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   uint32_t kmw;
   {
     const int t = max(t_sel, 0);
-    const uint4* kr = reinterpret_cast<const uint4*>(ksh + (size_t)t * kHeadDim + c0);
-    k0 = kr[0];
-    k1 = kr[1];
+    if constexpr (EX) {
+      const uint4* kr = reinterpret_cast<const uint4*>(ksh + (size_t)t * kHeadDim + c0);
+      k0 = kr[0];
+      k1 = kr[1];
+    } else {
+      k0 = k1 = (uint4){0u, 0u, 0u, 0u};
+    }
     // channels c0..c0+15 are the group-(part/2) fields of the chunks of
     // eighths 2*(part%2) and 2*(part%2)+1 (8*KB bits each)
 #pragma unroll
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + (size_t)(t / kTile) * v_tile_bytes(VB));
     vcode[j] = vt[dw];  // raw: shifted at use, after the loads have landed
     vmw[j] = vmeta[(size_t)(c / kGroup) * cap + t];
-    vx16[j] = vsh[(size_t)t * kHeadDim + c];
+    vx16[j] = EX ? vsh[(size_t)t * kHeadDim + c] : (uint16_t)0;
   }
 
   __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
@@ -254,7 +267,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const half2_t qq = __builtin_bit_cast(half2_t, qw[i]);
-          e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
+          if constexpr (EX) e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
           d = __builtin_amdgcn_fdot2(cp[i], qq, d, false);
         }
         ex[h] = e;
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     }
   }
   __syncthreads();
-  if (tid < 2 * G) {
+  if (tid < 2 * G && (EX || tid >= G)) {
     const int ty = tid / G, h = tid % G;
     float m = -INFINITY;
     for (int tl = 0; tl < kCorrChunk; ++tl) m = fmaxf(m, s_lg[ty][tl][h]);
@@ -292,7 +305,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     const int tl = tid >> 3, h = tid & 7;
     if (h < G) {
       const bool ok = s_t[tl] >= 0;
-      s_w[0][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[0][tl][h] - s_mx[0][h]) : 0.f;
+      if constexpr (EX) s_w[0][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[0][tl][h] - s_mx[0][h]) : 0.f;
       s_w[1][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[1][tl][h] - s_mx[1][h]) : 0.f;
     }
   }
@@ -312,7 +325,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
                           h2f((uint16_t)(vmw[j] >> 16)));
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      ea[h] = fmaf(s_w[0][tl][h], vx, ea[h]);
+      if constexpr (EX) ea[h] = fmaf(s_w[0][tl][h], vx, ea[h]);
       aa[h] = fmaf(s_w[1][tl][h], vq, aa[h]);
     }
   }
@@ -325,10 +338,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   for (int e = tid; e < G * kHeadDim; e += 256) {
     const int h = e / kHeadDim, cc = e % kHeadDim;
     float* rec = cs + ((head0 + h) * nchunk + chunk) * kCsStride;
-    rec[4 + cc] = s_part[0][0][h][cc] + s_part[0][1][h][cc];
+    if constexpr (EX) rec[4 + cc] = s_part[0][0][h][cc] + s_part[0][1][h][cc];
     rec[4 + kHeadDim + cc] = s_part[1][0][h][cc] + s_part[1][1][h][cc];
   }
-  if (tid < 2 * G) {
+  if (tid < 2 * G && (EX || tid >= G)) {
     const int ty = tid / G, h = tid % G;
     float l = 0.f;
     for (int tl = 0; tl < kCorrChunk; ++tl) l += s_w[ty][tl][h];
@@ -340,36 +353,43 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 
 template <int KB, int VB, int G>
 void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
-              const int32_t* idx, int k, const Workspace& w, hipStream_t s) {
-  chunk_kernel<KB, VB, G><<<dim3(w.nchunk, L.batch * L.n_kv_heads), 256, 0, s>>>(
-      static_cast<const uint8_t*>(cc.k_codes), static_cast<const uint8_t*>(cc.v_codes), cc.k_meta,
-      cc.v_meta, cc.k_shadow, cc.v_shadow, q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
-      w.nchunk);
+              const int32_t* idx, int k, const Workspace& w, bool ex, hipStream_t s) {
+  const dim3 grid(w.nchunk, L.batch * L.n_kv_heads);
+  if (ex)
+    chunk_kernel<KB, VB, G, true><<<grid, 256, 0, s>>>(
+        static_cast<const uint8_t*>(cc.k_codes), static_cast<const uint8_t*>(cc.v_codes), cc.k_meta,
+        cc.v_meta, cc.k_shadow, cc.v_shadow, q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
+        w.nchunk);
+  else
+    chunk_kernel<KB, VB, G, false><<<grid, 256, 0, s>>>(
+        static_cast<const uint8_t*>(cc.k_codes), static_cast<const uint8_t*>(cc.v_codes), cc.k_meta,
+        cc.v_meta, nullptr, nullptr, q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k, w.nchunk);
 }
 
 template <int KB, int VB>
 void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
-              const int32_t* idx, int k, const Workspace& w, hipStream_t s) {
+              const int32_t* idx, int k, const Workspace& w, bool ex, hipStream_t s) {
   if (L.n_q_heads / L.n_kv_heads == 4)
-    launch_t<KB, VB, 4>(L, cc, q, len, idx, k, w, s);
+    launch_t<KB, VB, 4>(L, cc, q, len, idx, k, w, ex, s);
   else
-    launch_t<KB, VB, 8>(L, cc, q, len, idx, k, w, s);
+    launch_t<KB, VB, 8>(L, cc, q, len, idx, k, w, ex, s);
 }
 
 }  // namespace
 
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
-                          float* out, hipStream_t s) {
+                          const float* hx, float* out, hipStream_t s) {
   (void)hipGetLastError();  // report only this call's launches
+  const bool ex = hx == nullptr;
   if (w.nchunk > 0) {
-    if (L.k_bits == 4 && L.v_bits == 4) launch_g<4, 4>(L, c, q, len, idx, k, w, s);
-    else if (L.k_bits == 4 && L.v_bits == 2) launch_g<4, 2>(L, c, q, len, idx, k, w, s);
-    else if (L.k_bits == 3 && L.v_bits == 4) launch_g<3, 4>(L, c, q, len, idx, k, w, s);
-    else launch_g<3, 2>(L, c, q, len, idx, k, w, s);
+    if (L.k_bits == 4 && L.v_bits == 4) launch_g<4, 4>(L, c, q, len, idx, k, w, ex, s);
+    else if (L.k_bits == 4 && L.v_bits == 2) launch_g<4, 2>(L, c, q, len, idx, k, w, ex, s);
+    else if (L.k_bits == 3 && L.v_bits == 4) launch_g<3, 4>(L, c, q, len, idx, k, w, ex, s);
+    else launch_g<3, 2>(L, c, q, len, idx, k, w, ex, s);
   }
-  combine_kernel<<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, out, len,
-                                                                 L.n_q_heads, w.nsplit, w.nchunk, k);
+  combine_kernel<<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
+                                                                 len, L.n_q_heads, w.nsplit, w.nchunk, k);
   return hipGetLastError();
 }
 

@@ -52,6 +52,33 @@ class DecodeStep:
                          self.out, stream)
         return self.out
 
+    def attend_hybrid(self, cache: bk.Cache, q, lens, n_threads: int = 0, select: bool = True):
+        """The same step with the exact half of the correction on the host
+        (qattn_exact_host over the cache's pinned host shadow), merged on the
+        GPU by qattn_correct_hybrid.  Synchronises the current stream once, to
+        hand the selected rows to the host."""
+        import torch
+        if cache.k_shadow.is_cuda:
+            raise ValueError("attend_hybrid needs a cache with its shadow in host memory")
+        if not hasattr(self, "_h_idx"):
+            L = self.layout
+            self._h_idx = torch.empty(self.idx.numel(), dtype=torch.int32, pin_memory=True)
+            self._h_q = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float16, pin_memory=True)
+            self._h_state = torch.empty(L.batch * L.n_q_heads * (L.head_dim + 2), dtype=torch.float32,
+                                        pin_memory=True)
+            self._d_state = torch.empty_like(self._h_state, device=self.out.device)
+        if select:  # else the caller has run qattn_decode_select for this step
+            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws)
+        self._h_idx.copy_(self.idx, non_blocking=True)
+        self._h_q.copy_(q.reshape(-1), non_blocking=True)
+        torch.cuda.current_stream().synchronize()
+        bk.qattn_exact_host(self.layout, cache.k_shadow, cache.v_shadow, self._h_q, lens, self._h_idx, self.k,
+                            self._h_state, n_threads)
+        self._d_state.copy_(self._h_state, non_blocking=True)
+        bk.qattn_correct_hybrid(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k,
+                                self._d_state, self.ws, self.out)
+        return self.out
+
     def step(self, cache: bk.Cache, q, k_new, v_new, pos, stream=None):
         """Append one token per sequence at pos[b], then attend over pos[b] + 1 tokens."""
         bk.kv_pack_append(self.layout, cache, k_new, v_new, 1, pos, stream)

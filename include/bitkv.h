@@ -21,13 +21,17 @@
  *   topk_select_blocks   or whole blocks of tokens by their best score
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
+ *   qattn_exact_host     (host) exact states of the selected tokens from a
+ *                        host copy of the shadow rows, for
+ *   qattn_correct_hybrid qattn_correct with those exact states
  *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All array arguments are DEVICE pointers unless the name ends in _host.
  *    Shadow pointers may also be device-visible pinned host memory (see
  *    bkv_cache).  The caller owns every buffer; the library never allocates,
- *    frees or synchronises, and keeps no state between calls.
+ *    frees or synchronises, and keeps no state between calls (the one
+ *    host-only computation, qattn_exact_host, uses OpenMP's thread pool).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work; results are ready when the stream is.
  *  - Errors: every call validates its arguments on the host before any launch
@@ -253,6 +257,47 @@ bkv_status qattn_correct(const bkv_layout* layout, const bkv_cache* cache,
                          const uint16_t* q, const int32_t* len_host,
                          const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream);
+
+/*
+ * qattn_correct_hybrid -- qattn_correct with the exact half computed
+ * elsewhere (JetFire README, introduction: "Approximate-then-Correct
+ * Attention on Hybrid Memory" -- the high-precision copy lives in host memory
+ * and the correction of the top-k tokens is computed from it there).
+ * exact_state [B][Hq][2 + head_dim] fp32 (device): per (b, query head) the
+ * exact softmax state of the selected tokens {m, l, a[0..D)} as
+ * qattn_exact_host writes it (m in log2 units, -inf when no token is
+ * selected).  The GPU computes only the selected tokens' approximate terms
+ * (from the packed cache; the shadow is not read) and merges as
+ * qattn_correct does.  Same workspace, idx and output contract as
+ * qattn_correct; the cache's shadow pointers are not used.
+ * Errors: as qattn_correct; BKV_E_NULL if exact_state is NULL.
+ */
+bkv_status qattn_correct_hybrid(const bkv_layout* layout, const bkv_cache* cache,
+                                const uint16_t* q, const int32_t* len_host,
+                                const int32_t* idx, int32_t k,
+                                const float* exact_state, void* ws,
+                                size_t ws_bytes, float* out, void* stream);
+
+/*
+ * qattn_exact_host -- HOST computation (runs on the calling thread and
+ * n_threads OpenMP threads, 0 = the OpenMP default; returns when done) of the
+ * exact state of the selected tokens for every (b, query head):
+ *   lambda_t = log2(e)/sqrt(D) * q_h . K_t for t in S (the first min(k, len)
+ *   entries of idx[b][kvh] that lie in [0, len)),
+ *   state[b][h] = {m = max lambda, l = sum 2^(lambda - m),
+ *                  a = sum 2^(lambda - m) V_t}     (m = -inf, l = a = 0 if S is empty)
+ * in fp32.  All pointers are HOST pointers: k_shadow_host/v_shadow_host the
+ * fp16 shadow rows in the cache's layout [B][Hkv][capacity][D] (e.g. the
+ * pinned host shadow of a cache made for it, once the step's append has
+ * completed), q_host [B][Hq][D] fp16, idx_host [B][Hkv][k], state_host
+ * [B][Hq][2 + D] fp32.  Touches no GPU.
+ * Errors: BKV_E_ARG if k < 0 or n_threads < 0; BKV_E_NULL; BKV_E_CAPACITY;
+ * layout errors as everywhere.
+ */
+bkv_status qattn_exact_host(const bkv_layout* layout, const uint16_t* k_shadow_host,
+                            const uint16_t* v_shadow_host, const uint16_t* q_host,
+                            const int32_t* len_host, const int32_t* idx_host,
+                            int32_t k, float* state_host, int32_t n_threads);
 
 /* Static text for a status code. */
 const char* bkv_status_string(bkv_status status);

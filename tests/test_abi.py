@@ -1,8 +1,11 @@
 """The C-ABI library loads, exports every entry point include/bitkv.h declares,
-and rejects bad arguments on the host before any launch (no GPU needed)."""
+and rejects bad arguments on the host before any launch (no GPU needed); the
+one host-only computation (qattn_exact_host) against fp64."""
 import ctypes as C
 import os
 import re
+
+import numpy as np
 
 import pytest
 
@@ -152,3 +155,50 @@ def test_status_strings(bk):
         assert bk._lib.bkv_status_string(s)
     with pytest.raises(bk.BitKVError):
         bk.bkv_workspace_bytes(L(bk, k_bits=7), 5, 1)
+
+
+def test_exact_host_state(bk):
+    """qattn_exact_host (host code) against the exact state in fp64 on small
+    inputs: ragged and empty sequences, -1 and out-of-range row entries, k
+    past the length, both GQA groups; and its argument errors."""
+    rng = np.random.default_rng(5)
+    for G in (4, 8):
+        B, Hkv, D, cap = 3, 2, 128, 96
+        lay = L(bk, batch=B, n_q_heads=G * Hkv, n_kv_heads=Hkv, capacity=cap)
+        K = (rng.standard_normal((B, Hkv, cap, D)) * 2).astype(np.float16)
+        V = rng.standard_normal((B, Hkv, cap, D)).astype(np.float16)
+        q = rng.standard_normal((B, G * Hkv, D)).astype(np.float16)
+        lens = np.array([96, 41, 0], np.int32)
+        k = 50
+        idx = np.full((B, Hkv, k), -1, np.int32)
+        for b in range(B):
+            for h in range(Hkv):
+                n = lens[b]
+                sel = rng.choice(n, size=min(k - 5, n), replace=False) if n else np.array([], int)
+                idx[b, h, :len(sel)] = np.sort(sel)
+                if n:
+                    idx[b, h, len(sel)] = n + 3  # outside [0, len): skipped
+        state = np.zeros((B, G * Hkv, D + 2), np.float32)
+        assert bk.qattn_exact_host(lay, K, V, q, lens, idx, k, state, 2) is None
+        for b in range(B):
+            for hq in range(G * Hkv):
+                kvh = hq // G
+                n = lens[b]
+                ts = [t for t in idx[b, kvh, :min(k, n)] if 0 <= t < n]
+                if not ts:
+                    assert state[b, hq, 0] == -np.inf and state[b, hq, 1] == 0 and not state[b, hq, 2:].any()
+                    continue
+                lam = K[b, kvh, ts].astype(np.float64) @ q[b, hq].astype(np.float64) / np.sqrt(D) / np.log(2)
+                m = lam.max()
+                w = np.exp2(lam - m)
+                np.testing.assert_allclose(state[b, hq, 0], m, rtol=1e-5, atol=1e-5)
+                np.testing.assert_allclose(state[b, hq, 1], w.sum(), rtol=1e-4)
+                np.testing.assert_allclose(state[b, hq, 2:], w @ V[b, kvh, ts].astype(np.float64), rtol=1e-4, atol=1e-4)
+    ex = "qattn_exact_host"
+    P = lambda a: a.ctypes.data_as(C.c_void_p)
+    assert bk.raw_status(ex, C.byref(lay), P(K), P(V), P(q), P(lens), P(idx), -1, P(state), 1) == 7
+    assert bk.raw_status(ex, C.byref(lay), P(K), P(V), P(q), P(lens), P(idx), 4, P(state), -1) == 7
+    assert bk.raw_status(ex, C.byref(lay), None, P(V), P(q), P(lens), P(idx), 4, P(state), 1) == 1
+    assert bk.raw_status(ex, C.byref(lay), P(K), P(V), P(q), P(lens), None, 4, P(state), 1) == 1
+    bad = np.array([97, 0, 0], np.int32)
+    assert bk.raw_status(ex, C.byref(lay), P(K), P(V), P(q), P(bad), P(idx), 4, P(state), 1) == 4

@@ -491,3 +491,37 @@ def test_decode_select_equals_two_calls(P, kb, vb, G):
                 assert np.array_equal(i1[b, h], want), (k, b, h)
         assert np.array_equal(i1, i0), k
         assert np.array_equal(o1, o0), k
+
+
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
+def test_hybrid_host_correction(P, kb, vb, G):
+    """The exact half of the correction on the host (qattn_exact_host over a
+    pinned host shadow) merged on the GPU (qattn_correct_hybrid): output
+    against the oracle on the GPU's rows, and against the all-GPU correction;
+    ragged and empty sequences, k >= len, k = 0."""
+    banner(f"hybrid host correction kb={kb} vb={vb} G={G}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("hyb", 3, 2 * G, 2, 128, 2000, kb, vb, 32, 48, 6, 1200 + G)
+    inp = P.make_inputs(w, L=1999)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, 2016, kb, vb)
+    hc = bk.allocate_cache(lay, shadow_on_host=True)
+    bk.kv_pack_append(lay, hc, P.to_dev(inp.K), P.to_dev(inp.V), 1999, [0] * w.B)
+    import oracle
+    oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, kb, vb, 32, 2016))
+    oc.append(inp.K, inp.V, np.zeros(w.B, np.int32))
+    lens = np.array([1999, 777, 0])
+    q = P.to_dev(inp.q)
+    for k in (48, 1000, 0):
+        st = DecodeStep(lay, k, 1999)
+        out_h = st.attend_hybrid(hc, q, lens, n_threads=4).clone()
+        torch.cuda.synchronize()
+        idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, max(k, 1))[:, :, :k]
+        out_g = st.attend(hc, q, lens)
+        torch.cuda.synchronize()
+        oh = out_h.cpu().numpy().reshape(w.B, w.Hq, 128)
+        og = out_g.cpu().numpy().reshape(w.B, w.Hq, 128)
+        orc = oc.decode(inp.q, lens, k, sel=idx if k > 0 else None)
+        P.assert_close(oh, orc["out"], f"hybrid vs oracle k={k}")
+        np.testing.assert_allclose(oh, og, rtol=1e-4, atol=1e-5)
