@@ -59,17 +59,18 @@ _lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, C.c_int32, _SZ]
 _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
-_lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, _P]
+_lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
+_lib.bkv_select_in_scan.argtypes = [_LP, C.c_int32, C.c_int32, C.c_int32, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 _lib.qattn_correct_hybrid.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P, _P]
 _lib.qattn_exact_host.argtypes = [_LP, _P, _P, _P, _P, _P, C.c_int32, _P, C.c_int32]
-for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append", "qattn_decode_approx",
+for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append", "qattn_decode_approx",
            "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
 
-EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "kv_pack_append",
+EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
             "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host")
 
@@ -163,13 +164,24 @@ def qattn_decode_approx(layout: Layout, cache: Cache, q, len_host, sigma, ws, st
                                                            ws_bytes, _stream(stream)))
 
 
-def qattn_decode_select(layout: Layout, cache: Cache, q, len_host, k: int, sigma, idx, ws, stream=None) -> None:
+SELECT_AUTO, SELECT_IN_SCAN, SELECT_TWO_LAUNCHES = 0, 1, 2
+
+
+def qattn_decode_select(layout: Layout, cache: Cache, q, len_host, k: int, sigma, idx, ws, stream=None,
+                        mode: int = SELECT_AUTO) -> None:
     lens = _host_i32(len_host)
     view = cache.view()
     ws_bytes = ws.numel() * ws.element_size()
     _check("qattn_decode_select", _lib.qattn_decode_select(C.byref(layout), C.byref(view), _ptr(q),
                                                            lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
-                                                           _ptr(ws), ws_bytes, _stream(stream)))
+                                                           _ptr(ws), ws_bytes, int(mode), _stream(stream)))
+
+
+def bkv_select_in_scan(layout: Layout, max_len: int, k: int, mode: int = SELECT_AUTO) -> bool:
+    out = C.c_int32()
+    _check("bkv_select_in_scan", _lib.bkv_select_in_scan(C.byref(layout), int(max_len), int(k), int(mode),
+                                                         C.byref(out)))
+    return bool(out.value)
 
 
 def topk_select(layout: Layout, sigma, len_host, k: int, idx, ws, stream=None) -> None:

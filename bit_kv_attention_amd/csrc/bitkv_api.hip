@@ -211,13 +211,35 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
              : BKV_E_HIP;
 }
 
+// Whether qattn_decode_select selects inside the scan's launch: the layout
+// must allow it (range <= kSelStage, nsplit * k <= kSelSlots); in the
+// automatic mode the ranges must also be long (>= kSelMinRange), where
+// rereading the scores in a launch of its own costs more than the selection
+// in the scan's tail.
+static bool select_in_scan(const Workspace& w, int chunk, int k, int mode) {
+  if (k <= 0 || mode == 2 || chunk > kSelStage || (long long)w.nsplit * k > kSelSlots) return false;
+  return mode == 1 || chunk >= kSelMinRange;
+}
+
+bkv_status bkv_select_in_scan(const bkv_layout* L, int32_t max_len, int32_t k, int32_t mode, int32_t* in_scan) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!in_scan) return BKV_E_NULL;
+  if (max_len < 0 || max_len > L->capacity) return BKV_E_CAPACITY;
+  if (k < 0 || mode < 0 || mode > 2) return BKV_E_ARG;
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(nullptr, *L, max_len, k, false);
+  *in_scan = select_in_scan(w, split_tokens(units, max_len), k, mode) ? 1 : 0;
+  return BKV_OK;
+}
+
 bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
                                const int32_t* len_host, int32_t k, float* sigma, int32_t* idx, void* ws,
-                               size_t ws_bytes, void* stream) {
+                               size_t ws_bytes, int32_t mode, void* stream) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
   if ((st = check_cache(c)) != BKV_OK) return st;
-  if (k < 0) return BKV_E_ARG;
+  if (k < 0 || mode < 0 || mode > 2) return BKV_E_ARG;
   if (!q || !sigma || !ws || (!idx && k > 0)) return BKV_E_NULL;
   SeqArg len;
   int max_len = 0;
@@ -227,7 +249,7 @@ bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const ui
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
   const int chunk = split_tokens(units, max_len);
   const hipStream_t s = (hipStream_t)stream;
-  if (k > 0 && chunk <= kSelStage && (long long)w.nsplit * k <= kSelSlots)  // selection inside the scan
+  if (select_in_scan(w, chunk, k, mode))
     return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
   if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, s) != hipSuccess) return BKV_E_HIP;
   if (k == 0) return BKV_OK;

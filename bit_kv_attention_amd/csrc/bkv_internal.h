@@ -102,6 +102,7 @@ constexpr int kTopkBlocksMax = 8192;  // blocks per unit for block selection (ce
 // unit's candidate slots (nsplit * k) merged in LDS.
 constexpr int kSelStage = 16384;
 constexpr int kSelSlots = 8192;
+constexpr int kSelMinRange = 8192;  // automatic mode: shorter ranges take two launches
 int topk_slice(int units, int max_len, int k);
 
 struct Workspace {

@@ -13,7 +13,8 @@
 //
 // Units (b, kvh) are spread over OpenMP threads.  Tokens go in runs of 64:
 // the run's logits, its maximum, a rescale of the running sums, then the
-// run's values, so nothing is allocated whatever k is.  The x86 path uses
+// run's values, so nothing is allocated whatever k is; a run's scattered rows
+// are prefetched together before they are used.  The x86 path uses
 // AVX2/FMA/F16C (16-byte half loads converted in registers); machines without
 // them take the plain loop.
 #include <immintrin.h>
@@ -125,6 +126,13 @@ inline __attribute__((always_inline)) void unit_state(const UnitArgs& a) {
       if (t >= 0 && t < a.n) ts[cnt++] = t;
     }
     if (cnt == 0) break;
+    // the run's rows are scattered 256-byte records: request them all before
+    // the first is used, so the memory system works on them together
+    for (int j = 0; j < cnt; ++j)
+      for (int x = 0; x < kD * 2; x += 64) {
+        __builtin_prefetch(reinterpret_cast<const char*>(a.ksh + (size_t)ts[j] * kD) + x, 0, 3);
+        __builtin_prefetch(reinterpret_cast<const char*>(a.vsh + (size_t)ts[j] * kD) + x, 0, 3);
+      }
     for (int j = 0; j < cnt; ++j) {
       R::row(a.ksh + (size_t)ts[j] * kD, f);
       for (int h = 0; h < a.G; ++h) lam[h][j] = sm2 * R::dot(q[h], f);

@@ -11,13 +11,15 @@ class DecodeStep:
     (topk_select_window); the rows of idx then hold k + window entries.
     block > 0 selects k whole blocks of `block` tokens instead
     (topk_select_blocks); the rows then hold k * block entries.  Plain top-k
-    runs as qattn_decode_select (scan and selection in one launch where it
-    fits) unless fused is False."""
+    runs as qattn_decode_select with select_mode (automatic: the selection in
+    the scan's launch where that is faster) unless fused is False, which makes
+    the two calls qattn_decode_approx and topk_select."""
 
     def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0,
-                 fused: bool = True):
+                 fused: bool = True, select_mode: int = bk.SELECT_AUTO):
         import torch
         self.fused = bool(fused)
+        self.select_mode = int(select_mode)
         self.layout = layout
         self.k = int(k)
         self.window = int(window)
@@ -36,7 +38,8 @@ class DecodeStep:
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
         if self.fused and self.block == 0 and self.window == 0:
-            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream)
+            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
+                                   self.select_mode)
             bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
                              self.out, stream)
             return self.out
@@ -68,7 +71,8 @@ class DecodeStep:
                                         pin_memory=True)
             self._d_state = torch.empty_like(self._h_state, device=self.out.device)
         if select:  # else the caller has run qattn_decode_select for this step
-            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws)
+            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws,
+                                   mode=self.select_mode)
         self._h_idx.copy_(self.idx, non_blocking=True)
         self._h_q.copy_(q.reshape(-1), non_blocking=True)
         torch.cuda.current_stream().synchronize()

@@ -171,20 +171,28 @@ bkv_status qattn_decode_approx(const bkv_layout* layout, const bkv_cache* cache,
 /*
  * qattn_decode_select -- qattn_decode_approx followed by topk_select with the
  * same layout, cache, q, lengths, k and workspace, with identical results
- * (sigma, the split states in ws and idx [B][Hkv][k]).  Where the workspace
- * layout allows (each scan workgroup's token range at most 16384 tokens and
- * its number of ranges per (b, kvh) times k at most 8192) the selection runs
- * inside the scan's launch: every workgroup keeps its range's sigma on chip,
- * leaves its range's top-min(k, len) candidates in ws, and the last
- * workgroup of each (b, kvh) to finish merges them; otherwise the two
- * launches run.  k == 0 is qattn_decode_approx (idx may then be NULL).  Size
- * ws with bkv_workspace_bytes(layout, max_len, k).
- * Errors: as qattn_decode_approx and topk_select.
+ * (sigma, the split states in ws and idx [B][Hkv][k]).  The selection can run
+ * inside the scan's launch: every scan workgroup keeps its token range's
+ * sigma on chip, leaves the range's top-min(k, len) candidates in ws, and
+ * the last workgroup of each (b, kvh) to finish merges them.  That needs
+ * each range at most 16384 tokens and ranges per (b, kvh) times k at most
+ * 8192.  mode: 0 = automatic (in the scan's launch when also each range is
+ * at least 8192 tokens long, where it is faster), 1 = in the scan's launch
+ * whenever possible, 2 = always the two launches.  k == 0 is
+ * qattn_decode_approx (idx may then be NULL).  Size ws with
+ * bkv_workspace_bytes(layout, max_len, k).
+ * Errors: BKV_E_ARG for a mode outside 0..2; otherwise as
+ * qattn_decode_approx and topk_select.
  */
 bkv_status qattn_decode_select(const bkv_layout* layout, const bkv_cache* cache,
                                const uint16_t* q, const int32_t* len_host,
                                int32_t k, float* sigma, int32_t* idx, void* ws,
-                               size_t ws_bytes, void* stream);
+                               size_t ws_bytes, int32_t mode, void* stream);
+
+/* Host only: *in_scan = 1 if qattn_decode_select with this layout, longest
+ * length max_len, k and mode selects inside the scan's launch, else 0. */
+bkv_status bkv_select_in_scan(const bkv_layout* layout, int32_t max_len, int32_t k,
+                              int32_t mode, int32_t* in_scan);
 
 /*
  * topk_select -- per (b, kvh): the min(k, len) tokens with the largest sigma,

@@ -473,8 +473,8 @@ def test_decode_select_equals_two_calls(P, kb, vb, G):
     q = P.to_dev(pair["q"])
     for k in (1, 37, 300, 500, 2600, 5000):  # 16 ranges per unit: 500 is the last in-launch budget
         runs = []
-        for fused in (True, False):
-            st = DecodeStep(pair["lay"], k, 3999, fused=fused)
+        for fused in (True, False):  # the selection in the scan's launch whenever possible, and two calls
+            st = DecodeStep(pair["lay"], k, 3999, fused=fused, select_mode=1)
             for _ in range(2):  # twice on one workspace
                 st.sigma.fill_(float("nan"))
                 st.idx.fill_(-7)
