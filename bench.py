@@ -103,9 +103,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     dev = torch.device("cuda:0")
     L = w.L
     cap = ((L + 31) // 32) * 32
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group)
     units = w.B * w.Hkv
-    ppt = packed_bytes_per_token(w.kbits, w.vbits)
+    ppt = packed_bytes_per_token(w.kbits, w.vbits, group=w.group)
     packed = units * L * ppt
     copies = args.copies or max(1, min(8, -(-600_000_000 // packed)))
 
@@ -139,6 +139,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     # When the library would run the scan and the top-k as two launches anyway,
     # the timed loop makes the two calls itself, so the scan launch is timed alone.
     fused = in_scan
+    # 1- and 2-bit keys: the unselected tokens' state from a second pass (see DecodeStep)
+    exclude = st.exclude and not hybrid
     nthr = args.cpu_threads or 16
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
@@ -189,6 +191,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
             select()
         if hybrid:
             st.attend_hybrid(cache, q, lens, nthr, select=False)
+        elif exclude:
+            bk.qattn_decode_unselected(lay, cache, q, lens, st.idx, st.row, st.ws)
+            bk.qattn_correct_unselected(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
         else:
             bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
     e1.record()
@@ -203,17 +208,23 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
                  lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
                  lambda c: st.attend_hybrid(c, q, lens, nthr, select=False))
-    elif fused:
-        names = ("kv_pack_append", "qattn_decode_select", "qattn_correct")
-        calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
-                 lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
-                 lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))
     else:
-        names = ("kv_pack_append", "qattn_decode_approx", "topk_select", "qattn_correct")
-        calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
-                 lambda c: bk.qattn_decode_approx(lay, c, q, lens, st.sigma, st.ws),
-                 lambda c: select(),
-                 lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))
+        if fused:
+            names = ["kv_pack_append", "qattn_decode_select"]
+            calls = [lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                     lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws)]
+        else:
+            names = ["kv_pack_append", "qattn_decode_approx", "topk_select"]
+            calls = [lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                     lambda c: bk.qattn_decode_approx(lay, c, q, lens, st.sigma, st.ws),
+                     lambda c: select()]
+        if exclude:
+            names += ["qattn_decode_unselected", "qattn_correct_unselected"]
+            calls += [lambda c: bk.qattn_decode_unselected(lay, c, q, lens, st.idx, st.row, st.ws),
+                      lambda c: bk.qattn_correct_unselected(lay, c, q, lens, st.idx, st.row, st.ws, st.out)]
+        else:
+            names += ["qattn_correct"]
+            calls += [lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(args.steps)]
     for i in range(args.steps):
@@ -255,7 +266,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                    "blocks": NB, "block": args.block if NB else 0,
                    "shadow": "host" if hybrid else args.shadow, "exact": args.exact,
                    "cache_copies": copies,
-                   "selection_in_scan_launch": bool(in_scan), "parallelism": "single GPU"},
+                   "selection_in_scan_launch": bool(in_scan), "unselected_second_pass": bool(exclude),
+                   "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
         "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": {n: round(v, 2) for n, v in kus.items()},
@@ -313,7 +325,7 @@ def cpu_baseline(w, inp, knew, vnew, threads):
     L = w.L
     cap = ((L + 31) // 32) * 32
     sel = [(u // w.Hkv, u % w.Hkv) for u in range(sample)]
-    s = oracle.Shape(1, w.G * sample, sample, 128, w.kbits, w.vbits, 32, cap)
+    s = oracle.Shape(1, w.G * sample, sample, 128, w.kbits, w.vbits, w.group, cap)
     # fold the sampled units into one batch row of `sample` KV heads
     K = np.stack([inp.K[b, h] for b, h in sel])[None]
     V = np.stack([inp.V[b, h] for b, h in sel])[None]

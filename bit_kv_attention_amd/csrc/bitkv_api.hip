@@ -105,8 +105,8 @@ static bkv_status check_layout(const bkv_layout* L) {
   if (L->n_q_heads % L->n_kv_heads != 0) return BKV_E_SHAPE;
   if (L->head_dim % L->group != 0) return BKV_E_SHAPE;
   if (L->capacity % kTile != 0) return BKV_E_SHAPE;
-  if (L->head_dim != kHeadDim || L->group != kGroup) return BKV_E_UNSUPPORTED;
-  if (L->k_bits != 3 && L->k_bits != 4) return BKV_E_UNSUPPORTED;
+  if (L->head_dim != kHeadDim || (L->group != kGroup && L->group != 2 * kGroup)) return BKV_E_UNSUPPORTED;
+  if (L->k_bits < 1 || L->k_bits > 4) return BKV_E_UNSUPPORTED;
   if (L->v_bits != 2 && L->v_bits != 4) return BKV_E_UNSUPPORTED;
   const int G = L->n_q_heads / L->n_kv_heads;
   if (G != 4 && G != 8) return BKV_E_UNSUPPORTED;
@@ -157,7 +157,7 @@ bkv_status bkv_cache_bytes(const bkv_layout* L, size_t* k_codes_bytes, size_t* v
   const size_t units = (size_t)L->batch * L->n_kv_heads;
   *k_codes_bytes = units * k_unit_bytes(L->k_bits, L->capacity);
   *v_codes_bytes = units * v_unit_bytes(L->v_bits, L->capacity);
-  *meta_bytes_each = units * kGroups * (size_t)L->capacity * sizeof(uint32_t);
+  *meta_bytes_each = units * (size_t)(kHeadDim / L->group) * (size_t)L->capacity * sizeof(uint32_t);
   *shadow_bytes_each = units * (size_t)L->capacity * kHeadDim * sizeof(uint16_t);
   return BKV_OK;
 }
@@ -205,7 +205,7 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
   const int units = L->batch * L->n_kv_heads;
   const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0,
+  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0, false,
                               (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
@@ -250,8 +250,9 @@ bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const ui
   const int chunk = split_tokens(units, max_len);
   const hipStream_t s = (hipStream_t)stream;
   if (select_in_scan(w, chunk, k, mode))
-    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
-  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, s) != hipSuccess) return BKV_E_HIP;
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, s) == hipSuccess ? BKV_OK
+                                                                                                : BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, s) != hipSuccess) return BKV_E_HIP;
   if (k == 0) return BKV_OK;
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
@@ -316,8 +317,48 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   const Workspace w = workspace_layout(ws, *L, max_len, k, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_correct(*L, *c, q, len, idx, k, w, nullptr, out, (hipStream_t)stream) == hipSuccess ? BKV_OK
+  return launch_correct(*L, *c, q, len, idx, k, w, nullptr, false, out, (hipStream_t)stream) == hipSuccess ? BKV_OK
                                                                                                    : BKV_E_HIP;
+}
+
+bkv_status qattn_decode_unselected(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                                   const int32_t* len_host, const int32_t* idx, int32_t k, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if (!q || !ws || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  const int chunk = split_tokens(units, max_len);
+  if (chunk > kSelStage) return BKV_E_UNSUPPORTED;
+  return launch_decode_approx(*L, *c, q, len, nullptr, w, chunk, const_cast<int32_t*>(idx), k, true,
+                              (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
+bkv_status qattn_correct_unselected(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                                    const int32_t* len_host, const int32_t* idx, int32_t k, void* ws,
+                                    size_t ws_bytes, float* out, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if (!q || !ws || !out || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_correct(*L, *c, q, len, idx, k, w, nullptr, true, out, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
 }
 
 bkv_status qattn_correct_hybrid(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
@@ -333,7 +374,7 @@ bkv_status qattn_correct_hybrid(const bkv_layout* L, const bkv_cache* c, const u
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   const Workspace w = workspace_layout(ws, *L, max_len, k, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_correct(*L, *c, q, len, idx, k, w, exact_state, out, (hipStream_t)stream) == hipSuccess
+  return launch_correct(*L, *c, q, len, idx, k, w, exact_state, false, out, (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
 }

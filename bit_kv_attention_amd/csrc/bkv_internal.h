@@ -10,8 +10,13 @@
 namespace bkv {
 
 constexpr int kHeadDim = 128;
+// The kernels work on 32-channel quarters of a row (one MFMA K-step each).
+// A quantisation group is one quarter (group 32) or two (group 64); the meta
+// planes are per group, and quarter g reads group g >> mshift (mshift =
+// log2(group / 32)).
 constexpr int kGroup = 32;
-constexpr int kGroups = kHeadDim / kGroup;  // 4
+constexpr int kGroups = kHeadDim / kGroup;  // 4 quarters
+__host__ __device__ inline int meta_planes(int mshift) { return kGroups >> mshift; }
 constexpr int kTile = 32;                   // tokens per V tile and per scan step
 constexpr int kMaxBatch = 256;
 constexpr int kScanWaves = 8;               // waves per workgroup of the approximate scan
@@ -128,19 +133,22 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
 hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_new,
                               const uint16_t* v_new, int n_new, const SeqArg& pos, hipStream_t s);
 // ksel > 0: the same launch also writes the top-ksel rows to idx (its split
-// length chunk <= kSelStage and nsplit * ksel <= kSelSlots).
+// length chunk <= kSelStage and nsplit * ksel <= kSelSlots).  skip: the
+// split states leave out the tokens of the rows of idx (ksel entries per
+// unit; chunk <= kSelStage); sigma is not written.
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                int32_t* idx, int ksel, hipStream_t s);
+                                int32_t* idx, int ksel, bool skip, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
                               int32_t* idx, hipStream_t s);
 // Rows of k + W entries per unit (W: the recent window, 0 for none).
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);
-// hx: exact states from elsewhere ([B][Hq][kStateFloats]), or null.
+// hx: exact states from elsewhere ([B][Hq][kStateFloats]), or null.  rest:
+// the split states already leave the selected tokens out (no subtraction).
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
-                          const float* hx, float* out, hipStream_t s);
+                          const float* hx, bool rest, float* out, hipStream_t s);
 
 }  // namespace bkv

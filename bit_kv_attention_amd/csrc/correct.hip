@@ -85,7 +85,8 @@ struct RecBatch {
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                            const float* __restrict__ pacc, const float* __restrict__ cs,
                                                            const float* __restrict__ hx, float* __restrict__ out,
-                                                           SeqArg lens, int Hq, int nsplit, int nchunk, int k) {
+                                                           SeqArg lens, int Hq, int nsplit, int nchunk, int k,
+                                                           int rest) {
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
   const int n = lens.v[b];
   const size_t rec = (size_t)b * Hq + h;
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   // approximate terms of the selected tokens; a batch's loads of all three
   // are issued before any is used
   const int nap = (kk < n) ? nsplit : 0;  // every token selected: the scan state is not needed
-  const int nsel = (kk < n) ? nc : 0;
+  const int nsel = (kk < n && !rest) ? nc : 0;  // rest: the split states already leave S out
   Online ex, ap, sel;
   const int nex = hx ? 0 : nc;  // exact records from the chunks
   if (hx) {
@@ -125,6 +126,13 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
     o[c] = ap.a / ap.l;
     return;
   }
+  if (rest) {  // a plain merge of the unselected tokens' state and the selected tokens' exact state
+    const float mp = fmaxf(ap.m, ex.m);
+    const float fa = __builtin_amdgcn_exp2f(ap.m - mp);
+    const float fe = (ex.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ex.m - mp);
+    o[c] = (fa * ap.a + fe * ex.a) / (fa * ap.l + fe * ex.l);
+    return;
+  }
   const float M = ap.m;
   const float fs = sel.scale_to(M);
   const float A = ap.a - fs * sel.a, L = fmaxf(ap.l - fs * sel.l, 0.f);
@@ -135,13 +143,16 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
 
 // EX = false: only the approximate terms (the exact state comes from
 // elsewhere, see qattn_correct_hybrid); the shadow rows are not read.
-template <int KB, int VB, int G, bool EX>
+// AP = false: only the exact terms (the approximate state already leaves the
+// selected tokens out, see qattn_decode_unselected); the packed cache is not
+// read.
+template <int KB, int VB, int G, bool EX, bool AP = true>
 __global__ __launch_bounds__(256) void chunk_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ k_shadow, const uint16_t* __restrict__ v_shadow,
     const uint16_t* __restrict__ q, const int32_t* __restrict__ idx, float* __restrict__ cs, SeqArg lens, int Hq,
-    int Hkv, int cap, int k, int nchunk) {
+    int Hkv, int cap, int k, int nchunk, int mshift) {
   const int u = blockIdx.y;
   const int chunk = blockIdx.x;
   const int b = u / Hkv;
@@ -182,8 +193,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 
   const uint8_t* kbase = k_codes + (size_t)u * k_unit_bytes(KB, cap);
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
-  const uint32_t* kmeta = k_meta + (size_t)u * kGroups * cap;
-  const uint32_t* vmeta = v_meta + (size_t)u * kGroups * cap;
+  const uint32_t* kmeta = k_meta + (size_t)u * meta_planes(mshift) * cap;
+  const uint32_t* vmeta = v_meta + (size_t)u * meta_planes(mshift) * cap;
   const uint16_t* ksh = k_shadow + (size_t)u * cap * kHeadDim;
   const uint16_t* vsh = v_shadow + (size_t)u * cap * kHeadDim;
 
@@ -212,10 +223,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     for (int x = 0; x < 2; ++x) {
       const uint32_t* ch = reinterpret_cast<const uint32_t*>(kbase + k_chunk_offset(KB, t, 2 * (part & 1) + x));
       const int d0 = (8 * KB * (part >> 1)) >> 5, d1 = min(d0 + 1, KB - 1);
-      kraw[x][0] = ch[d0];
-      kraw[x][1] = ch[d1];
+      kraw[x][0] = AP ? ch[d0] : 0u;
+      kraw[x][1] = AP ? ch[d1] : 0u;
     }
-    kmw = kmeta[(size_t)(c0 / kGroup) * cap + t];
+    kmw = AP ? kmeta[(size_t)((c0 / kGroup) >> mshift) * cap + t] : 0u;
   }
   // value loads: one thread per (channel, half of the chunk)
   const int c = tid & (kHeadDim - 1);
@@ -229,8 +240,8 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     int dw, bit;
     v_code_pos(VB, t % kTile, c, dw, bit);
     const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + (size_t)(t / kTile) * v_tile_bytes(VB));
-    vcode[j] = vt[dw];  // raw: shifted at use, after the loads have landed
-    vmw[j] = vmeta[(size_t)(c / kGroup) * cap + t];
+    vcode[j] = AP ? vt[dw] : 0u;  // raw: shifted at use, after the loads have landed
+    vmw[j] = AP ? vmeta[(size_t)((c / kGroup) >> mshift) * cap + t] : 0u;
     vx16[j] = EX ? vsh[(size_t)t * kHeadDim + c] : (uint16_t)0;
   }
 
@@ -268,10 +279,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(
         for (int i = 0; i < 8; ++i) {
           const half2_t qq = __builtin_bit_cast(half2_t, qw[i]);
           if constexpr (EX) e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
-          d = __builtin_amdgcn_fdot2(cp[i], qq, d, false);
+          if constexpr (AP) d = __builtin_amdgcn_fdot2(cp[i], qq, d, false);
         }
         ex[h] = e;
-        ap[h] = fmaf(s, d, z * s_qs[h][part]);
+        ap[h] = AP ? fmaf(s, d, z * s_qs[h][part]) : 0.f;
       }
     }
     // sum over the token's 8 threads (lanes 8m..8m+7): quads by DPP, then the
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     }
   }
   __syncthreads();
-  if (tid < 2 * G && (EX || tid >= G)) {
+  if (tid < 2 * G && (EX || tid >= G) && (AP || tid < G)) {
     const int ty = tid / G, h = tid % G;
     float m = -INFINITY;
     for (int tl = 0; tl < kCorrChunk; ++tl) m = fmaxf(m, s_lg[ty][tl][h]);
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     if (h < G) {
       const bool ok = s_t[tl] >= 0;
       if constexpr (EX) s_w[0][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[0][tl][h] - s_mx[0][h]) : 0.f;
-      s_w[1][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[1][tl][h] - s_mx[1][h]) : 0.f;
+      if constexpr (AP) s_w[1][tl][h] = ok ? __builtin_amdgcn_exp2f(s_lg[1][tl][h] - s_mx[1][h]) : 0.f;
     }
   }
   __syncthreads();
@@ -326,7 +337,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if constexpr (EX) ea[h] = fmaf(s_w[0][tl][h], vx, ea[h]);
-      aa[h] = fmaf(s_w[1][tl][h], vq, aa[h]);
+      if constexpr (AP) aa[h] = fmaf(s_w[1][tl][h], vq, aa[h]);
     }
   }
 #pragma unroll
@@ -339,9 +350,9 @@ __global__ __launch_bounds__(256) void chunk_kernel(
     const int h = e / kHeadDim, cc = e % kHeadDim;
     float* rec = cs + ((head0 + h) * nchunk + chunk) * kCsStride;
     if constexpr (EX) rec[4 + cc] = s_part[0][0][h][cc] + s_part[0][1][h][cc];
-    rec[4 + kHeadDim + cc] = s_part[1][0][h][cc] + s_part[1][1][h][cc];
+    if constexpr (AP) rec[4 + kHeadDim + cc] = s_part[1][0][h][cc] + s_part[1][1][h][cc];
   }
-  if (tid < 2 * G && (EX || tid >= G)) {
+  if (tid < 2 * G && (EX || tid >= G) && (AP || tid < G)) {
     const int ty = tid / G, h = tid % G;
     float l = 0.f;
     for (int tl = 0; tl < kCorrChunk; ++tl) l += s_w[ty][tl][h];
@@ -351,45 +362,60 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   }
 }
 
+// Chunk terms: kBoth (exact and approximate), kExactOnly (the split states
+// leave the selected tokens out), kApproxOnly (the exact state comes from
+// elsewhere).
+enum ChunkTerms { kBoth, kExactOnly, kApproxOnly };
+
 template <int KB, int VB, int G>
 void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
-              const int32_t* idx, int k, const Workspace& w, bool ex, hipStream_t s) {
+              const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   const dim3 grid(w.nchunk, L.batch * L.n_kv_heads);
-  if (ex)
-    chunk_kernel<KB, VB, G, true><<<grid, 256, 0, s>>>(
-        static_cast<const uint8_t*>(cc.k_codes), static_cast<const uint8_t*>(cc.v_codes), cc.k_meta,
-        cc.v_meta, cc.k_shadow, cc.v_shadow, q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
-        w.nchunk);
+  const int mshift = L.group == 64 ? 1 : 0;
+  const uint8_t* kc = static_cast<const uint8_t*>(cc.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(cc.v_codes);
+  if (terms == kBoth)
+    chunk_kernel<KB, VB, G, true, true><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
+                                                              idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity,
+                                                              k, w.nchunk, mshift);
+  else if (terms == kExactOnly)
+    chunk_kernel<KB, VB, G, true, false><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow,
+                                                               q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads,
+                                                               L.capacity, k, w.nchunk, mshift);
   else
-    chunk_kernel<KB, VB, G, false><<<grid, 256, 0, s>>>(
-        static_cast<const uint8_t*>(cc.k_codes), static_cast<const uint8_t*>(cc.v_codes), cc.k_meta,
-        cc.v_meta, nullptr, nullptr, q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k, w.nchunk);
+    chunk_kernel<KB, VB, G, false, true><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
+                                                               w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
+                                                               w.nchunk, mshift);
 }
 
 template <int KB, int VB>
 void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
-              const int32_t* idx, int k, const Workspace& w, bool ex, hipStream_t s) {
+              const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   if (L.n_q_heads / L.n_kv_heads == 4)
-    launch_t<KB, VB, 4>(L, cc, q, len, idx, k, w, ex, s);
+    launch_t<KB, VB, 4>(L, cc, q, len, idx, k, w, terms, s);
   else
-    launch_t<KB, VB, 8>(L, cc, q, len, idx, k, w, ex, s);
+    launch_t<KB, VB, 8>(L, cc, q, len, idx, k, w, terms, s);
 }
 
 }  // namespace
 
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
-                          const float* hx, float* out, hipStream_t s) {
+                          const float* hx, bool rest, float* out, hipStream_t s) {
   (void)hipGetLastError();  // report only this call's launches
-  const bool ex = hx == nullptr;
+  const ChunkTerms t = hx ? kApproxOnly : (rest ? kExactOnly : kBoth);
   if (w.nchunk > 0) {
-    if (L.k_bits == 4 && L.v_bits == 4) launch_g<4, 4>(L, c, q, len, idx, k, w, ex, s);
-    else if (L.k_bits == 4 && L.v_bits == 2) launch_g<4, 2>(L, c, q, len, idx, k, w, ex, s);
-    else if (L.k_bits == 3 && L.v_bits == 4) launch_g<3, 4>(L, c, q, len, idx, k, w, ex, s);
-    else launch_g<3, 2>(L, c, q, len, idx, k, w, ex, s);
+    const bool v4 = L.v_bits == 4;
+    switch (L.k_bits) {
+      case 4: v4 ? launch_g<4, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<4, 2>(L, c, q, len, idx, k, w, t, s); break;
+      case 3: v4 ? launch_g<3, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<3, 2>(L, c, q, len, idx, k, w, t, s); break;
+      case 2: v4 ? launch_g<2, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<2, 2>(L, c, q, len, idx, k, w, t, s); break;
+      default: v4 ? launch_g<1, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<1, 2>(L, c, q, len, idx, k, w, t, s);
+    }
   }
   combine_kernel<<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
-                                                                 len, L.n_q_heads, w.nsplit, w.nchunk, k);
+                                                                 len, L.n_q_heads, w.nsplit, w.nchunk, k,
+                                                                 rest ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -86,7 +86,7 @@ constexpr int kRowRor8 = 0x128;
 // there (to within 2^(BITS-25)).  The MFMA sums with fp32 rounding only.
 template <int BITS>
 __device__ inline half8 unpack_keys(uint32_t y) {
-  constexpr uint32_t M = (BITS == 4) ? 0x000F000Fu : 0x00070007u;
+  constexpr uint32_t M = ((1u << BITS) - 1) * 0x00010001u;
   // gfx9 VOP3 takes no literal: with the masks in SGPRs and the bias in a
   // VGPR each AND and OR becomes one v_and_or_b32.
   uint32_t m0, m1, bias;
@@ -162,7 +162,7 @@ struct Step {
 template <int KB, int VB, int G>
 __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__ kbase,
                                  const uint8_t* __restrict__ vbase, const uint32_t* __restrict__ kmeta,
-                                 const uint32_t* __restrict__ vmeta, int cap, int t0, int lane) {
+                                 const uint32_t* __restrict__ vmeta, int cap, int t0, int lane, int mshift) {
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     const uint8_t* blk = kbase + (size_t)(t0 / kKBlock + tt) * k_block_bytes(KB) + (size_t)lane * k_chunk_bytes(KB);
@@ -170,16 +170,22 @@ __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__
       const u32x4 x = *reinterpret_cast<const u32x4*>(blk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) S.kc[tt][i] = x[i];
-    } else {
+    } else if constexpr (KB == 3) {
       const u32x3 x = *reinterpret_cast<const u32x3*>(blk);
 #pragma unroll
       for (int i = 0; i < 3; ++i) S.kc[tt][i] = x[i];
+    } else if constexpr (KB == 2) {
+      const uint2 x = *reinterpret_cast<const uint2*>(blk);
+      S.kc[tt][0] = x.x;
+      S.kc[tt][1] = x.y;
+    } else {
+      S.kc[tt][0] = *reinterpret_cast<const uint32_t*>(blk);
     }
   }
   const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB) + (size_t)lane * 16;
 #pragma unroll
   for (int pc = 0; pc < VB / 2; ++pc) S.vd[pc] = *reinterpret_cast<const u32x4*>(vt + 1024 * pc);
-  const uint32_t* mp = (lane < 32 ? kmeta : vmeta) + (size_t)((lane & 31) >> 3) * cap + t0 + 4 * (lane & 7);
+  const uint32_t* mp = (lane < 32 ? kmeta : vmeta) + (size_t)(((lane & 31) >> 3) >> mshift) * cap + t0 + 4 * (lane & 7);
   S.meta = *reinterpret_cast<const u32x4*>(mp);
 }
 
@@ -210,13 +216,15 @@ struct WaveState {
 template <int VB>
 constexpr int kZS = (VB == 4) ? 2 : 4;
 
-// One 32-token step.  MASK: the step straddles the sequence end.
-template <int KB, int VB, int G, bool MASK>
+// One 32-token step.  MASK: the step straddles the sequence end.  SKIP: the
+// tokens whose bit is set in skipw (bit 16tt + 4kb + i for token
+// t0 + 16tt + 4kb + i) are left out, as if past the end.
+template <int KB, int VB, int G, bool MASK, bool SKIP = false>
 __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
                                           const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const half8 (&bq)[kGroups],
                                           const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
                                           floatx4* __restrict__ sig_row, int t0, int len, int n, int kb,
-                                          float c_s2) {
+                                          float c_s2, uint32_t skipw = 0) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // -- scores: D[T][tt] rows = tokens 4kb+i of token tile tt, column n --------
   floatx4 d[NT][2];
@@ -231,10 +239,16 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
       uint32_t y;
       if constexpr (KB == 4) {
         y = cur.kc[tt][g];
-      } else {  // 24-bit field g at bit 24g of the 96-bit chunk; codes 4..7 to the high half
+      } else if constexpr (KB == 3) {  // 24-bit field g at bit 24g of the 96-bit chunk; codes 4..7 to the high half
         const int d0 = (24 * g) >> 5, d1 = (d0 + 1 < 3) ? d0 + 1 : 2;
         const uint32_t x = __builtin_amdgcn_alignbit(cur.kc[tt][d1], cur.kc[tt][d0], (24 * g) & 31);
         y = (x & 0xFFFFu) | ((x << 4) & 0xFFFF0000u);
+      } else if constexpr (KB == 2) {  // 16-bit field g at bit 16g
+        const uint32_t x = cur.kc[tt][g >> 1] >> (16 * (g & 1));
+        y = (x & 0xFFu) | ((x << 8) & 0x00FF0000u);
+      } else {  // 8-bit field g at bit 8g
+        const uint32_t x = cur.kc[tt][0] >> (8 * g);
+        y = (x & 0xFu) | ((x << 12) & 0x000F0000u);
       }
       const int T = (G == 8) ? (g >> 1) : 0;
       d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys<KB>(y), bq[g], d[T][tt], 0, 0, 0);
@@ -261,6 +275,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         part += dpp<kRowRor8>(part);
       }
       if constexpr (MASK) part = ((t0 + 16 * tt + 4 * kb + i) < len) ? part : -INFINITY;
+      if constexpr (SKIP) part = ((skipw >> (16 * tt + 4 * kb + i)) & 1u) ? -INFINITY : part;
       // selection score: max over the query heads of the group (the positive
       // factor 1/sqrt(D) commutes with the max and is applied when stored)
       float sg = part;
@@ -337,13 +352,16 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // topk_select finds): each workgroup keeps its split's selection scores in
 // LDS, leaves the split's top-min(kk, split length) composites in index order
 // in cand, and the unit's last workgroup to finish merges them into idx.
-template <int KB, int VB, int G, bool SEL>
+// SKIP: the softmax state leaves out the tokens listed in the first
+// min(ksel, len) entries of the unit's row of idx (the workgroup marks those
+// of its split in an LDS bitmap first); no selection score is stored.
+template <int KB, int VB, int G, bool SEL, bool SKIP = false>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel) {
+    uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel, int mshift) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -362,8 +380,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
 
   const uint8_t* kbase = k_codes + (size_t)u * k_unit_bytes(KB, cap);
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
-  const uint32_t* kmeta = k_meta + (size_t)u * kGroups * cap;
-  const uint32_t* vmeta = v_meta + (size_t)u * kGroups * cap;
+  const uint32_t* kmeta = k_meta + (size_t)u * meta_planes(mshift) * cap;
+  const uint32_t* vmeta = v_meta + (size_t)u * meta_planes(mshift) * cap;
 
   // ---- query operands, staged through LDS ------------------------------------
   __shared__ uint16_t s_q[G][kHeadDim];
@@ -377,6 +395,19 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
       float s = 0.f;
       for (int c = 0; c < kGroup; ++c) s += (float)__builtin_bit_cast(_Float16, s_q[hh][g * kGroup + c]);
       s_qsum[hh][g] = s;
+    }
+    __syncthreads();
+  }
+  // SKIP: bit t - t_begin marks a listed token of the split
+  __shared__ uint32_t s_skip[SKIP ? kSelStage / 32 : 1];
+  if constexpr (SKIP) {
+    for (int i = tid; i < kSelStage / 32; i += 64 * kScanWaves) s_skip[i] = 0u;
+    __syncthreads();
+    const int kk = min(ksel, len);
+    const int32_t* row = idx + (size_t)u * ksel;
+    for (int j = tid; j < kk; j += 64 * kScanWaves) {
+      const int t = row[j];
+      if (t >= t_begin && t < t_end) atomicOr(&s_skip[(t - t_begin) >> 5], 1u << ((t - t_begin) & 31));
     }
     __syncthreads();
   }
@@ -434,7 +465,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     if (i < sig_count) {
       const int t = sig_first + kScanWaves * kTile * i + 4 * (lane & 7);
       const floatx4 v = s_sig[wv][i][lane & 7] * c_sig;
-      *reinterpret_cast<floatx4*>(sig + t) = v;
+      if constexpr (!SKIP) *reinterpret_cast<floatx4*>(sig + t) = v;
       if constexpr (SEL) *reinterpret_cast<floatx4*>(&s_split[t - t_begin]) = v;
     }
     wave_lds_order();
@@ -465,11 +496,12 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
   // copies (a copy of registers with loads in flight would wait for them).
   auto full_step = [&](Step<KB, VB, G>& cur, Step<KB, VB, G>& nxt, int t0) {
     const int tn = (t0 + kScanWaves * kTile) < t_end ? t0 + kScanWaves * kTile : t0;
-    load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane);
+    load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane, mshift);
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, false>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2);
+    scan_step<KB, VB, G, false, SKIP>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
+                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     if (++sig_count == kSigBatch) flush_sig();
   };
   // The step that straddles the end of the split (at most one per wave).
@@ -477,12 +509,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, true>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2);
+    scan_step<KB, VB, G, true, SKIP>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
+                                     SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
   Step<KB, VB, G> sa, sb;
   int t0 = t_begin + kTile * wv;
-  if (t0 < t_end) load_step<KB, VB, G>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane);
+  if (t0 < t_end) load_step<KB, VB, G>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
   for (;;) {
     if (t0 + kTile > t_end) {
       if (t0 < t_end) last_step(sa, t0);
@@ -612,39 +645,51 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
 
 template <int KB, int VB, int G>
 hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, hipStream_t s) {
   dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
+  const int mshift = L.group == 64 ? 1 : 0;
+  const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(c.v_codes);
   (void)hipGetLastError();  // report only this launch's status
-  if (ksel > 0)
+  if (skip)
+    decode_approx_kernel<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift);
+  else if (ksel > 0)
     decode_approx_kernel<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
-        static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
-        c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
-        L.n_kv_heads, L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel);
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift);
   else
     decode_approx_kernel<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
-        static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta,
-        c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads,
-        L.n_kv_heads, L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0);
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
 hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, hipStream_t s) {
   const int G = L.n_q_heads / L.n_kv_heads;
-  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
-  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                int32_t* idx, int ksel, hipStream_t s) {
-  if (L.k_bits == 4 && L.v_bits == 4) return launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
-  if (L.k_bits == 4 && L.v_bits == 2) return launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
-  if (L.k_bits == 3 && L.v_bits == 4) return launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
-  return launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, s);
+                                int32_t* idx, int ksel, bool skip, hipStream_t s) {
+  const bool v4 = L.v_bits == 4;
+  switch (L.k_bits) {
+    case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
+                      : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+    case 3: return v4 ? launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
+                      : launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+    case 2: return v4 ? launch_g<2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
+                      : launch_g<2, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+    default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
+                       : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+  }
 }
 
 }  // namespace bkv

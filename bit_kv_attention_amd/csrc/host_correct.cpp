@@ -171,7 +171,7 @@ bkv_status check(const bkv_layout* L) {
       L->capacity <= 0 || L->n_q_heads % L->n_kv_heads != 0 || L->head_dim % L->group != 0 || L->capacity % 32 != 0)
     return BKV_E_SHAPE;
   const int G = L->n_q_heads / L->n_kv_heads;
-  if (L->head_dim != kD || L->group != kGroupSize || (L->k_bits != 3 && L->k_bits != 4) ||
+  if (L->head_dim != kD || (L->group != kGroupSize && L->group != 2 * kGroupSize) || L->k_bits < 1 || L->k_bits > 4 ||
       (L->v_bits != 2 && L->v_bits != 4) || (G != 4 && G != 8) || L->batch > 256)
     return BKV_E_UNSUPPORTED;
   return BKV_OK;

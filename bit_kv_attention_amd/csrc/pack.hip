@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, uint32_t* __restrict__ k_meta,
     uint32_t* __restrict__ v_meta, uint16_t* __restrict__ k_shadow, uint16_t* __restrict__ v_shadow,
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, int n_new, SeqArg pos,
-    int Hkv, int cap) {
+    int Hkv, int cap, int mshift) {
   const int u = __builtin_amdgcn_workgroup_id_y();
   const int b = u / Hkv;
   const int p0 = pos.v[b];
@@ -87,6 +87,8 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
           __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)), (sub & 1) != 0);
     merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)),
           __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)), (sub & 2) != 0);
+    if (mshift)  // group 64: the quarter pair's lanes (tid ^ 4) hold the group's other half
+      merge(__shfl_xor(mn, 4), __shfl_xor(mx, 4), (grp & 1) != 0);
     const _Float16 s16 = (_Float16)((mx - mn) / qmax);
     const _Float16 z16 = (_Float16)mn;
     const float s = (float)s16, z = (float)z16;
@@ -100,8 +102,8 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
       }
       code[j] = (uint32_t)cd;
     }
-    if (sub == 0)
-      (kv ? v_meta : k_meta)[((size_t)u * kGroups + grp) * cap + t] =
+    if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
+      (kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + t] =
           (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
     *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + c0) = w4;
     if (kv == 0) {
@@ -161,7 +163,7 @@ hipError_t launch_kv(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_
   (void)hipGetLastError();  // report only this launch's status
   pack_append_kernel<KB, VB><<<grid, 256, 0, s>>>(
       static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
-      c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity);
+      c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, L.group == 64 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -169,10 +171,13 @@ hipError_t launch_kv(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_
 
 hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_new,
                               const uint16_t* v_new, int n_new, const SeqArg& pos, hipStream_t s) {
-  if (L.k_bits == 4 && L.v_bits == 4) return launch_kv<4, 4>(L, c, k_new, v_new, n_new, pos, s);
-  if (L.k_bits == 4 && L.v_bits == 2) return launch_kv<4, 2>(L, c, k_new, v_new, n_new, pos, s);
-  if (L.k_bits == 3 && L.v_bits == 4) return launch_kv<3, 4>(L, c, k_new, v_new, n_new, pos, s);
-  return launch_kv<3, 2>(L, c, k_new, v_new, n_new, pos, s);
+  const bool v4 = L.v_bits == 4;
+  switch (L.k_bits) {
+    case 4: return v4 ? launch_kv<4, 4>(L, c, k_new, v_new, n_new, pos, s) : launch_kv<4, 2>(L, c, k_new, v_new, n_new, pos, s);
+    case 3: return v4 ? launch_kv<3, 4>(L, c, k_new, v_new, n_new, pos, s) : launch_kv<3, 2>(L, c, k_new, v_new, n_new, pos, s);
+    case 2: return v4 ? launch_kv<2, 4>(L, c, k_new, v_new, n_new, pos, s) : launch_kv<2, 2>(L, c, k_new, v_new, n_new, pos, s);
+    default: return v4 ? launch_kv<1, 4>(L, c, k_new, v_new, n_new, pos, s) : launch_kv<1, 2>(L, c, k_new, v_new, n_new, pos, s);
+  }
 }
 
 }  // namespace bkv

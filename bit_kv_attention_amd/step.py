@@ -16,9 +16,14 @@ class DecodeStep:
     the two calls qattn_decode_approx and topk_select."""
 
     def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0,
-                 fused: bool = True, select_mode: int = bk.SELECT_AUTO):
+                 fused: bool = True, select_mode: int = bk.SELECT_AUTO, exclude: bool | None = None):
         import torch
         self.fused = bool(fused)
+        # exclude: a second approximate pass over the unselected tokens, merged
+        # with the selected tokens' exact terms instead of subtracting their
+        # approximate ones (default for 1- and 2-bit keys, whose approximate
+        # logits can overshoot by far more than fp32 subtraction survives)
+        self.exclude = (layout.k_bits <= 2) if exclude is None else bool(exclude)
         self.select_mode = int(select_mode)
         self.layout = layout
         self.k = int(k)
@@ -37,6 +42,8 @@ class DecodeStep:
 
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
+        if self.exclude:
+            return self._attend_exclude(cache, q, lens, stream)
         if self.fused and self.block == 0 and self.window == 0:
             bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
                                    self.select_mode)
@@ -53,6 +60,22 @@ class DecodeStep:
             bk.topk_select(self.layout, self.sigma, lens, self.k, self.idx, self.ws, stream)
         bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.row > 0 else None, self.row, self.ws,
                          self.out, stream)
+        return self.out
+
+    def _attend_exclude(self, cache: bk.Cache, q, lens, stream=None):
+        if self.block > 0:
+            bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
+            if self.k > 0:
+                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, stream)
+        elif self.window > 0:
+            bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
+            bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
+        else:
+            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
+                                   self.select_mode)
+        idx = self.idx if self.row > 0 else None
+        bk.qattn_decode_unselected(self.layout, cache, q, lens, idx, self.row, self.ws, stream)
+        bk.qattn_correct_unselected(self.layout, cache, q, lens, idx, self.row, self.ws, self.out, stream)
         return self.out
 
     def attend_hybrid(self, cache: bk.Cache, q, lens, n_threads: int = 0, select: bool = True):

@@ -57,7 +57,13 @@ WORKLOADS = [
     Workload("qwen30b_k3v2_L32768", 4, 32, 4, 128, 32768, 3, 2, 32, 256, 0, 1003),
     Workload("llama70b_k3v2_L131072", 4, 64, 8, 128, 131072, 3, 2, 32, 512, 256, 1004),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# The 8B shape with the aggressive codecs of the TailorKV review (1- and
+# 2-bit keys, 2-bit values, groups of 64 channels).
+CODEC_WORKLOADS = [
+    Workload("llama8b_k2v2g64_L32768", 4, 32, 8, 128, 32768, 2, 2, 64, 256, 64, 1005),
+    Workload("llama8b_k1v2g64_L32768", 4, 32, 8, 128, 32768, 1, 2, 64, 256, 64, 1006),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + CODEC_WORKLOADS}
 
 
 def _f16(x: np.ndarray) -> np.ndarray:

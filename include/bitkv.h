@@ -21,6 +21,9 @@
  *   topk_select_blocks   or whole blocks of tokens by their best score
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
+ *   qattn_decode_unselected, qattn_correct_unselected
+ *                        the approximate pass over the unselected tokens only,
+ *                        then the exact terms merged in (no subtraction)
  *   qattn_exact_host     (host) exact states of the selected tokens from a
  *                        host copy of the shadow rows, for
  *   qattn_correct_hybrid qattn_correct with those exact states
@@ -38,7 +41,7 @@
  *    and returns a status; it never aborts, throws or prints.  On any status
  *    other than BKV_OK nothing was enqueued, except BKV_E_HIP, which reports
  *    a failed launch (hipGetLastError) of one of the call's kernels.
- *  - Supported shapes: head_dim 128, group 32, k_bits in {3, 4},
+ *  - Supported shapes: head_dim 128, group 32 or 64, k_bits in {1, 2, 3, 4},
  *    v_bits in {2, 4}, n_q_heads / n_kv_heads in {4, 8}, capacity a positive
  *    multiple of 32, batch in [1, 256].  Others return BKV_E_UNSUPPORTED or
  *    BKV_E_SHAPE.
@@ -265,6 +268,39 @@ bkv_status qattn_correct(const bkv_layout* layout, const bkv_cache* cache,
                          const uint16_t* q, const int32_t* len_host,
                          const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream);
+
+/*
+ * qattn_decode_unselected -- the approximate pass of qattn_decode_approx
+ * restricted to the tokens that are NOT selected: per (b, kvh) the tokens
+ * listed in the first min(k, len) entries of idx[b][kvh] (as topk_select
+ * writes them; negative or out-of-range entries list nothing) are left out of
+ * the split states it writes to ws; sigma is not written.  Together with
+ * qattn_correct_unselected it computes the same output as qattn_correct, but
+ * merges the exact terms of the selected tokens with a state that never
+ * contained their approximate terms, instead of subtracting those: the
+ * subtraction loses everything in fp32 when the selected tokens' approximate
+ * weights dwarf the rest (as with 1- and 2-bit keys, whose approximate logits
+ * can overshoot by tens of nats).  Costs a second pass over the packed cache.
+ * Needs each scan range (split) at most 16384 tokens (BKV_E_UNSUPPORTED
+ * otherwise); idx entries must be distinct.
+ */
+bkv_status qattn_decode_unselected(const bkv_layout* layout, const bkv_cache* cache,
+                                   const uint16_t* q, const int32_t* len_host,
+                                   const int32_t* idx, int32_t k, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/*
+ * qattn_correct_unselected -- the output from the split states written by
+ * qattn_decode_unselected (same idx, k, lengths and ws) and the exact terms of
+ * the selected tokens: out = (sum over unselected of e^{s_hat} V_hat + sum over
+ * selected of e^{s} V) / (the same sums of the weights), merged in log2
+ * units without any subtraction.  Same arguments, workspace and errors as
+ * qattn_correct.
+ */
+bkv_status qattn_correct_unselected(const bkv_layout* layout, const bkv_cache* cache,
+                                    const uint16_t* q, const int32_t* len_host,
+                                    const int32_t* idx, int32_t k, void* ws,
+                                    size_t ws_bytes, float* out, void* stream);
 
 /*
  * qattn_correct_hybrid -- qattn_correct with the exact half computed

@@ -49,6 +49,8 @@ def test_cache_and_workspace_sizes(bk):
     assert vb == units * 1024 * 32
     assert mb == units * 4 * 1024 * 4
     assert sb == units * 1024 * 128 * 2
+    kb2, _, mb64, _ = bk.bkv_cache_bytes(L(bk, k_bits=2, group=64))  # 2-bit keys; one meta word per 64 channels
+    assert kb2 == units * 1024 * 128 * 2 // 8 and mb64 == units * 2 * 1024 * 4
     w1 = bk.bkv_workspace_bytes(L(bk), 1024, 64)
     w0 = bk.bkv_workspace_bytes(L(bk), 0, 0)
     assert w1 >= 4 * 32 * 130 * 4 + 4 * 32 * 2 * 260 * 4 and w0 > 0
@@ -71,8 +73,14 @@ def test_unsupported_head_dim_and_group(bk):
     out = C.c_size_t()
     lay = bk.Layout(4, 32, 8, 64, 4, 4, 32, 1024)
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
-    lay = bk.Layout(4, 32, 8, 128, 4, 4, 64, 1024)
+    lay = bk.Layout(4, 32, 8, 128, 4, 4, 16, 1024)  # groups of 32 and 64 channels only
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
+    lay = bk.Layout(4, 32, 8, 128, 4, 4, 128, 1024)
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
+    lay = bk.Layout(4, 32, 8, 128, 5, 4, 32, 1024)  # key bits 1..4
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
+    lay = bk.Layout(4, 32, 8, 128, 2, 4, 64, 1024)
+    assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 0
     assert bk.raw_status("bkv_workspace_bytes", None, 10, 4, C.byref(out)) == 1
     lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024)
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, -1, C.byref(out)) == 7
@@ -136,6 +144,19 @@ def test_host_error_paths(bk):
     assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 4, 1000, FAKE, FAKE, need, None) == 5
     assert bk.raw_status(tw, C.byref(lay), FAKE, P(lens), 0, 0, None, None, 0, None) == 0
     assert bk.raw_status(tw, C.byref(lay), FAKE, P(l2), 4, 4, FAKE, FAKE, 1 << 30, None) == 4
+    # the unselected-token pass and its merge; the in-launch selection
+    for fn, extra in (("qattn_decode_unselected", ()), ("qattn_correct_unselected", (FAKE,))):
+        pre = (C.byref(lay), C.byref(cv), FAKE, P(lens))
+        assert bk.raw_status(fn, *pre, FAKE, -1, FAKE, need, *extra, None) == 7
+        assert bk.raw_status(fn, *pre, None, 4, FAKE, need, *extra, None) == 1
+        assert bk.raw_status(fn, *pre, FAKE, 4, FAKE, 64, *extra, None) == 5
+        assert bk.raw_status(fn, C.byref(lay), C.byref(cv), FAKE, P(l2), FAKE, 4, FAKE, need, *extra, None) == 4
+    ds = "qattn_decode_select"
+    pre = (C.byref(lay), C.byref(cv), FAKE, P(lens))
+    assert bk.raw_status(ds, *pre, -1, FAKE, FAKE, FAKE, need, 0, None) == 7
+    assert bk.raw_status(ds, *pre, 4, FAKE, FAKE, FAKE, need, 3, None) == 7
+    assert bk.raw_status(ds, *pre, 4, FAKE, None, FAKE, need, 0, None) == 1
+    assert bk.raw_status(ds, *pre, 4, FAKE, FAKE, FAKE, 64, 0, None) == 5
     # block selection: block not a power of two in [32, 1024], negative or
     # overflowing budget, NULL idx, bad length, the empty budget
     tb = "topk_select_blocks"

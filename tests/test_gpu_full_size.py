@@ -30,7 +30,7 @@ def test_full_size_sampled_units(P, wi):
     cap = ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1)
     kn, vn = make_new_tokens(w, 1, inp.outlier_ch)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group)
     gc = bk.allocate_cache(lay)
     bk.kv_pack_append(lay, gc, P.to_dev(inp.K), P.to_dev(inp.V), L - 1, [0] * w.B)
     st = DecodeStep(lay, w.k, L)
@@ -45,7 +45,7 @@ def test_full_size_sampled_units(P, wi):
     for u in sorted({0, units - 1}):
         b, h = divmod(u, w.Hkv)
         print(f"[case] {w.name} unit {u}", flush=True)
-        oc = oracle.Cache(oracle.Shape(1, w.G, 1, 128, w.kbits, w.vbits, 32, cap))
+        oc = oracle.Cache(oracle.Shape(1, w.G, 1, 128, w.kbits, w.vbits, w.group, cap))
         oc.append(inp.K[b:b + 1, h:h + 1], inp.V[b:b + 1, h:h + 1], np.zeros(1, np.int32))
         oc.append(kn[0][b:b + 1, h:h + 1], vn[0][b:b + 1, h:h + 1], np.array([L - 1], np.int32))
         for name, ob in P.orc_buffers(oc).items():

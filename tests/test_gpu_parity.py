@@ -10,6 +10,8 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 COMBOS = [(kb, vb, G) for kb in (4, 3) for vb in (4, 2) for G in (4, 8)]
+# the low-bit codecs of the TailorKV review (1- and 2-bit keys) and groups of 64
+CODECS = [(2, 2, 4, 64), (1, 2, 8, 64), (2, 4, 8, 32), (1, 4, 4, 32), (4, 4, 4, 64), (3, 2, 8, 64)]
 
 
 @pytest.fixture(scope="module")
@@ -22,20 +24,21 @@ def banner(msg):
     print(f"\n[case] {msg}", flush=True)
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2), (4, 2), (3, 4)])
-def test_pack_bit_exact(P, kb, vb):
+@pytest.mark.parametrize("kb,vb,g", [(4, 4, 32), (3, 2, 32), (4, 2, 32), (3, 4, 32), (2, 2, 32), (1, 4, 32),
+                                     (2, 2, 64), (1, 2, 64), (4, 4, 64), (3, 2, 64)])
+def test_pack_bit_exact(P, kb, vb, g):
     """Bulk prefill into a partial tile, a multi-token append with ragged
     positions (one sequence rewrites slots), then a single-token append."""
     import torch
     from bit_kv_attention_amd import binding as bk
     import oracle
-    banner(f"pack kb={kb} vb={vb}")
-    w = P.Workload("pack", 2, 8, 2, 128, 200, kb, vb, 32, 8, 3, 31)
+    banner(f"pack kb={kb} vb={vb} g={g}")
+    w = P.Workload("pack", 2, 8, 2, 128, 200, kb, vb, g, 8, 3, 31)
     inp = P.make_inputs(w, L=120)
     cap = 160
-    lay = bk.make_layout(2, 8, 2, cap, kb, vb)
+    lay = bk.make_layout(2, 8, 2, cap, kb, vb, group=g)
     gc = bk.allocate_cache(lay)
-    oc = oracle.Cache(oracle.Shape(2, 8, 2, 128, kb, vb, 32, cap))
+    oc = oracle.Cache(oracle.Shape(2, 8, 2, 128, kb, vb, g, cap))
     steps = [(inp.K[:, :, :77], inp.V[:, :, :77], [0, 0]),
              (inp.K[:, :, 77:117], inp.V[:, :, 77:117], [77, 60]),
              (inp.K[:, :, 117:118], inp.V[:, :, 117:118], [117, 100])]
@@ -81,20 +84,20 @@ def special_rows(rng, n):
     return x
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2)])
-def test_pack_special_values(P, kb, vb):
+@pytest.mark.parametrize("kb,vb,g", [(4, 4, 32), (3, 2, 32), (2, 2, 64), (1, 2, 64)])
+def test_pack_special_values(P, kb, vb, g):
     """Edge-value groups, bulk then one token at a time, bit-exact."""
     import torch
     from bit_kv_attention_amd import binding as bk
     import oracle
-    banner(f"pack special values kb={kb} vb={vb}")
+    banner(f"pack special values kb={kb} vb={vb} g={g}")
     rng = np.random.default_rng(7)
     B, Hkv, n, cap = 2, 2, 48, 64
     K = special_rows(rng, B * Hkv * n).reshape(B, Hkv, n, 128)
     V = special_rows(rng, B * Hkv * n)[::-1].copy().reshape(B, Hkv, n, 128)
-    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, kb, vb)
+    lay = bk.make_layout(B, 4 * Hkv, Hkv, cap, kb, vb, group=g)
     gc = bk.allocate_cache(lay)
-    oc = oracle.Cache(oracle.Shape(B, 4 * Hkv, Hkv, 128, kb, vb, 32, cap))
+    oc = oracle.Cache(oracle.Shape(B, 4 * Hkv, Hkv, 128, kb, vb, g, cap))
     steps = [(0, 40)] + [(t, t + 1) for t in range(40, n)]
     for a, e in steps:
         Kn, Vn = K[:, :, a:e], V[:, :, a:e]
@@ -106,10 +109,10 @@ def test_pack_special_values(P, kb, vb):
         assert np.array_equal(g[name], o[name]), name
 
 
-@pytest.mark.parametrize("kb,vb,G", COMBOS)
-def test_step_parity_small(P, kb, vb, G):
-    banner(f"step kb={kb} vb={vb} G={G}")
-    w = P.Workload("small", 2, 2 * G, 2, 128, 1000, kb, vb, 32, 24, 6, 100 + 10 * kb + vb + G)
+@pytest.mark.parametrize("kb,vb,G,g", [c + (32,) for c in COMBOS] + CODECS)
+def test_step_parity_small(P, kb, vb, G, g):
+    banner(f"step kb={kb} vb={vb} G={G} g={g}")
+    w = P.Workload("small", 2, 2 * G, 2, 128, 1000, kb, vb, g, 24, 6, 100 + 10 * kb + vb + G + g)
     pair = P.build_pair(w, L=1000, cap=1024)
     lens = np.array([1000, 651])
     k = 24
@@ -456,25 +459,25 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs):
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
 
 
-@pytest.mark.parametrize("kb,vb,G", COMBOS)
-def test_decode_select_equals_two_calls(P, kb, vb, G):
+@pytest.mark.parametrize("kb,vb,G,g", [c + (32,) for c in COMBOS] + [(2, 2, 4, 64), (1, 2, 8, 64)])
+def test_decode_select_equals_two_calls(P, kb, vb, G, g):
     """qattn_decode_select (selection inside the scan's launch) against
     qattn_decode_approx + topk_select on the same inputs: identical sigma, rows
     and output, rows exact against the oracle's top-k of that sigma; ragged and
     empty sequences, k = 1, k >= len, and a budget past the in-launch limit
     (two launches)."""
-    banner(f"decode_select kb={kb} vb={vb} G={G}")
+    banner(f"decode_select kb={kb} vb={vb} G={G} g={g}")
     import torch
     import oracle
     from bit_kv_attention_amd.step import DecodeStep
-    w = P.Workload("sel", 4, 2 * G, 2, 128, 4000, kb, vb, 32, 32, 6, 900 + 10 * kb + vb + G)
+    w = P.Workload("sel", 4, 2 * G, 2, 128, 4000, kb, vb, g, 32, 6, 900 + 10 * kb + vb + G)
     pair = P.build_pair(w, L=4000, cap=4000)
     lens = np.array([3999, 2500, 1, 0])  # (the prefill filled 3999 slots)
     q = P.to_dev(pair["q"])
     for k in (1, 37, 300, 500, 2600, 5000):  # 16 ranges per unit: 500 is the last in-launch budget
         runs = []
         for fused in (True, False):  # the selection in the scan's launch whenever possible, and two calls
-            st = DecodeStep(pair["lay"], k, 3999, fused=fused, select_mode=1)
+            st = DecodeStep(pair["lay"], k, 3999, fused=fused, select_mode=1, exclude=False)
             for _ in range(2):  # twice on one workspace
                 st.sigma.fill_(float("nan"))
                 st.idx.fill_(-7)
@@ -525,3 +528,33 @@ def test_hybrid_host_correction(P, kb, vb, G):
         orc = oc.decode(inp.q, lens, k, sel=idx if k > 0 else None)
         P.assert_close(oh, orc["out"], f"hybrid vs oracle k={k}")
         np.testing.assert_allclose(oh, og, rtol=1e-4, atol=1e-5)
+
+
+@pytest.mark.parametrize("kb,vb,G,g", [(4, 4, 4, 32), (3, 2, 8, 32), (2, 2, 8, 64), (1, 2, 4, 64), (1, 4, 8, 32)])
+def test_exclude_path(P, kb, vb, G, g):
+    """qattn_decode_unselected + qattn_correct_unselected (the unselected
+    tokens' approximate state merged with the selected tokens' exact terms)
+    against the oracle on the GPU's rows; ragged and empty sequences, k >= len,
+    k = 0, two calls in a row; for 3- and 4-bit keys also against the
+    subtracting qattn_correct."""
+    banner(f"exclude path kb={kb} vb={vb} G={G} g={g}")
+    import torch
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("exc", 3, 2 * G, 2, 128, 3000, kb, vb, g, 40, 6, 1300 + 10 * kb + G + g)
+    pair = P.build_pair(w, L=3000, cap=3008)
+    lens = np.array([2999, 1400, 0])
+    q = P.to_dev(pair["q"])
+    for k in (40, 1500, 0):
+        st = DecodeStep(pair["lay"], k, 2999, exclude=True)
+        for _ in range(2):
+            out = st.attend(pair["gc"], q, lens)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+        idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, max(k, 1))[:, :, :k]
+        orc = pair["oc"].decode(pair["q"], lens, k, sel=idx if k > 0 else None)
+        P.assert_close(o, orc["out"], f"exclude vs oracle k={k}")
+        if kb >= 3:
+            st2 = DecodeStep(pair["lay"], k, 2999, exclude=False)
+            o2 = st2.attend(pair["gc"], q, lens)
+            torch.cuda.synchronize()
+            np.testing.assert_allclose(o, o2.cpu().numpy().reshape(w.B, w.Hq, 128), rtol=2e-3, atol=2e-4)

@@ -46,9 +46,9 @@ def dequant_np(orc, X, g, bits):
     return s * codes + z
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2)])
-def test_k_all_equals_dense_fp16_attention(orc, kb, vb):
-    w = small_workload(kbits=kb, vbits=vb)
+@pytest.mark.parametrize("kb,vb,g", [(4, 4, 32), (3, 2, 32), (2, 2, 64), (1, 2, 64)])
+def test_k_all_equals_dense_fp16_attention(orc, kb, vb, g):
+    w = small_workload(kbits=kb, vbits=vb, group=g)
     inp = make_inputs(w)
     cache = build(orc, w, inp)
     lens = np.full(w.B, w.L)
@@ -60,14 +60,15 @@ def test_k_all_equals_dense_fp16_attention(orc, kb, vb):
     np.testing.assert_allclose(r2["out"], ref, rtol=1e-11, atol=1e-12)
 
 
-@pytest.mark.parametrize("kb,vb", [(4, 4), (3, 2), (4, 2), (3, 4)])
-def test_k_zero_equals_attention_over_dequantised_cache(orc, kb, vb):
-    w = small_workload(kbits=kb, vbits=vb)
+@pytest.mark.parametrize("kb,vb,g", [(4, 4, 32), (3, 2, 32), (4, 2, 32), (3, 4, 32), (2, 2, 32), (1, 4, 32),
+                                     (4, 4, 64), (2, 2, 64), (1, 2, 64)])
+def test_k_zero_equals_attention_over_dequantised_cache(orc, kb, vb, g):
+    w = small_workload(kbits=kb, vbits=vb, group=g)
     inp = make_inputs(w)
     cache = build(orc, w, inp)
     r = cache.decode(inp.q, np.full(w.B, w.L), k=0, want_approx=True)
-    Kh = dequant_np(orc, inp.K, 32, kb)
-    Vh = dequant_np(orc, inp.V, 32, vb)
+    Kh = dequant_np(orc, inp.K, g, kb)
+    Vh = dequant_np(orc, inp.V, g, vb)
     ref = dense(inp.q.astype(np.float64), Kh, Vh, w.G)
     np.testing.assert_allclose(r["out"], ref, rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(r["out_approx"], ref, rtol=1e-11, atol=1e-12)

@@ -77,7 +77,7 @@ def test_one_element_group_is_exact(orc):
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
-@pytest.mark.parametrize("g", [4, 32, 128])
+@pytest.mark.parametrize("g", [4, 32, 64, 128])
 def test_error_within_half_step(orc, bits, g):
     """|x - x_hat| <= s16/2 per element, plus the fp32 rounding of (x - z)/s
     (at most 2^-22 of the larger magnitude)."""

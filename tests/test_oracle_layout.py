@@ -37,7 +37,7 @@ def test_v_tile_is_a_partition(orc, bits):
     assert orc.v_bitpos(32, 0, D, bits) == 32 * D * bits
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_k_block_is_a_partition(orc, bits):
     D = 128
     owner = np.full(16 * D * bits, -1, dtype=np.int64)
@@ -69,7 +69,7 @@ def k_block_closed_form(codes16, bits):
     return np.frombuffer(val.to_bytes(nbytes, "little"), dtype=np.uint8)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_k_blocks_closed_form(orc, bits):
     """Packed K blocks equal an independently built integer (see
     k_block_closed_form); the last block is partly filled and the rows past
@@ -96,10 +96,10 @@ def test_k_blocks_closed_form(orc, bits):
     assert not cache.k_codes[3 * bb:].any()
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_v_roundtrip_and_meta_and_shadow(orc, bits):
+@pytest.mark.parametrize("bits,group", [(2, 32), (4, 32), (2, 64), (4, 64)])
+def test_v_roundtrip_and_meta_and_shadow(orc, bits, group):
     rng = np.random.default_rng(20 + bits)
-    s = orc.Shape(B=2, Hq=4, Hkv=2, D=128, kbits=4, vbits=bits, group=32, cap=96)
+    s = orc.Shape(B=2, Hq=4, Hkv=2, D=128, kbits=4, vbits=bits, group=group, cap=96)
     cache = orc.Cache(s)
     n = 70
     K = rng.standard_normal((2, 2, n, 128)).astype(np.float16)
@@ -108,7 +108,7 @@ def test_v_roundtrip_and_meta_and_shadow(orc, bits):
     ub = 96 * 128 * bits // 8
     for u in range(4):
         b, h = divmod(u, 2)
-        codes, vs, vz = orc.quantize_rows(V[b, h], 32, bits)
+        codes, vs, vz = orc.quantize_rows(V[b, h], group, bits)
         base = cache.v_codes[u * ub:(u + 1) * ub]
         for t in range(0, n, 7):
             for c in range(0, 128, 5):
