@@ -141,6 +141,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     fused = in_scan
     # 1- and 2-bit keys: the unselected tokens' state from a second pass (see DecodeStep)
     exclude = st.exclude and not hybrid
+    exclude_scores = exclude and not NB and not W and not args.two_launch
     nthr = args.cpu_threads or 16
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
@@ -179,20 +180,28 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         cache = caches[i % copies]
         bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
         ev_i = sev[i // SAMPLE] if i % SAMPLE == 0 else None
-        if ev_i:
-            ev_i[0].record()
-        if fused:
+        ev_scan = ev_i if not exclude else None  # the dominant launch: the scan, or the second pass
+        ev_rest = ev_i if exclude else None
+        if ev_scan:
+            ev_scan[0].record()
+        if exclude_scores:  # scores and rows only, then the second pass below
+            bk.qattn_score_select(lay, cache, q, lens, w.k, st.sigma, st.idx, st.ws)
+        elif fused:
             bk.qattn_decode_select(lay, cache, q, lens, w.k, st.sigma, st.idx, st.ws)
         else:
             bk.qattn_decode_approx(lay, cache, q, lens, st.sigma, st.ws)
-        if ev_i:
-            ev_i[1].record()
-        if not fused:
+        if ev_scan:
+            ev_scan[1].record()
+        if not fused and not exclude_scores:
             select()
         if hybrid:
             st.attend_hybrid(cache, q, lens, nthr, select=False)
         elif exclude:
+            if ev_rest:
+                ev_rest[0].record()
             bk.qattn_decode_unselected(lay, cache, q, lens, st.idx, st.row, st.ws)
+            if ev_rest:
+                ev_rest[1].record()
             bk.qattn_correct_unselected(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
         else:
             bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
@@ -209,7 +218,11 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                  lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
                  lambda c: st.attend_hybrid(c, q, lens, nthr, select=False))
     else:
-        if fused:
+        if exclude_scores:
+            names = ["kv_pack_append", "qattn_score_select"]
+            calls = [lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
+                     lambda c: bk.qattn_score_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws)]
+        elif fused:
             names = ["kv_pack_append", "qattn_decode_select"]
             calls = [lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
                      lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws)]
@@ -243,7 +256,10 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     # packed codes + meta of K and V for every token of every unit, the fp32
     # selection score written per token, and the split partial states written
     # (plus, with the selection in the same launch, the k indices per unit).
-    scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L) + (units * w.k * 4 if in_scan else 0)
+    if exclude:  # the second pass: packed bytes and split states, the rows read (no sigma)
+        scan_bytes = units * L * ppt + scan_partial_bytes(lay, L) + units * st.row * 4
+    else:
+        scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L) + (units * w.k * 4 if in_scan else 0)
     scan_s = scan_us_timed / 1e6
     achieved = scan_bytes / scan_s / 1e9
     traffic = measured_traffic(w.name)
@@ -272,7 +288,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": {n: round(v, 2) for n, v in kus.items()},
         "wall_s_timed_region": round(t_wall, 3),
-        "roofline": {"kernel": "qattn_decode_select (scan + top-k launch)" if in_scan else "qattn_decode_approx (scan launch)", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": ("qattn_decode_unselected (second pass)" if exclude else
+                               "qattn_decode_select (scan + top-k launch)" if in_scan else
+                               "qattn_decode_approx (scan launch)"), "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": scan_bytes,
                      "kernel_us_per_launch": round(scan_us_timed, 2), "launches_timed": len(sev)},

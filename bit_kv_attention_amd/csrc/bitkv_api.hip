@@ -205,7 +205,7 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
   const int units = L->batch * L->n_kv_heads;
   const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0, false,
+  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0, false, false,
                               (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
@@ -250,9 +250,9 @@ bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const ui
   const int chunk = split_tokens(units, max_len);
   const hipStream_t s = (hipStream_t)stream;
   if (select_in_scan(w, chunk, k, mode))
-    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, s) == hipSuccess ? BKV_OK
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, false, s) == hipSuccess ? BKV_OK
                                                                                                 : BKV_E_HIP;
-  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, s) != hipSuccess) return BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, false, s) != hipSuccess) return BKV_E_HIP;
   if (k == 0) return BKV_OK;
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
@@ -321,6 +321,30 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
                                                                                                    : BKV_E_HIP;
 }
 
+bkv_status qattn_score_select(const bkv_layout* L, const bkv_cache* c, const uint16_t* q, const int32_t* len_host,
+                              int32_t k, float* sigma, int32_t* idx, void* ws, size_t ws_bytes, int32_t mode,
+                              void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0 || mode < 0 || mode > 2) return BKV_E_ARG;
+  if (!q || !sigma || !ws || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  const int chunk = split_tokens(units, max_len);
+  const hipStream_t s = (hipStream_t)stream;
+  if (select_in_scan(w, chunk, k, mode))
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, true, s) == hipSuccess ? BKV_OK
+                                                                                               : BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, true, s) != hipSuccess) return BKV_E_HIP;
+  if (k == 0) return BKV_OK;
+  return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
+}
+
 bkv_status qattn_decode_unselected(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
                                    const int32_t* len_host, const int32_t* idx, int32_t k, void* ws,
                                    size_t ws_bytes, void* stream) {
@@ -337,7 +361,7 @@ bkv_status qattn_decode_unselected(const bkv_layout* L, const bkv_cache* c, cons
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
   const int chunk = split_tokens(units, max_len);
   if (chunk > kSelStage) return BKV_E_UNSUPPORTED;
-  return launch_decode_approx(*L, *c, q, len, nullptr, w, chunk, const_cast<int32_t*>(idx), k, true,
+  return launch_decode_approx(*L, *c, q, len, nullptr, w, chunk, const_cast<int32_t*>(idx), k, true, false,
                               (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;

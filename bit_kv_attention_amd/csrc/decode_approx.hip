@@ -159,7 +159,7 @@ struct Step {
   u32x4 meta;           // lane < 32: key meta, else value meta (group, 4 tokens)
 };
 
-template <int KB, int VB, int G>
+template <int KB, int VB, int G, bool SIGONLY = false>
 __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__ kbase,
                                  const uint8_t* __restrict__ vbase, const uint32_t* __restrict__ kmeta,
                                  const uint32_t* __restrict__ vmeta, int cap, int t0, int lane, int mshift) {
@@ -182,11 +182,13 @@ __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__
       S.kc[tt][0] = *reinterpret_cast<const uint32_t*>(blk);
     }
   }
-  const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB) + (size_t)lane * 16;
+  if constexpr (!SIGONLY) {  // (scores only: no values)
+    const uint8_t* vt = vbase + (size_t)(t0 / kTile) * v_tile_bytes(VB) + (size_t)lane * 16;
 #pragma unroll
-  for (int pc = 0; pc < VB / 2; ++pc) S.vd[pc] = *reinterpret_cast<const u32x4*>(vt + 1024 * pc);
+    for (int pc = 0; pc < VB / 2; ++pc) S.vd[pc] = *reinterpret_cast<const u32x4*>(vt + 1024 * pc);
+  }
   const uint32_t* mp = (lane < 32 ? kmeta : vmeta) + (size_t)(((lane & 31) >> 3) >> mshift) * cap + t0 + 4 * (lane & 7);
-  S.meta = *reinterpret_cast<const u32x4*>(mp);
+  if (!SIGONLY || lane < 32) S.meta = *reinterpret_cast<const u32x4*>(mp);
 }
 
 // Meta of a step in the wave's LDS slot: 16-byte cells
@@ -218,8 +220,9 @@ constexpr int kZS = (VB == 4) ? 2 : 4;
 
 // One 32-token step.  MASK: the step straddles the sequence end.  SKIP: the
 // tokens whose bit is set in skipw (bit 16tt + 4kb + i for token
-// t0 + 16tt + 4kb + i) are left out, as if past the end.
-template <int KB, int VB, int G, bool MASK, bool SKIP = false>
+// t0 + 16tt + 4kb + i) are left out, as if past the end.  SIGONLY: only the
+// selection scores.
+template <int KB, int VB, int G, bool MASK, bool SKIP = false, bool SIGONLY = false>
 __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
                                           const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const half8 (&bq)[kGroups],
                                           const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
@@ -288,6 +291,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
     if (n == 0)
       sig_row[4 * tt + kb] = (floatx4){sg4[0], sg4[1], sg4[2], sg4[3]};
   }
+  if constexpr (SIGONLY) return;
 
   // -- online softmax (log2 units) --------------------------------------------
   // (max(x) * c == max(x * c) for c > 0, rounding included)
@@ -355,7 +359,9 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // SKIP: the softmax state leaves out the tokens listed in the first
 // min(ksel, len) entries of the unit's row of idx (the workgroup marks those
 // of its split in an LDS bitmap first); no selection score is stored.
-template <int KB, int VB, int G, bool SEL, bool SKIP = false>
+// SIGONLY: only the selection scores (and SEL's selection): no values are
+// read and no split state is written.
+template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
@@ -496,11 +502,11 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
   // copies (a copy of registers with loads in flight would wait for them).
   auto full_step = [&](Step<KB, VB, G>& cur, Step<KB, VB, G>& nxt, int t0) {
     const int tn = (t0 + kScanWaves * kTile) < t_end ? t0 + kScanWaves * kTile : t0;
-    load_step<KB, VB, G>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane, mshift);
+    load_step<KB, VB, G, SIGONLY>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane, mshift);
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, false, SKIP>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
+    scan_step<KB, VB, G, false, SKIP, SIGONLY>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
                                       SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     if (++sig_count == kSigBatch) flush_sig();
   };
@@ -509,13 +515,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, true, SKIP>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
+    scan_step<KB, VB, G, true, SKIP, SIGONLY>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
   Step<KB, VB, G> sa, sb;
   int t0 = t_begin + kTile * wv;
-  if (t0 < t_end) load_step<KB, VB, G>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
+  if (t0 < t_end) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
   for (;;) {
     if (t0 + kTile > t_end) {
       if (t0 < t_end) last_step(sa, t0);
@@ -533,6 +539,9 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
   if (sig_count > 0) flush_sig();
 
   // ---- combine the waves of the workgroup -----------------------------------
+  if constexpr (SIGONLY) {
+    __syncthreads();  // (orders every flush before the selection below)
+  } else {
   ws.l_part += __shfl_xor(ws.l_part, 16);
   ws.l_part += __shfl_xor(ws.l_part, 32);
   float z_tot[NT];
@@ -591,6 +600,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
       pl[rec] = l;
     }
   }
+  }  // !SIGONLY
 
   if constexpr (SEL) {
     // ---- the split's top-min(kk, split length), then the unit's merge -----------
@@ -645,13 +655,22 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
 
 template <int KB, int VB, int G>
 hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, bool sigonly,
+                    hipStream_t s) {
   dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
   const int mshift = L.group == 64 ? 1 : 0;
   const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(c.v_codes);
   (void)hipGetLastError();  // report only this launch's status
-  if (skip)
+  if (sigonly && ksel > 0)
+    decode_approx_kernel<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift);
+  else if (sigonly)
+    decode_approx_kernel<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift);
+  else if (skip)
     decode_approx_kernel<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift);
@@ -668,27 +687,28 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 
 template <int KB, int VB>
 hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
-                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, hipStream_t s) {
+                    float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, bool sigonly,
+                    hipStream_t s) {
   const int G = L.n_q_heads / L.n_kv_heads;
-  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
-  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                int32_t* idx, int ksel, bool skip, hipStream_t s) {
+                                int32_t* idx, int ksel, bool skip, bool sigonly, hipStream_t s) {
   const bool v4 = L.v_bits == 4;
   switch (L.k_bits) {
-    case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
-                      : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
-    case 3: return v4 ? launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
-                      : launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
-    case 2: return v4 ? launch_g<2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
-                      : launch_g<2, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
-    default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s)
-                       : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, s);
+    case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
+                      : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+    case 3: return v4 ? launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
+                      : launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+    case 2: return v4 ? launch_g<2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
+                      : launch_g<2, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+    default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
+                       : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
   }
 }
 

@@ -70,9 +70,9 @@ class DecodeStep:
         elif self.window > 0:
             bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
             bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
-        else:
-            bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
-                                   self.select_mode)
+        else:  # scores and rows only: the state comes from the second pass
+            bk.qattn_score_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
+                                  self.select_mode)
         idx = self.idx if self.row > 0 else None
         bk.qattn_decode_unselected(self.layout, cache, q, lens, idx, self.row, self.ws, stream)
         bk.qattn_correct_unselected(self.layout, cache, q, lens, idx, self.row, self.ws, self.out, stream)

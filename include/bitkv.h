@@ -21,6 +21,7 @@
  *   topk_select_blocks   or whole blocks of tokens by their best score
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
+ *   qattn_score_select   sigma and the top-k rows only (no softmax state)
  *   qattn_decode_unselected, qattn_correct_unselected
  *                        the approximate pass over the unselected tokens only,
  *                        then the exact terms merged in (no subtraction)
@@ -268,6 +269,17 @@ bkv_status qattn_correct(const bkv_layout* layout, const bkv_cache* cache,
                          const uint16_t* q, const int32_t* len_host,
                          const int32_t* idx, int32_t k, void* ws,
                          size_t ws_bytes, float* out, void* stream);
+
+/*
+ * qattn_score_select -- the selection scores and top-k rows of
+ * qattn_decode_select (identical sigma and idx, same mode and workspace),
+ * without the softmax state: the value codes are not read and no split state
+ * is written.  The first pass of the exclusion path below.
+ */
+bkv_status qattn_score_select(const bkv_layout* layout, const bkv_cache* cache,
+                              const uint16_t* q, const int32_t* len_host,
+                              int32_t k, float* sigma, int32_t* idx, void* ws,
+                              size_t ws_bytes, int32_t mode, void* stream);
 
 /*
  * qattn_decode_unselected -- the approximate pass of qattn_decode_approx

@@ -558,3 +558,29 @@ def test_exclude_path(P, kb, vb, G, g):
             o2 = st2.attend(pair["gc"], q, lens)
             torch.cuda.synchronize()
             np.testing.assert_allclose(o, o2.cpu().numpy().reshape(w.B, w.Hq, 128), rtol=2e-3, atol=2e-4)
+
+
+@pytest.mark.parametrize("kb,vb,G,g", [(4, 4, 4, 32), (1, 2, 8, 64)])
+def test_score_select_equals_decode_select(P, kb, vb, G, g):
+    """qattn_score_select writes the same sigma and rows as qattn_decode_select,
+    in the scan's launch and as two launches."""
+    banner(f"score_select kb={kb} vb={vb} G={G} g={g}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("ss", 3, 2 * G, 2, 128, 3000, kb, vb, g, 40, 6, 1500 + G + g)
+    pair = P.build_pair(w, L=3000, cap=3008)
+    lens = np.array([2999, 1400, 0])
+    q = P.to_dev(pair["q"])
+    for k in (40, 500):
+        for mode in (1, 2):
+            a = DecodeStep(pair["lay"], k, 2999)
+            b = DecodeStep(pair["lay"], k, 2999)
+            bk.qattn_decode_select(pair["lay"], pair["gc"], q, lens, k, a.sigma, a.idx, a.ws, mode=mode)
+            bk.qattn_score_select(pair["lay"], pair["gc"], q, lens, k, b.sigma, b.idx, b.ws, mode=mode)
+            torch.cuda.synchronize()
+            sa = a.sigma.cpu().numpy().reshape(w.B, w.Hkv, -1)
+            sb = b.sigma.cpu().numpy().reshape(w.B, w.Hkv, -1)
+            for bb in range(w.B):
+                assert np.array_equal(sa[bb, :, :lens[bb]], sb[bb, :, :lens[bb]]), (k, mode)
+            assert torch.equal(a.idx, b.idx), (k, mode)
