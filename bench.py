@@ -58,6 +58,8 @@ def main(argv=None) -> int:
     ap.add_argument("--exact", choices=["gpu", "host"], default="gpu",
                     help="host: the exact half of the correction on the host's cores from a pinned host "
                          "shadow (qattn_exact_host + qattn_correct_hybrid)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with kv_pack_append before the scan instead of inside its launch")
     ap.add_argument("--two-launch", action="store_true",
                     help="run the scan and the top-k as two calls (qattn_decode_approx, topk_select)")
     ap.add_argument("--window", type=int, default=0,
@@ -142,6 +144,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     # 1- and 2-bit keys: the unselected tokens' state from a second pass (see DecodeStep)
     exclude = st.exclude and not hybrid
     exclude_scores = exclude and not NB and not W and not args.two_launch
+    # the plain step appends the new token inside the scan's launch (qattn_decode_step)
+    step_launch = st.fused and not NB and not W and not exclude and not hybrid and not args.separate_append
     nthr = args.cpu_threads or 16
     pos = [L - 1] * w.B  # each step writes the newest token at slot L-1, then attends over L
     lens = [L] * w.B
@@ -156,6 +160,9 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
 
     def step(i):
         cache = caches[i % copies]
+        if step_launch:
+            st.step(cache, q, kn, vn, pos)
+            return
         bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
         if hybrid:
             st.attend_hybrid(cache, q, lens, nthr)
@@ -178,8 +185,18 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     e0.record()
     for i in range(args.steps):
         cache = caches[i % copies]
-        bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
         ev_i = sev[i // SAMPLE] if i % SAMPLE == 0 else None
+        if step_launch:  # the append inside the scan's launch (with the top-k too where that is faster)
+            if ev_i:
+                ev_i[0].record()
+            bk.qattn_decode_step(lay, cache, kn, vn, q, lens, w.k if in_scan else 0, st.sigma, st.idx, st.ws)
+            if ev_i:
+                ev_i[1].record()
+            if not in_scan:
+                select()
+            bk.qattn_correct(lay, cache, q, lens, st.idx, st.row, st.ws, st.out)
+            continue
+        bk.kv_pack_append(lay, cache, kn, vn, 1, pos)
         ev_scan = ev_i if not exclude else None  # the dominant launch: the scan, or the second pass
         ev_rest = ev_i if exclude else None
         if ev_scan:
@@ -217,6 +234,12 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         calls = (lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, pos),
                  lambda c: bk.qattn_decode_select(lay, c, q, lens, w.k, st.sigma, st.idx, st.ws),
                  lambda c: st.attend_hybrid(c, q, lens, nthr, select=False))
+    elif step_launch:
+        names = ["qattn_decode_step"] + ([] if in_scan else ["topk_select"]) + ["qattn_correct"]
+        calls = [lambda c: bk.qattn_decode_step(lay, c, kn, vn, q, lens, w.k if in_scan else 0, st.sigma, st.idx,
+                                                st.ws)] + \
+                ([] if in_scan else [lambda c: select()]) + \
+                [lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out)]
     else:
         if exclude_scores:
             names = ["kv_pack_append", "qattn_score_select"]
@@ -260,6 +283,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         scan_bytes = units * L * ppt + scan_partial_bytes(lay, L) + units * st.row * 4
     else:
         scan_bytes = units * L * (ppt + 4) + scan_partial_bytes(lay, L) + (units * w.k * 4 if in_scan else 0)
+        if step_launch:  # + the appended rows read and the token's codes, meta and shadow rows written
+            scan_bytes += units * (2 * 256 + ppt + 2 * 256)
     scan_s = scan_us_timed / 1e6
     achieved = scan_bytes / scan_s / 1e9
     traffic = measured_traffic(w.name)
@@ -282,13 +307,16 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
                    "blocks": NB, "block": args.block if NB else 0,
                    "shadow": "host" if hybrid else args.shadow, "exact": args.exact,
                    "cache_copies": copies,
-                   "selection_in_scan_launch": bool(in_scan), "unselected_second_pass": bool(exclude),
+                   "selection_in_scan_launch": bool(in_scan), "append_in_scan_launch": bool(step_launch),
+                   "unselected_second_pass": bool(exclude),
                    "parallelism": "single GPU"},
         "packed_kv_GBps": round(packed_gbps, 1),
         "packed_kv_frac_of_hbm_peak": round(packed_gbps / HBM_PEAK_GBPS, 4),
         "kernel_us": {n: round(v, 2) for n, v in kus.items()},
         "wall_s_timed_region": round(t_wall, 3),
         "roofline": {"kernel": ("qattn_decode_unselected (second pass)" if exclude else
+                               "qattn_decode_step (append + scan + top-k launch)" if step_launch and in_scan else
+                               "qattn_decode_step (append + scan launch)" if step_launch else
                                "qattn_decode_select (scan + top-k launch)" if in_scan else
                                "qattn_decode_approx (scan launch)"), "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),

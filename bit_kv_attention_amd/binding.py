@@ -60,6 +60,7 @@ _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
+_lib.qattn_decode_step.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
 _lib.bkv_select_in_scan.argtypes = [_LP, C.c_int32, C.c_int32, C.c_int32, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
@@ -76,7 +77,7 @@ for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_p
 EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
             "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
-            "qattn_correct_unselected", "qattn_score_select")
+            "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step")
 
 
 def _check(fn: str, st: int) -> None:
@@ -179,6 +180,16 @@ def qattn_decode_select(layout: Layout, cache: Cache, q, len_host, k: int, sigma
     _check("qattn_decode_select", _lib.qattn_decode_select(C.byref(layout), C.byref(view), _ptr(q),
                                                            lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
                                                            _ptr(ws), ws_bytes, int(mode), _stream(stream)))
+
+
+def qattn_decode_step(layout: Layout, cache: Cache, k_new, v_new, q, len_host, k: int, sigma, idx, ws, stream=None,
+                      mode: int = SELECT_AUTO) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_decode_step", _lib.qattn_decode_step(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new),
+                                                       _ptr(q), lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
+                                                       _ptr(ws), ws_bytes, int(mode), _stream(stream)))
 
 
 def bkv_select_in_scan(layout: Layout, max_len: int, k: int, mode: int = SELECT_AUTO) -> bool:

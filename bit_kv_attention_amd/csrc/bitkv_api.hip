@@ -205,7 +205,7 @@ bkv_status qattn_decode_approx(const bkv_layout* L, const bkv_cache* c, const ui
   const int units = L->batch * L->n_kv_heads;
   const Workspace w = workspace_layout(ws, *L, max_len, 0, false);
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
-  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0, false, false,
+  return launch_decode_approx(*L, *c, q, len, sigma, w, split_tokens(units, max_len), nullptr, 0, false, false, nullptr, nullptr,
                               (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;
@@ -250,9 +250,9 @@ bkv_status qattn_decode_select(const bkv_layout* L, const bkv_cache* c, const ui
   const int chunk = split_tokens(units, max_len);
   const hipStream_t s = (hipStream_t)stream;
   if (select_in_scan(w, chunk, k, mode))
-    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, false, s) == hipSuccess ? BKV_OK
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, false, nullptr, nullptr, s) == hipSuccess ? BKV_OK
                                                                                                 : BKV_E_HIP;
-  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, false, s) != hipSuccess) return BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, false, nullptr, nullptr, s) != hipSuccess) return BKV_E_HIP;
   if (k == 0) return BKV_OK;
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
@@ -321,6 +321,35 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
                                                                                                    : BKV_E_HIP;
 }
 
+bkv_status qattn_decode_step(const bkv_layout* L, const bkv_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                             const uint16_t* q, const int32_t* len_host, int32_t k, float* sigma, int32_t* idx,
+                             void* ws, size_t ws_bytes, int32_t mode, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0 || mode < 0 || mode > 2) return BKV_E_ARG;
+  if (!k_new || !v_new || !q || !sigma || !ws || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  for (int b = 0; b < L->batch; ++b)
+    if (len.v[b] < 1) return BKV_E_CAPACITY;  // the new token goes to len - 1
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  const int chunk = split_tokens(units, max_len);
+  const hipStream_t s = (hipStream_t)stream;
+  if (select_in_scan(w, chunk, k, mode))
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, false, k_new, v_new, s) ==
+                   hipSuccess
+               ? BKV_OK
+               : BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, false, k_new, v_new, s) != hipSuccess)
+    return BKV_E_HIP;
+  if (k == 0) return BKV_OK;
+  return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
+}
+
 bkv_status qattn_score_select(const bkv_layout* L, const bkv_cache* c, const uint16_t* q, const int32_t* len_host,
                               int32_t k, float* sigma, int32_t* idx, void* ws, size_t ws_bytes, int32_t mode,
                               void* stream) {
@@ -338,9 +367,9 @@ bkv_status qattn_score_select(const bkv_layout* L, const bkv_cache* c, const uin
   const int chunk = split_tokens(units, max_len);
   const hipStream_t s = (hipStream_t)stream;
   if (select_in_scan(w, chunk, k, mode))
-    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, true, s) == hipSuccess ? BKV_OK
+    return launch_decode_approx(*L, *c, q, len, sigma, w, chunk, idx, k, false, true, nullptr, nullptr, s) == hipSuccess ? BKV_OK
                                                                                                : BKV_E_HIP;
-  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, true, s) != hipSuccess) return BKV_E_HIP;
+  if (launch_decode_approx(*L, *c, q, len, sigma, w, chunk, nullptr, 0, false, true, nullptr, nullptr, s) != hipSuccess) return BKV_E_HIP;
   if (k == 0) return BKV_OK;
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
@@ -361,7 +390,7 @@ bkv_status qattn_decode_unselected(const bkv_layout* L, const bkv_cache* c, cons
   if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
   const int chunk = split_tokens(units, max_len);
   if (chunk > kSelStage) return BKV_E_UNSUPPORTED;
-  return launch_decode_approx(*L, *c, q, len, nullptr, w, chunk, const_cast<int32_t*>(idx), k, true, false,
+  return launch_decode_approx(*L, *c, q, len, nullptr, w, chunk, const_cast<int32_t*>(idx), k, true, false, nullptr, nullptr,
                               (hipStream_t)stream) == hipSuccess
              ? BKV_OK
              : BKV_E_HIP;

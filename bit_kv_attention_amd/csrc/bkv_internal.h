@@ -136,10 +136,12 @@ hipError_t launch_pack_append(const bkv_layout& L, const bkv_cache& c, const uin
 // length chunk <= kSelStage and nsplit * ksel <= kSelSlots).  skip: the
 // split states leave out the tokens of the rows of idx (ksel entries per
 // unit; chunk <= kSelStage); sigma is not written.  sigonly: only sigma (and
-// with ksel > 0 the rows); no split states.
+// with ksel > 0 the rows); no split states.  k_new/v_new (non-null, with
+// neither skip nor sigonly): first append one token per sequence at len - 1.
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                int32_t* idx, int ksel, bool skip, bool sigonly, hipStream_t s);
+                                int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
+                                const uint16_t* v_new, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
                               int32_t* idx, hipStream_t s);

@@ -39,6 +39,7 @@
 //    and V meta) and handed out through a per-wave LDS slot.  Selection scores
 //    are staged in LDS and stored every 8 steps as one coalesced store.
 #include "bkv_internal.h"
+#include "quant_lane.h"
 #include "select_lds.h"
 
 namespace bkv {
@@ -361,13 +362,18 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // of its split in an LDS bitmap first); no selection score is stored.
 // SIGONLY: only the selection scores (and SEL's selection): no values are
 // read and no split state is written.
-template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false>
+// APPEND: first quantise and store the new token of each sequence at
+// position len - 1 (what kv_pack_append does for one token): the workgroup
+// whose split holds that position does it before its scan reads the cache.
+// (The cache pointers carry no __restrict__: this launch writes through them.)
+template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false, bool APPEND = false>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
-    const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
-    const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
+    const uint8_t* k_codes, const uint8_t* v_codes, const uint32_t* k_meta, const uint32_t* v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
-    uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel, int mshift) {
+    uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel, int mshift,
+    uint16_t* k_shadow, uint16_t* v_shadow, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -403,6 +409,52 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
       s_qsum[hh][g] = s;
     }
     __syncthreads();
+  }
+  if constexpr (APPEND) {
+    const int p = len - 1;  // the new token
+    if (p >= t_begin && p < t_end) {  // (the same in the whole workgroup)
+      __shared__ uint8_t s_newv[kHeadDim];  // its value codes
+      if (tid < 32) {  // 16 lanes for K, 16 for V, four per quarter
+        const int sub = tid & 3, grp = (tid >> 2) & 3, kv = (tid >> 4) & 1;
+        const int c0 = grp * kGroup + sub * 8;
+        const uint4 w4 = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + (size_t)u * kHeadDim + c0);
+        float x[8];
+        halves8(w4, x);
+        uint32_t code[8];
+        const uint32_t mw = quantise_lane(x, sub, grp, mshift, (float)((1 << (kv ? VB : KB)) - 1), code);
+        if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
+          const_cast<uint32_t*>(kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + p] =
+              mw;
+        *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + p) * kHeadDim + c0) = w4;
+        if (kv == 0) {
+          store_key_codes<KB>(const_cast<uint8_t*>(k_codes) + (size_t)u * k_unit_bytes(KB, cap), p, sub, grp, code);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s_newv[c0 + j] = (uint8_t)code[j];
+        }
+      }
+      __syncthreads();
+      // its slot in the value tile: token r is in quarter qq = (r mod 16)/4 at
+      // slot j; lanes 16qq..16qq+15 hold it, each in 2*VB dwords of 4/VB columns
+      constexpr int kCpd = 4 / VB;
+      const int r = p % kTile, qq = (r & 15) >> 2, j = 4 * (r >> 4) + (r & 3);
+      if (tid < 32 * VB) {
+        const int l = 16 * qq + (tid & 15), d = tid >> 4;
+        uint32_t* vt = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(v_codes) + (size_t)u * v_unit_bytes(VB, cap) +
+                                                   (size_t)(p / kTile) * v_tile_bytes(VB));
+        const int dw = 256 * (d >> 2) + 4 * l + (d & 3);
+        uint32_t word = vt[dw];
+#pragma unroll
+        for (int sb = 0; sb < kCpd; ++sb) {
+          const int c = 16 * (d * kCpd + sb) + (l & 15);
+          const int bit = 16 * (j >> 2) + 4 * VB * sb + VB * (j & 3);
+          const uint32_t m = ((1u << VB) - 1) << bit;
+          word = (word & ~m) | ((uint32_t)s_newv[c] << bit);
+        }
+        vt[dw] = word;
+      }
+      __syncthreads();  // (its stores are visible to the workgroup's loads below)
+    }
   }
   // SKIP: bit t - t_begin marks a listed token of the split
   __shared__ uint32_t s_skip[SKIP ? kSelStage / 32 : 1];
@@ -656,59 +708,68 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
 template <int KB, int VB, int G>
 hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                     float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, bool sigonly,
-                    hipStream_t s) {
+                    const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
   dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
   const int mshift = L.group == 64 ? 1 : 0;
   const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(c.v_codes);
   (void)hipGetLastError();  // report only this launch's status
-  if (sigonly && ksel > 0)
+  if (k_new && ksel > 0)
+    decode_approx_kernel<KB, VB, G, true, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
+  else if (k_new)
+    decode_approx_kernel<KB, VB, G, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
+  else if (sigonly && ksel > 0)
     decode_approx_kernel<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift);
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (sigonly)
     decode_approx_kernel<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (skip)
     decode_approx_kernel<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (ksel > 0)
     decode_approx_kernel<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift);
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else
     decode_approx_kernel<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
 template <int KB, int VB>
 hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                     float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, bool skip, bool sigonly,
-                    hipStream_t s) {
+                    const uint16_t* k_new, const uint16_t* v_new, hipStream_t s) {
   const int G = L.n_q_heads / L.n_kv_heads;
-  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
-  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+  if (G == 4) return launch_t<KB, VB, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+  return launch_t<KB, VB, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
-                                int32_t* idx, int ksel, bool skip, bool sigonly, hipStream_t s) {
+                                int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
+                                const uint16_t* v_new, hipStream_t s) {
   const bool v4 = L.v_bits == 4;
   switch (L.k_bits) {
-    case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
-                      : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
-    case 3: return v4 ? launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
-                      : launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
-    case 2: return v4 ? launch_g<2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
-                      : launch_g<2, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
-    default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s)
-                       : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, s);
+    case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
+                      : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+    case 3: return v4 ? launch_g<3, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
+                      : launch_g<3, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+    case 2: return v4 ? launch_g<2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
+                      : launch_g<2, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+    default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
+                       : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
   }
 }
 

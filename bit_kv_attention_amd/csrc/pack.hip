@@ -1,24 +1,17 @@
-// pack.hip -- quantise and store appended tokens.
+// pack.hip -- quantise and store appended tokens (the quantiser itself, and
+// why it is bit-exact, is in quant_lane.h): the codes go into the packed
+// layouts, (s, z) into the meta planes and the fp16 row verbatim into the
+// shadow.
 //
-// Per token, per K/V, per group of 32 channels (the asymmetric per-group
-// quantiser of the HACK review on Pith, Eq. (4): zero point = group minimum,
-// step = range / (2^b - 1); fp16 zero point and scale as in the TailorKV
-// review's free-parameter list):
-//   z = min x,  s = fp16((max - min) / (2^b - 1))   [fp32 subtract, IEEE divide]
-//   code = clamp(rint((x - z) / s), 0, 2^b - 1)     [stored fp16 s and z; 0 if s == 0]
-// then the codes go into the packed layouts, (s, z) into the meta planes and
-// the fp16 row verbatim into the shadow.
-//
-// One workgroup per (32-token tile, unit).  Four lanes share one group of
-// one token (8 channels each): partial min/max per lane, merged across the
-// four lanes with ties resolved toward the lower channels, so the result --
-// including the sign of a zero minimum -- is that of one sequential pass in
-// channel order.  A lane's 8 key codes are exactly one group's share of one
-// key chunk (4*KB bytes: its eighth of each of the 4 groups), so keys go
-// straight to HBM.  Value dwords mix 8 tokens and are rebuilt from codes in
-// LDS with a read-modify-write (slots of tokens outside the append keep
-// their bits); their loads are issued before the quantiser runs.
+// One workgroup per (32-token tile, unit); 32 lanes per token (16 for K, 16
+// for V, four per 32-channel quarter).  A lane's 8 key codes are exactly one
+// quarter's share of one key chunk (4*KB bytes: its eighth of each of the 4
+// quarters), so keys go straight to HBM.  Value dwords mix 8 tokens and are
+// rebuilt from codes in LDS with a read-modify-write (slots of tokens outside
+// the append keep their bits); their loads are issued before the quantiser
+// runs.
 #include "bkv_internal.h"
+#include "quant_lane.h"
 
 // The codec must match a plain IEEE evaluation operation for operation.
 #pragma clang fp contract(off)
@@ -62,63 +55,15 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     if (t < t_lo || t >= t_hi) continue;
     const uint16_t* src = (kv ? v_new : k_new) + ((size_t)u * n_new + (t - p0)) * kHeadDim + c0;
     const uint4 w4 = *reinterpret_cast<const uint4*>(src);
-    const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
     float x[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] & 0xFFFFu));
-      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] >> 16));
-    }
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (x[j] < mn) mn = x[j];
-      if (x[j] > mx) mx = x[j];
-    }
-    // merge with the neighbouring lanes of the quad (tid ^ 1, then tid ^ 2, by
-    // DPP), lower channels first on ties
-    auto merge = [&](float omn, float omx, bool hi) {  // hi: the partner holds the lower channels
-      const float lmn = hi ? omn : mn, umn = hi ? mn : omn;
-      const float lmx = hi ? omx : mx, umx = hi ? mx : omx;
-      mn = (umn < lmn) ? umn : lmn;
-      mx = (umx > lmx) ? umx : lmx;
-    };
-    merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, true)),
-          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)), (sub & 1) != 0);
-    merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)),
-          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)), (sub & 2) != 0);
-    if (mshift)  // group 64: the quarter pair's lanes (tid ^ 4) hold the group's other half
-      merge(__shfl_xor(mn, 4), __shfl_xor(mx, 4), (grp & 1) != 0);
-    const _Float16 s16 = (_Float16)((mx - mn) / qmax);
-    const _Float16 z16 = (_Float16)mn;
-    const float s = (float)s16, z = (float)z16;
+    halves8(w4, x);
     uint32_t code[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int cd = 0;
-      if (s != 0.0f) {
-        const float rr = __builtin_rintf((x[j] - z) / s);
-        cd = rr < 0.0f ? 0 : (rr > qmax ? (int)qmax : (int)rr);
-      }
-      code[j] = (uint32_t)cd;
-    }
+    const uint32_t meta = quantise_lane(x, sub, grp, mshift, qmax, code);
     if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
-      (kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + t] =
-          (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+      (kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + t] = meta;
     *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + c0) = w4;
     if (kv == 0) {
-      // chunk (eighth sub) of token t: codes (g, j) at bit KB(8g + j), so this
-      // group's 8 codes fill bytes KB*grp .. KB*grp + KB - 1
-      uint32_t f = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f |= code[j] << (KB * j);
-      uint8_t* chunk = k_codes + (size_t)u * k_unit_bytes(KB, cap) + k_chunk_offset(KB, t, sub) + KB * grp;
-      if (KB == 4) {
-        *reinterpret_cast<uint32_t*>(chunk) = f;
-      } else {
-#pragma unroll
-        for (int i = 0; i < KB; ++i) chunk[i] = (uint8_t)(f >> (8 * i));
-      }
+      store_key_codes<KB>(k_codes + (size_t)u * k_unit_bytes(KB, cap), t, sub, grp, code);
     } else {
       uint2 cw;
       cw.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);

@@ -1,0 +1,90 @@
+// quant_lane.h -- the per-group quantiser of appended tokens, shared by the
+// append kernel and the scan's in-launch append (both must produce the same
+// bits).
+//
+// Per token, per K/V, per group (the asymmetric per-group quantiser of the
+// HACK review on Pith, Eq. (4): zero point = group minimum, step = range /
+// (2^b - 1); fp16 zero point and scale as in the TailorKV review's
+// free-parameter list):
+//   z = min x,  s = fp16((max - min) / (2^b - 1))   [fp32 subtract, IEEE divide]
+//   code = clamp(rint((x - z) / s), 0, 2^b - 1)     [stored fp16 s and z; 0 if s == 0]
+//
+// Four lanes share one 32-channel quarter of a row (8 channels each; lane
+// sub = l & 3, quarter grp = (l >> 2) & 3 of a 16-lane set): partial min/max
+// per lane, merged across the four lanes (and, for groups of 64, with the
+// quarter pair's lanes l ^ 4) with ties resolved toward the lower channels,
+// so the result -- including the sign of a zero minimum -- is that of one
+// sequential pass in channel order.  Every lane of the set must be active.
+#pragma once
+
+#include "bkv_internal.h"
+
+namespace bkv {
+
+// x: this lane's 8 values; returns the group's meta word (fp16 scale low,
+// fp16 zero high) and the lane's 8 codes.
+__device__ inline uint32_t quantise_lane(const float (&x)[8], int sub, int grp, int mshift, float qmax,
+                                         uint32_t (&code)[8]) {
+#pragma clang fp contract(off)
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (x[j] < mn) mn = x[j];
+    if (x[j] > mx) mx = x[j];
+  }
+  auto merge = [&](float omn, float omx, bool hi) {  // hi: the partner holds the lower channels
+    const float lmn = hi ? omn : mn, umn = hi ? mn : omn;
+    const float lmx = hi ? omx : mx, umx = hi ? mx : omx;
+    mn = (umn < lmn) ? umn : lmn;
+    mx = (umx > lmx) ? umx : lmx;
+  };
+  merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0xB1, 0xF, 0xF, true)),
+        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0xB1, 0xF, 0xF, true)), (sub & 1) != 0);
+  merge(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mn), 0x4E, 0xF, 0xF, true)),
+        __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(mx), 0x4E, 0xF, 0xF, true)), (sub & 2) != 0);
+  if (mshift)  // group 64: the quarter pair's lanes (l ^ 4) hold the group's other half
+    merge(__shfl_xor(mn, 4), __shfl_xor(mx, 4), (grp & 1) != 0);
+  const _Float16 s16 = (_Float16)((mx - mn) / qmax);
+  const _Float16 z16 = (_Float16)mn;
+  const float s = (float)s16, z = (float)z16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int cd = 0;
+    if (s != 0.0f) {
+      const float rr = __builtin_rintf((x[j] - z) / s);
+      cd = rr < 0.0f ? 0 : (rr > qmax ? (int)qmax : (int)rr);
+    }
+    code[j] = (uint32_t)cd;
+  }
+  return (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
+}
+
+// The 8 fp16 values of a 16-byte piece as floats (exact).
+__device__ inline void halves8(const uint4& w4, float (&x)[8]) {
+  const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] & 0xFFFFu));
+    x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(ww[j] >> 16));
+  }
+}
+
+// The 8 codes of a lane into its key chunk: chunk (eighth sub) of token t
+// holds codes (g, j) at bit KB(8g + j), so quarter grp's 8 codes fill bytes
+// KB*grp .. KB*grp + KB - 1.
+template <int KB>
+__device__ inline void store_key_codes(uint8_t* __restrict__ unit_codes, int t, int sub, int grp,
+                                       const uint32_t (&code)[8]) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f |= code[j] << (KB * j);
+  uint8_t* chunk = unit_codes + k_chunk_offset(KB, t, sub) + KB * grp;
+  if (KB == 4) {
+    *reinterpret_cast<uint32_t*>(chunk) = f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < KB; ++i) chunk[i] = (uint8_t)(f >> (8 * i));
+  }
+}
+
+}  // namespace bkv

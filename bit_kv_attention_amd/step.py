@@ -107,7 +107,15 @@ class DecodeStep:
         return self.out
 
     def step(self, cache: bk.Cache, q, k_new, v_new, pos, stream=None):
-        """Append one token per sequence at pos[b], then attend over pos[b] + 1 tokens."""
-        bk.kv_pack_append(self.layout, cache, k_new, v_new, 1, pos, stream)
+        """Append one token per sequence at pos[b], then attend over pos[b] + 1
+        tokens.  The plain top-k step appends inside the scan's launch
+        (qattn_decode_step)."""
         lens = [int(p) + 1 for p in pos]
+        if self.fused and not self.exclude and self.block == 0 and self.window == 0 and min(lens) >= 1:
+            bk.qattn_decode_step(self.layout, cache, k_new, v_new, q, lens, self.k, self.sigma, self.idx, self.ws,
+                                 stream, self.select_mode)
+            bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.ws,
+                             self.out, stream)
+            return self.out
+        bk.kv_pack_append(self.layout, cache, k_new, v_new, 1, pos, stream)
         return self.attend(cache, q, lens, stream)

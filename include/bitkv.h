@@ -16,6 +16,7 @@
  *   kv_pack_append       quantise + pack the new token(s), write the shadow
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
  *   qattn_decode_select  the same and topk_select, in one launch where it fits
+ *   qattn_decode_step    kv_pack_append of one token + qattn_decode_select, one launch
  *   topk_select          top-k tokens per KV head by the selection score
  *   topk_select_window   the same, plus the newest tokens always selected
  *   topk_select_blocks   or whole blocks of tokens by their best score
@@ -192,6 +193,23 @@ bkv_status qattn_decode_select(const bkv_layout* layout, const bkv_cache* cache,
                                const uint16_t* q, const int32_t* len_host,
                                int32_t k, float* sigma, int32_t* idx, void* ws,
                                size_t ws_bytes, int32_t mode, void* stream);
+
+/*
+ * qattn_decode_step -- kv_pack_append of one token per sequence at position
+ * len_host[b] - 1 (k_new, v_new [B][Hkv][D] fp16, device) followed by
+ * qattn_decode_select over len_host[b] tokens, in the scan's launch: the scan
+ * workgroup whose token range holds that position quantises and stores the
+ * token (codes, meta, shadow row; the same bits kv_pack_append writes)
+ * before it reads the cache.  Results identical to the two calls; mode as in
+ * qattn_decode_select.
+ * Errors: BKV_E_CAPACITY if some len_host[b] < 1 or > capacity; otherwise as
+ * qattn_decode_select.
+ */
+bkv_status qattn_decode_step(const bkv_layout* layout, const bkv_cache* cache,
+                             const uint16_t* k_new, const uint16_t* v_new,
+                             const uint16_t* q, const int32_t* len_host, int32_t k,
+                             float* sigma, int32_t* idx, void* ws, size_t ws_bytes,
+                             int32_t mode, void* stream);
 
 /* Host only: *in_scan = 1 if qattn_decode_select with this layout, longest
  * length max_len, k and mode selects inside the scan's launch, else 0. */

@@ -584,3 +584,46 @@ def test_score_select_equals_decode_select(P, kb, vb, G, g):
             for bb in range(w.B):
                 assert np.array_equal(sa[bb, :, :lens[bb]], sb[bb, :, :lens[bb]]), (k, mode)
             assert torch.equal(a.idx, b.idx), (k, mode)
+
+
+@pytest.mark.parametrize("kb,vb,G,g", [(4, 4, 4, 32), (3, 2, 8, 32), (4, 2, 8, 64), (2, 2, 4, 64), (1, 4, 8, 32)])
+def test_decode_step_equals_append_then_select(P, kb, vb, G, g):
+    """qattn_decode_step (the append inside the scan's launch) against
+    kv_pack_append + qattn_decode_select on two copies of one cache: the
+    cache bytes after the step are equal, and so are sigma, the rows and the
+    corrected output; the new tokens sit at a split start, a tile start, the
+    middle of a tile and slot 0; both selection modes; three steps in a row."""
+    banner(f"decode_step kb={kb} vb={vb} G={G} g={g}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("dstep", 4, 2 * G, 2, 128, 3000, kb, vb, g, 32, 6, 1700 + 10 * kb + G + g)
+    inp = P.make_inputs(w, L=2900)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, 3008, kb, vb, group=g)
+    caches = [bk.allocate_cache(lay) for _ in range(2)]
+    pre = [2048, 1535, 1000, 0]  # tokens already in the cache per sequence
+    for c in caches:
+        bk.kv_pack_append(lay, c, P.to_dev(inp.K), P.to_dev(inp.V), 2900, [0] * w.B)
+    knew, vnew = P.make_new_tokens(w, 3, inp.outlier_ch)
+    q = P.to_dev(inp.q)
+    for mode in (1, 2):
+        steps = [DecodeStep(lay, w.k, 3008, select_mode=mode) for _ in range(2)]
+        for i in range(3):
+            lens = [p + 1 + i for p in pre]
+            kn, vn = P.to_dev(knew[i]), P.to_dev(vnew[i])
+            bk.qattn_decode_step(lay, caches[0], kn, vn, q, lens, w.k, steps[0].sigma, steps[0].idx, steps[0].ws,
+                                 mode=mode)
+            bk.kv_pack_append(lay, caches[1], kn, vn, 1, [n - 1 for n in lens])
+            bk.qattn_decode_select(lay, caches[1], q, lens, w.k, steps[1].sigma, steps[1].idx, steps[1].ws, mode=mode)
+            for st, c in zip(steps, caches):
+                bk.qattn_correct(lay, c, q, lens, st.idx, w.k, st.ws, st.out)
+            torch.cuda.synchronize()
+            ga, gb = P.gpu_buffers(caches[0]), P.gpu_buffers(caches[1])
+            for name in ga:
+                assert np.array_equal(ga[name], gb[name]), (mode, i, name)
+            sa = steps[0].sigma.cpu().numpy().reshape(w.B, w.Hkv, -1)
+            sb = steps[1].sigma.cpu().numpy().reshape(w.B, w.Hkv, -1)
+            for b in range(w.B):
+                assert np.array_equal(sa[b, :, :lens[b]], sb[b, :, :lens[b]]), (mode, i, b)
+            assert torch.equal(steps[0].idx, steps[1].idx), (mode, i)
+            assert torch.equal(steps[0].out, steps[1].out), (mode, i)
