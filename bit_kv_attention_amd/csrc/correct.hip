@@ -79,20 +79,27 @@ struct RecBatch {
   }
 };
 
-// One workgroup per (b, query head), one thread per channel.  hx (may be
+// One workgroup per (b, query head): kCombineGroups groups of one thread per
+// channel take the record batches in turn (so long record lists are read in
+// parallel), then the first group merges the groups' states.  hx (may be
 // null): the exact state of the selected tokens per (b, query head),
 // {m, l, a[0..D)}, in place of the chunk records' exact parts.
-__global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
+// (One group when every list fits one batch: no barrier, no LDS.)
+template <int kCombineGroups>
+__global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                            const float* __restrict__ pacc, const float* __restrict__ cs,
                                                            const float* __restrict__ hx, float* __restrict__ out,
                                                            SeqArg lens, int Hq, int nsplit, int nchunk, int k,
                                                            int rest) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x & (kHeadDim - 1);
+  // the group is the same in a whole wave: kept scalar, so the record loop and
+  // the loads of each record's max and denominator stay scalar too
+  const int grp = (kCombineGroups > 1) ? __builtin_amdgcn_readfirstlane(threadIdx.x / kHeadDim) : 0;
   const int n = lens.v[b];
   const size_t rec = (size_t)b * Hq + h;
   float* o = out + rec * kHeadDim;
   if (n == 0) {
-    o[c] = 0.f;
+    if (grp == 0) o[c] = 0.f;
     return;
   }
   const int kk = min(k, n);
@@ -105,11 +112,11 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
   const int nsel = (kk < n && !rest) ? nc : 0;  // rest: the split states already leave S out
   Online ex, ap, sel;
   const int nex = hx ? 0 : nc;  // exact records from the chunks
-  if (hx) {
+  if (hx && grp == 0) {
     const float* x = hx + rec * kStateFloats;
     ex.add(x[0], x[1], x[2 + c]);
   }
-  for (int j0 = 0; j0 < max(nc, nap); j0 += kRecBatch) {
+  for (int j0 = grp * kRecBatch; j0 < max(nc, nap); j0 += kCombineGroups * kRecBatch) {
     RecBatch be, ba, bs;
     be.load(ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nex, j0);
     ba.load(pm + rec * nsplit, pl + rec * nsplit, pacc + rec * nsplit * kHeadDim + c, 1, kHeadDim, nap, j0);
@@ -117,6 +124,24 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(const float* __restri
     be.into(ex);
     ba.into(ap);
     bs.into(sel);
+  }
+  if constexpr (kCombineGroups > 1) {
+  // the other groups' states to the first group
+  __shared__ float s_st[kCombineGroups - 1][3][3][kHeadDim];  // [group - 1][ex/ap/sel][m/l/a][c]
+  if (grp > 0) {
+    float* d = &s_st[grp - 1][0][0][c];
+    d[0 * kHeadDim] = ex.m, d[1 * kHeadDim] = ex.l, d[2 * kHeadDim] = ex.a;
+    d[3 * kHeadDim] = ap.m, d[4 * kHeadDim] = ap.l, d[5 * kHeadDim] = ap.a;
+    d[6 * kHeadDim] = sel.m, d[7 * kHeadDim] = sel.l, d[8 * kHeadDim] = sel.a;
+  }
+  __syncthreads();
+  if (grp > 0) return;
+#pragma unroll
+  for (int g = 0; g < kCombineGroups - 1; ++g) {
+    ex.add(s_st[g][0][0][c], s_st[g][0][1][c], s_st[g][0][2][c]);
+    ap.add(s_st[g][1][0][c], s_st[g][1][1][c], s_st[g][1][2][c]);
+    sel.add(s_st[g][2][0][c], s_st[g][2][1][c], s_st[g][2][2][c]);
+  }
   }
   if (kk == n) {
     o[c] = ex.a / ex.l;
@@ -413,9 +438,14 @@ hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_
       default: v4 ? launch_g<1, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<1, 2>(L, c, q, len, idx, k, w, t, s);
     }
   }
-  combine_kernel<<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
-                                                                 len, L.n_q_heads, w.nsplit, w.nchunk, k,
-                                                                 rest ? 1 : 0);
+  if (w.nchunk <= kRecBatch && w.nsplit <= kRecBatch)  // every record list fits one batch
+    combine_kernel<1><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
+                                                                     len, L.n_q_heads, w.nsplit, w.nchunk, k,
+                                                                     rest ? 1 : 0);
+  else
+    combine_kernel<4><<<dim3(L.n_q_heads, L.batch), kHeadDim * 4, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx,
+                                                                         out, len, L.n_q_heads, w.nsplit, w.nchunk,
+                                                                         k, rest ? 1 : 0);
   return hipGetLastError();
 }
 
