@@ -152,7 +152,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
 
     def select():
         if NB > 0:
-            bk.topk_select_blocks(lay, st.sigma, lens, NB, args.block, st.idx)
+            bk.topk_select_blocks(lay, st.sigma, lens, NB, args.block, st.idx, st.ws)
         elif W > 0:
             bk.topk_select_window(lay, st.sigma, lens, w.k, W, st.idx, st.ws)
         else:

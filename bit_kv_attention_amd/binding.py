@@ -63,7 +63,7 @@ _lib.qattn_decode_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.
 _lib.qattn_decode_step.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
 _lib.bkv_select_in_scan.argtypes = [_LP, C.c_int32, C.c_int32, C.c_int32, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
-_lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P]
+_lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 _lib.qattn_score_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
 _lib.qattn_decode_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P]
@@ -214,10 +214,12 @@ def topk_select_window(layout: Layout, sigma, len_host, k: int, window: int, idx
                                                          _stream(stream)))
 
 
-def topk_select_blocks(layout: Layout, sigma, len_host, n_blocks: int, block: int, idx, stream=None) -> None:
+def topk_select_blocks(layout: Layout, sigma, len_host, n_blocks: int, block: int, idx, ws, stream=None) -> None:
     lens = _host_i32(len_host)
+    ws_bytes = ws.numel() * ws.element_size()
     _check("topk_select_blocks", _lib.topk_select_blocks(C.byref(layout), _ptr(sigma), lens.ctypes.data,
-                                                         int(n_blocks), int(block), _ptr(idx), _stream(stream)))
+                                                         int(n_blocks), int(block), _ptr(idx), _ptr(ws), ws_bytes,
+                                                         _stream(stream)))
 
 
 def qattn_correct(layout: Layout, cache: Cache, q, len_host, idx, k: int, ws, out, stream=None) -> None:

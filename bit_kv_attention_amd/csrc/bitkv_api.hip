@@ -89,6 +89,9 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
     slots = fs > slots ? fs : slots;
   }
   w.tkc = reinterpret_cast<uint64_t*>(take((size_t)units * slots * 8));
+  // block selection: one key per block of at least 32 tokens
+  w.bkstride = (max_len + 31) / 32;
+  w.bkeys = reinterpret_cast<uint32_t*>(take((size_t)units * w.bkstride * 4));
   w.bytes = off;
   return w;
 }
@@ -286,22 +289,27 @@ bkv_status topk_select_window(const bkv_layout* L, const float* sigma, const int
 }
 
 bkv_status topk_select_blocks(const bkv_layout* L, const float* sigma, const int32_t* len_host,
-                              int32_t n_blocks, int32_t block, int32_t* idx, void* stream) {
+                              int32_t n_blocks, int32_t block, int32_t* idx, void* ws, size_t ws_bytes,
+                              void* stream) {
   bkv_status st = check_layout(L);
   if (st != BKV_OK) return st;
   if (n_blocks < 0 || block < 32 || block > 1024 || (block & (block - 1)) != 0 ||
       (long long)n_blocks * block > 0x7FFFFFFF)
     return BKV_E_ARG;
   if ((L->capacity + block - 1) / block > kTopkBlocksMax) return BKV_E_UNSUPPORTED;
-  if (!sigma || (!idx && n_blocks > 0)) return BKV_E_NULL;
+  if (!sigma || ((!idx || !ws) && n_blocks > 0)) return BKV_E_NULL;
   SeqArg len;
   int max_len = 0;
   if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
   if (n_blocks == 0) return BKV_OK;
+  const Workspace w = workspace_layout(ws, *L, max_len, n_blocks * block, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
   int lgb = 0;
   while ((1 << lgb) < block) ++lgb;
-  return launch_topk_blocks(*L, sigma, len, n_blocks, lgb, idx, (hipStream_t)stream) == hipSuccess ? BKV_OK
-                                                                                                 : BKV_E_HIP;
+  return launch_topk_blocks(*L, sigma, len, max_len, n_blocks, lgb, idx, w.bkeys, w.bkstride, w.tkctr,
+                            (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
 }
 
 bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,

@@ -103,6 +103,7 @@ constexpr int kTopkSliceMin = 2048;
 constexpr int kTopkGridMin = 256;
 constexpr int kTopkMergeMax = 16384;
 constexpr int kTopkBlocksMax = 8192;  // blocks per unit for block selection (ceil(capacity / block))
+constexpr int kTopkBlockSpan = 8192;  // tokens per workgroup of the block maxima
 // Top-k inside the approximate scan: a split's scores staged in LDS, and the
 // unit's candidate slots (nsplit * k) merged in LDS.
 constexpr int kSelStage = 16384;
@@ -114,6 +115,8 @@ struct Workspace {
   Partials part;
   float* cs;  // [B][Hq][nchunk][kCsStride]
   uint64_t* tkc;  // [U][top-k candidate slots] (composite keys)
+  uint32_t* bkeys;  // [U][bkstride] block-selection keys
+  int bkstride;
   uint32_t* tkctr;  // [U] arrivals of the top-k slice workgroups (zero between calls)
   int nsplit;
   int nchunk;
@@ -143,8 +146,9 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
-hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
-                              int32_t* idx, hipStream_t s);
+// bkeys: kstride block keys per unit; counter: one arrival counter per unit.
+hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int nb,
+                              int lgb, int32_t* idx, uint32_t* bkeys, int kstride, uint32_t* counter, hipStream_t s);
 // Rows of k + W entries per unit (W: the recent window, 0 for none).
 hipError_t launch_topk(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int k, int W,
                        int32_t* idx, uint64_t* cand, uint32_t* counter, hipStream_t s);

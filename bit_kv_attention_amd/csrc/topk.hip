@@ -322,29 +322,41 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
 }
 
 // ---- block selection -----------------------------------------------------
-// One workgroup per unit.  Block j holds tokens [j*bs, min(n, j*bs + bs)) and
-// scores the largest sigma among them (Jet-QSparse abstract: the dense scan's
-// scores choose whole 128-token blocks per KV head).  The block maxima come
-// from coalesced 16-byte loads (a wave covers 256 contiguous tokens per load,
-// bs/4 lanes per block reduce by butterfly shuffles; a block longer than 256
-// tokens takes several loads of one wave) into LDS; the select finds the
-// kb-th largest (score, block) composite as the token top-k does; the chosen
-// blocks are ranked in ascending order and the row is written as their
-// tokens, block r at [r*bs, r*bs + bs), -1 past n.
+// Block j holds tokens [j*bs, min(n, j*bs + bs)) and scores the largest sigma
+// among them (Jet-QSparse abstract: the dense scan's scores choose whole
+// 128-token blocks per KV head).  Workgroup (slice s, unit) reads the scores
+// of tokens [s*kBlkSpan, s*kBlkSpan + kBlkSpan) with coalesced 16-byte loads
+// (a wave covers 256 contiguous tokens per load, bs/4 lanes per block reduce
+// by butterfly shuffles; a block longer than 256 tokens takes several loads
+// of one wave) and stores its blocks' keys with agent-scope stores; the
+// unit's last workgroup to arrive loads all nblk keys into LDS, finds the
+// kb-th largest (score, block) composite as the token top-k does, ranks the
+// chosen blocks in ascending order and writes the row as their tokens, block
+// r at [r*bs, r*bs + bs), -1 past n.
 constexpr int kBlkMax = kTopkBlocksMax;
 constexpr int kBlkPer = kBlkMax / kThreads;
 constexpr int kBlkBatch = 4;  // spans per wave with loads in flight together
+constexpr int kBlkSpan = kTopkBlockSpan;  // tokens per workgroup (a multiple of every block size)
+
+__device__ inline void st_dev32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t ld_dev32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __restrict__ sigma,
                                                                int32_t* __restrict__ idx, SeqArg lens, int Hkv,
-                                                               int cap, int nb, int lgb) {
+                                                               int cap, int nb, int lgb, uint32_t* __restrict__ bkeys,
+                                                               int kstride, uint32_t* __restrict__ counter) {
   __shared__ uint32_t s_bkey[kBlkMax];  // float_key of each block's largest score; then the chosen blocks
   __shared__ uint32_t s_hist[kHistBins];
   __shared__ int s_wsum[kWaves];
   __shared__ int s_res[4];
+  __shared__ int s_last;
   __shared__ float s_mm[2 * kWaves];
   __shared__ uint64_t s_small[65];
-  const int u = blockIdx.x;
+  const int sl = blockIdx.x, u = blockIdx.y;
   const int n = lens.v[u / Hkv];
   const int bs = 1 << lgb;
   const int nblk = (n + bs - 1) >> lgb;
@@ -352,17 +364,20 @@ __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __re
   const int row = nb << lgb;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t* __restrict__ out = idx + (size_t)u * row;
-  if (kb == nblk) {  // every block (or none): the tokens in order
-    for (int i = tid; i < row; i += kThreads) out[i] = (i < n) ? i : -1;
+  if (kb == nblk) {  // every block (or none): the tokens in order, by the first slice; nothing arrives
+    if (sl == 0)
+      for (int i = tid; i < row; i += kThreads) out[i] = (i < n) ? i : -1;
     return;
   }
 
-  // block maxima: wave wv takes spans of max(bs, 256) tokens
+  // block maxima of this slice: wave wv takes spans of max(bs, 256) tokens
+  uint32_t* __restrict__ ukeys = bkeys + (size_t)u * kstride;
   const float* __restrict__ sg = sigma + (size_t)u * cap;
   const int span = bs > 256 ? bs : 256;
-  const int nspan = (n + span - 1) / span;
+  const int sp_lo = sl * (kBlkSpan / span);
+  const int sp_hi = min((n + span - 1) / span, sp_lo + kBlkSpan / span);
   const int G = (bs < 256 ? bs : 256) / 4;  // lanes per block in one load
-  for (int s0 = wv; s0 < nspan; s0 += kBlkBatch * kWaves) {
+  for (int s0 = sp_lo + wv; s0 < sp_hi; s0 += kBlkBatch * kWaves) {
     float m[kBlkBatch];
 #pragma unroll
     for (int i = 0; i < kBlkBatch; ++i) m[i] = -INFINITY;
@@ -376,8 +391,9 @@ __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __re
 #pragma unroll
       for (int i = 0; i < kBlkBatch; ++i) {
         const int t = (s0 + i * kWaves) * span + c + 4 * lane;
-        const float a = fmaxf(t < n ? x[i].x : -INFINITY, t + 1 < n ? x[i].y : -INFINITY);
-        const float b = fmaxf(t + 2 < n ? x[i].z : -INFINITY, t + 3 < n ? x[i].w : -INFINITY);
+        const bool in = s0 + i * kWaves < sp_hi;
+        const float a = fmaxf(in && t < n ? x[i].x : -INFINITY, in && t + 1 < n ? x[i].y : -INFINITY);
+        const float b = fmaxf(in && t + 2 < n ? x[i].z : -INFINITY, in && t + 3 < n ? x[i].w : -INFINITY);
         m[i] = fmaxf(m[i], fmaxf(a, b));
       }
     }
@@ -385,9 +401,17 @@ __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __re
     for (int i = 0; i < kBlkBatch; ++i) {
       for (int off = 1; off < G; off <<= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], off));
       const int j = ((s0 + i * kWaves) * span + 4 * lane) >> lgb;
-      if ((lane & (G - 1)) == 0 && j < nblk) s_bkey[j] = float_key(m[i]);
+      if ((lane & (G - 1)) == 0 && s0 + i * kWaves < sp_hi && j < nblk) st_dev32(&ukeys[j], float_key(m[i]));
     }
   }
+
+  // ---- arrival; the unit's last workgroup selects --------------------------------
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's keys are written
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  for (int j = tid; j < nblk; j += kThreads) s_bkey[j] = ld_dev32(&ukeys[j]);
   __syncthreads();
 
   // the kb best blocks: entry j = i*kThreads + tid
@@ -414,15 +438,18 @@ __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __re
     const int t = (int)s_bkey[i >> lgb] * bs + (i & (bs - 1));  // i >> lgb < kb = nb here
     out[i] = (t < n) ? t : -1;
   }
+  if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
 }
 
 }  // namespace
 
-hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int nb, int lgb,
-                              int32_t* idx, hipStream_t s) {
+hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int nb,
+                              int lgb, int32_t* idx, uint32_t* bkeys, int kstride, uint32_t* counter, hipStream_t s) {
   const int units = L.batch * L.n_kv_heads;
+  const int ns = (max_len + kBlkSpan - 1) / kBlkSpan;
   (void)hipGetLastError();  // report only this call's launch
-  topk_blocks_kernel<<<units, kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, nb, lgb);
+  topk_blocks_kernel<<<dim3(ns > 0 ? ns : 1, units), kThreads, 0, s>>>(sigma, idx, len, L.n_kv_heads, L.capacity, nb,
+                                                                       lgb, bkeys, kstride, counter);
   return hipGetLastError();
 }
 

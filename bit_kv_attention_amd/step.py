@@ -53,7 +53,7 @@ class DecodeStep:
         bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
         if self.block > 0:
             if self.k > 0:
-                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, stream)
+                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, self.ws, stream)
         elif self.window > 0:
             bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
         elif self.k > 0:
@@ -66,7 +66,7 @@ class DecodeStep:
         if self.block > 0:
             bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
             if self.k > 0:
-                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, stream)
+                bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, self.ws, stream)
         elif self.window > 0:
             bk.qattn_decode_approx(self.layout, cache, q, lens, self.sigma, self.ws, stream)
             bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)

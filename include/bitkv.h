@@ -125,8 +125,8 @@ bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
                            size_t* shadow_bytes_each);
 
 /* Workspace bytes that cover qattn_decode_approx, topk_select and
- * qattn_correct for every step whose longest sequence has at most max_len
- * tokens and whose top-k budget is k.  Host only.  One workspace serves the
+ * qattn_correct (and every variant below) for every step whose longest
+ * sequence has at most max_len tokens and whose row length is k.  Host only.  One workspace serves the
  * three calls of a step (the scan's split states, the top-k candidates and
  * arrival counters and the correction's chunk states live in it).  Zero-fill
  * it once after allocating it; every call leaves the counters at zero again.
@@ -258,16 +258,18 @@ bkv_status topk_select_window(const bkv_layout* layout, const float* sigma,
  * idx [B][Hkv][n_blocks * block] int32 (device): the chosen blocks in
  * ascending order, chosen block r as its tokens at idx[r*block ..
  * r*block + block) (-1 past len), then -1; qattn_correct takes it with
- * n_blocks * block as its k (size ws with bkv_workspace_bytes(layout,
- * max_len, n_blocks * block)).  Needs no workspace.  n_blocks == 0 enqueues
- * nothing.
+ * n_blocks * block as its k.  Uses the block-key region and the arrival
+ * counters of ws: size it with bkv_workspace_bytes(layout, max_len,
+ * n_blocks * block).  n_blocks == 0 enqueues nothing.
  * Errors: BKV_E_ARG unless block is a power of two in [32, 1024],
  * n_blocks >= 0 and n_blocks * block fits int32; BKV_E_UNSUPPORTED if
- * ceil(capacity / block) > 8192; BKV_E_CAPACITY for a bad length.
+ * ceil(capacity / block) > 8192; BKV_E_CAPACITY for a bad length;
+ * BKV_E_WORKSPACE if ws is too small.
  */
 bkv_status topk_select_blocks(const bkv_layout* layout, const float* sigma,
                               const int32_t* len_host, int32_t n_blocks,
-                              int32_t block, int32_t* idx, void* stream);
+                              int32_t block, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply

@@ -161,14 +161,16 @@ def test_host_error_paths(bk):
     # overflowing budget, NULL idx, bad length, the empty budget
     tb = "topk_select_blocks"
     for blk in (0, 16, 48, 2048, -128):
-        assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, blk, FAKE, None) == 7, blk
-    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), -1, 128, FAKE, None) == 7
-    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 2**24, 1024, FAKE, None) == 7
-    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, 128, None, None) == 1
-    assert bk.raw_status(tb, C.byref(lay), FAKE, P(l2), 4, 128, FAKE, None) == 4
-    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 0, 128, None, None) == 0
+        assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, blk, FAKE, FAKE, need, None) == 7, blk
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), -1, 128, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 2**24, 1024, FAKE, FAKE, need, None) == 7
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, 128, None, FAKE, need, None) == 1
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, 128, FAKE, None, need, None) == 1
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 4, 128, FAKE, FAKE, 64, None) == 5
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(l2), 4, 128, FAKE, FAKE, need, None) == 4
+    assert bk.raw_status(tb, C.byref(lay), FAKE, P(lens), 0, 128, None, None, 0, None) == 0
     big = L(bk, capacity=32 * 8192 + 32)  # 8193 blocks of 32 tokens
-    assert bk.raw_status(tb, C.byref(big), FAKE, P(lens), 4, 32, FAKE, None) == 3
+    assert bk.raw_status(tb, C.byref(big), FAKE, P(lens), 4, 32, FAKE, FAKE, need, None) == 3
 
 
 def test_status_strings(bk):

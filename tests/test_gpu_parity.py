@@ -405,9 +405,10 @@ def test_topk_blocks_on_given_scores(P, L, nb, bs, ties):
     row = nb * bs
     sigd = torch.from_numpy(sig.reshape(-1)).cuda()
     idxd = torch.empty(B * Hkv * row, dtype=torch.int32, device="cuda")
+    ws = torch.zeros((bk.bkv_workspace_bytes(lay, L, row) + 3) // 4, dtype=torch.float32, device="cuda")
     for rep in range(2):
         idxd.fill_(-7)
-        bk.topk_select_blocks(lay, sigd, lens, nb, bs, idxd)
+        bk.topk_select_blocks(lay, sigd, lens, nb, bs, idxd, ws)
         torch.cuda.synchronize()
         idx = idxd.cpu().numpy().reshape(B, Hkv, row)
         for b in range(B):
