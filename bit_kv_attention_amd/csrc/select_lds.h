@@ -1,5 +1,6 @@
 // select_lds.h -- workgroup-wide selection of the need-th largest composite
-// (score, index) key, shared by the top-k kernels.
+// (score, index) key, and the merge of per-slice candidates, shared by the
+// top-k kernels and the scan's in-launch selection.
 //
 // A token's composite key is (order-preserving bits of its score) << 32 | ~t:
 // larger means a larger score, or an equal score and a lower index, and no
@@ -317,116 +318,6 @@ __device__ __attribute__((always_inline)) inline void merge_unit(const uint64_t*
 #pragma unroll
     for (int j = 0; j < kPer; ++j)
       if (sel[j]) out[at[j]] = (int32_t)~(uint32_t)(v[j] & 0xFFFFFFFFu);
-  }
-}
-
-
-// hist_select over entries that live in LDS or are computed on the fly:
-// get(i) gives the composite of entry i for i < count (all nonzero); any
-// count.  Same steps and LDS arrays as hist_select; the radix fallback reads
-// get() directly.
-template <int NT, typename Get>
-__device__ inline uint64_t hist_select_lds(Get get, int count, int need, uint32_t* s_hist, int* s_wsum, int* s_res,
-                                           float* s_mm, uint64_t* s_small) {
-  constexpr int NW = NT / 64;
-  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = tid; i < count; i += NT) {
-    const float x = key_value((uint32_t)(get(i) >> 32));
-    lo = fminf(lo, x);
-    hi = fmaxf(hi, x);
-  }
-  lo = wave_minmax<false>(lo);
-  hi = wave_minmax<true>(hi);
-  for (int i = tid; i < kHistBins; i += NT) s_hist[i] = 0u;
-  if (lane == 0) {
-    s_mm[wv] = lo;
-    s_mm[NW + wv] = hi;
-  }
-  if (tid == 0) s_res[2] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    lo = fminf(lo, s_mm[w]);
-    hi = fmaxf(hi, s_mm[NW + w]);
-  }
-  const float scale = (float)kHistBins / (hi - lo);
-  auto bin = [&](uint64_t cc) {
-    const float f = (key_value((uint32_t)(cc >> 32)) - lo) * scale;
-    return (int)fminf(fmaxf(f, 0.0f), (float)(kHistBins - 1));
-  };
-  for (int i = tid; i < count; i += NT) atomicAdd(&s_hist[bin(get(i))], 1u);
-  __syncthreads();
-  constexpr int per = kHistBins / NT;
-  const int top = kHistBins - 1 - tid * per;
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < per; ++i) mine += (int)s_hist[top - i];
-  int total;
-  int above = block_excl_scan<NW>(mine, s_wsum, total);
-  if (above < need && above + mine >= need) {
-    for (int i = 0; i < per; ++i) {
-      const int h = (int)s_hist[top - i];
-      if (above + h >= need) {
-        s_res[0] = top - i;
-        s_res[1] = above;
-        break;
-      }
-      above += h;
-    }
-  }
-  __syncthreads();
-  const int D = s_res[0];
-  const int need2 = need - s_res[1];
-  const int mD = (int)s_hist[D];
-  if (mD > 64) {  // many entries share bin D: radix select among them
-    __syncthreads();  // s_hist is reused
-    auto getD = [&](int i) {
-      const uint64_t cc = get(i);
-      return (bin(cc) == D) ? cc : 0ull;
-    };
-    return lds_threshold<NT>(getD, count, need2, s_hist, s_wsum, s_res);
-  }
-  for (int i = tid; i < count; i += NT) {
-    const uint64_t cc = get(i);
-    if (bin(cc) == D) s_small[atomicAdd(&s_res[2], 1)] = cc;
-  }
-  __syncthreads();
-  if (wv == 0) {  // rank the (distinct) entries of bin D
-    const uint64_t x = lane < mD ? s_small[lane] : 0ull;
-    int rank = 0;
-    for (int i = 0; i < mD; ++i) rank += s_small[i] > x ? 1 : 0;
-    if (lane < mD && rank == need2 - 1) s_small[64] = x;
-  }
-  __syncthreads();
-  return s_small[64];
-}
-
-// Entries i < count with keep(i) true, in ascending i, get their rank among
-// the kept ones: put(i, rank).  Entry i = j*NT + tid; per (j, wave) one
-// ballot count, one block scan over them (at most NT counts: count <= NT*NT/64
-// entries).  s_tmp: ceil(count/NT)*NT/64 ints.
-template <int NT, typename Keep, typename Put>
-__device__ inline void ordered_put(int count, Keep keep, Put put, int* s_wsum, int* s_tmp) {
-  constexpr int NW = NT / 64;
-  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
-  const int per = (count + NT - 1) / NT;
-  for (int j = 0; j < per; ++j) {
-    const uint64_t mask = __ballot(keep(j * NT + tid));
-    if (lane == 0) s_tmp[j * NW + wv] = __popcll(mask);
-  }
-  __syncthreads();
-  const int cnt = (tid < per * NW) ? s_tmp[tid] : 0;
-  int total;
-  const int before = block_excl_scan<NW>(cnt, s_wsum, total);
-  if (tid < per * NW) s_tmp[tid] = before;
-  __syncthreads();
-  const uint64_t below = (1ull << lane) - 1;
-  for (int j = 0; j < per; ++j) {
-    const int i = j * NT + tid;
-    const bool k = keep(i);
-    const uint64_t mask = __ballot(k);
-    if (k) put(i, s_tmp[j * NW + wv] + __popcll(mask & below));
   }
 }
 
