@@ -86,6 +86,9 @@ class DecodeStep:
         import torch
         if cache.k_shadow.is_cuda:
             raise ValueError("attend_hybrid needs a cache with its shadow in host memory")
+        if self.exclude:
+            raise ValueError("attend_hybrid subtracts the selected tokens' approximate terms, which 1- and 2-bit "
+                             "keys do not survive in fp32: use attend()")
         if not hasattr(self, "_h_idx"):
             L = self.layout
             self._h_idx = torch.empty(self.idx.numel(), dtype=torch.int32, pin_memory=True)
