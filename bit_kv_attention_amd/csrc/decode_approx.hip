@@ -314,11 +314,14 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
   }
 
   // p[tt][r] is the weight x 2^-o of slot r's value scale (see unpack_values)
+  // (SKIP can leave a wave with nothing but skipped tokens so far: m_new is
+  // then -inf and the reference 0 keeps every weight at exactly 0)
+  const float m_ref = (SKIP && m_new == -INFINITY) ? 0.f : m_new;
   float p[2][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int o = value_slot_exp<VB>(i);
-    const float nm = -m_new - (float)o;
+    const float nm = -m_ref - (float)o;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       p[tt][i] = __builtin_amdgcn_exp2f(fmaf(s2[tt][i], c_s2, nm));

@@ -628,3 +628,25 @@ def test_decode_step_equals_append_then_select(P, kb, vb, G, g):
                 assert np.array_equal(sa[b, :, :lens[b]], sb[b, :, :lens[b]]), (mode, i, b)
             assert torch.equal(steps[0].idx, steps[1].idx), (mode, i)
             assert torch.equal(steps[0].out, steps[1].out), (mode, i)
+
+
+@pytest.mark.parametrize("kb,vb,G,g,window,block", [(2, 2, 4, 64, 50, 0), (1, 2, 8, 64, 0, 64), (4, 4, 4, 32, 0, 128)])
+def test_exclude_path_window_and_blocks(P, kb, vb, G, g, window, block):
+    """The exclusion path with a recent window and with block selection: the
+    output against the oracle on the GPU's rows (k + window, or n_blocks *
+    block entries)."""
+    banner(f"exclude path kb={kb} vb={vb} G={G} g={g} window={window} block={block}")
+    import torch
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("excwb", 3, 2 * G, 2, 128, 3000, kb, vb, g, 24, 6, 1900 + 10 * kb + G + g + window + block)
+    pair = P.build_pair(w, L=3000, cap=3008)
+    lens = np.array([2999, 777, 0])
+    q = P.to_dev(pair["q"])
+    k = 6 if block else 24
+    st = DecodeStep(pair["lay"], k, 2999, window=window, block=block, exclude=True)
+    out = st.attend(pair["gc"], q, lens)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, st.row)
+    orc = pair["oc"].decode(pair["q"], lens, st.row, sel=idx)
+    P.assert_close(o, orc["out"], "exclude (window/blocks) vs oracle")
