@@ -63,6 +63,9 @@ def lib():
             getattr(L, f).restype = C.c_size_t
         L.orc_pack_append.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P]
         L.orc_decode.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P, P, P, P, P, P]
+        L.orc_decode_q.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P, C.c_int,
+                                   P, P, P, P, P]
+        L.orc_quantize_query.argtypes = [P, C.c_int, C.c_int, P, P]
         L.orc_topk.argtypes = [P, C.c_int, C.c_int, P]
         L.orc_topk_window.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
         L.orc_topk_blocks.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
@@ -109,6 +112,17 @@ def quantize_rows(x16: np.ndarray, group: int, bits: int):
     meta = np.zeros(x16.shape[:-1] + (D // group,), dtype=np.uint32)
     lib().orc_quantize_rows(_p(x16.view(np.uint16)), n, D, group, bits, _p(codes), _p(meta))
     return codes, (meta & 0xFFFF).astype(np.uint16), (meta >> 16).astype(np.uint16)
+
+
+def quantize_query(q16: np.ndarray, group: int):
+    """O1q on one query row.  q16: [D] float16.
+    Returns (codes int8 [D], scales float32 [D/group])."""
+    q16 = np.ascontiguousarray(q16, dtype=np.float16).reshape(-1)
+    D = q16.shape[0]
+    codes = np.zeros(D, dtype=np.int8)
+    scales = np.zeros(D // group, dtype=np.float32)
+    lib().orc_quantize_query(_p(q16.view(np.uint16)), D, group, _p(codes), _p(scales))
+    return codes, scales
 
 
 def k_bitpos(t: int, c: int, D: int, bits: int) -> int:
@@ -171,8 +185,10 @@ class Cache:
                               _p(self.v_meta), _p(self.k_shadow), _p(self.v_shadow),
                               _p(k_new.view(np.uint16)), _p(v_new.view(np.uint16)), n, _p(pos))
 
-    def decode(self, q: np.ndarray, lens, k: int, sel=None, want_approx=False, want_exact=False):
-        """O3..O5.  q: [B][Hq][D] float16.  Returns dict(sigma, idx, out[, out_approx, out_exact])."""
+    def decode(self, q: np.ndarray, lens, k: int, sel=None, want_approx=False, want_exact=False,
+               qbits: int = 0):
+        """O3..O5.  q: [B][Hq][D] float16.  qbits = 8: approximate logits against
+        the INT8 query (O1q).  Returns dict(sigma, idx, out[, out_approx, out_exact])."""
         s = self.s
         q = np.ascontiguousarray(q, dtype=np.float16)
         assert q.shape == (s.B, s.Hq, s.D)
@@ -187,10 +203,10 @@ class Cache:
             sel_arr = np.ascontiguousarray(sel, dtype=np.int32)
             assert sel_arr.shape == (s.B, s.Hkv, k)
         cs = s.c()
-        lib().orc_decode(C.byref(cs), _p(self.k_codes), _p(self.v_codes), _p(self.k_meta),
-                         _p(self.v_meta), _p(self.k_shadow), _p(self.v_shadow),
-                         _p(q.view(np.uint16)), _p(lens), int(k), _p(sel_arr), _p(sigma),
-                         _p(idx), _p(out), _p(oa), _p(oe))
+        lib().orc_decode_q(C.byref(cs), _p(self.k_codes), _p(self.v_codes), _p(self.k_meta),
+                           _p(self.v_meta), _p(self.k_shadow), _p(self.v_shadow),
+                           _p(q.view(np.uint16)), _p(lens), int(k), _p(sel_arr), int(qbits),
+                           _p(sigma), _p(idx), _p(out), _p(oa), _p(oe))
         r = {"sigma": sigma, "idx": idx, "out": out}
         if want_approx:
             r["out_approx"] = oa

@@ -118,6 +118,35 @@ void orc_quantize_rows(const uint16_t* x, int n, int D, int g, int bits,
   }
 }
 
+/* O1q: the query of one head quantised to INT8 per partition of g channels,
+ * for scores in the HACK review's homomorphic form (Eq. (4): both operands of
+ * a product quantised partition-wise, the product taken on the integer codes).
+ * Reading: the query partition is symmetric, q ~= s*q' with q' in
+ * [-127, 127] and no offset (zero point 0), so Eq. (4)'s term with the key
+ * codes' sums vanishes:  s = amax / 127 (fp32, correctly rounded divide),
+ * q' = rint(q / s) (ties to even), q' = 0 if s == 0.  The scale stays fp32:
+ * the query is not stored. */
+void orc_quantize_query(const uint16_t* q, int D, int g, int8_t* codes,
+                        float* scales) {
+  for (int p = 0; p < D / g; ++p) {
+    float amax = 0.0f;
+    for (int i = 0; i < g; ++i) {
+      const float v = fabsf(orc_f16_to_f32(q[p * g + i]));
+      if (v > amax) amax = v;
+    }
+    const float s = amax / 127.0f;
+    for (int i = 0; i < g; ++i) {
+      int code = 0;
+      if (s != 0.0f) {
+        const float r = rintf(orc_f16_to_f32(q[p * g + i]) / s);
+        code = r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
+      }
+      codes[p * g + i] = (int8_t)code;
+    }
+    scales[p] = s;
+  }
+}
+
 /* -------------------------------------------------------------- O2 layout */
 
 /* K: blocks of 16 tokens.  Channel c has group g = c / 32, eighth
@@ -367,6 +396,19 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
                 const int32_t* len, int k, const int32_t* sel_in,
                 double* sigma, int32_t* idx, double* out, double* out_approx,
                 double* out_exact) {
+  orc_decode_q(s, k_codes, v_codes, k_meta, v_meta, k_shadow, v_shadow, q, len,
+               k, sel_in, 0, sigma, idx, out, out_approx, out_exact);
+}
+
+/* qbits = 8: the approximate logits (O3) use the dequantised INT8 query
+ * s*q' (O1q) in place of q; the exact logits of the correction keep q. */
+void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
+                  const uint8_t* v_codes, const uint32_t* k_meta,
+                  const uint32_t* v_meta, const uint16_t* k_shadow,
+                  const uint16_t* v_shadow, const uint16_t* q,
+                  const int32_t* len, int k, const int32_t* sel_in, int qbits,
+                  double* sigma, int32_t* idx, double* out, double* out_approx,
+                  double* out_exact) {
   const int G = s->Hq / s->Hkv;
   const int D = s->D;
   const double sm = 1.0 / sqrt((double)D);
@@ -386,6 +428,20 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
     memset(all, 1, (size_t)nn);
     double* sig = sigma + (size_t)u * s->cap;
 
+    /* the query of the approximate logits: q, or its INT8 form s*q' */
+    double* qa = (double*)malloc((size_t)G * D * sizeof(double));
+    for (int i = 0; i < G; ++i) {
+      const uint16_t* qh = q + ((size_t)b * s->Hq + (size_t)kvh * G + i) * D;
+      if (qbits == 8) {
+        int8_t qc[ORC_MAX_D];
+        float qs[ORC_MAX_D];
+        orc_quantize_query(qh, D, s->group, qc, qs);
+        for (int c = 0; c < D; ++c) qa[(size_t)i * D + c] = (double)qs[c / s->group] * qc[c];
+      } else {
+        for (int c = 0; c < D; ++c) qa[(size_t)i * D + c] = orc_f16_to_f32(qh[c]);
+      }
+    }
+
     /* O3: approximate logits and the selection score. */
     for (int t = 0; t < n; ++t) {
       double best = -INFINITY;
@@ -394,7 +450,7 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
         double acc = 0.0, ex = 0.0;
         for (int c = 0; c < D; ++c) {
           const double qc = orc_f16_to_f32(qh[c]);
-          acc += qc * orc_k_hat(s, k_codes, k_meta, u, t, c);
+          acc += qa[(size_t)i * D + c] * orc_k_hat(s, k_codes, k_meta, u, t, c);
           ex += qc * (double)orc_f16_to_f32(k_shadow[((size_t)u * s->cap + t) * D + c]);
         }
         shat[(size_t)i * nn + t] = sm * acc;
@@ -427,6 +483,7 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
       if (out_exact)
         attend_head(s, u, n, sh, se, all, v_codes, v_meta, v_shadow, out_exact + h * D);
     }
+    free(qa);
     free(shat);
     free(sexact);
     free(in_s);

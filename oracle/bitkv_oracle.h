@@ -38,6 +38,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#define ORC_MAX_D 1024 /* largest head_dim the oracle takes */
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -102,6 +104,20 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
                 const int32_t* len, int k, const int32_t* sel_in,
                 double* sigma, int32_t* idx, double* out, double* out_approx,
                 double* out_exact);
+/* orc_decode with the approximate logits taken against the INT8 query
+ * (qbits = 8, see orc_quantize_query) or against q itself (qbits = 0). */
+void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
+                  const uint8_t* v_codes, const uint32_t* k_meta,
+                  const uint32_t* v_meta, const uint16_t* k_shadow,
+                  const uint16_t* v_shadow, const uint16_t* q,
+                  const int32_t* len, int k, const int32_t* sel_in, int qbits,
+                  double* sigma, int32_t* idx, double* out, double* out_approx,
+                  double* out_exact);
+
+/* O1q: symmetric INT8 codes of one query row per partition of g channels
+ * (codes[D], scales[D/g]); see the definition in bitkv_oracle.c. */
+void orc_quantize_query(const uint16_t* q, int D, int g, int8_t* codes,
+                        float* scales);
 
 /* O4 on its own: the min(k, n) largest of sigma[0..n) by (value desc, index
  * asc), written ascending to idx[0..), rest of idx[0..k) set to -1. */
