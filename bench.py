@@ -105,7 +105,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     dev = torch.device("cuda:0")
     L = w.L
     cap = ((L + 31) // 32) * 32
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
     units = w.B * w.Hkv
     ppt = packed_bytes_per_token(w.kbits, w.vbits, group=w.group)
     packed = units * L * ppt
@@ -303,7 +303,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
-                   "group": w.group, "top_k": 0 if NB else w.k, "recent_window": W,
+                   "group": w.group, "query_bits": w.query_bits, "top_k": 0 if NB else w.k,
+                   "recent_window": W,
                    "blocks": NB, "block": args.block if NB else 0,
                    "shadow": "host" if hybrid else args.shadow, "exact": args.exact,
                    "cache_copies": copies,
@@ -382,7 +383,7 @@ def cpu_baseline(w, inp, knew, vnew, threads):
     cache.append(K, V, np.zeros(1, np.int32))
     t = time.perf_counter()
     cache.append(kn, vn, np.array([L - 1], np.int32))
-    cache.decode(q, np.array([L], np.int32), w.k)
+    cache.decode(q, np.array([L], np.int32), w.k, qbits=w.query_bits)
     dt = time.perf_counter() - t
     t_step = dt * units / sample
     return {"value": round(w.B / t_step, 4), "unit": "tokens/s", "cores": sample, "kind": "oracle",

@@ -41,7 +41,7 @@ class BitKVError(RuntimeError):
 
 class Layout(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("batch", "n_q_heads", "n_kv_heads", "head_dim", "k_bits",
-                                         "v_bits", "group", "capacity")]
+                                         "v_bits", "group", "capacity", "query_bits")]
 
 
 class CacheView(C.Structure):
@@ -107,8 +107,9 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-def make_layout(batch, n_q_heads, n_kv_heads, capacity, k_bits, v_bits, head_dim=128, group=32) -> Layout:
-    return Layout(batch, n_q_heads, n_kv_heads, head_dim, k_bits, v_bits, group, capacity)
+def make_layout(batch, n_q_heads, n_kv_heads, capacity, k_bits, v_bits, head_dim=128, group=32,
+                query_bits=0) -> Layout:
+    return Layout(batch, n_q_heads, n_kv_heads, head_dim, k_bits, v_bits, group, capacity, query_bits)
 
 
 def bkv_cache_bytes(layout: Layout):

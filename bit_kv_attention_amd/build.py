@@ -18,7 +18,10 @@ LIB = os.path.join(HERE, "libbitkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "topk.hip", "correct.hip", "host_correct.cpp"]
+SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "decode_approx.hip:q8", "topk.hip", "correct.hip",
+           "host_correct.cpp"]
+# "file:variant" builds the file again into its own object with extra defines
+VARIANT_DEFINES = {"q8": ["-DBKV_QUERY_INT8=1"]}
 # host-only source (the host-side exact correction), OpenMP over host threads
 CXX = os.environ.get("CXX", "g++")
 CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-fopenmp", "-I", os.path.join(ROOT, "include")]
@@ -40,16 +43,18 @@ FLAGS = [
 EXTRA = {"decode_approx.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(entry: str) -> str:
+    src, _, variant = entry.partition(":")
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + (f"_{variant}" if variant else "") + ".o")
     if src.endswith(".cpp"):
         cmd = [CXX, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *VARIANT_DEFINES.get(variant, []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"compile failed on {src}")
+        raise RuntimeError(f"compile failed on {entry}")
     return obj
 
 

@@ -114,6 +114,7 @@ static bkv_status check_layout(const bkv_layout* L) {
   const int G = L->n_q_heads / L->n_kv_heads;
   if (G != 4 && G != 8) return BKV_E_UNSUPPORTED;
   if (L->batch > kMaxBatch) return BKV_E_UNSUPPORTED;
+  if (L->query_bits != 0 && L->query_bits != 8) return BKV_E_UNSUPPORTED;
   return BKV_OK;
 }
 

@@ -145,6 +145,12 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s);
+// The same with the INT8 query (layouts with query_bits = 8; launch_decode_approx
+// forwards those here).
+hipError_t launch_decode_approx_q8(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
+                                   const SeqArg& len, float* sigma, const Workspace& w, int chunk,
+                                   int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
+                                   const uint16_t* v_new, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 // bkeys: kstride block keys per unit; counter: one arrival counter per unit.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int nb,

@@ -24,6 +24,7 @@
 //           record independent of the others, batched), then the formula
 //           above.
 #include "bkv_internal.h"
+#include "quant_lane.h"
 
 namespace bkv {
 namespace {
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
 // AP = false: only the exact terms (the approximate state already leaves the
 // selected tokens out, see qattn_decode_unselected); the packed cache is not
 // read.
-template <int KB, int VB, int G, bool EX, bool AP = true>
+// Q8: the approximate logits take the INT8 query of the scan (quant_lane.h).
+template <int KB, int VB, int G, bool EX, bool AP = true, bool Q8 = false>
 __global__ __launch_bounds__(256) void chunk_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
@@ -192,6 +194,9 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 
   __shared__ uint4 s_qh[G][kHeadDim / 8];  // the query rows as fp16 pairs
   __shared__ float s_qs[G][kHeadDim / 16];  // sums of 16-channel runs of the query rows
+  __shared__ uint4 s_q8h[Q8 ? G : 1][kHeadDim / 8];   // Q8: the codes q' as fp16 pairs
+  __shared__ float s_q8s[Q8 ? G : 1][kHeadDim / 16];  // Q8: s * (sum of q' over a 16-channel run)
+  __shared__ float s_q8c[Q8 ? G : 1][kHeadDim / 16];  // Q8: the scale s of the run's group
   __shared__ int s_t[kCorrChunk];
   __shared__ float s_lg[2][kCorrChunk][G];  // logits, log2 units: [exact/approx]
   __shared__ float s_w[2][kCorrChunk][G];   // weights
@@ -211,6 +216,32 @@ __global__ __launch_bounds__(256) void chunk_kernel(
       for (int j = 0; j < 4; ++j) r += h2f((uint16_t)(ww[j] & 0xFFFFu)) + h2f((uint16_t)(ww[j] >> 16));
       r += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(r), 0xB1, 0xF, 0xF, true));  // + neighbour
       if ((tid & 1) == 0) (&s_qs[0][0])[tid >> 1] = r;
+      if constexpr (Q8) {
+        // a group is 4 << mshift neighbouring threads (whole waves take part)
+        float x[8];
+        halves8(w, x);
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+        for (int m = 1; m < (4 << mshift); m <<= 1)
+          a = fmaxf(a, __int_as_float(__builtin_amdgcn_ds_bpermute(((tid & 63) ^ m) << 2, __float_as_int(a))));
+        const float sc = query_scale_i8(a);
+        uint32_t pk[4];
+        int cs8 = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = query_code_i8(x[2 * j], sc), c1 = query_code_i8(x[2 * j + 1], sc);
+          cs8 += c0 + c1;
+          const half2_t hp = {(_Float16)(float)c0, (_Float16)(float)c1};
+          pk[j] = __builtin_bit_cast(uint32_t, hp);
+        }
+        (&s_q8h[0][0])[tid] = (uint4){pk[0], pk[1], pk[2], pk[3]};
+        cs8 += __builtin_amdgcn_mov_dpp(cs8, 0xB1, 0xF, 0xF, true);
+        if ((tid & 1) == 0) {
+          (&s_q8s[0][0])[tid >> 1] = sc * (float)cs8;
+          (&s_q8c[0][0])[tid >> 1] = sc;
+        }
+      }
     }
     if (tid < kCorrChunk) s_t[tid] = (ii < kk && tv >= 0 && tv < n) ? tv : -1;
   }
@@ -299,15 +330,25 @@ __global__ __launch_bounds__(256) void chunk_kernel(
       for (int h = 0; h < G; ++h) {
         const uint4 qa = s_qh[h][2 * part], qb = s_qh[h][2 * part + 1];
         const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        uint32_t qw8[8];
+        if constexpr (Q8) {  // q' as exact fp16 integers: q' . code is an exact integer sum
+          const uint4 ra = s_q8h[h][2 * part], rb = s_q8h[h][2 * part + 1];
+          const uint32_t r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qw8[i] = r8[i];
+        }
         float e = 0.f, d = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const half2_t qq = __builtin_bit_cast(half2_t, qw[i]);
           if constexpr (EX) e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
-          if constexpr (AP) d = __builtin_amdgcn_fdot2(cp[i], qq, d, false);
+          if constexpr (AP) d = __builtin_amdgcn_fdot2(cp[i], Q8 ? __builtin_bit_cast(half2_t, qw8[i]) : qq, d, false);
         }
         ex[h] = e;
-        ap[h] = AP ? fmaf(s, d, z * s_qs[h][part]) : 0.f;
+        if constexpr (Q8)
+          ap[h] = AP ? fmaf(s, d * s_q8c[h][part], z * s_q8s[h][part]) : 0.f;
+        else
+          ap[h] = AP ? fmaf(s, d, z * s_qs[h][part]) : 0.f;
       }
     }
     // sum over the token's 8 threads (lanes 8m..8m+7): quads by DPP, then the
@@ -392,7 +433,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 // elsewhere).
 enum ChunkTerms { kBoth, kExactOnly, kApproxOnly };
 
-template <int KB, int VB, int G>
+template <int KB, int VB, int G, bool Q8>
 void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
               const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   const dim3 grid(w.nchunk, L.batch * L.n_kv_heads);
@@ -400,7 +441,7 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
   const uint8_t* kc = static_cast<const uint8_t*>(cc.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(cc.v_codes);
   if (terms == kBoth)
-    chunk_kernel<KB, VB, G, true, true><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
+    chunk_kernel<KB, VB, G, true, true, Q8><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
                                                               idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity,
                                                               k, w.nchunk, mshift);
   else if (terms == kExactOnly)
@@ -408,7 +449,7 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
                                                                q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads,
                                                                L.capacity, k, w.nchunk, mshift);
   else
-    chunk_kernel<KB, VB, G, false, true><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
+    chunk_kernel<KB, VB, G, false, true, Q8><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
                                                                w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
                                                                w.nchunk, mshift);
 }
@@ -416,10 +457,13 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
 template <int KB, int VB>
 void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
               const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
+  const bool q8 = L.query_bits == 8;
   if (L.n_q_heads / L.n_kv_heads == 4)
-    launch_t<KB, VB, 4>(L, cc, q, len, idx, k, w, terms, s);
+    q8 ? launch_t<KB, VB, 4, true>(L, cc, q, len, idx, k, w, terms, s)
+       : launch_t<KB, VB, 4, false>(L, cc, q, len, idx, k, w, terms, s);
   else
-    launch_t<KB, VB, 8>(L, cc, q, len, idx, k, w, terms, s);
+    q8 ? launch_t<KB, VB, 8, true>(L, cc, q, len, idx, k, w, terms, s)
+       : launch_t<KB, VB, 8, false>(L, cc, q, len, idx, k, w, terms, s);
 }
 
 }  // namespace

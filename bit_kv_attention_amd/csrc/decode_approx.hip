@@ -38,12 +38,35 @@
 //    share, are loaded once (one 16-byte load per lane covers the step's K
 //    and V meta) and handed out through a per-wave LDS slot.  Selection scores
 //    are staged in LDS and stored every 8 steps as one coalesced store.
+//
+// INT8 query (HACK review on Pith, Eq. (4), both operands of Q.K^T quantised):
+// this file is built a second time with BKV_QUERY_INT8=1.  That build
+// quantises each query group to symmetric INT8 codes q' with an fp32 scale s
+// (quant_lane.h), takes the scores on v_mfma_i32_16x16x32_i8 with A = the
+// key codes as bytes and B = q' (exact integer sums), and applies s with the
+// key group's scale: s_hat = sum_g s_k * (s * (q' . k')) + z_k * (s * sum q').
+// Key codes become bytes with two or three VALU operations per 8 codes (no
+// fp16 conversion); a lane's 8 bytes take the channels in the order
+// key_byte_channel gives, and the query operand follows the same order.
 #include "bkv_internal.h"
 #include "quant_lane.h"
 #include "select_lds.h"
 
+#ifndef BKV_QUERY_INT8
+#define BKV_QUERY_INT8 0
+#endif
+#if BKV_QUERY_INT8
+#define BKV_SCAN_KERNEL decode_approx_q8_kernel
+#define BKV_SCAN_LAUNCH launch_decode_approx_q8
+#else
+#define BKV_SCAN_KERNEL decode_approx_kernel
+#define BKV_SCAN_LAUNCH launch_decode_approx
+#endif
+
 namespace bkv {
 namespace {
+
+constexpr bool kQ8 = BKV_QUERY_INT8 != 0;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -102,6 +125,41 @@ __device__ inline half8 unpack_keys(uint32_t y) {
   for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x[i]) - k1024);
   return __builtin_bit_cast(half8, r);
 }
+
+// INT8 query: the 8 codes of y (as for unpack_keys) as bytes.  4 bits: bytes
+// hold channels (0,2,4,6 | 1,3,5,7) -- one AND, one shift and AND; fewer
+// bits: (0,1,4,5 | 2,3,6,7).  The query operand takes the same order.
+__host__ __device__ constexpr int key_byte_channel(int bits, int i) {
+  return (bits == 4) ? ((i & 3) * 2 + (i >> 2)) : ((i & 1) + 4 * ((i >> 1) & 1) + 2 * (i >> 2));
+}
+template <int BITS>
+__device__ inline long unpack_key_bytes(uint32_t y) {
+  uint32_t lo, hi;
+  if constexpr (BITS == 4) {
+    lo = y & 0x0F0F0F0Fu;
+    hi = (y >> 4) & 0x0F0F0F0Fu;
+  } else {
+    constexpr uint32_t M = ((1u << BITS) - 1) * 0x00010001u;
+    lo = (y & M) | (((y >> BITS) & M) << 8);
+    hi = ((y >> (2 * BITS)) & M) | (((y >> (3 * BITS)) & M) << 8);
+  }
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+template <bool Q8>
+struct QueryOperand {
+  typedef half8 type;
+};
+template <>
+struct QueryOperand<true> {
+  typedef long type;
+};
+// (dependent on KB so that the branch of the other build is not instantiated)
+template <int KB>
+using QOp = typename QueryOperand<kQ8 && (KB > 0)>::type;
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+// Lane l's value from lane l ^ m of the wave.
+__device__ inline int lane_xor(int v, int m, int lane) { return __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, v); }
 
 // Values: the masked bits are used as fp16 bit patterns directly, i.e. the
 // subnormals c * 2^(o-24) for a code masked at bit o (patterns below 0x800 are
@@ -225,8 +283,9 @@ constexpr int kZS = (VB == 4) ? 2 : 4;
 // selection scores.
 template <int KB, int VB, int G, bool MASK, bool SKIP = false, bool SIGONLY = false>
 __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
-                                          const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const half8 (&bq)[kGroups],
-                                          const float (&qs)[Step<KB, VB, G>::NT], WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
+                                          const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const QOp<KB> (&bq)[kGroups],
+                                          const float (&qs)[Step<KB, VB, G>::NT], const float (&qsc)[Step<KB, VB, G>::NT],
+                                          WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
                                           floatx4* __restrict__ sig_row, int t0, int len, int n, int kb,
                                           float c_s2, uint32_t skipw = 0) {
   constexpr int NT = Step<KB, VB, G>::NT;
@@ -236,6 +295,11 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
   for (int T = 0; T < NT; ++T)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) d[T][tt] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  intx4 di[NT][2];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) di[T][tt] = (intx4){0, 0, 0, 0};
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
@@ -255,8 +319,19 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
         y = (x & 0xFu) | ((x << 12) & 0x000F0000u);
       }
       const int T = (G == 8) ? (g >> 1) : 0;
-      d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys<KB>(y), bq[g], d[T][tt], 0, 0, 0);
+      if constexpr (kQ8)
+        di[T][tt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack_key_bytes<KB>(y), bq[g], di[T][tt], 0, 0, 0);
+      else
+        d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys<KB>(y), bq[g], d[T][tt], 0, 0, 0);
     }
+  }
+  if constexpr (kQ8) {  // integer sums (|q' . k'| < 2^16: exact) times the query group's scale
+#pragma unroll
+    for (int T = 0; T < NT; ++T)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[T][tt][i] = (float)di[T][tt][i] * qsc[T];
   }
 
   // -- per-(token, group) scale and zero, reduce over groups ------------------
@@ -370,7 +445,7 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // whose split holds that position does it before its scan reads the cache.
 // (The cache pointers carry no __restrict__: this launch writes through them.)
 template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false, bool APPEND = false>
-__global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx_kernel(
+__global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERNEL(
     const uint8_t* k_codes, const uint8_t* v_codes, const uint32_t* k_meta, const uint32_t* v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
@@ -400,12 +475,32 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
 
   // ---- query operands, staged through LDS ------------------------------------
   __shared__ uint16_t s_q[G][kHeadDim];
-  __shared__ float s_qsum[G][kGroups];
+  __shared__ float s_qsum[G][kGroups];   // per quarter: sum of q (INT8: s * sum of q')
+  __shared__ int8_t s_q8[kQ8 ? G : 1][kHeadDim];  // INT8: the codes q'
+  __shared__ float s_qsc[kQ8 ? G : 1][kGroups];   // INT8: the scale s of each quarter's group
   {
     const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
     if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
     __syncthreads();
-    if (tid < G * kGroups) {
+    if constexpr (kQ8) {
+      // one entry per thread, whole waves: a wave holds 64 channels of one head,
+      // a group is 32 << mshift of its lanes
+      for (int e = tid; e < G * kHeadDim; e += 64 * kScanWaves) {
+        const int hh = e / kHeadDim, c = e % kHeadDim;
+        const float x = (float)__builtin_bit_cast(_Float16, s_q[hh][c]);
+        float a = fabsf(x);
+        for (int m = 1; m < (kGroup << mshift); m <<= 1) a = fmaxf(a, __int_as_float(lane_xor(__float_as_int(a), m, lane)));
+        const float sc = query_scale_i8(a);
+        const int code = query_code_i8(x, sc);
+        s_q8[hh][c] = (int8_t)code;
+        int sum = code;
+        for (int m = 1; m < kGroup; m <<= 1) sum += lane_xor(sum, m, lane);
+        if ((c & (kGroup - 1)) == 0) {
+          s_qsum[hh][c / kGroup] = sc * (float)sum;
+          s_qsc[hh][c / kGroup] = sc;
+        }
+      }
+    } else if (tid < G * kGroups) {
       const int hh = tid / kGroups, g = tid % kGroups;
       float s = 0.f;
       for (int c = 0; c < kGroup; ++c) s += (float)__builtin_bit_cast(_Float16, s_q[hh][g * kGroup + c]);
@@ -474,13 +569,28 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
   }
   // column (g', h) of N-tile T: g' = n/4 (G = 4) or 2T + n/8 (G = 8)
   const int h = (G == 8) ? (n & 7) : (n & 3);
-  half8 bq[kGroups];
-  float qs[NT];
+  QOp<KB> bq[kGroups];
+  float qs[NT], qsc[NT];
 #pragma unroll
-  for (int T = 0; T < NT; ++T) qs[T] = s_qsum[h][(G == 8) ? (2 * T + (n >> 3)) : (n >> 2)];
+  for (int T = 0; T < NT; ++T) {
+    const int gq = (G == 8) ? (2 * T + (n >> 3)) : (n >> 2);
+    qs[T] = s_qsum[h][gq];
+    if constexpr (kQ8)
+      qsc[T] = s_qsc[h][gq];
+    else
+      qsc[T] = 1.0f;
+  }
 #pragma unroll
   for (int g = 0; g < kGroups; ++g) {
     const int gq = (G == 8) ? (2 * (g >> 1) + (n >> 3)) : (n >> 2);
+    if constexpr (kQ8) {  // the codes of channels 32g + 8kb + key_byte_channel(i), in column (g, h) only
+      uint64_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v |= (uint64_t)(uint8_t)s_q8[h][g * kGroup + 8 * kb + key_byte_channel(KB, i)] << (8 * i);
+      bq[g] = (gq == g) ? (long)v : 0l;
+      continue;
+    } else {
     half8 v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // slots of pairs 1 and 3 carry 2^-KB (see unpack_keys)
@@ -491,6 +601,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
       v[2 * r + 1] = (gq == g) ? (_Float16)(q1 * sc) : (_Float16)0.0f;
     }
     bq[g] = v;
+    }
   }
 
   const float sm = 1.0f / sqrtf((float)kHeadDim);
@@ -561,7 +672,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, false, SKIP, SIGONLY>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
+    scan_step<KB, VB, G, false, SKIP, SIGONLY>(cur, km, vm, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
                                       SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     if (++sig_count == kSigBatch) flush_sig();
   };
@@ -570,7 +681,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void decode_approx
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, true, SKIP, SIGONLY>(cur, km, vm, bq, qs, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
+    scan_step<KB, VB, G, true, SKIP, SIGONLY>(cur, km, vm, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
@@ -718,31 +829,31 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
   const uint8_t* vc = static_cast<const uint8_t*>(c.v_codes);
   (void)hipGetLastError();  // report only this launch's status
   if (k_new && ksel > 0)
-    decode_approx_kernel<KB, VB, G, true, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, true, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
   else if (k_new)
-    decode_approx_kernel<KB, VB, G, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
   else if (sigonly && ksel > 0)
-    decode_approx_kernel<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (sigonly)
-    decode_approx_kernel<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (skip)
-    decode_approx_kernel<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else if (ksel > 0)
-    decode_approx_kernel<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
   else
-    decode_approx_kernel<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
+    BKV_SCAN_KERNEL<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
         L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
   return hipGetLastError();
@@ -759,10 +870,14 @@ hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 
 }  // namespace
 
-hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
+hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s) {
+#if !BKV_QUERY_INT8
+  if (L.query_bits == 8)
+    return launch_decode_approx_q8(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+#endif
   const bool v4 = L.v_bits == 4;
   switch (L.k_bits) {
     case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)

@@ -87,4 +87,24 @@ __device__ inline void store_key_codes(uint8_t* __restrict__ unit_codes, int t, 
   }
 }
 
+// ---- the INT8 query of the approximate scores -------------------------------
+// (HACK review on Pith, Eq. (4): both operands of Q.K^T quantised per
+// partition, the product formed on the integer codes.)  The query's partition
+// is the layout's group and is symmetric: s = amax / 127 in fp32 (correctly
+// rounded divide), q' = rint(q / s) in [-127, 127], 0 when s == 0.  With a
+// zero point of 0, Eq. (4) for a key group s_k*k' + z_k keeps two terms:
+//   q_hat . k_hat = s * (s_k * (q' . k') + z_k * sum(q')).
+// The scan and the correction both quantise with these two functions, so
+// their codes agree bit for bit.
+__device__ inline float query_scale_i8(float amax) {
+#pragma clang fp contract(off)
+  return amax / 127.0f;
+}
+__device__ inline int query_code_i8(float x, float s) {
+#pragma clang fp contract(off)
+  if (s == 0.0f) return 0;
+  const float r = __builtin_rintf(x / s);
+  return (int)fminf(fmaxf(r, -127.0f), 127.0f);
+}
+
 }  // namespace bkv

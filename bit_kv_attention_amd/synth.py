@@ -40,6 +40,7 @@ class Workload:
     seed: int
     n_outlier: int = 4
     outlier_scale: float = 8.0
+    query_bits: int = 0  # 8: approximate scores against the INT8 query (HACK's Eq. (4))
 
     @property
     def G(self) -> int:
@@ -62,6 +63,8 @@ WORKLOADS = [
 CODEC_WORKLOADS = [
     Workload("llama8b_k2v2g64_L32768", 4, 32, 8, 128, 32768, 2, 2, 64, 256, 64, 1005),
     Workload("llama8b_k1v2g64_L32768", 4, 32, 8, 128, 32768, 1, 2, 64, 256, 64, 1006),
+    # HACK's INT8-query scores on the 8B K4V4 cache
+    Workload("llama8b_k4v4_q8_L32768", 4, 32, 8, 128, 32768, 4, 4, 32, 256, 64, 1007, query_bits=8),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + CODEC_WORKLOADS}
 

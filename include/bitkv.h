@@ -78,10 +78,18 @@ typedef struct {
   int32_t n_q_heads;  /* Hq                                                 */
   int32_t n_kv_heads; /* Hkv; units are the B*Hkv (batch, KV head) pairs    */
   int32_t head_dim;   /* D (128)                                            */
-  int32_t k_bits;     /* bits per key code (3 or 4)                         */
+  int32_t k_bits;     /* bits per key code (1, 2, 3 or 4)                   */
   int32_t v_bits;     /* bits per value code (2 or 4)                       */
-  int32_t group;      /* channels per quantisation group along D (32)       */
+  int32_t group;      /* channels per quantisation group along D (32, 64)   */
   int32_t capacity;   /* token slots per unit, multiple of 32               */
+  int32_t query_bits; /* query of the approximate scores: 0 = the fp16 query
+                       * as given; 8 = that query quantised per group to
+                       * symmetric INT8 (HACK review on Pith, Eq. (4): both
+                       * operands of Q.K^T quantised, the product taken on the
+                       * integer codes; here s = amax/127 in fp32,
+                       * q' = rint(q/s) in [-127, 127], so the term with the
+                       * key code sums is zero).  The exact logits of the
+                       * correction always use the fp16 query.              */
 } bkv_layout;
 
 /*

@@ -65,7 +65,7 @@ def build_pair(w: Workload, L: int, cap: int | None = None):
     cap = cap or ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1) if L > 1 else None
     k1, v1 = make_new_tokens(w, 1, inp.outlier_ch if inp else make_inputs(w, L=1).outlier_ch)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
     gc = bk.allocate_cache(lay)
     oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, w.kbits, w.vbits, w.group, cap))
     q = inp.q if inp else make_inputs(w, L=1).q

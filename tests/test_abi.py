@@ -81,6 +81,9 @@ def test_unsupported_head_dim_and_group(bk):
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 3
     lay = bk.Layout(4, 32, 8, 128, 2, 4, 64, 1024)
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == 0
+    for qb, want in ((8, 0), (4, 3), (16, 3), (-1, 3)):  # query of the approximate scores: fp16 or INT8
+        lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024, qb)
+        assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == want, qb
     assert bk.raw_status("bkv_workspace_bytes", None, 10, 4, C.byref(out)) == 1
     lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024)
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, -1, C.byref(out)) == 7

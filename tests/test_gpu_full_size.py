@@ -33,7 +33,7 @@ def test_full_size_sampled_units(P, name):
     cap = ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1)
     kn, vn = make_new_tokens(w, 1, inp.outlier_ch)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
     gc = bk.allocate_cache(lay)
     bk.kv_pack_append(lay, gc, P.to_dev(inp.K), P.to_dev(inp.V), L - 1, [0] * w.B)
     st = DecodeStep(lay, w.k, L)
@@ -54,12 +54,12 @@ def test_full_size_sampled_units(P, name):
         for name, ob in P.orc_buffers(oc).items():
             assert np.array_equal(g_buf[name][u], ob), (name, u)
         q = np.ascontiguousarray(inp.q[b:b + 1, h * w.G:(h + 1) * w.G])
-        ref = oc.decode(q, np.array([L], np.int32), w.k)
+        ref = oc.decode(q, np.array([L], np.int32), w.k, qbits=w.query_bits)
         np.testing.assert_allclose(g_sig[u, :L], ref["sigma"][0, 0, :L], rtol=1e-5, atol=2e-5)
         assert np.array_equal(g_idx[u], oracle.topk(g_sig[u, :L].astype(np.float64), w.k))
         P.assert_topk_near_tie(g_idx[u], ref["idx"][0, 0], ref["sigma"][0, 0], L, f"unit {u}")
         if w.planted and w.kbits >= 3:  # (1- and 2-bit keys may rank a planted token lower)
             assert set(inp.planted_pos[b, h].tolist()) <= set(g_idx[u].tolist())
-        ref_s = oc.decode(q, np.array([L], np.int32), w.k, sel=g_idx[u].reshape(1, 1, -1))
+        ref_s = oc.decode(q, np.array([L], np.int32), w.k, sel=g_idx[u].reshape(1, 1, -1), qbits=w.query_bits)
         P.assert_close(g_out[b, h * w.G:(h + 1) * w.G], ref_s["out"][0], f"unit {u} vs oracle(S_gpu)")
         P.assert_close(g_out[b, h * w.G:(h + 1) * w.G], ref["out"][0], f"unit {u} vs oracle(S_oracle)")

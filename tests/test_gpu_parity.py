@@ -650,3 +650,63 @@ def test_exclude_path_window_and_blocks(P, kb, vb, G, g, window, block):
     idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, st.row)
     orc = pair["oc"].decode(pair["q"], lens, st.row, sel=idx)
     P.assert_close(o, orc["out"], "exclude (window/blocks) vs oracle")
+
+
+# INT8 query of the approximate scores (HACK review on Pith, Eq. (4)): every
+# key width, both value widths, both GQA group sizes, groups of 32 and 64.
+Q8_CASES = [(4, 4, 4, 32), (3, 2, 8, 32), (2, 2, 4, 64), (1, 2, 8, 64), (4, 2, 8, 64), (3, 4, 4, 32)]
+
+
+@pytest.mark.parametrize("kb,vb,G,g", Q8_CASES)
+def test_query_int8_step_parity(P, kb, vb, G, g):
+    """Scores, selection and output against the oracle with qbits = 8."""
+    banner(f"int8 query kb={kb} vb={vb} G={G} g={g}")
+    w = P.Workload("q8", 2, 2 * G, 2, 128, 1000, kb, vb, g, 24, 6, 300 + 10 * kb + vb + G + g, query_bits=8)
+    pair = P.build_pair(w, L=1000, cap=1024)
+    lens = np.array([1000, 651])
+    k = 24
+    r = P.run_step(pair, lens, k)
+    orc = pair["oc"].decode(pair["q"], lens, k, qbits=8)
+    orc16 = pair["oc"].decode(pair["q"], lens, k)
+    import oracle
+    for b in range(w.B):
+        n = lens[b]
+        np.testing.assert_allclose(r["sigma"][b, :, :n], orc["sigma"][b, :, :n], rtol=1e-5, atol=2e-5)
+        # the INT8 query moves the scores off the fp16-query ones
+        assert not np.allclose(r["sigma"][b, :, :n], orc16["sigma"][b, :, :n], rtol=1e-6, atol=1e-7)
+        for h in range(w.Hkv):
+            want = oracle.topk(r["sigma"][b, h, :n].astype(np.float64), k)
+            assert np.array_equal(r["idx"][b, h], want), (b, h)
+            P.assert_topk_near_tie(r["idx"][b, h], orc["idx"][b, h], orc["sigma"][b, h], n, f"b{b}h{h}")
+    orc_s = pair["oc"].decode(pair["q"], lens, k, sel=r["idx"], qbits=8)
+    P.assert_close(r["out"], orc_s["out"], "out vs oracle(S_gpu)")
+    P.assert_close(r["out"], orc["out"], "out vs oracle(S_oracle)")
+
+
+@pytest.mark.parametrize("kb,vb,G,g", [(4, 4, 4, 32), (2, 2, 8, 64)])
+def test_query_int8_decode_step_and_ends(P, kb, vb, G, g):
+    """The one-launch step (append in the scan) with the INT8 query; k = 0 is
+    the approximate output against the INT8 query, k = len the exact one."""
+    import torch
+    from bit_kv_attention_amd.step import DecodeStep
+    banner(f"int8 query step/ends kb={kb} vb={vb} G={G} g={g}")
+    w = P.Workload("q8s", 2, 2 * G, 2, 128, 900, kb, vb, g, 16, 4, 400 + kb + G, query_bits=8)
+    pair = P.build_pair(w, L=900, cap=928)
+    lens = np.array([900, 517])
+    pos = [int(x) - 1 for x in lens]
+    pair["oc"].append(pair["k1"], pair["v1"], np.array(pos, np.int32))
+    st = DecodeStep(pair["lay"], 16, 900)
+    out = st.step(pair["gc"], P.to_dev(pair["q"]), P.to_dev(pair["k1"]), P.to_dev(pair["v1"]), pos)
+    torch.cuda.synchronize()
+    g_buf, o_buf = P.gpu_buffers(pair["gc"]), P.orc_buffers(pair["oc"])
+    for name in g_buf:
+        assert np.array_equal(g_buf[name], o_buf[name]), name
+    got = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, 16)
+    P.assert_close(got, pair["oc"].decode(pair["q"], lens, 16, sel=idx, qbits=8)["out"], "step vs oracle(S_gpu)")
+    for k, key in ((0, "out_approx"), (900, "out_exact")):
+        st2 = DecodeStep(pair["lay"], k, 900)
+        o2 = st2.attend(pair["gc"], P.to_dev(pair["q"]), lens.tolist())
+        torch.cuda.synchronize()
+        ref = pair["oc"].decode(pair["q"], lens, k, want_approx=True, want_exact=True, qbits=8)
+        P.assert_close(o2.cpu().numpy().reshape(w.B, w.Hq, 128), ref[key], f"k={k}")
