@@ -34,7 +34,7 @@ def build(force: bool = True) -> str:
 
 
 class _Shape(C.Structure):
-    _fields_ = [(n, C.c_int32) for n in ("B", "Hq", "Hkv", "D", "kbits", "vbits", "group", "cap")]
+    _fields_ = [(n, C.c_int32) for n in ("B", "Hq", "Hkv", "D", "kbits", "vbits", "group", "cap", "kfmt")]
 
 
 _lib = None
@@ -66,6 +66,9 @@ def lib():
         L.orc_decode_q.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P, C.c_int,
                                    P, P, P, P, P]
         L.orc_quantize_query.argtypes = [P, C.c_int, C.c_int, P, P]
+        L.orc_quantize_group_mx.argtypes = [P, C.c_int, P, P]
+        L.orc_e2m1_value.argtypes = [C.c_uint32]
+        L.orc_e2m1_value.restype = C.c_double
         L.orc_topk.argtypes = [P, C.c_int, C.c_int, P]
         L.orc_topk_window.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
         L.orc_topk_blocks.argtypes = [P, C.c_int, C.c_int, C.c_int, P]
@@ -114,6 +117,29 @@ def quantize_rows(x16: np.ndarray, group: int, bits: int):
     return codes, (meta & 0xFFFF).astype(np.uint16), (meta >> 16).astype(np.uint16)
 
 
+def quantize_rows_mx(x16: np.ndarray, group: int):
+    """O1mx on rows of fp16 values.  x16: [..., D] float16.
+    Returns (codes uint8 [..., D] = sign << 3 | E2M1 index, scale16 uint16 [..., D/g])."""
+    x16 = np.ascontiguousarray(x16, dtype=np.float16)
+    D = x16.shape[-1]
+    rows = x16.reshape(-1, D)
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    sc = np.zeros((rows.shape[0], D // group), dtype=np.uint16)
+    for r in range(rows.shape[0]):
+        for p in range(D // group):
+            seg = np.ascontiguousarray(rows[r, p * group:(p + 1) * group])
+            cs = np.zeros(group, dtype=np.uint8)
+            s16 = np.zeros(1, dtype=np.uint16)
+            lib().orc_quantize_group_mx(_p(seg.view(np.uint16)), group, _p(cs), _p(s16))
+            codes[r, p * group:(p + 1) * group] = cs
+            sc[r, p] = s16[0]
+    return codes.reshape(x16.shape), sc.reshape(x16.shape[:-1] + (D // group,))
+
+
+def e2m1_value(code: int) -> float:
+    return float(lib().orc_e2m1_value(int(code)))
+
+
 def quantize_query(q16: np.ndarray, group: int):
     """O1q on one query row.  q16: [D] float16.
     Returns (codes int8 [D], scales float32 [D/group])."""
@@ -150,9 +176,10 @@ class Shape:
     vbits: int
     group: int
     cap: int
+    kfmt: int = 0  # keys: 0 affine integer codes, 1 MXFP4
 
     def c(self) -> _Shape:
-        return _Shape(self.B, self.Hq, self.Hkv, self.D, self.kbits, self.vbits, self.group, self.cap)
+        return _Shape(self.B, self.Hq, self.Hkv, self.D, self.kbits, self.vbits, self.group, self.cap, self.kfmt)
 
 
 class Cache:

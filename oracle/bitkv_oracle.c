@@ -118,6 +118,52 @@ void orc_quantize_rows(const uint16_t* x, int n, int D, int g, int bits,
   }
 }
 
+/* O1mx: MXFP4 keys (Jet-QSparse abstract: FP4 keys; the OCP Microscaling
+ * formats define the block): a block of g channels shares the scale
+ * 2^X with X = floor(log2(amax)) - 2 (2 = the largest exponent of E2M1),
+ * and each element is x / 2^X rounded to the nearest E2M1 magnitude
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even mantissa, larger
+ * magnitudes clamped to 6) with its sign.  Readings: the scale is stored as
+ * an fp16 power of two in the low half of the meta word (zero half 0), so X
+ * is clamped below at -24, the smallest fp16 power of two; an all-zero block
+ * has scale 0; a result of magnitude 0 carries no sign. */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(uint32_t code) {
+  const double m = kE2M1[code & 7u];
+  return (code & 8u) ? -m : m;
+}
+
+void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
+                           uint16_t* scale16) {
+  double amax = 0.0;
+  for (int i = 0; i < g; ++i) {
+    const double v = fabs((double)orc_f16_to_f32(x[i]));
+    if (v > amax) amax = v;
+  }
+  if (amax == 0.0) {
+    for (int i = 0; i < g; ++i) codes[i] = 0;
+    *scale16 = 0;
+    return;
+  }
+  int e;
+  frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+  int X = e - 1 - 2;
+  if (X < -24) X = -24;
+  const double sc = ldexp(1.0, X);
+  for (int i = 0; i < g; ++i) {
+    const double v = (double)orc_f16_to_f32(x[i]);
+    const double a = fabs(v) / sc;
+    int best = 0;
+    for (int j = 1; j < 8; ++j) { /* nearest; on a tie keep the even index */
+      const double dj = fabs(a - kE2M1[j]), db = fabs(a - kE2M1[best]);
+      if (dj < db || (dj == db && (j & 1) == 0)) best = j;
+    }
+    codes[i] = (uint8_t)(best | ((v < 0.0 && best != 0) ? 8 : 0));
+  }
+  *scale16 = orc_f32_to_f16((float)sc);
+}
+
 /* O1q: the query of one head quantised to INT8 per partition of g channels,
  * for scores in the HACK review's homomorphic form (Eq. (4): both operands of
  * a product quantised partition-wise, the product taken on the integer codes).
@@ -243,7 +289,15 @@ void orc_pack_append(const orc_shape* s, uint8_t* k_codes, uint8_t* v_codes,
         const int t = pos[b] + j;
         const size_t src = (((size_t)u * n_new) + j) * D;
         /* keys */
-        orc_quantize_rows(k_new + src, 1, D, g, s->kbits, codes, meta);
+        if (s->kfmt == 1) {
+          for (int grp = 0; grp < ng; ++grp) {
+            uint16_t s16;
+            orc_quantize_group_mx(k_new + src + (size_t)grp * g, g, codes + (size_t)grp * g, &s16);
+            meta[grp] = s16;
+          }
+        } else {
+          orc_quantize_rows(k_new + src, 1, D, g, s->kbits, codes, meta);
+        }
         for (int c = 0; c < D; ++c)
           orc_set_bits(k_codes + (size_t)u * k_unit_bytes(s),
                        orc_k_bitpos(t, c, D, s->kbits), s->kbits, codes[c]);
@@ -275,7 +329,10 @@ double orc_k_hat(const orc_shape* s, const uint8_t* k_codes,
                  const uint32_t* k_meta, int u, int t, int c) {
   const uint32_t code = orc_get_bits(k_codes + (size_t)u * k_unit_bytes(s),
                                      orc_k_bitpos(t, c, s->D, s->kbits), s->kbits);
-  return dequant(k_meta[meta_index(s, u, c / s->group, t)], code);
+  const uint32_t meta = k_meta[meta_index(s, u, c / s->group, t)];
+  if (s->kfmt == 1) /* MXFP4: the E2M1 value times the block's power of two */
+    return orc_e2m1_value(code) * (double)orc_f16_to_f32((uint16_t)(meta & 0xFFFFu));
+  return dequant(meta, code);
 }
 
 double orc_v_hat(const orc_shape* s, const uint8_t* v_codes,

@@ -47,6 +47,7 @@ extern "C" {
 /* Shape of one attention layer's cache.  D % group == 0, cap % 32 == 0. */
 typedef struct {
   int32_t B, Hq, Hkv, D, kbits, vbits, group, cap;
+  int32_t kfmt; /* keys: 0 = affine integer codes (O1), 1 = MXFP4 (O1mx) */
 } orc_shape;
 
 /* ---- fp16 <-> fp32 (own implementation; pinned against numpy) ---- */
@@ -113,6 +114,15 @@ void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
                   const int32_t* len, int k, const int32_t* sel_in, int qbits,
                   double* sigma, int32_t* idx, double* out, double* out_approx,
                   double* out_exact);
+
+/* O1mx: one block of g fp16 values to MXFP4 (OCP Microscaling formats:
+ * E2M1 elements sharing one power-of-two scale; see bitkv_oracle.c).
+ * codes[i] = sign << 3 | E2M1 magnitude index; *scale16 = fp16 bits of the
+ * scale (0 for an all-zero block). */
+void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
+                           uint16_t* scale16);
+/* the value of an E2M1 code (sign << 3 | magnitude index) */
+double orc_e2m1_value(uint32_t code);
 
 /* O1q: symmetric INT8 codes of one query row per partition of g channels
  * (codes[D], scales[D/g]); see the definition in bitkv_oracle.c. */
