@@ -105,7 +105,8 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
     dev = torch.device("cuda:0")
     L = w.L
     cap = ((L + 31) // 32) * 32
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits,
+                         key_format=w.key_format)
     units = w.B * w.Hkv
     ppt = packed_bytes_per_token(w.kbits, w.vbits, group=w.group)
     packed = units * L * ppt
@@ -303,7 +304,7 @@ def bench_one(w, args, torch, bk, DecodeStep, make_inputs, make_new_tokens):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
-                   "group": w.group, "query_bits": w.query_bits, "top_k": 0 if NB else w.k,
+                   "group": w.group, "query_bits": w.query_bits, "key_format": "mxfp4" if w.key_format else "affine", "top_k": 0 if NB else w.k,
                    "recent_window": W,
                    "blocks": NB, "block": args.block if NB else 0,
                    "shadow": "host" if hybrid else args.shadow, "exact": args.exact,
@@ -372,7 +373,7 @@ def cpu_baseline(w, inp, knew, vnew, threads):
     L = w.L
     cap = ((L + 31) // 32) * 32
     sel = [(u // w.Hkv, u % w.Hkv) for u in range(sample)]
-    s = oracle.Shape(1, w.G * sample, sample, 128, w.kbits, w.vbits, w.group, cap)
+    s = oracle.Shape(1, w.G * sample, sample, 128, w.kbits, w.vbits, w.group, cap, w.key_format)
     # fold the sampled units into one batch row of `sample` KV heads
     K = np.stack([inp.K[b, h] for b, h in sel])[None]
     V = np.stack([inp.V[b, h] for b, h in sel])[None]

@@ -41,7 +41,8 @@ class BitKVError(RuntimeError):
 
 class Layout(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("batch", "n_q_heads", "n_kv_heads", "head_dim", "k_bits",
-                                         "v_bits", "group", "capacity", "query_bits")]
+                                         "v_bits", "group", "capacity", "query_bits",
+                                         "key_format")]
 
 
 class CacheView(C.Structure):
@@ -108,8 +109,9 @@ def _stream(stream) -> int | None:
 
 
 def make_layout(batch, n_q_heads, n_kv_heads, capacity, k_bits, v_bits, head_dim=128, group=32,
-                query_bits=0) -> Layout:
-    return Layout(batch, n_q_heads, n_kv_heads, head_dim, k_bits, v_bits, group, capacity, query_bits)
+                query_bits=0, key_format=0) -> Layout:
+    return Layout(batch, n_q_heads, n_kv_heads, head_dim, k_bits, v_bits, group, capacity, query_bits,
+                  key_format)
 
 
 def bkv_cache_bytes(layout: Layout):

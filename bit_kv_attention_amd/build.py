@@ -18,10 +18,10 @@ LIB = os.path.join(HERE, "libbitkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "decode_approx.hip:q8", "topk.hip", "correct.hip",
-           "host_correct.cpp"]
+SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "decode_approx.hip:q8", "decode_approx.hip:mx",
+           "topk.hip", "correct.hip", "host_correct.cpp"]
 # "file:variant" builds the file again into its own object with extra defines
-VARIANT_DEFINES = {"q8": ["-DBKV_QUERY_INT8=1"]}
+VARIANT_DEFINES = {"q8": ["-DBKV_QUERY_INT8=1"], "mx": ["-DBKV_KEY_MXFP4=1"]}
 # host-only source (the host-side exact correction), OpenMP over host threads
 CXX = os.environ.get("CXX", "g++")
 CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-fopenmp", "-I", os.path.join(ROOT, "include")]

@@ -115,6 +115,8 @@ static bkv_status check_layout(const bkv_layout* L) {
   if (G != 4 && G != 8) return BKV_E_UNSUPPORTED;
   if (L->batch > kMaxBatch) return BKV_E_UNSUPPORTED;
   if (L->query_bits != 0 && L->query_bits != 8) return BKV_E_UNSUPPORTED;
+  if (L->key_format != 0 && L->key_format != 1) return BKV_E_UNSUPPORTED;
+  if (L->key_format == 1 && (L->k_bits != 4 || L->group != kGroup || L->query_bits != 0)) return BKV_E_UNSUPPORTED;
   return BKV_OK;
 }
 

@@ -145,9 +145,13 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s);
-// The same with the INT8 query (layouts with query_bits = 8; launch_decode_approx
-// forwards those here).
+// The same with the INT8 query (layouts with query_bits = 8) and with MXFP4
+// keys (key_format = 1); launch_decode_approx forwards those layouts here.
 hipError_t launch_decode_approx_q8(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
+                                   const SeqArg& len, float* sigma, const Workspace& w, int chunk,
+                                   int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
+                                   const uint16_t* v_new, hipStream_t s);
+hipError_t launch_decode_approx_mx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                    const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                    int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                    const uint16_t* v_new, hipStream_t s);

@@ -173,7 +173,9 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
 // selected tokens out, see qattn_decode_unselected); the packed cache is not
 // read.
 // Q8: the approximate logits take the INT8 query of the scan (quant_lane.h).
-template <int KB, int VB, int G, bool EX, bool AP = true, bool Q8 = false>
+// MX: the key codes are MXFP4 (E2M1 numbers, one power-of-two scale per group
+// of 32, no zero point).
+template <int KB, int VB, int G, bool EX, bool AP = true, bool Q8 = false, bool MX = false>
 __global__ __launch_bounds__(256) void chunk_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
@@ -323,9 +325,12 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t lo = (uint32_t)(bits >> (KB * 2 * i)) & M, hi = (uint32_t)(bits >> (KB * (2 * i + 1))) & M;
-        cp[i] = __builtin_bit_cast(half2_t, lo | (hi << 16) | 0x64006400u) - k1024;
+        if constexpr (MX)  // the fp16 pattern of the E2M1 value * 2^-14 (exact)
+          cp[i] = __builtin_bit_cast(half2_t, ((lo & 7u) << 9) | ((lo & 8u) << 12) | ((hi & 7u) << 25) | ((hi & 8u) << 28));
+        else
+          cp[i] = __builtin_bit_cast(half2_t, lo | (hi << 16) | 0x64006400u) - k1024;
       }
-      const float s = h2f((uint16_t)(kmw & 0xFFFFu)), z = h2f((uint16_t)(kmw >> 16));
+      const float s = h2f((uint16_t)(kmw & 0xFFFFu)) * (MX ? 16384.0f : 1.0f), z = h2f((uint16_t)(kmw >> 16));
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const uint4 qa = s_qh[h][2 * part], qb = s_qh[h][2 * part + 1];
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 // elsewhere).
 enum ChunkTerms { kBoth, kExactOnly, kApproxOnly };
 
-template <int KB, int VB, int G, bool Q8>
+template <int KB, int VB, int G, bool Q8, bool MX = false>
 void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
               const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   const dim3 grid(w.nchunk, L.batch * L.n_kv_heads);
@@ -441,7 +446,7 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
   const uint8_t* kc = static_cast<const uint8_t*>(cc.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(cc.v_codes);
   if (terms == kBoth)
-    chunk_kernel<KB, VB, G, true, true, Q8><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
+    chunk_kernel<KB, VB, G, true, true, Q8, MX><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
                                                               idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity,
                                                               k, w.nchunk, mshift);
   else if (terms == kExactOnly)
@@ -449,7 +454,7 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
                                                                q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads,
                                                                L.capacity, k, w.nchunk, mshift);
   else
-    chunk_kernel<KB, VB, G, false, true, Q8><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
+    chunk_kernel<KB, VB, G, false, true, Q8, MX><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
                                                                w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
                                                                w.nchunk, mshift);
 }
@@ -458,6 +463,15 @@ template <int KB, int VB>
 void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
               const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   const bool q8 = L.query_bits == 8;
+  if constexpr (KB == 4) {
+    if (L.key_format == 1) {  // (fp16 query only)
+      if (L.n_q_heads / L.n_kv_heads == 4)
+        launch_t<4, VB, 4, false, true>(L, cc, q, len, idx, k, w, terms, s);
+      else
+        launch_t<4, VB, 8, false, true>(L, cc, q, len, idx, k, w, terms, s);
+      return;
+    }
+  }
   if (L.n_q_heads / L.n_kv_heads == 4)
     q8 ? launch_t<KB, VB, 4, true>(L, cc, q, len, idx, k, w, terms, s)
        : launch_t<KB, VB, 4, false>(L, cc, q, len, idx, k, w, terms, s);

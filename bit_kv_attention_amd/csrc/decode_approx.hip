@@ -48,6 +48,15 @@
 // Key codes become bytes with two or three VALU operations per 8 codes (no
 // fp16 conversion); a lane's 8 bytes take the channels in the order
 // key_byte_channel gives, and the query operand follows the same order.
+//
+// MXFP4 keys (Jet-QSparse abstract: FP4 keys; OCP Microscaling block format):
+// a third build, BKV_KEY_MXFP4=1, for 4-bit keys whose codes are E2M1
+// numbers with one power-of-two scale per group of 32 (quant_lane.h).  An
+// E2M1 code becomes an exact fp16 operand with three VALU operations per two
+// codes (unpack_keys_mx: its bits are the fp16 pattern of value * 2^-14), the
+// scores run on the same fp16 MFMA with the group's scale applied after it,
+// and the 2^14 is folded into the constants that turn scores into sigma and
+// log2 units.
 #include "bkv_internal.h"
 #include "quant_lane.h"
 #include "select_lds.h"
@@ -55,9 +64,15 @@
 #ifndef BKV_QUERY_INT8
 #define BKV_QUERY_INT8 0
 #endif
+#ifndef BKV_KEY_MXFP4
+#define BKV_KEY_MXFP4 0
+#endif
 #if BKV_QUERY_INT8
 #define BKV_SCAN_KERNEL decode_approx_q8_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_q8
+#elif BKV_KEY_MXFP4
+#define BKV_SCAN_KERNEL decode_approx_mx_kernel
+#define BKV_SCAN_LAUNCH launch_decode_approx_mx
 #else
 #define BKV_SCAN_KERNEL decode_approx_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx
@@ -67,6 +82,7 @@ namespace bkv {
 namespace {
 
 constexpr bool kQ8 = BKV_QUERY_INT8 != 0;
+constexpr bool kMX = BKV_KEY_MXFP4 != 0;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -123,6 +139,20 @@ __device__ inline half8 unpack_keys(uint32_t y) {
   u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, x[i]) - k1024);
+  return __builtin_bit_cast(half8, r);
+}
+
+// MXFP4 keys: E2M1 code c (sign bit 3, magnitude bits e1 e0 m) is the fp16
+// pattern ((c & 7) << 9) | ((c & 8) << 12) = its value * 2^-14 exactly (the
+// magnitude bits become the exponent's two low bits and the mantissa's top
+// bit; index 1, the value 0.5, becomes the subnormal 2^-15).  Pair r is
+// (code r, code r + 4) from the nibbles at 4r and 16 + 4r of the key dword.
+__device__ inline half8 unpack_keys_mx(uint32_t y) {
+  u32x4 r;
+  r[0] = ((y << 9) & 0x0E000E00u) | ((y << 12) & 0x80008000u);
+  r[1] = ((y << 5) & 0x0E000E00u) | ((y << 8) & 0x80008000u);
+  r[2] = ((y << 1) & 0x0E000E00u) | ((y << 4) & 0x80008000u);
+  r[3] = ((y >> 3) & 0x0E000E00u) | (y & 0x80008000u);
   return __builtin_bit_cast(half8, r);
 }
 
@@ -321,6 +351,8 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
       const int T = (G == 8) ? (g >> 1) : 0;
       if constexpr (kQ8)
         di[T][tt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(unpack_key_bytes<KB>(y), bq[g], di[T][tt], 0, 0, 0);
+      else if constexpr (kMX)
+        d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys_mx(y), bq[g], d[T][tt], 0, 0, 0);
       else
         d[T][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(unpack_keys<KB>(y), bq[g], d[T][tt], 0, 0, 0);
     }
@@ -519,7 +551,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
         float x[8];
         halves8(w4, x);
         uint32_t code[8];
-        const uint32_t mw = quantise_lane(x, sub, grp, mshift, (float)((1 << (kv ? VB : KB)) - 1), code);
+        const uint32_t mw = (kMX && kv == 0) ? quantise_lane_mx(x, code)
+                                             : quantise_lane(x, sub, grp, mshift, (float)((1 << (kv ? VB : KB)) - 1), code);
         if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
           const_cast<uint32_t*>(kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + p] =
               mw;
@@ -594,7 +627,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     half8 v;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {  // slots of pairs 1 and 3 carry 2^-KB (see unpack_keys)
-      const float sc = (r & 1) ? 1.0f / (float)(1 << KB) : 1.0f;
+      const float sc = ((r & 1) && !kMX) ? 1.0f / (float)(1 << KB) : 1.0f;
       const float q0 = (float)__builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + r]);
       const float q1 = (float)__builtin_bit_cast(_Float16, s_q[h][g * kGroup + 8 * kb + 4 + r]);
       v[2 * r] = (gq == g) ? (_Float16)(q0 * sc) : (_Float16)0.0f;
@@ -604,7 +637,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     }
   }
 
-  const float sm = 1.0f / sqrtf((float)kHeadDim);
+  // (MXFP4 keys: the MFMA saw values * 2^-14)
+  const float sm = (1.0f / sqrtf((float)kHeadDim)) * (kMX ? 16384.0f : 1.0f);
   const float c_sig = sm;
   const float c_s2 = sm * kLog2e;
   float* sig = sigma + (size_t)u * cap;
@@ -874,10 +908,16 @@ hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s) {
-#if !BKV_QUERY_INT8
+#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4
   if (L.query_bits == 8)
     return launch_decode_approx_q8(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+  if (L.key_format == 1)
+    return launch_decode_approx_mx(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
 #endif
+#if BKV_KEY_MXFP4  // (4-bit keys only)
+  return L.v_bits == 4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
+                       : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+#else
   const bool v4 = L.v_bits == 4;
   switch (L.k_bits) {
     case 4: return v4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
@@ -889,6 +929,7 @@ hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16
     default: return v4 ? launch_g<1, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
                        : launch_g<1, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
   }
+#endif
 }
 
 }  // namespace bkv

@@ -19,7 +19,8 @@
 namespace bkv {
 namespace {
 
-template <int KB, int VB>
+// MXK: MXFP4 keys (quantise_lane_mx) instead of affine codes.
+template <int KB, int VB, bool MXK = false>
 __global__ __launch_bounds__(256) void pack_append_kernel(
     uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, uint32_t* __restrict__ k_meta,
     uint32_t* __restrict__ v_meta, uint16_t* __restrict__ k_shadow, uint16_t* __restrict__ v_shadow,
@@ -58,7 +59,8 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     float x[8];
     halves8(w4, x);
     uint32_t code[8];
-    const uint32_t meta = quantise_lane(x, sub, grp, mshift, qmax, code);
+    const uint32_t meta =
+        (MXK && kv == 0) ? quantise_lane_mx(x, code) : quantise_lane(x, sub, grp, mshift, qmax, code);
     if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
       (kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + t] = meta;
     *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + c0) = w4;
@@ -106,9 +108,14 @@ hipError_t launch_kv(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_
   }
   dim3 grid(tiles, L.batch * L.n_kv_heads);
   (void)hipGetLastError();  // report only this launch's status
-  pack_append_kernel<KB, VB><<<grid, 256, 0, s>>>(
-      static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
-      c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, L.group == 64 ? 1 : 0);
+  if (KB == 4 && L.key_format == 1)
+    pack_append_kernel<KB, VB, true><<<grid, 256, 0, s>>>(
+        static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
+        c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, 0);
+  else
+    pack_append_kernel<KB, VB><<<grid, 256, 0, s>>>(
+        static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
+        c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, L.group == 64 ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -59,6 +59,37 @@ __device__ inline uint32_t quantise_lane(const float (&x)[8], int sub, int grp, 
   return (uint32_t)__builtin_bit_cast(uint16_t, s16) | ((uint32_t)__builtin_bit_cast(uint16_t, z16) << 16);
 }
 
+// MXFP4 keys (Jet-QSparse abstract: FP4 keys; the OCP Microscaling block
+// format): the 32 channels of a quarter share the scale 2^X with
+// X = floor(log2(amax)) - 2, clamped at -24 so that it is an fp16 value;
+// each code is sign << 3 | the E2M1 magnitude index of |x| / 2^X, rounded to
+// nearest with ties to the even index and clamped at 6.  Meta word: fp16 2^X
+// low, 0 high (0 for an all-zero quarter).  Same lane set as quantise_lane
+// (a quad per quarter, groups of 32 only).
+__device__ inline uint32_t quantise_lane_mx(const float (&x)[8], uint32_t (&code)[8]) {
+#pragma clang fp contract(off)
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));
+  if (a == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) code[j] = 0u;
+    return 0u;
+  }
+  // a >= 2^-24 is a normal fp32 number: its exponent field is floor(log2 a)
+  const int X = max((int)((__float_as_uint(a) >> 23) & 0xFFu) - 127 - 2, -24);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = __builtin_amdgcn_ldexpf(fabsf(x[j]), -X);  // exact
+    const int idx = (r > 0.25f) + (r >= 0.75f) + (r > 1.25f) + (r >= 1.75f) + (r > 2.5f) + (r >= 3.5f) + (r > 5.0f);
+    code[j] = (uint32_t)(idx | ((x[j] < 0.0f && idx != 0) ? 8 : 0));
+  }
+  const uint32_t s16 = (X >= -14) ? (uint32_t)(X + 15) << 10 : 1u << (X + 24);
+  return s16;
+}
+
 // The 8 fp16 values of a 16-byte piece as floats (exact).
 __device__ inline void halves8(const uint4& w4, float (&x)[8]) {
   const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};

@@ -90,6 +90,16 @@ typedef struct {
                        * q' = rint(q/s) in [-127, 127], so the term with the
                        * key code sums is zero).  The exact logits of the
                        * correction always use the fp16 query.              */
+  int32_t key_format; /* key codes: 0 = affine (s * code + z per group, k_bits
+                       * bits); 1 = MXFP4 (Jet-QSparse abstract: FP4 keys;
+                       * OCP Microscaling block format): each group of 32
+                       * shares a power-of-two scale 2^X, X = floor(log2
+                       * amax) - 2 (clamped at -24), stored as fp16 in the
+                       * meta word's low half (high half 0), and a code is
+                       * sign << 3 | the E2M1 magnitude index (0, 0.5, 1,
+                       * 1.5, 2, 3, 4, 6) of x / 2^X, nearest, ties to the
+                       * even index, clamped at 6.  Needs k_bits 4, group 32,
+                       * query_bits 0; the key bit layout is that of K4.    */
 } bkv_layout;
 
 /*

@@ -65,9 +65,10 @@ def build_pair(w: Workload, L: int, cap: int | None = None):
     cap = cap or ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1) if L > 1 else None
     k1, v1 = make_new_tokens(w, 1, inp.outlier_ch if inp else make_inputs(w, L=1).outlier_ch)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits,
+                         key_format=w.key_format)
     gc = bk.allocate_cache(lay)
-    oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, w.kbits, w.vbits, w.group, cap))
+    oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, w.kbits, w.vbits, w.group, cap, w.key_format))
     q = inp.q if inp else make_inputs(w, L=1).q
     if L > 1:
         bk.kv_pack_append(lay, gc, to_dev(inp.K), to_dev(inp.V), L - 1, [0] * w.B)

@@ -84,6 +84,12 @@ def test_unsupported_head_dim_and_group(bk):
     for qb, want in ((8, 0), (4, 3), (16, 3), (-1, 3)):  # query of the approximate scores: fp16 or INT8
         lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024, qb)
         assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == want, qb
+    # key format: MXFP4 needs 4-bit keys, groups of 32 and the fp16 query
+    for args, want in (((4, 32, 0, 1), 0), ((3, 32, 0, 1), 3), ((4, 64, 0, 1), 3), ((4, 32, 8, 1), 3),
+                       ((4, 32, 0, 2), 3)):
+        kb, g, qb, kf = args
+        lay = bk.Layout(4, 32, 8, 128, kb, 4, g, 1024, qb, kf)
+        assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == want, args
     assert bk.raw_status("bkv_workspace_bytes", None, 10, 4, C.byref(out)) == 1
     lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024)
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, -1, C.byref(out)) == 7

@@ -1,5 +1,5 @@
 """GPU parity at the full sizes of the five decode-attention workloads and the
-two low-bit codec workloads, in the launch configuration the benchmark times:
+low-bit codec workloads (1- and 2-bit keys, the INT8 query, MXFP4 keys), in the launch configuration the benchmark times:
 the whole batch runs on the GPU; the oracle recomputes sampled (batch, KV head)
 units one by one."""
 import numpy as np
@@ -33,7 +33,8 @@ def test_full_size_sampled_units(P, name):
     cap = ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1)
     kn, vn = make_new_tokens(w, 1, inp.outlier_ch)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits,
+                         key_format=w.key_format)
     gc = bk.allocate_cache(lay)
     bk.kv_pack_append(lay, gc, P.to_dev(inp.K), P.to_dev(inp.V), L - 1, [0] * w.B)
     st = DecodeStep(lay, w.k, L)
@@ -48,7 +49,7 @@ def test_full_size_sampled_units(P, name):
     for u in sorted({0, units - 1}):
         b, h = divmod(u, w.Hkv)
         print(f"[case] {w.name} unit {u}", flush=True)
-        oc = oracle.Cache(oracle.Shape(1, w.G, 1, 128, w.kbits, w.vbits, w.group, cap))
+        oc = oracle.Cache(oracle.Shape(1, w.G, 1, 128, w.kbits, w.vbits, w.group, cap, w.key_format))
         oc.append(inp.K[b:b + 1, h:h + 1], inp.V[b:b + 1, h:h + 1], np.zeros(1, np.int32))
         oc.append(kn[0][b:b + 1, h:h + 1], vn[0][b:b + 1, h:h + 1], np.array([L - 1], np.int32))
         for name, ob in P.orc_buffers(oc).items():

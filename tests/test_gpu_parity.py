@@ -710,3 +710,64 @@ def test_query_int8_decode_step_and_ends(P, kb, vb, G, g):
         torch.cuda.synchronize()
         ref = pair["oc"].decode(pair["q"], lens, k, want_approx=True, want_exact=True, qbits=8)
         P.assert_close(o2.cpu().numpy().reshape(w.B, w.Hq, 128), ref[key], f"k={k}")
+
+
+# MXFP4 keys (E2M1 codes, one power-of-two scale per group of 32): both value
+# widths and both GQA group sizes.
+MX_CASES = [(4, 4), (2, 8), (4, 8), (2, 4)]
+
+
+@pytest.mark.parametrize("vb,G", MX_CASES)
+def test_mxfp4_keys_step_parity(P, vb, G):
+    """Pack bit-exact, then scores, selection and output against the oracle
+    with MXFP4 keys."""
+    banner(f"mxfp4 keys vb={vb} G={G}")
+    import oracle
+    w = P.Workload("mx", 2, 2 * G, 2, 128, 1000, 4, vb, 32, 24, 6, 500 + vb + G, key_format=1)
+    pair = P.build_pair(w, L=1000, cap=1024)
+    lens = np.array([1000, 651])
+    k = 24
+    r = P.run_step(pair, lens, k)
+    g_buf, o_buf = P.gpu_buffers(pair["gc"]), P.orc_buffers(pair["oc"])
+    for name in g_buf:
+        assert np.array_equal(g_buf[name], o_buf[name]), name
+    orc = pair["oc"].decode(pair["q"], lens, k)
+    for b in range(w.B):
+        n = lens[b]
+        np.testing.assert_allclose(r["sigma"][b, :, :n], orc["sigma"][b, :, :n], rtol=1e-5, atol=2e-5)
+        for h in range(w.Hkv):
+            want = oracle.topk(r["sigma"][b, h, :n].astype(np.float64), k)
+            assert np.array_equal(r["idx"][b, h], want), (b, h)
+            P.assert_topk_near_tie(r["idx"][b, h], orc["idx"][b, h], orc["sigma"][b, h], n, f"b{b}h{h}")
+    orc_s = pair["oc"].decode(pair["q"], lens, k, sel=r["idx"])
+    P.assert_close(r["out"], orc_s["out"], "out vs oracle(S_gpu)")
+    P.assert_close(r["out"], orc["out"], "out vs oracle(S_oracle)")
+
+
+@pytest.mark.parametrize("vb,G", [(4, 4), (2, 8)])
+def test_mxfp4_keys_decode_step_and_ends(P, vb, G):
+    """The one-launch step (MXFP4 append inside the scan), then k = 0 (the
+    approximate output over the MXFP4 keys) and k = len (exact)."""
+    import torch
+    from bit_kv_attention_amd.step import DecodeStep
+    banner(f"mxfp4 keys step/ends vb={vb} G={G}")
+    w = P.Workload("mxs", 2, 2 * G, 2, 128, 900, 4, vb, 32, 16, 4, 600 + vb + G, key_format=1)
+    pair = P.build_pair(w, L=900, cap=928)
+    lens = np.array([900, 517])
+    pos = [int(x) - 1 for x in lens]
+    pair["oc"].append(pair["k1"], pair["v1"], np.array(pos, np.int32))
+    st = DecodeStep(pair["lay"], 16, 900)
+    out = st.step(pair["gc"], P.to_dev(pair["q"]), P.to_dev(pair["k1"]), P.to_dev(pair["v1"]), pos)
+    torch.cuda.synchronize()
+    g_buf, o_buf = P.gpu_buffers(pair["gc"]), P.orc_buffers(pair["oc"])
+    for name in g_buf:
+        assert np.array_equal(g_buf[name], o_buf[name]), name
+    got = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, 16)
+    P.assert_close(got, pair["oc"].decode(pair["q"], lens, 16, sel=idx)["out"], "step vs oracle(S_gpu)")
+    for k, key in ((0, "out_approx"), (900, "out_exact")):
+        st2 = DecodeStep(pair["lay"], k, 900)
+        o2 = st2.attend(pair["gc"], P.to_dev(pair["q"]), lens.tolist())
+        torch.cuda.synchronize()
+        ref = pair["oc"].decode(pair["q"], lens, k, want_approx=True, want_exact=True)
+        P.assert_close(o2.cpu().numpy().reshape(w.B, w.Hq, 128), ref[key], f"k={k}")
