@@ -695,13 +695,16 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     }
   };
 
-  // One whole step: prefetch the wave's next step into `nxt` (unconditionally
-  // -- the last step re-reads its own bytes -- so that the compiler's wait for
-  // this step's data counts those loads), then score and accumulate `cur`.
-  // The loop is unrolled twice so the two register sets alternate without
-  // copies (a copy of registers with loads in flight would wait for them).
+  // One whole step: prefetch the wave's step kAhead steps on into `nxt`
+  // (unconditionally -- past the end it re-reads this step's bytes -- so that
+  // the compiler's wait for this step's data counts those loads), then score
+  // and accumulate `cur`.  The loop is unrolled kAhead + 1 times so the
+  // register sets rotate without copies (a copy of registers with loads in
+  // flight would wait for them).  Scores only (keys only, small steps): two
+  // steps in flight; otherwise one (two measured slower there).
+  constexpr int kAhead = SIGONLY ? 2 : 1;
   auto full_step = [&](Step<KB, VB, G>& cur, Step<KB, VB, G>& nxt, int t0) {
-    const int tn = (t0 + kScanWaves * kTile) < t_end ? t0 + kScanWaves * kTile : t0;
+    const int tn = (t0 + kAhead * kScanWaves * kTile) < t_end ? t0 + kAhead * kScanWaves * kTile : t0;
     load_step<KB, VB, G, SIGONLY>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane, mshift);
     u32x4 km[2][NT], vm[NT][2];
     meta_cells(cur.meta, km, vm);
@@ -719,15 +722,36 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
-  Step<KB, VB, G> sa, sb;
+  Step<KB, VB, G> sa, sb, sc;
   int t0 = t_begin + kTile * wv;
-  if (t0 < t_end) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
+  if constexpr (kAhead == 1) {
+    if (t0 < t_end) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
+    for (;;) {
+      if (t0 + kTile > t_end) {
+        if (t0 < t_end) last_step(sa, t0);
+        break;
+      }
+      full_step(sa, sb, t0);
+      t0 += kScanWaves * kTile;
+      if (t0 + kTile > t_end) {
+        if (t0 < t_end) last_step(sb, t0);
+        break;
+      }
+      full_step(sb, sa, t0);
+      t0 += kScanWaves * kTile;
+    }
+  } else {
+  if (t0 < t_end) {
+    load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
+    const int t1 = (t0 + kScanWaves * kTile) < t_end ? t0 + kScanWaves * kTile : t0;
+    load_step<KB, VB, G, SIGONLY>(sb, kbase, vbase, kmeta, vmeta, cap, t1, lane, mshift);
+  }
   for (;;) {
     if (t0 + kTile > t_end) {
       if (t0 < t_end) last_step(sa, t0);
       break;
     }
-    full_step(sa, sb, t0);
+    full_step(sa, sc, t0);
     t0 += kScanWaves * kTile;
     if (t0 + kTile > t_end) {
       if (t0 < t_end) last_step(sb, t0);
@@ -735,6 +759,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     }
     full_step(sb, sa, t0);
     t0 += kScanWaves * kTile;
+    if (t0 + kTile > t_end) {
+      if (t0 < t_end) last_step(sc, t0);
+      break;
+    }
+    full_step(sc, sb, t0);
+    t0 += kScanWaves * kTile;
+  }
   }
   if (sig_count > 0) flush_sig();
 
