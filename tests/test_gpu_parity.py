@@ -340,16 +340,18 @@ def test_topk_window_on_given_scores(P, L, k, W):
         assert np.array_equal(st.idx.cpu().numpy().reshape(B, Hkv, k), idx)
 
 
-@pytest.mark.parametrize("kb,vb,G,W", [(4, 4, 4, 64), (3, 2, 8, 200)])
-def test_step_parity_window(P, kb, vb, G, W):
+@pytest.mark.parametrize("kb,vb,G,W,fmt", [(4, 4, 4, 64, ""), (3, 2, 8, 200, ""), (4, 4, 4, 64, "q8"),
+                                            (4, 2, 8, 100, "mx")])
+def test_step_parity_window(P, kb, vb, G, W, fmt):
     """A whole step with a recent window: the GPU's rows against the oracle's
     selection on the GPU's scores (exact), the output against the oracle on
     the GPU's rows and on its own."""
-    banner(f"step window kb={kb} vb={vb} G={G} W={W}")
+    banner(f"step window kb={kb} vb={vb} G={G} W={W} {fmt}")
+    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
     import torch
     import oracle
     from bit_kv_attention_amd.step import DecodeStep
-    w = P.Workload("win", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 500 + G + W)
+    w = P.Workload("win", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 500 + G + W, query_bits=qb, key_format=kf)
     pair = P.build_pair(w, L=3000, cap=3008)
     lens = np.array([3000, 1234, W // 3])
     k = 32
@@ -363,7 +365,7 @@ def test_step_parity_window(P, kb, vb, G, W):
     out = out.cpu().numpy().reshape(w.B, w.Hq, 128)
     sigma = st.sigma.cpu().numpy().reshape(w.B, w.Hkv, pair["cap"])
     idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, k + W)
-    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True)
+    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True, qbits=qb)
     sel_o = np.full_like(idx, -1)
     for b in range(w.B):
         n = lens[b]
@@ -374,9 +376,9 @@ def test_step_parity_window(P, kb, vb, G, W):
             sel_o[b, h] = oracle.topk_window(orc["sigma"][b, h, :n], k, W)
             kk = min(k, n - min(W, n))  # the selected part of the row
             P.assert_topk_near_tie(idx[b, h, :kk], sel_o[b, h, :kk], orc["sigma"][b, h], n - min(W, n), f"b{b}h{h}")
-    orc_s = pair["oc"].decode(pair["q"], lens, k + W, sel=idx)
+    orc_s = pair["oc"].decode(pair["q"], lens, k + W, sel=idx, qbits=qb)
     P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
-    orc_o = pair["oc"].decode(pair["q"], lens, k + W, sel=sel_o)
+    orc_o = pair["oc"].decode(pair["q"], lens, k + W, sel=sel_o, qbits=qb)
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
 
 
@@ -417,18 +419,20 @@ def test_topk_blocks_on_given_scores(P, L, nb, bs, ties):
                 assert np.array_equal(idx[b, h], want), (rep, b, h)
 
 
-@pytest.mark.parametrize("kb,vb,G,nb,bs", [(4, 4, 4, 6, 128), (3, 2, 8, 20, 32)])
-def test_step_parity_blocks(P, kb, vb, G, nb, bs):
+@pytest.mark.parametrize("kb,vb,G,nb,bs,fmt", [(4, 4, 4, 6, 128, ""), (3, 2, 8, 20, 32, ""),
+                                               (2, 2, 8, 10, 64, "q8"), (4, 4, 4, 6, 128, "mx")])
+def test_step_parity_blocks(P, kb, vb, G, nb, bs, fmt):
     """A whole step with block selection: the GPU's rows against the oracle's
     block selection on the GPU's scores (exact) and on its own (chosen blocks
     may differ only by near-ties of the block score), the output against the
     oracle on both rows."""
-    banner(f"step blocks kb={kb} vb={vb} G={G} nb={nb} bs={bs}")
+    banner(f"step blocks kb={kb} vb={vb} G={G} nb={nb} bs={bs} {fmt}")
+    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
     import torch
     import oracle
     from bit_kv_attention_amd import binding as bk
     from bit_kv_attention_amd.step import DecodeStep
-    w = P.Workload("blk", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 700 + G + nb)
+    w = P.Workload("blk", 3, 2 * G, 2, 128, 3000, kb, vb, 32, 32, 6, 700 + G + nb, query_bits=qb, key_format=kf)
     pair = P.build_pair(w, L=3000, cap=3008)
     lens = np.array([3000, 1234, 77])
     pos = [int(x) - 1 for x in lens]
@@ -440,7 +444,7 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs):
     out = out.cpu().numpy().reshape(w.B, w.Hq, 128)
     sigma = st.sigma.cpu().numpy().reshape(w.B, w.Hkv, pair["cap"])
     idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, nb * bs)
-    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True)
+    orc = pair["oc"].decode(pair["q"], lens, 0, want_approx=True, qbits=qb)
     sel_o = np.full_like(idx, -1)
     for b in range(w.B):
         n = lens[b]
@@ -454,9 +458,9 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs):
             kbk = min(nb, nblk)
             P.assert_topk_near_tie(idx[b, h, ::bs][:kbk] // bs, sel_o[b, h, ::bs][:kbk] // bs, bscore, nblk,
                                    f"b{b}h{h}")
-    orc_s = pair["oc"].decode(pair["q"], lens, nb * bs, sel=idx)
+    orc_s = pair["oc"].decode(pair["q"], lens, nb * bs, sel=idx, qbits=qb)
     P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
-    orc_o = pair["oc"].decode(pair["q"], lens, nb * bs, sel=sel_o)
+    orc_o = pair["oc"].decode(pair["q"], lens, nb * bs, sel=sel_o, qbits=qb)
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
 
 
@@ -497,23 +501,24 @@ def test_decode_select_equals_two_calls(P, kb, vb, G, g):
         assert np.array_equal(o1, o0), k
 
 
-@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
-def test_hybrid_host_correction(P, kb, vb, G):
+@pytest.mark.parametrize("kb,vb,G,fmt", [(4, 4, 4, ""), (3, 2, 8, ""), (3, 4, 4, "q8"), (4, 2, 8, "mx")])
+def test_hybrid_host_correction(P, kb, vb, G, fmt):
     """The exact half of the correction on the host (qattn_exact_host over a
     pinned host shadow) merged on the GPU (qattn_correct_hybrid): output
     against the oracle on the GPU's rows, and against the all-GPU correction;
     ragged and empty sequences, k >= len, k = 0."""
-    banner(f"hybrid host correction kb={kb} vb={vb} G={G}")
+    banner(f"hybrid host correction kb={kb} vb={vb} G={G} {fmt}")
+    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
     import torch
     from bit_kv_attention_amd import binding as bk
     from bit_kv_attention_amd.step import DecodeStep
     w = P.Workload("hyb", 3, 2 * G, 2, 128, 2000, kb, vb, 32, 48, 6, 1200 + G)
     inp = P.make_inputs(w, L=1999)
-    lay = bk.make_layout(w.B, w.Hq, w.Hkv, 2016, kb, vb)
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, 2016, kb, vb, query_bits=qb, key_format=kf)
     hc = bk.allocate_cache(lay, shadow_on_host=True)
     bk.kv_pack_append(lay, hc, P.to_dev(inp.K), P.to_dev(inp.V), 1999, [0] * w.B)
     import oracle
-    oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, kb, vb, 32, 2016))
+    oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, kb, vb, 32, 2016, kf))
     oc.append(inp.K, inp.V, np.zeros(w.B, np.int32))
     lens = np.array([1999, 777, 0])
     q = P.to_dev(inp.q)
@@ -526,7 +531,7 @@ def test_hybrid_host_correction(P, kb, vb, G):
         torch.cuda.synchronize()
         oh = out_h.cpu().numpy().reshape(w.B, w.Hq, 128)
         og = out_g.cpu().numpy().reshape(w.B, w.Hq, 128)
-        orc = oc.decode(inp.q, lens, k, sel=idx if k > 0 else None)
+        orc = oc.decode(inp.q, lens, k, sel=idx if k > 0 else None, qbits=qb)
         P.assert_close(oh, orc["out"], f"hybrid vs oracle k={k}")
         np.testing.assert_allclose(oh, og, rtol=1e-4, atol=1e-5)
 
