@@ -12,7 +12,8 @@
  * parameters").  Top-k is taken per KV head (Jet-QSparse abstract: the
  * selection budget is per KV head).
  *
- * One decode step is four calls on one stream:
+ * A decode step is a few of these calls on one stream (the plainest: append,
+ * approximate pass, top-k, correction):
  *   kv_pack_append       quantise + pack the new token(s), write the shadow
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
  *   qattn_decode_select  the same and topk_select, in one launch where it fits
@@ -45,8 +46,9 @@
  *    a failed launch (hipGetLastError) of one of the call's kernels.
  *  - Supported shapes: head_dim 128, group 32 or 64, k_bits in {1, 2, 3, 4},
  *    v_bits in {2, 4}, n_q_heads / n_kv_heads in {4, 8}, capacity a positive
- *    multiple of 32, batch in [1, 256].  Others return BKV_E_UNSUPPORTED or
- *    BKV_E_SHAPE.
+ *    multiple of 32, batch in [1, 256], query_bits 0 or 8, key_format 0 or 1
+ *    (MXFP4: k_bits 4, group 32, query_bits 0).  Others return
+ *    BKV_E_UNSUPPORTED or BKV_E_SHAPE.
  *  - Query head h attends with KV head h / (n_q_heads / n_kv_heads).
  *  - Softmax scale 1/sqrt(head_dim); no mask inside the cached tokens.
  *  - Inputs must be finite fp16 values.
