@@ -54,17 +54,26 @@ constexpr int kRecBatch = 16;
 
 // Records j0..j0+kRecBatch-1 of a set (max m[j*sm], denominator l[j*sm],
 // value v[j*sv]); past cnt they are empty.  Loads are clamped and
-// unconditional so that a whole batch is in flight at once.
+// unconditional so that a whole batch is in flight at once.  The batch's
+// maxima and denominators, the same for every lane, arrive as one vector
+// load each (lane i % kRecBatch takes record j0 + i % kRecBatch) and are
+// read out of those lanes: as scalar loads they were 2 * kRecBatch loads
+// per set that the scalar unit's few outstanding requests serialise.
 struct RecBatch {
   float m[kRecBatch], l[kRecBatch], v[kRecBatch];
   __device__ void load(const float* __restrict__ pm_, const float* __restrict__ pl_, const float* __restrict__ pv,
                        size_t sm, size_t sv, int cnt, int j0) {
+    const size_t jl = (size_t)max(min(j0 + (int)(__builtin_amdgcn_workitem_id_x() % kRecBatch), cnt - 1), 0);
+    const float mv = pm_[jl * sm], lv = pl_[jl * sm];
 #pragma unroll
     for (int i = 0; i < kRecBatch; ++i) {
       const size_t j = (size_t)max(min(j0 + i, cnt - 1), 0);
-      m[i] = pm_[j * sm];
-      l[i] = pl_[j * sm];
       v[i] = pv[j * sv];
+    }
+#pragma unroll
+    for (int i = 0; i < kRecBatch; ++i) {
+      m[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), i));
+      l[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), i));
     }
 #pragma unroll
     for (int i = 0; i < kRecBatch; ++i) {
