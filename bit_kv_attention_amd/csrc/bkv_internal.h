@@ -100,7 +100,7 @@ constexpr int kStateFloats = 2 + kHeadDim;  // one exact state {m, l, a[0..D)}
 // kTopkMergeMax; otherwise S = 0 selects the single-workgroup kernel.
 constexpr int kTopkSliceMax = 8192;
 constexpr int kTopkSliceMin = 2048;
-constexpr int kTopkGridMin = 256;
+constexpr int kTopkGridMin = 128;
 constexpr int kTopkMergeMax = 16384;
 constexpr int kTopkBlocksMax = 8192;  // blocks per unit for block selection (ceil(capacity / block))
 constexpr int kTopkBlockSpan = 8192;  // tokens per workgroup of the block maxima
