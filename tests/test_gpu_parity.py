@@ -464,18 +464,22 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs, fmt):
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
 
 
-@pytest.mark.parametrize("kb,vb,G,g", [c + (32,) for c in COMBOS] + [(2, 2, 4, 64), (1, 2, 8, 64)])
-def test_decode_select_equals_two_calls(P, kb, vb, G, g):
+@pytest.mark.parametrize("kb,vb,G,g,fmt", [c + (32, "") for c in COMBOS] + [(2, 2, 4, 64, ""), (1, 2, 8, 64, ""),
+                                            (4, 4, 4, 32, "q8"), (2, 2, 8, 64, "q8"),
+                                            (4, 2, 4, 32, "mx"), (4, 4, 8, 32, "mx")])
+def test_decode_select_equals_two_calls(P, kb, vb, G, g, fmt):
     """qattn_decode_select (selection inside the scan's launch) against
     qattn_decode_approx + topk_select on the same inputs: identical sigma, rows
     and output, rows exact against the oracle's top-k of that sigma; ragged and
     empty sequences, k = 1, k >= len, and a budget past the in-launch limit
     (two launches)."""
-    banner(f"decode_select kb={kb} vb={vb} G={G} g={g}")
+    banner(f"decode_select kb={kb} vb={vb} G={G} g={g} {fmt}")
+    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
     import torch
     import oracle
     from bit_kv_attention_amd.step import DecodeStep
-    w = P.Workload("sel", 4, 2 * G, 2, 128, 4000, kb, vb, g, 32, 6, 900 + 10 * kb + vb + G)
+    w = P.Workload("sel", 4, 2 * G, 2, 128, 4000, kb, vb, g, 32, 6, 900 + 10 * kb + vb + G, query_bits=qb,
+                   key_format=kf)
     pair = P.build_pair(w, L=4000, cap=4000)
     lens = np.array([3999, 2500, 1, 0])  # (the prefill filled 3999 slots)
     q = P.to_dev(pair["q"])
@@ -499,6 +503,11 @@ def test_decode_select_equals_two_calls(P, kb, vb, G, g):
                 assert np.array_equal(i1[b, h], want), (k, b, h)
         assert np.array_equal(i1, i0), k
         assert np.array_equal(o1, o0), k
+        if fmt and k == 37:  # the in-launch scores are the codec's own
+            orc = pair["oc"].decode(pair["q"], lens, k, qbits=qb)
+            for b in range(w.B):
+                n = lens[b]
+                np.testing.assert_allclose(s1[b, :, :n], orc["sigma"][b, :, :n], rtol=1e-5, atol=2e-5)
 
 
 @pytest.mark.parametrize("kb,vb,G,fmt", [(4, 4, 4, ""), (3, 2, 8, ""), (3, 4, 4, "q8"), (4, 2, 8, "mx")])
