@@ -50,7 +50,7 @@ struct Online {
   __device__ float scale_to(float ref) const { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - ref); }
 };
 
-constexpr int kRecBatch = 16;
+constexpr int kRecBatchMax = 16;  // records per batch: 16, or 8 when every list fits 8
 
 // Records j0..j0+kRecBatch-1 of a set (max m[j*sm], denominator l[j*sm],
 // value v[j*sv]); past cnt they are empty.  Loads are clamped and
@@ -59,6 +59,7 @@ constexpr int kRecBatch = 16;
 // load each (lane i % kRecBatch takes record j0 + i % kRecBatch) and are
 // read out of those lanes: as scalar loads they were 2 * kRecBatch loads
 // per set that the scalar unit's few outstanding requests serialise.
+template <int kRecBatch>
 struct RecBatch {
   float m[kRecBatch], l[kRecBatch], v[kRecBatch];
   __device__ void load(const float* __restrict__ pm_, const float* __restrict__ pl_, const float* __restrict__ pv,
@@ -95,7 +96,7 @@ struct RecBatch {
 // null): the exact state of the selected tokens per (b, query head),
 // {m, l, a[0..D)}, in place of the chunk records' exact parts.
 // (One group when every list fits one batch: no barrier, no LDS.)
-template <int kCombineGroups>
+template <int kCombineGroups, int kRecBatch = kRecBatchMax>
 __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(const float* __restrict__ pm, const float* __restrict__ pl,
                                                            const float* __restrict__ pacc, const float* __restrict__ cs,
                                                            const float* __restrict__ hx, float* __restrict__ out,
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
     ex.add(x[0], x[1], x[2 + c]);
   }
   for (int j0 = grp * kRecBatch; j0 < max(nc, nap); j0 += kCombineGroups * kRecBatch) {
-    RecBatch be, ba, bs;
+    RecBatch<kRecBatch> be, ba, bs;
     be.load(ps, ps + 1, ps + 4 + c, kCsStride, kCsStride, nex, j0);
     ba.load(pm + rec * nsplit, pl + rec * nsplit, pacc + rec * nsplit * kHeadDim + c, 1, kHeadDim, nap, j0);
     bs.load(ps + 2, ps + 3, ps + 4 + kHeadDim + c, kCsStride, kCsStride, nsel, j0);
@@ -505,7 +506,11 @@ hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_
       default: v4 ? launch_g<1, 4>(L, c, q, len, idx, k, w, t, s) : launch_g<1, 2>(L, c, q, len, idx, k, w, t, s);
     }
   }
-  if (w.nchunk <= kRecBatch && w.nsplit <= kRecBatch)  // every record list fits one batch
+  if (w.nchunk <= 8 && w.nsplit <= 8)  // every record list fits one batch of 8
+    combine_kernel<1, 8><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
+                                                                        len, L.n_q_heads, w.nsplit, w.nchunk, k,
+                                                                        rest ? 1 : 0);
+  else if (w.nchunk <= kRecBatchMax && w.nsplit <= kRecBatchMax)  // every record list fits one batch
     combine_kernel<1><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
                                                                      len, L.n_q_heads, w.nsplit, w.nchunk, k,
                                                                      rest ? 1 : 0);
