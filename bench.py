@@ -73,7 +73,7 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the method shards by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the method shards by "
               "KV head or by context length without changing the kernels); run with --gpus 1.",
               file=sys.stderr)
         return 2
