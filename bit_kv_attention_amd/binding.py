@@ -71,6 +71,8 @@ _lib.qattn_decode_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.
 _lib.qattn_correct_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 _lib.qattn_correct_hybrid.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P, _P]
 _lib.qattn_exact_host.argtypes = [_LP, _P, _P, _P, _P, _P, C.c_int32, _P, C.c_int32]
+_lib.qattn_decode_fused.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]
+_lib.bkv_fused_supported.argtypes = [_LP, C.c_int32, C.c_int32, _P]
 for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append", "qattn_decode_approx",
            "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
@@ -78,7 +80,8 @@ for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_p
 EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
             "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
-            "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step")
+            "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step", "qattn_decode_fused",
+            "bkv_fused_supported")
 
 
 def _check(fn: str, st: int) -> None:
@@ -193,6 +196,23 @@ def qattn_decode_step(layout: Layout, cache: Cache, k_new, v_new, q, len_host, k
     _check("qattn_decode_step", _lib.qattn_decode_step(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new),
                                                        _ptr(q), lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
                                                        _ptr(ws), ws_bytes, int(mode), _stream(stream)))
+
+
+def qattn_decode_fused(layout: Layout, cache: Cache, k_new, v_new, q, len_host, k: int, sigma, idx, out, ws,
+                       stream=None) -> None:
+    """The whole step in one launch; k_new = v_new = None: no append."""
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_decode_fused", _lib.qattn_decode_fused(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new),
+                                                         _ptr(q), lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx),
+                                                         _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def bkv_fused_supported(layout: Layout, max_len: int, k: int) -> bool:
+    out = C.c_int32()
+    _check("bkv_fused_supported", _lib.bkv_fused_supported(C.byref(layout), int(max_len), int(k), C.byref(out)))
+    return bool(out.value)
 
 
 def bkv_select_in_scan(layout: Layout, max_len: int, k: int, mode: int = SELECT_AUTO) -> bool:

@@ -74,7 +74,16 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
     off = align256(off + bytes);
     return p;
   };
+  // Regions that must stay zero between calls come first, at offsets that
+  // depend on the layout only (a later call with other lengths finds them in
+  // place): the top-k arrival counters, the fused step's counters and flag
+  // word, and its per-unit score histograms.
   w.tkctr = reinterpret_cast<uint32_t*>(take((size_t)units * 4));
+  const bool fusable = units <= kFMaxUnits;
+  w.fused = FusedArgs{};
+  w.fused.ctr = reinterpret_cast<uint32_t*>(take((size_t)units * 3 * 4 + 4));
+  if (w.fused.ctr) w.fused.flag = w.fused.ctr + (size_t)units * 3;
+  if (fusable) w.fused.hist = reinterpret_cast<uint32_t*>(take((size_t)units * kFBins * 4));
   const size_t recs = (size_t)L.batch * L.n_q_heads * w.nsplit;
   w.part.acc = reinterpret_cast<float*>(take(recs * kHeadDim * 4));
   w.part.m = reinterpret_cast<float*>(take(recs * 4));
@@ -92,6 +101,17 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
   // block selection: one key per block of at least 32 tokens
   w.bkstride = (max_len + 31) / 32;
   w.bkeys = reinterpret_cast<uint32_t*>(take((size_t)units * w.bkstride * 4));
+  if (fusable) {  // the fused step's per-split counts and threshold-bin lists
+    w.fused.dcnt = reinterpret_cast<uint32_t*>(take((size_t)units * w.nsplit * 4));
+    w.fused.scnt = reinterpret_cast<uint32_t*>(take((size_t)units * w.nsplit * 4));
+    // one slot per token of each split: nsplit * split length < length + split
+    // length (split length nondecreasing in the length), and the fused step
+    // takes splits of at most kSelStage tokens
+    const int chunk = split_tokens(units, max_len);
+    const size_t per_unit = bound ? (size_t)max_len + (chunk < kSelStage ? chunk : kSelStage)
+                                  : (chunk <= kSelStage ? (size_t)w.nsplit * chunk : 0);
+    w.fused.dlist = reinterpret_cast<uint64_t*>(take((size_t)units * per_unit * 8));
+  }
   w.bytes = off;
   return w;
 }
@@ -359,6 +379,54 @@ bkv_status qattn_decode_step(const bkv_layout* L, const bkv_cache* c, const uint
     return BKV_E_HIP;
   if (k == 0) return BKV_OK;
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
+}
+
+// Whether the fused step can run this call: a plain layout (fp16 query,
+// affine keys of 3 or 4 bits), splits that fit the LDS stage, the per-split
+// lists and the unit barriers' limits.
+static bool fused_shape_ok(const bkv_layout* L, const Workspace& w, int chunk, int k) {
+  const int units = L->batch * L->n_kv_heads;
+  if (L->query_bits != 0 || L->key_format != 0 || L->k_bits < 3) return false;
+  if (units > kFMaxUnits || w.nsplit > kFMaxSplits || chunk > kSelStage) return false;
+  return (long long)w.nsplit * k <= kSelSlots;
+}
+
+bkv_status bkv_fused_supported(const bkv_layout* L, int32_t max_len, int32_t k, int32_t* supported) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!supported) return BKV_E_NULL;
+  if (max_len < 0 || max_len > L->capacity) return BKV_E_CAPACITY;
+  if (k < 0) return BKV_E_ARG;
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(nullptr, *L, max_len, k, false);
+  *supported = fused_shape_ok(L, w, split_tokens(units, max_len), k) ? 1 : 0;
+  return BKV_OK;
+}
+
+bkv_status qattn_decode_fused(const bkv_layout* L, const bkv_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                              const uint16_t* q, const int32_t* len_host, int32_t k, float* sigma, int32_t* idx,
+                              float* out, void* ws, size_t ws_bytes, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return BKV_E_NULL;
+  if (!q || !sigma || !out || !ws || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  if (k_new)
+    for (int b = 0; b < L->batch; ++b)
+      if (len.v[b] < 1) return BKV_E_CAPACITY;  // the new token goes to len - 1
+  const int units = L->batch * L->n_kv_heads;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  const int chunk = split_tokens(units, max_len);
+  if (!fused_shape_ok(L, w, chunk, k)) return BKV_E_UNSUPPORTED;
+  const hipError_t e = launch_decode_fused(*L, *c, q, len, sigma, w, chunk, idx, k, k_new, v_new, out,
+                                           (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BKV_E_UNSUPPORTED;
+  return e == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
 
 bkv_status qattn_score_select(const bkv_layout* L, const bkv_cache* c, const uint16_t* q, const int32_t* len_host,

@@ -111,6 +111,31 @@ constexpr int kSelSlots = 8192;
 constexpr int kSelMinRange = 8192;  // automatic mode: shorter ranges take two launches
 int topk_slice(int units, int max_len, int k);
 
+// The fused step (qattn_decode_fused): scan, selection, correction and output
+// in one launch.  Its selection histograms the selection scores into
+// kFBins bins of the top kFBinBits bits of their order-preserving keys (sign,
+// exponent and 4 mantissa bits), per split in LDS and per unit in the
+// workspace; the threshold bin's entries meet in per-split lists in the
+// workspace (ranked in LDS when at most kFDList).  At most kFMaxSplits splits
+// per unit and kFMaxUnits units.
+constexpr int kFBinBits = 13;
+constexpr int kFBins = 1 << kFBinBits;
+constexpr int kFDList = 4096;
+constexpr int kFMaxSplits = 64;
+constexpr int kFMaxUnits = 256;
+constexpr int kFPass = 64;  // selected tokens per correction pass of the fused tail
+
+// Workspace pointers of the fused step (all zero for the other launches).
+struct FusedArgs {
+  float* out;      // [B][Hq][D] the corrected output
+  uint32_t* ctr;   // [U][3] arrival counters (zero between calls)
+  uint32_t* hist;  // [U][kFBins] score histogram per unit (zero between calls)
+  uint64_t* dlist; // [U][nsplit][split length] threshold-bin composites
+  uint32_t* dcnt;  // [U][nsplit] threshold-bin entries per split
+  uint32_t* scnt;  // [U][nsplit] selected tokens per split
+  uint32_t* flag;  // bit 0: a unit barrier gave up waiting (never expected)
+};
+
 struct Workspace {
   Partials part;
   float* cs;  // [B][Hq][nchunk][kCsStride]
@@ -118,6 +143,7 @@ struct Workspace {
   uint32_t* bkeys;  // [U][bkstride] block-selection keys
   int bkstride;
   uint32_t* tkctr;  // [U] arrivals of the top-k slice workgroups (zero between calls)
+  FusedArgs fused;  // (out left null; null regions when the units exceed kFMaxUnits)
   int nsplit;
   int nchunk;
   size_t bytes;  // total bytes this step needs
@@ -145,6 +171,13 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s);
+// The fused step: (append,) scan, top-ksel and correction into out, one
+// launch whose workgroups of a unit meet at barriers.  hipErrorNotSupported
+// when the layout has no fused kernel or the grid does not fit the device at
+// once (nothing launched).
+hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                               float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
+                               const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s);
 // The same with the INT8 query (layouts with query_bits = 8) and with MXFP4
 // keys (key_format = 1); launch_decode_approx forwards those layouts here.
 hipError_t launch_decode_approx_q8(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,

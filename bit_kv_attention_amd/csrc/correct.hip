@@ -24,6 +24,7 @@
 //           record independent of the others, batched), then the formula
 //           above.
 #include "bkv_internal.h"
+#include "correct_lane.h"
 #include "quant_lane.h"
 
 namespace bkv {
@@ -32,8 +33,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ inline float h2f(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
 
 // Running softmax state: max m (log2 units), scaled sums a and l.
 struct Online {
@@ -272,110 +271,31 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   const int tl = tid >> 3;
   const int part = tid & 7;
   const int t_sel = s_t[tl];
-  const int c0 = 16 * part;
-  uint4 k0, k1;
-  uint32_t kraw[2][2];
-  uint32_t kmw;
-  {
-    const int t = max(t_sel, 0);
-    if constexpr (EX) {
-      const uint4* kr = reinterpret_cast<const uint4*>(ksh + (size_t)t * kHeadDim + c0);
-      k0 = kr[0];
-      k1 = kr[1];
-    } else {
-      k0 = k1 = (uint4){0u, 0u, 0u, 0u};
-    }
-    // channels c0..c0+15 are the group-(part/2) fields of the chunks of
-    // eighths 2*(part%2) and 2*(part%2)+1 (8*KB bits each)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const uint32_t* ch = reinterpret_cast<const uint32_t*>(kbase + k_chunk_offset(KB, t, 2 * (part & 1) + x));
-      const int d0 = (8 * KB * (part >> 1)) >> 5, d1 = min(d0 + 1, KB - 1);
-      kraw[x][0] = AP ? ch[d0] : 0u;
-      kraw[x][1] = AP ? ch[d1] : 0u;
-    }
-    kmw = AP ? kmeta[(size_t)((c0 / kGroup) >> mshift) * cap + t] : 0u;
-  }
+  KeyRun<KB, EX, AP> kr;
+  kr.load(ksh, kbase, kmeta, cap, max(t_sel, 0), part, mshift);
   // value loads: one thread per (channel, half of the chunk)
   const int c = tid & (kHeadDim - 1);
   const int half = tid >> 7;
   constexpr int kHalf = kCorrChunk / 2;
   uint16_t vx16[kHalf];
-  uint32_t vcode[kHalf], vmw[kHalf];
+  ValueCode<VB> vcd[kHalf];
 #pragma unroll
   for (int j = 0; j < kHalf; ++j) {
     const int t = max(s_t[half * kHalf + j], 0);
-    int dw, bit;
-    v_code_pos(VB, t % kTile, c, dw, bit);
-    const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + (size_t)(t / kTile) * v_tile_bytes(VB));
-    vcode[j] = AP ? vt[dw] : 0u;  // raw: shifted at use, after the loads have landed
-    vmw[j] = AP ? vmeta[(size_t)((c / kGroup) >> mshift) * cap + t] : 0u;
+    if constexpr (AP) vcd[j].load(vbase, vmeta, cap, t, c, mshift);
     vx16[j] = EX ? vsh[(size_t)t * kHeadDim + c] : (uint16_t)0;
   }
 
   __builtin_amdgcn_sched_barrier(0);  // keep every load above ahead of the math below
 
-  // ---- logits: 8 threads per token, 16 channels each ------------------------
-  // fp16 pairs through v_dot2_f32_f16 (exact products, fp32 sums): the exact
-  // key pairs, and for the approximate logit the codes as exact fp16
-  // integers, whose dot product with q takes the group's scale once, plus
-  // zero x (sum of q over the run) -- the scan's own form of the score.
+  // ---- logits: 8 threads per token, 16 channels each (correct_lane.h) -------
   {
     float ex[G], ap[G];
-    {
-      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-      const int sh = (8 * KB * (part >> 1)) & 31;
-      uint32_t fld[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) fld[x] = (uint32_t)((((uint64_t)kraw[x][1] << 32) | kraw[x][0]) >> sh);
-      const uint64_t bits = ((uint64_t)fld[0] & ((1ull << (8 * KB)) - 1)) | ((uint64_t)fld[1] << (8 * KB));
-      constexpr uint32_t M = (1u << KB) - 1;
-      const half2_t k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-      half2_t cp[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t lo = (uint32_t)(bits >> (KB * 2 * i)) & M, hi = (uint32_t)(bits >> (KB * (2 * i + 1))) & M;
-        if constexpr (MX)  // the fp16 pattern of the E2M1 value * 2^-14 (exact)
-          cp[i] = __builtin_bit_cast(half2_t, ((lo & 7u) << 9) | ((lo & 8u) << 12) | ((hi & 7u) << 25) | ((hi & 8u) << 28));
-        else
-          cp[i] = __builtin_bit_cast(half2_t, lo | (hi << 16) | 0x64006400u) - k1024;
-      }
-      const float s = h2f((uint16_t)(kmw & 0xFFFFu)) * (MX ? 16384.0f : 1.0f), z = h2f((uint16_t)(kmw >> 16));
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint4 qa = s_qh[h][2 * part], qb = s_qh[h][2 * part + 1];
-        const uint32_t qw[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-        uint32_t qw8[8];
-        if constexpr (Q8) {  // q' as exact fp16 integers: q' . code is an exact integer sum
-          const uint4 ra = s_q8h[h][2 * part], rb = s_q8h[h][2 * part + 1];
-          const uint32_t r8[8] = {ra.x, ra.y, ra.z, ra.w, rb.x, rb.y, rb.z, rb.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) qw8[i] = r8[i];
-        }
-        float e = 0.f, d = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const half2_t qq = __builtin_bit_cast(half2_t, qw[i]);
-          if constexpr (EX) e = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, kw[i]), qq, e, false);
-          if constexpr (AP) d = __builtin_amdgcn_fdot2(cp[i], Q8 ? __builtin_bit_cast(half2_t, qw8[i]) : qq, d, false);
-        }
-        ex[h] = e;
-        if constexpr (Q8)
-          ap[h] = AP ? fmaf(s, d * s_q8c[h][part], z * s_q8s[h][part]) : 0.f;
-        else
-          ap[h] = AP ? fmaf(s, d, z * s_qs[h][part]) : 0.f;
-      }
-    }
-    // sum over the token's 8 threads (lanes 8m..8m+7): quads by DPP, then the
-    // other quad (row_ror:12 brings lane l+4 to lanes 0 and 8 of each row)
+    run_logits<KB, G, EX, AP, Q8, MX>(kr, part, s_qh, s_qs, s_q8h, s_q8s, s_q8c, ex, ap);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0xB1, 0xF, 0xF, true));
-      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0xB1, 0xF, 0xF, true));
-      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0x4E, 0xF, 0xF, true));
-      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0x4E, 0xF, 0xF, true));
-      ex[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ex[h]), 0x12C, 0xF, 0xF, true));
-      ap[h] += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ap[h]), 0x12C, 0xF, 0xF, true));
+      ex[h] = sum8(ex[h]);
+      ap[h] = sum8(ap[h]);
     }
     if (part == 0) {
 #pragma unroll
@@ -411,10 +331,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   for (int j = 0; j < kHalf; ++j) {
     const int tl = half * kHalf + j;
     const float vx = h2f(vx16[j]);
-    int dw, bit;
-    v_code_pos(VB, max(s_t[tl], 0) % kTile, c, dw, bit);
-    const float vq = fmaf(h2f((uint16_t)(vmw[j] & 0xFFFFu)), (float)((vcode[j] >> bit) & ((1u << VB) - 1)),
-                          h2f((uint16_t)(vmw[j] >> 16)));
+    const float vq = AP ? vcd[j].value(max(s_t[tl], 0), c) : 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       if constexpr (EX) ea[h] = fmaf(s_w[0][tl][h], vx, ea[h]);

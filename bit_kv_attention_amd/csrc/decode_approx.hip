@@ -58,6 +58,7 @@
 // and the 2^14 is folded into the constants that turn scores into sigma and
 // log2 units.
 #include "bkv_internal.h"
+#include "fused_tail.h"
 #include "quant_lane.h"
 #include "select_lds.h"
 
@@ -476,14 +477,18 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // position len - 1 (what kv_pack_append does for one token): the workgroup
 // whose split holds that position does it before its scan reads the cache.
 // (The cache pointers carry no __restrict__: this launch writes through them.)
-template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false, bool APPEND = false>
+// FUSE: the fused step -- after the scan the same launch selects the unit's
+// top-ksel tokens and corrects them into fa.out (fused_tail.h); every
+// workgroup of the grid must be resident at once.
+template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false, bool APPEND = false,
+          bool FUSE = false>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERNEL(
     const uint8_t* k_codes, const uint8_t* v_codes, const uint32_t* k_meta, const uint32_t* v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel, int mshift,
     uint16_t* k_shadow, uint16_t* v_shadow, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new) {
+    const uint16_t* __restrict__ v_new, FusedArgs fa) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -505,14 +510,19 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   const uint32_t* kmeta = k_meta + (size_t)u * meta_planes(mshift) * cap;
   const uint32_t* vmeta = v_meta + (size_t)u * meta_planes(mshift) * cap;
 
+  // FUSE: the split's histogram of selection scores (fused_tail.h)
+  __shared__ uint32_t s_fh[FUSE ? kFBins : 1];
+
   // ---- query operands, staged through LDS ------------------------------------
-  __shared__ uint16_t s_q[G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G][kHeadDim];
   __shared__ float s_qsum[G][kGroups];   // per quarter: sum of q (INT8: s * sum of q')
   __shared__ int8_t s_q8[kQ8 ? G : 1][kHeadDim];  // INT8: the codes q'
   __shared__ float s_qsc[kQ8 ? G : 1][kGroups];   // INT8: the scale s of each quarter's group
   {
     const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
     if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
+    if constexpr (FUSE)  // the split's score histogram starts empty
+      for (int i = tid; i < kFBins; i += 64 * kScanWaves) s_fh[i] = 0u;
     __syncthreads();
     if constexpr (kQ8) {
       // one entry per thread, whole waves: a wave holds 64 channels of one head,
@@ -661,8 +671,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   // Selection scores go through a per-wave LDS buffer of kSigBatch steps and
   // leave as one coalesced 16-byte-per-lane store (no stores in the steps).
   __shared__ floatx4 s_sig[kScanWaves][kSigBatch][8];
-  // SEL: the split's selection scores, as stored ([t - t_begin])
-  __shared__ __attribute__((aligned(16))) float s_split[SEL ? kSelStage : 1];
+  // SEL, FUSE: the split's selection scores, as stored ([t - t_begin])
+  __shared__ __attribute__((aligned(16))) float s_split[(SEL || FUSE) ? kSelStage : 1];
   int sig_count = 0;   // steps staged
   int sig_first = 0;   // t0 of the first staged step
   auto flush_sig = [&]() {
@@ -672,7 +682,12 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
       const int t = sig_first + kScanWaves * kTile * i + 4 * (lane & 7);
       const floatx4 v = s_sig[wv][i][lane & 7] * c_sig;
       if constexpr (!SKIP) *reinterpret_cast<floatx4*>(sig + t) = v;
-      if constexpr (SEL) *reinterpret_cast<floatx4*>(&s_split[t - t_begin]) = v;
+      if constexpr (SEL || FUSE) *reinterpret_cast<floatx4*>(&s_split[t - t_begin]) = v;
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (t + x < t_end) atomicAdd(&s_fh[fbin(v[x])], 1u);
+      }
     }
     wave_lds_order();
     sig_count = 0;
@@ -809,7 +824,11 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   }
   __syncthreads();
 
-  for (int e = tid; e < G * kHeadDim; e += 64 * kScanWaves) {
+  constexpr int NR = G * kHeadDim / (64 * kScanWaves);  // (head, channel) pairs per thread
+  float rm[NR], rl[NR], ra[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int e = tid + 64 * kScanWaves * r;
     const int hh = e / kHeadDim;
     const int c = e - hh * kHeadDim;
     float M = s_m[0][hh];
@@ -824,12 +843,55 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
         l += f * s_l[x][hh];
       }
     }
-    const size_t rec = ((size_t)b * Hq + (size_t)kvh * G + hh) * nsplit + split;
-    pacc[rec * kHeadDim + c] = a;
-    if (c == 0) {
-      pm[rec] = M;
-      pl[rec] = l;
+    if constexpr (FUSE) {
+      rm[r] = M;
+      rl[r] = l;
+      ra[r] = a;
+    } else {
+      const size_t rec = ((size_t)b * Hq + (size_t)kvh * G + hh) * nsplit + split;
+      pacc[rec * kHeadDim + c] = a;
+      if (c == 0) {
+        pm[rec] = M;
+        pl[rec] = l;
+      }
     }
+  }
+  if constexpr (FUSE) {
+    FusedCtx<G> x;
+    x.tid = tid;
+    x.u = u;
+    x.b = b;
+    x.kvh = kvh;
+    x.split = split;
+    x.len = len;
+    x.t_begin = t_begin;
+    x.t_end = t_end;
+    x.nsplit = nsplit;
+    x.chunk = chunk;
+    x.ksel = ksel;
+    x.cap = cap;
+    x.mshift = mshift;
+    x.Hq = Hq;
+    x.kbase = kbase;
+    x.vbase = vbase;
+    x.kmeta = kmeta;
+    x.vmeta = vmeta;
+    x.ksh = k_shadow + (size_t)u * cap * kHeadDim;
+    x.vsh = v_shadow + (size_t)u * cap * kHeadDim;
+    x.pm = pm;
+    x.pl = pl;
+    x.pacc = pacc;
+    x.tkc = cand;
+    x.idx = idx;
+    x.fa = fa;
+    x.s_q = s_q;
+    x.s_split = s_split;
+    x.s_fh = s_fh;
+    x.s_acc = &s_acc[0][0][0];
+    x.s_lg = reinterpret_cast<float*>(&s_meta[0][0]);
+    x.s_w = reinterpret_cast<float*>(&s_sig[0][0][0]);
+    fused_tail<KB, VB, G>(x, rm, rl, ra);
+    return;
   }
   }  // !SIGONLY
 
@@ -873,11 +935,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
         if (sel[j]) st_dev64(&dst[at[j]], c[j]);
       for (int j = cnt + tid; j < ksel; j += NT) st_dev64(&dst[j], 0ull);  // the split's unused slots
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's candidates are written
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == (uint32_t)nsplit - 1);
-    __syncthreads();
-    if (!s_last) return;
+    if (!arrive_is_last(&counter[u], (uint32_t)nsplit, &s_last)) return;
     merge_unit<NT, true, kSelSlots>(ucand, idx, u, len, 0, ksel, 0, chunk, reinterpret_cast<uint64_t*>(s_split),
                                     s_hist, s_wsum, s_res, s_mm, s_small);
     if (tid == 0) counter[u] = 0u;  // ready for the next call on this workspace
@@ -896,31 +954,74 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
   if (k_new && ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{});
   else if (k_new)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{});
   else if (sigonly && ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
   else if (sigonly)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
   else if (skip)
     BKV_SCAN_KERNEL<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
   else if (ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr);
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
   else
     BKV_SCAN_KERNEL<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr);
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+  return hipGetLastError();
+}
+
+
+// Resident workgroups of a launch of fn (512 threads) on the current device,
+// or 0 if unknown.
+static int resident_workgroups(const void* fn, int& cache) {
+  int per = cache;
+  if (per == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fn, 64 * kScanWaves, 0) != hipSuccess) return 0;
+    cache = per;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per * cus;
+}
+
+template <int KB, int VB, int G>
+hipError_t launch_fused_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                          float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, const uint16_t* k_new,
+                          const uint16_t* v_new, float* out, hipStream_t s) {
+  const dim3 grid(w.nsplit, L.batch * L.n_kv_heads);
+  const int mshift = L.group == 64 ? 1 : 0;
+  const uint8_t* kc = static_cast<const uint8_t*>(c.k_codes);
+  const uint8_t* vc = static_cast<const uint8_t*>(c.v_codes);
+  FusedArgs fa = w.fused;
+  fa.out = out;
+  // the unit barriers need every workgroup resident at once
+  static int occ_append = 0, occ_plain = 0;  // (per kernel; the same on every device of this build)
+  const void* fn = k_new ? reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true>)
+                         : reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, true>);
+  if ((long long)resident_workgroups(fn, k_new ? occ_append : occ_plain) < (long long)grid.x * grid.y)
+    return hipErrorNotSupported;
+  (void)hipGetLastError();  // report only this launch's status
+  if (k_new)
+    BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, fa);
+  else
+    BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+        kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
+        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, nullptr, nullptr, fa);
   return hipGetLastError();
 }
 
@@ -934,6 +1035,26 @@ hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 }
 
 }  // namespace
+
+#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4
+hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                               float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
+                               const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s) {
+  if (L.query_bits != 0 || L.key_format != 0 || L.k_bits < 3) return hipErrorNotSupported;
+  const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
+  const bool v4 = L.v_bits == 4;
+  if (L.k_bits == 4) {
+    if (v4) return g4 ? launch_fused_t<4, 4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+                      : launch_fused_t<4, 4, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+    return g4 ? launch_fused_t<4, 2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+              : launch_fused_t<4, 2, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+  }
+  if (v4) return g4 ? launch_fused_t<3, 4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+                    : launch_fused_t<3, 4, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+  return g4 ? launch_fused_t<3, 2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+            : launch_fused_t<3, 2, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+}
+#endif
 
 hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,

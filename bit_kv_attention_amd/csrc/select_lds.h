@@ -235,13 +235,74 @@ __device__ inline void write_tail(int32_t* __restrict__ out, int kk, int n, int 
   for (int i = (int)__builtin_amdgcn_workitem_id_x(); i < stride - kk; i += NT) out[kk + i] = (i < nw) ? n + i : -1;
 }
 
-// Candidates cross workgroups through agent-scope atomic stores and loads,
-// which the device performs at its coherence point (no cache maintenance).
+// Data crosses workgroups of one launch only through agent-scope atomic
+// stores, loads and read-modify-writes.  gfx950 performs those at the
+// device's coherence point: they do not stay in (or read from) an XCD's own
+// L2, which the other XCDs do not see.  A workgroup hands data over by
+// waiting in every wave until its own atomic stores are performed
+// (s_waitcnt vmcnt(0)), then -- after a barrier -- incrementing a counter;
+// a receiver issues its atomic loads only after it has read the count.  No
+// cache-wide release or acquire is needed for data that never sits in a
+// non-coherent cache, and none is taken: on this device an agent-scope
+// release fence writes back the XCD's whole L2 and an acquire fence
+// invalidates it, which measured several microseconds per arrival.
 __device__ inline void st_dev64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline uint64_t ld_dev64(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t ld_dev32(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_devf(float* p, float v) { st_dev32(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
+__device__ inline float ld_devf(const float* p) { return __uint_as_float(ld_dev32(reinterpret_cast<const uint32_t*>(p))); }
+
+// Every wave waits until its memory operations are performed, then the
+// workgroup meets at a barrier (the builtin wait is a scheduling barrier for
+// the compiler too).
+__device__ inline void wg_drain() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Arrival of a workgroup at a counter shared by the n workgroups of a unit;
+// true (in every thread) in the workgroup that brings it to n.  What the
+// workgroups stored with st_dev* before arriving, the last one reads with
+// ld_dev* after.
+__device__ inline bool arrive_is_last(uint32_t* ctr, uint32_t n, int* s_flag) {
+  wg_drain();
+  if (__builtin_amdgcn_workitem_id_x() == 0)
+    *s_flag = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1;
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// A barrier across the n workgroups of a unit within one launch (they are
+// all resident: the launcher checks that the grid fits the device at once).
+// After arriving, one thread polls the counter until it reads n.  The poll
+// is bounded (kSpinMax polls of about 64 clocks each plus the load, on the
+// order of a second): past it the flag word gets bit 0 and the workgroup goes
+// on, so a launch always ends.  The counter is left at n; the unit's last
+// workgroup of the launch resets it.
+constexpr int kSpinMax = 1 << 20;
+__device__ inline void unit_barrier(uint32_t* ctr, uint32_t n, uint32_t* flag) {
+  wg_drain();
+  if (__builtin_amdgcn_workitem_id_x() == 0) {
+    __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0;; ++it) {
+      if (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n) break;
+      if (it == kSpinMax) {
+        __hip_atomic_fetch_or(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
 }
 
 // Output positions of the selected entries held as entry j*NW*64 + 64w + lane
@@ -249,7 +310,8 @@ __device__ inline uint64_t ld_dev64(const uint64_t* p) {
 // count comes from a ballot, one block scan over the PER*NW counts places
 // them.  s_tmp: PER*NW ints.
 template <int PER, int NW>
-__device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER], int* s_wsum, int* s_tmp) {
+__device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER], int* s_wsum, int* s_tmp,
+                                         int* total_out = nullptr) {
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
   const uint64_t below = (1ull << lane) - 1;
   uint64_t mask[PER];
@@ -262,6 +324,7 @@ __device__ inline void ordered_positions(const bool (&sel)[PER], int (&at)[PER],
   const int cnt = (tid < PER * NW) ? s_tmp[tid] : 0;
   int total;
   const int before = block_excl_scan<NW>(cnt, s_wsum, total);  // (its barriers order the reads above)
+  if (total_out) *total_out = total;
   if (tid < PER * NW) s_tmp[tid] = before;
   __syncthreads();
 #pragma unroll

@@ -212,8 +212,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 // as 0), finds the kk-th largest composite T there and writes the candidates
 // >= T in slot order, which is ascending token order, then clears the counter.
 // Candidates cross workgroups through agent-scope atomic stores and loads,
-// which the device performs at its coherence point (no cache maintenance);
-// a workgroup has finished all its memory operations before it arrives.
+// handed over by the arrival of select_lds.h (arrive_is_last).
 constexpr int kLocalThreads = kThreads;
 constexpr int kLocalMax = kTopkSliceMax;   // slice tokens in LDS
 constexpr int kMergeMax = kTopkMergeMax;   // candidate slots in LDS per unit
@@ -293,11 +292,7 @@ __global__ __launch_bounds__(kLocalThreads) void topk_slices_kernel(const float*
 
   if (!FUSED) return;
   // ---- arrival; the unit's last workgroup merges ------------------------------
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's candidates are written
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
+  if (!arrive_is_last(&counter[u], gridDim.x, &s_last)) return;
 
   merge_unit<kThreads, true, kLocalMax * 4 / 8>(ucand, idx, u, n, nw, k, W, S, reinterpret_cast<uint64_t*>(s_v), s_hist,
                                       s_wsum, s_res, s_mm, s_small);
@@ -338,12 +333,6 @@ constexpr int kBlkPer = kBlkMax / kThreads;
 constexpr int kBlkBatch = 4;  // spans per wave with loads in flight together
 constexpr int kBlkSpan = kTopkBlockSpan;  // tokens per workgroup (a multiple of every block size)
 
-__device__ inline void st_dev32(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint32_t ld_dev32(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __restrict__ sigma,
                                                                int32_t* __restrict__ idx, SeqArg lens, int Hkv,
@@ -406,11 +395,7 @@ __global__ __launch_bounds__(kThreads) void topk_blocks_kernel(const float* __re
   }
 
   // ---- arrival; the unit's last workgroup selects --------------------------------
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's keys are written
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&counter[u], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
+  if (!arrive_is_last(&counter[u], gridDim.x, &s_last)) return;
   for (int j = tid; j < nblk; j += kThreads) s_bkey[j] = ld_dev32(&ukeys[j]);
   __syncthreads();
 

@@ -13,10 +13,14 @@ class DecodeStep:
     (topk_select_blocks); the rows then hold k * block entries.  Plain top-k
     runs as qattn_decode_select with select_mode (automatic: the selection in
     the scan's launch where that is faster) unless fused is False, which makes
-    the two calls qattn_decode_approx and topk_select."""
+    the two calls qattn_decode_approx and topk_select.  one_launch runs the
+    plain top-k step as qattn_decode_fused: scan, selection and correction in
+    one launch (falling back to the separate launches for a call the library
+    cannot run that way)."""
 
     def __init__(self, layout: bk.Layout, k: int, max_len: int, device="cuda", window: int = 0, block: int = 0,
-                 fused: bool = True, select_mode: int = bk.SELECT_AUTO, exclude: bool | None = None):
+                 fused: bool = True, select_mode: int = bk.SELECT_AUTO, exclude: bool | None = None,
+                 one_launch: bool | None = None):
         import torch
         self.fused = bool(fused)
         # exclude: a second approximate pass over the unselected tokens, merged
@@ -39,11 +43,19 @@ class DecodeStep:
         self.ws = torch.zeros(max(1, (ws_bytes + 3) // 4), dtype=torch.float32, device=device)
         self.idx = torch.empty(L.batch * L.n_kv_heads * max(self.row, 1), dtype=torch.int32, device=device)
         self.out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32, device=device)
+        plain = self.fused and not self.exclude and self.block == 0 and self.window == 0
+        if one_launch is None:  # (opt-in while the separate launches are faster)
+            one_launch = False
+        elif one_launch and not plain:
+            raise ValueError("one_launch runs the plain top-k step only")
+        self.one_launch = bool(one_launch)
 
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
         if self.exclude:
             return self._attend_exclude(cache, q, lens, stream)
+        if self.one_launch and self._fused(cache, None, None, q, lens, stream):
+            return self.out
         if self.fused and self.block == 0 and self.window == 0:
             bk.qattn_decode_select(self.layout, cache, q, lens, self.k, self.sigma, self.idx, self.ws, stream,
                                    self.select_mode)
@@ -61,6 +73,18 @@ class DecodeStep:
         bk.qattn_correct(self.layout, cache, q, lens, self.idx if self.row > 0 else None, self.row, self.ws,
                          self.out, stream)
         return self.out
+
+    def _fused(self, cache, k_new, v_new, q, lens, stream) -> bool:
+        """qattn_decode_fused; False (nothing enqueued) when the library cannot
+        run this call in one launch (e.g. the device cannot hold its grid)."""
+        try:
+            bk.qattn_decode_fused(self.layout, cache, k_new, v_new, q, lens, self.k, self.sigma,
+                                  self.idx if self.k > 0 else None, self.out, self.ws, stream)
+        except bk.BitKVError as e:
+            if e.status != 3:  # BKV_E_UNSUPPORTED
+                raise
+            return False
+        return True
 
     def _attend_exclude(self, cache: bk.Cache, q, lens, stream=None):
         if self.block > 0:
@@ -114,6 +138,8 @@ class DecodeStep:
         tokens.  The plain top-k step appends inside the scan's launch
         (qattn_decode_step)."""
         lens = [int(p) + 1 for p in pos]
+        if self.one_launch and self._fused(cache, k_new, v_new, q, lens, stream):
+            return self.out
         if self.fused and not self.exclude and self.block == 0 and self.window == 0 and min(lens) >= 1:
             bk.qattn_decode_step(self.layout, cache, k_new, v_new, q, lens, self.k, self.sigma, self.idx, self.ws,
                                  stream, self.select_mode)

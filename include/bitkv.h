@@ -18,6 +18,7 @@
  *   qattn_decode_approx  approximate scores, selection score, split softmax.V
  *   qattn_decode_select  the same and topk_select, in one launch where it fits
  *   qattn_decode_step    kv_pack_append of one token + qattn_decode_select, one launch
+ *   qattn_decode_fused   the whole step (append, scan, top-k, correction) in one launch
  *   topk_select          top-k tokens per KV head by the selection score
  *   topk_select_window   the same, plus the newest tokens always selected
  *   topk_select_blocks   or whole blocks of tokens by their best score
@@ -158,7 +159,11 @@ bkv_status bkv_workspace_bytes(const bkv_layout* layout, int32_t max_len,
                                int32_t k, size_t* bytes);
 
 /*
- * kv_pack_append -- quantise and store n_new tokens per sequence.
+ * kv_pack_append -- quantise and store n_new tokens per sequence (HACK review
+ * on Pith, Eq. (4) and "What carries the argument": per-partition asymmetric
+ * quantisation x ~= s*x' + m with m the partition minimum; TailorKV review on
+ * Pith, "Assumptions & free parameters": fp16 zero point and scale per group;
+ * JetFire README, introduction: the exact copy kept beside the low-bit cache).
  * For each (b, kvh) and j < n_new the token k_new/v_new[b][kvh][j][0..D)
  * (fp16, device) goes to slot t = pos_host[b] + j: per group of 32 channels
  * the fp16 zero z = min, scale s = fp16((max - min) / (2^bits - 1)) computed
@@ -293,7 +298,10 @@ bkv_status topk_select_blocks(const bkv_layout* layout, const float* sigma,
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply
- * the exact correction: for the selected tokens S (idx, as written by
+ * the exact correction (JetFire README, introduction: the approximate
+ * attention over the low-bit cache is corrected for the top-k tokens with
+ * their high-precision keys and values; standard softmax attention as in the
+ * TailorKV review's Eq. 3): for the selected tokens S (idx, as written by
  * topk_select; negative entries are skipped) the approximate logit and value
  * are replaced by the exact ones from the shadow rows,
  *   lambda_t = (1/sqrt(D)) q . K_t,  nu_t = V_t        (t in S)
@@ -394,6 +402,42 @@ bkv_status qattn_exact_host(const bkv_layout* layout, const uint16_t* k_shadow_h
                             const uint16_t* v_shadow_host, const uint16_t* q_host,
                             const int32_t* len_host, const int32_t* idx_host,
                             int32_t k, float* state_host, int32_t n_threads);
+
+/*
+ * qattn_decode_fused -- one whole decode step in ONE launch (JetFire README,
+ * introduction: approximate attention over the low-bit cache, top-k
+ * selection per KV head -- Jet-QSparse abstract: the budget is per KV head --
+ * and exact correction of the selected tokens): optionally the append of one
+ * token per sequence at len_host[b] - 1 (k_new, v_new [B][Hkv][D] fp16,
+ * device, as qattn_decode_step; both NULL for no append), the approximate
+ * scan, the per-(b, kvh) top-min(k, len) selection by sigma (ties to the
+ * lower index) and the corrected output.  Results: sigma as
+ * qattn_decode_approx, idx [B][Hkv][k] as topk_select (the same set and
+ * order), out [B][Hq][D] fp32 as qattn_correct on that set (k == 0: the
+ * approximate output; k >= len: exact attention).  The scan's workgroups of
+ * a (b, kvh) pair meet at barriers inside the launch, so the grid must be
+ * resident on the device at once; the call checks that and the shape.
+ * Workspace: bkv_workspace_bytes(layout, max_len, k), zero-filled once
+ * (the call keeps its counters and histograms at zero between calls).
+ * Errors: BKV_E_UNSUPPORTED when the fused step cannot run this call (query
+ * bits, key format, k_bits < 3, more than 256 (b, kvh) pairs, more than 64
+ * scan ranges per pair, ranges over 16384 tokens, ranges per pair times k
+ * over 8192, or a grid larger than the device holds at once -- nothing is
+ * enqueued; bkv_fused_supported says which shapes qualify); BKV_E_NULL if
+ * only one of k_new, v_new is NULL; otherwise as qattn_decode_step and
+ * qattn_correct.
+ */
+bkv_status qattn_decode_fused(const bkv_layout* layout, const bkv_cache* cache,
+                              const uint16_t* k_new, const uint16_t* v_new,
+                              const uint16_t* q, const int32_t* len_host, int32_t k,
+                              float* sigma, int32_t* idx, float* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/* Host only: *supported = 1 if the shape of a qattn_decode_fused call with
+ * this layout, longest length max_len and k qualifies (the call can still
+ * return BKV_E_UNSUPPORTED when the device cannot hold its grid at once). */
+bkv_status bkv_fused_supported(const bkv_layout* layout, int32_t max_len, int32_t k,
+                               int32_t* supported);
 
 /* Static text for a status code. */
 const char* bkv_status_string(bkv_status status);

@@ -486,7 +486,7 @@ def test_decode_select_equals_two_calls(P, kb, vb, G, g, fmt):
     for k in (1, 37, 300, 500, 2600, 5000):  # 16 ranges per unit: 500 is the last in-launch budget
         runs = []
         for fused in (True, False):  # the selection in the scan's launch whenever possible, and two calls
-            st = DecodeStep(pair["lay"], k, 3999, fused=fused, select_mode=1, exclude=False)
+            st = DecodeStep(pair["lay"], k, 3999, fused=fused, select_mode=1, exclude=False, one_launch=False)
             for _ in range(2):  # twice on one workspace
                 st.sigma.fill_(float("nan"))
                 st.idx.fill_(-7)
@@ -532,7 +532,7 @@ def test_hybrid_host_correction(P, kb, vb, G, fmt):
     lens = np.array([1999, 777, 0])
     q = P.to_dev(inp.q)
     for k in (48, 1000, 0):
-        st = DecodeStep(lay, k, 1999)
+        st = DecodeStep(lay, k, 1999, one_launch=False)
         out_h = st.attend_hybrid(hc, q, lens, n_threads=4).clone()
         torch.cuda.synchronize()
         idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, max(k, 1))[:, :, :k]
