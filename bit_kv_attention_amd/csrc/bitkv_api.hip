@@ -76,14 +76,13 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
   };
   // Regions that must stay zero between calls come first, at offsets that
   // depend on the layout only (a later call with other lengths finds them in
-  // place): the top-k arrival counters, the fused step's counters and flag
-  // word, and its per-unit score histograms.
+  // place): the top-k arrival counters, the fused step's counters and its
+  // flag word.
   w.tkctr = reinterpret_cast<uint32_t*>(take((size_t)units * 4));
   const bool fusable = units <= kFMaxUnits;
   w.fused = FusedArgs{};
-  w.fused.ctr = reinterpret_cast<uint32_t*>(take((size_t)units * 3 * 4 + 4));
-  if (w.fused.ctr) w.fused.flag = w.fused.ctr + (size_t)units * 3;
-  if (fusable) w.fused.hist = reinterpret_cast<uint32_t*>(take((size_t)units * kFBins * 4));
+  w.fused.ctr = reinterpret_cast<uint32_t*>(take((size_t)units * 2 * 4 + 4));
+  if (w.fused.ctr) w.fused.flag = w.fused.ctr + (size_t)units * 2;
   const size_t recs = (size_t)L.batch * L.n_q_heads * w.nsplit;
   w.part.acc = reinterpret_cast<float*>(take(recs * kHeadDim * 4));
   w.part.m = reinterpret_cast<float*>(take(recs * 4));
@@ -103,7 +102,7 @@ Workspace workspace_layout(void* ws, const bkv_layout& L, int max_len, int k, bo
   w.bkeys = reinterpret_cast<uint32_t*>(take((size_t)units * w.bkstride * 4));
   if (fusable) {  // the fused step's per-split counts and threshold-bin lists
     w.fused.dcnt = reinterpret_cast<uint32_t*>(take((size_t)units * w.nsplit * 4));
-    w.fused.scnt = reinterpret_cast<uint32_t*>(take((size_t)units * w.nsplit * 4));
+    w.fused.dsv = reinterpret_cast<uint32_t*>(take((size_t)units * w.nsplit * 4));
     // one slot per token of each split: nsplit * split length < length + split
     // length (split length nondecreasing in the length), and the fused step
     // takes splits of at most kSelStage tokens

@@ -112,15 +112,13 @@ constexpr int kSelMinRange = 8192;  // automatic mode: shorter ranges take two l
 int topk_slice(int units, int max_len, int k);
 
 // The fused step (qattn_decode_fused): scan, selection, correction and output
-// in one launch.  Its selection histograms the selection scores into
-// kFBins bins of the top kFBinBits bits of their order-preserving keys (sign,
-// exponent and 4 mantissa bits), per split in LDS and per unit in the
-// workspace; the threshold bin's entries meet in per-split lists in the
-// workspace (ranked in LDS when at most kFDList).  At most kFMaxSplits splits
-// per unit and kFMaxUnits units.
+// in one launch.  Its selection histograms the selection scores into kFBins
+// bins of the top kFBinBits bits of their order-preserving keys (sign,
+// exponent and 4 mantissa bits) per split in LDS; each split lists its
+// highest entries in the workspace (fused_tail.h).  At most kFMaxSplits
+// splits per unit and kFMaxUnits units.
 constexpr int kFBinBits = 13;
 constexpr int kFBins = 1 << kFBinBits;
-constexpr int kFDList = 4096;
 constexpr int kFMaxSplits = 64;
 constexpr int kFMaxUnits = 256;
 constexpr int kFPass = 64;  // selected tokens per correction pass of the fused tail
@@ -128,11 +126,10 @@ constexpr int kFPass = 64;  // selected tokens per correction pass of the fused 
 // Workspace pointers of the fused step (all zero for the other launches).
 struct FusedArgs {
   float* out;      // [B][Hq][D] the corrected output
-  uint32_t* ctr;   // [U][3] arrival counters (zero between calls)
-  uint32_t* hist;  // [U][kFBins] score histogram per unit (zero between calls)
-  uint64_t* dlist; // [U][nsplit][split length] threshold-bin composites
-  uint32_t* dcnt;  // [U][nsplit] threshold-bin entries per split
-  uint32_t* scnt;  // [U][nsplit] selected tokens per split
+  uint32_t* ctr;   // [U][2] arrival counters (zero between calls)
+  uint64_t* dlist; // [U][nsplit][split length] each split's listed composites
+  uint32_t* dcnt;  // [U][nsplit] list sizes
+  uint32_t* dsv;   // [U][nsplit] the lowest bin each split lists
   uint32_t* flag;  // bit 0: a unit barrier gave up waiting (never expected)
 };
 

@@ -512,6 +512,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
 
   // FUSE: the split's histogram of selection scores (fused_tail.h)
   __shared__ uint32_t s_fh[FUSE ? kFBins : 1];
+  __shared__ uint32_t s_top;  // FUSE: the highest bin of the split's scores
 
   // ---- query operands, staged through LDS ------------------------------------
   __shared__ __attribute__((aligned(16))) uint16_t s_q[G][kHeadDim];
@@ -521,8 +522,10 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   {
     const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
     if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
-    if constexpr (FUSE)  // the split's score histogram starts empty
+    if constexpr (FUSE) {  // the split's score histogram starts empty
       for (int i = tid; i < kFBins; i += 64 * kScanWaves) s_fh[i] = 0u;
+      if (tid == 0) s_top = 0u;
+    }
     __syncthreads();
     if constexpr (kQ8) {
       // one entry per thread, whole waves: a wave holds 64 channels of one head,
@@ -552,10 +555,14 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   }
   if constexpr (APPEND) {
     const int p = len - 1;  // the new token
-    if (p >= t_begin && p < t_end) {  // (the same in the whole workgroup)
+    // The wave whose steps hold it quantises and stores it before its first
+    // load and waits for its own stores (the step with the token is its
+    // last, and no other wave reads that step); the other waves start
+    // scanning at once.
+    if (p >= t_begin && p < t_end && wv == (((p - t_begin) >> 5) & (kScanWaves - 1))) {
       __shared__ uint8_t s_newv[kHeadDim];  // its value codes
-      if (tid < 32) {  // 16 lanes for K, 16 for V, four per quarter
-        const int sub = tid & 3, grp = (tid >> 2) & 3, kv = (tid >> 4) & 1;
+      if (lane < 32) {  // 16 lanes for K, 16 for V, four per quarter
+        const int sub = lane & 3, grp = (lane >> 2) & 3, kv = (lane >> 4) & 1;
         const int c0 = grp * kGroup + sub * 8;
         const uint4 w4 = *reinterpret_cast<const uint4*>((kv ? v_new : k_new) + (size_t)u * kHeadDim + c0);
         float x[8];
@@ -574,15 +581,16 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
           for (int j = 0; j < 8; ++j) s_newv[c0 + j] = (uint8_t)code[j];
         }
       }
-      __syncthreads();
+      wave_lds_order();
       // its slot in the value tile: token r is in quarter qq = (r mod 16)/4 at
-      // slot j; lanes 16qq..16qq+15 hold it, each in 2*VB dwords of 4/VB columns
+      // slot j; lanes 16qq..16qq+15 of the tile hold it, each in 2*VB dwords
+      // of 4/VB columns (32*VB dwords, two per lane of this wave for V4)
       constexpr int kCpd = 4 / VB;
       const int r = p % kTile, qq = (r & 15) >> 2, j = 4 * (r >> 4) + (r & 3);
-      if (tid < 32 * VB) {
-        const int l = 16 * qq + (tid & 15), d = tid >> 4;
-        uint32_t* vt = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(v_codes) + (size_t)u * v_unit_bytes(VB, cap) +
-                                                   (size_t)(p / kTile) * v_tile_bytes(VB));
+      uint32_t* vt = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(v_codes) + (size_t)u * v_unit_bytes(VB, cap) +
+                                                 (size_t)(p / kTile) * v_tile_bytes(VB));
+      for (int e = lane; e < 32 * VB; e += 64) {
+        const int l = 16 * qq + (e & 15), d = e >> 4;
         const int dw = 256 * (d >> 2) + 4 * l + (d & 3);
         uint32_t word = vt[dw];
 #pragma unroll
@@ -594,7 +602,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
         }
         vt[dw] = word;
       }
-      __syncthreads();  // (its stores are visible to the workgroup's loads below)
+      __builtin_amdgcn_s_waitcnt(0);  // (its stores are done before this wave loads the step)
     }
   }
   // SKIP: bit t - t_begin marks a listed token of the split
@@ -673,6 +681,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   __shared__ floatx4 s_sig[kScanWaves][kSigBatch][8];
   // SEL, FUSE: the split's selection scores, as stored ([t - t_begin])
   __shared__ __attribute__((aligned(16))) float s_split[(SEL || FUSE) ? kSelStage : 1];
+  uint32_t fmaxb = 0;  // FUSE: this lane's highest bin so far
   int sig_count = 0;   // steps staged
   int sig_first = 0;   // t0 of the first staged step
   auto flush_sig = [&]() {
@@ -685,8 +694,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
       if constexpr (SEL || FUSE) *reinterpret_cast<floatx4*>(&s_split[t - t_begin]) = v;
       if constexpr (FUSE) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-          if (t + x < t_end) atomicAdd(&s_fh[fbin(v[x])], 1u);
+        for (int x = 0; x < 4; ++x) {
+          if (t + x < t_end) {
+            const uint32_t bn = fbin(v[x]);
+            atomicAdd(&s_fh[bn], 1u);
+            fmaxb = max(fmaxb, bn);
+          }
+        }
       }
     }
     wave_lds_order();
@@ -857,7 +871,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     }
   }
   if constexpr (FUSE) {
+    {  // the split's top bin (bins are below 2^13: exact as floats)
+      const float wm = wave_minmax<true>((float)fmaxb);
+      if (lane == 0) atomicMax(&s_top, (uint32_t)wm);
+      __syncthreads();
+    }
     FusedCtx<G> x;
+    x.top_bin = s_top;
     x.tid = tid;
     x.u = u;
     x.b = b;
@@ -881,7 +901,6 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     x.pm = pm;
     x.pl = pl;
     x.pacc = pacc;
-    x.tkc = cand;
     x.idx = idx;
     x.fa = fa;
     x.s_q = s_q;

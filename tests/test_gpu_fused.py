@@ -27,7 +27,7 @@ def banner(msg):
 def flag_word(st, lay):
     """Bit 0 set = a unit barrier of the fused step stopped waiting."""
     units = lay.batch * lay.n_kv_heads
-    off = ((units * 4 + 255) // 256) * 256 + units * 12
+    off = ((units * 4 + 255) // 256) * 256 + units * 8
     return int(st.ws.cpu().numpy().view(np.uint32)[off // 4])
 
 
