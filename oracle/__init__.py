@@ -58,7 +58,8 @@ def lib():
         L.orc_v_bitpos.restype = C.c_uint64
         L.orc_get_bits.argtypes = [P, C.c_uint64, C.c_int]
         L.orc_get_bits.restype = C.c_uint32
-        for f in ("orc_k_codes_bytes", "orc_v_codes_bytes", "orc_meta_bytes", "orc_shadow_bytes"):
+        for f in ("orc_k_codes_bytes", "orc_v_codes_bytes", "orc_meta_bytes", "orc_k_meta_bytes",
+                  "orc_shadow_bytes"):
             getattr(L, f).argtypes = [C.POINTER(_Shape)]
             getattr(L, f).restype = C.c_size_t
         L.orc_pack_append.argtypes = [C.POINTER(_Shape), P, P, P, P, P, P, P, P, C.c_int, P]
@@ -67,6 +68,9 @@ def lib():
                                    P, P, P, P, P]
         L.orc_quantize_query.argtypes = [P, C.c_int, C.c_int, P, P]
         L.orc_quantize_group_mx.argtypes = [P, C.c_int, P, P]
+        L.orc_quantize_block_mx8.argtypes = [P, C.c_int, P, P]
+        L.orc_k_bitpos_mx8.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.orc_k_bitpos_mx8.restype = C.c_uint64
         L.orc_e2m1_value.argtypes = [C.c_uint32]
         L.orc_e2m1_value.restype = C.c_double
         L.orc_topk.argtypes = [P, C.c_int, C.c_int, P]
@@ -136,6 +140,26 @@ def quantize_rows_mx(x16: np.ndarray, group: int):
     return codes.reshape(x16.shape), sc.reshape(x16.shape[:-1] + (D // group,))
 
 
+def quantize_rows_mx8(x16: np.ndarray):
+    """O1mx8 on rows of fp16 values, blocks of 32 channels.  x16: [..., D] float16.
+    Returns (codes uint8 [..., D] = sign << 3 | E2M1 index, e8 uint8 [..., D/32]
+    = X + 127, the block's scale being 2^X)."""
+    x16 = np.ascontiguousarray(x16, dtype=np.float16)
+    D = x16.shape[-1]
+    rows = x16.reshape(-1, D)
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    e8 = np.zeros((rows.shape[0], D // 32), dtype=np.uint8)
+    for r in range(rows.shape[0]):
+        for p in range(D // 32):
+            seg = np.ascontiguousarray(rows[r, p * 32:(p + 1) * 32])
+            cs = np.zeros(32, dtype=np.uint8)
+            e = np.zeros(1, dtype=np.uint8)
+            lib().orc_quantize_block_mx8(_p(seg.view(np.uint16)), 32, _p(cs), _p(e))
+            codes[r, p * 32:(p + 1) * 32] = cs
+            e8[r, p] = e[0]
+    return codes.reshape(x16.shape), e8.reshape(x16.shape[:-1] + (D // 32,))
+
+
 def e2m1_value(code: int) -> float:
     return float(lib().orc_e2m1_value(int(code)))
 
@@ -153,6 +177,10 @@ def quantize_query(q16: np.ndarray, group: int):
 
 def k_bitpos(t: int, c: int, D: int, bits: int) -> int:
     return int(lib().orc_k_bitpos(t, c, D, bits))
+
+
+def k_bitpos_mx8(t: int, c: int, D: int) -> int:
+    return int(lib().orc_k_bitpos_mx8(t, c, D))
 
 
 def v_bitpos(t: int, c: int, D: int, bits: int) -> int:
@@ -176,7 +204,7 @@ class Shape:
     vbits: int
     group: int
     cap: int
-    kfmt: int = 0  # keys: 0 affine integer codes, 1 MXFP4
+    kfmt: int = 0  # keys: 0 affine codes; 1 MXFP4, fp16 query; 2 MXFP4 (E8M0 scales), FP4 query
 
     def c(self) -> _Shape:
         return _Shape(self.B, self.Hq, self.Hkv, self.D, self.kbits, self.vbits, self.group, self.cap, self.kfmt)
@@ -191,9 +219,8 @@ class Cache:
         L = lib()
         self.k_codes = np.zeros(L.orc_k_codes_bytes(C.byref(cs)), dtype=np.uint8)
         self.v_codes = np.zeros(L.orc_v_codes_bytes(C.byref(cs)), dtype=np.uint8)
-        nmeta = L.orc_meta_bytes(C.byref(cs)) // 4
-        self.k_meta = np.zeros(nmeta, dtype=np.uint32)
-        self.v_meta = np.zeros(nmeta, dtype=np.uint32)
+        self.k_meta = np.zeros((L.orc_k_meta_bytes(C.byref(cs)) + 3) // 4, dtype=np.uint32)
+        self.v_meta = np.zeros(L.orc_meta_bytes(C.byref(cs)) // 4, dtype=np.uint32)
         nsh = L.orc_shadow_bytes(C.byref(cs)) // 2
         self.k_shadow = np.zeros(nsh, dtype=np.uint16)
         self.v_shadow = np.zeros(nsh, dtype=np.uint16)
@@ -245,6 +272,12 @@ class Cache:
     def k_meta_planes(self):
         s = self.s
         return self.k_meta.reshape(s.B, s.Hkv, s.D // s.group, s.cap)
+
+    def k_scales_e8(self):
+        """Key format 2: the E8M0 bytes [B][Hkv][cap][D/32]."""
+        s = self.s
+        n = s.B * s.Hkv * s.cap * (s.D // 32)
+        return self.k_meta.view(np.uint8)[:n].reshape(s.B, s.Hkv, s.cap, s.D // 32)
 
     def v_meta_planes(self):
         s = self.s

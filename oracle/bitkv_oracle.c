@@ -134,22 +134,24 @@ double orc_e2m1_value(uint32_t code) {
   return (code & 8u) ? -m : m;
 }
 
-void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
-                           uint16_t* scale16) {
+/* The block's largest magnitude; *X = floor(log2(amax)) - 2 when amax > 0. */
+static double mx_amax(const uint16_t* x, int g, int* X) {
   double amax = 0.0;
   for (int i = 0; i < g; ++i) {
     const double v = fabs((double)orc_f16_to_f32(x[i]));
     if (v > amax) amax = v;
   }
-  if (amax == 0.0) {
-    for (int i = 0; i < g; ++i) codes[i] = 0;
-    *scale16 = 0;
-    return;
+  if (amax > 0.0) {
+    int e;
+    frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+    *X = e - 1 - 2;
   }
-  int e;
-  frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
-  int X = e - 1 - 2;
-  if (X < -24) X = -24;
+  return amax;
+}
+
+/* Each element of the block as sign << 3 | the E2M1 index nearest to
+ * |x| / 2^X (ties to the even index; above 6 the nearest is 6). */
+static void mx_codes(const uint16_t* x, int g, int X, uint8_t* codes) {
   const double sc = ldexp(1.0, X);
   for (int i = 0; i < g; ++i) {
     const double v = (double)orc_f16_to_f32(x[i]);
@@ -161,7 +163,38 @@ void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
     }
     codes[i] = (uint8_t)(best | ((v < 0.0 && best != 0) ? 8 : 0));
   }
-  *scale16 = orc_f32_to_f16((float)sc);
+}
+
+void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
+                           uint16_t* scale16) {
+  int X = 0;
+  if (mx_amax(x, g, &X) == 0.0) {
+    for (int i = 0; i < g; ++i) codes[i] = 0;
+    *scale16 = 0;
+    return;
+  }
+  if (X < -24) X = -24;
+  mx_codes(x, g, X, codes);
+  *scale16 = orc_f32_to_f16((float)ldexp(1.0, X));
+}
+
+/* O1mx8: the same block rule with the scale stored as its E8M0 exponent byte
+ * (the OCP Microscaling formats keep the shared scale as E8M0, value
+ * 2^(byte - 127)) -- the key format whose scores take the FP4 query, and that
+ * query itself (Jet-QSparse abstract: FP4 keys and an FP4 query-key product).
+ * Readings: X is not clamped (fp16 inputs give X in [-26, 13], inside
+ * E8M0's range); an all-zero block stores X = 0 (byte 127): its codes are
+ * all 0, so the scale does not matter. */
+void orc_quantize_block_mx8(const uint16_t* x, int g, uint8_t* codes,
+                            uint8_t* e8) {
+  int X = 0;
+  if (mx_amax(x, g, &X) == 0.0) {
+    for (int i = 0; i < g; ++i) codes[i] = 0;
+    *e8 = 127;
+    return;
+  }
+  mx_codes(x, g, X, codes);
+  *e8 = (uint8_t)(X + 127);
 }
 
 /* O1q: the query of one head quantised to INT8 per partition of g channels,
@@ -210,6 +243,15 @@ uint64_t orc_k_bitpos(int t, int c, int D, int bits) {
   const uint64_t chunk = (uint64_t)e * 16u + (uint64_t)(t % 16);
   return (uint64_t)(t / 16) * 16u * (uint64_t)D * bits + chunk * chunk_bits +
          (uint64_t)g * field_bits + (uint64_t)j * bits;
+}
+
+/* K in key format 2 (4-bit E2M1 codes): blocks of 16 tokens, each
+ * (D/32)*16 chunks of 16 bytes; chunk 16*g + (t mod 16) holds the 32 codes
+ * of channels 32g .. 32g+31 of token t, channel 32g + j at bits 4j..4j+3
+ * (two codes a byte, the lower channel in the low half). */
+uint64_t orc_k_bitpos_mx8(int t, int c, int D) {
+  const uint64_t chunk = 16u * (uint64_t)(c / 32) + (uint64_t)(t % 16);
+  return (uint64_t)(t / 16) * 16u * (uint64_t)D * 4u + chunk * 128u + 4u * (uint64_t)(c % 32);
 }
 
 /* V (bits 2 or 4): tiles of 32 tokens.  Token r of the tile (r = t mod 32)
@@ -267,6 +309,18 @@ size_t orc_v_codes_bytes(const orc_shape* s) { return units_of(s) * v_unit_bytes
 size_t orc_meta_bytes(const orc_shape* s) {
   return units_of(s) * (size_t)(s->D / s->group) * s->cap * sizeof(uint32_t);
 }
+/* Key format 2 keeps one E8M0 byte per (token, 32-channel block),
+ * [B][Hkv][cap][D/32]; the other formats use the meta planes. */
+size_t orc_k_meta_bytes(const orc_shape* s) {
+  if (s->kfmt == 2) return units_of(s) * (size_t)s->cap * (size_t)(s->D / 32);
+  return orc_meta_bytes(s);
+}
+static size_t k_scale_index(const orc_shape* s, int u, int t, int blk) {
+  return ((size_t)u * s->cap + t) * (size_t)(s->D / 32) + blk;
+}
+static uint64_t k_code_bitpos(const orc_shape* s, int t, int c) {
+  return s->kfmt == 2 ? orc_k_bitpos_mx8(t, c, s->D) : orc_k_bitpos(t, c, s->D, s->kbits);
+}
 size_t orc_shadow_bytes(const orc_shape* s) {
   return units_of(s) * (size_t)s->cap * s->D * sizeof(uint16_t);
 }
@@ -289,7 +343,11 @@ void orc_pack_append(const orc_shape* s, uint8_t* k_codes, uint8_t* v_codes,
         const int t = pos[b] + j;
         const size_t src = (((size_t)u * n_new) + j) * D;
         /* keys */
-        if (s->kfmt == 1) {
+        if (s->kfmt == 2) {
+          for (int blk = 0; blk < D / 32; ++blk)
+            orc_quantize_block_mx8(k_new + src + (size_t)blk * 32, 32, codes + (size_t)blk * 32,
+                                   (uint8_t*)k_meta + k_scale_index(s, u, t, blk));
+        } else if (s->kfmt == 1) {
           for (int grp = 0; grp < ng; ++grp) {
             uint16_t s16;
             orc_quantize_group_mx(k_new + src + (size_t)grp * g, g, codes + (size_t)grp * g, &s16);
@@ -299,9 +357,9 @@ void orc_pack_append(const orc_shape* s, uint8_t* k_codes, uint8_t* v_codes,
           orc_quantize_rows(k_new + src, 1, D, g, s->kbits, codes, meta);
         }
         for (int c = 0; c < D; ++c)
-          orc_set_bits(k_codes + (size_t)u * k_unit_bytes(s),
-                       orc_k_bitpos(t, c, D, s->kbits), s->kbits, codes[c]);
-        for (int grp = 0; grp < ng; ++grp) k_meta[meta_index(s, u, grp, t)] = meta[grp];
+          orc_set_bits(k_codes + (size_t)u * k_unit_bytes(s), k_code_bitpos(s, t, c), s->kbits, codes[c]);
+        if (s->kfmt != 2)
+          for (int grp = 0; grp < ng; ++grp) k_meta[meta_index(s, u, grp, t)] = meta[grp];
         memcpy(k_shadow + ((size_t)u * s->cap + t) * D, k_new + src, (size_t)D * 2);
         /* values */
         orc_quantize_rows(v_new + src, 1, D, g, s->vbits, codes, meta);
@@ -327,8 +385,9 @@ static double dequant(uint32_t meta, uint32_t code) {
 
 double orc_k_hat(const orc_shape* s, const uint8_t* k_codes,
                  const uint32_t* k_meta, int u, int t, int c) {
-  const uint32_t code = orc_get_bits(k_codes + (size_t)u * k_unit_bytes(s),
-                                     orc_k_bitpos(t, c, s->D, s->kbits), s->kbits);
+  const uint32_t code = orc_get_bits(k_codes + (size_t)u * k_unit_bytes(s), k_code_bitpos(s, t, c), s->kbits);
+  if (s->kfmt == 2) /* the E2M1 value times 2^(E8M0 byte - 127) */
+    return ldexp(orc_e2m1_value(code), (int)((const uint8_t*)k_meta)[k_scale_index(s, u, t, c / 32)] - 127);
   const uint32_t meta = k_meta[meta_index(s, u, c / s->group, t)];
   if (s->kfmt == 1) /* MXFP4: the E2M1 value times the block's power of two */
     return orc_e2m1_value(code) * (double)orc_f16_to_f32((uint16_t)(meta & 0xFFFFu));
@@ -458,7 +517,9 @@ void orc_decode(const orc_shape* s, const uint8_t* k_codes,
 }
 
 /* qbits = 8: the approximate logits (O3) use the dequantised INT8 query
- * s*q' (O1q) in place of q; the exact logits of the correction keep q. */
+ * s*q' (O1q) in place of q; key format 2: they use the MXFP4 query (O1mx8 on
+ * each 32-channel block of each query head), so each score is the FP4 query
+ * times the FP4 keys.  The exact logits of the correction keep q. */
 void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
                   const uint8_t* v_codes, const uint32_t* k_meta,
                   const uint32_t* v_meta, const uint16_t* k_shadow,
@@ -485,11 +546,19 @@ void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
     memset(all, 1, (size_t)nn);
     double* sig = sigma + (size_t)u * s->cap;
 
-    /* the query of the approximate logits: q, or its INT8 form s*q' */
+    /* the query of the approximate logits: q, its INT8 form s*q', or (key
+     * format 2) its MXFP4 form, the E2M1 values times each block's 2^X */
     double* qa = (double*)malloc((size_t)G * D * sizeof(double));
     for (int i = 0; i < G; ++i) {
       const uint16_t* qh = q + ((size_t)b * s->Hq + (size_t)kvh * G + i) * D;
-      if (qbits == 8) {
+      if (s->kfmt == 2) {
+        for (int blk = 0; blk < D / 32; ++blk) {
+          uint8_t qc[32], e8;
+          orc_quantize_block_mx8(qh + (size_t)blk * 32, 32, qc, &e8);
+          for (int j = 0; j < 32; ++j)
+            qa[(size_t)i * D + blk * 32 + j] = ldexp(orc_e2m1_value(qc[j]), (int)e8 - 127);
+        }
+      } else if (qbits == 8) {
         int8_t qc[ORC_MAX_D];
         float qs[ORC_MAX_D];
         orc_quantize_query(qh, D, s->group, qc, qs);

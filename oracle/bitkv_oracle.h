@@ -32,6 +32,9 @@
  *  - the per-KV-head selection score is the max over the query heads of the
  *    group of the approximate logit; ties go to the lower token index.
  *  - softmax scale 1/sqrt(D), no mask inside the cached tokens.
+ *  - key format 2 (Jet-QSparse abstract: FP4 keys and an FP4 query-key
+ *    product): the query of the approximate scores is quantised by the same
+ *    MX block rule as the keys; the exact logits keep the fp16 query.
  */
 #ifndef BITKV_ORACLE_H
 #define BITKV_ORACLE_H
@@ -47,7 +50,10 @@ extern "C" {
 /* Shape of one attention layer's cache.  D % group == 0, cap % 32 == 0. */
 typedef struct {
   int32_t B, Hq, Hkv, D, kbits, vbits, group, cap;
-  int32_t kfmt; /* keys: 0 = affine integer codes (O1), 1 = MXFP4 (O1mx) */
+  int32_t kfmt; /* keys: 0 = affine integer codes (O1); 1 = MXFP4 with fp16
+                 * scales in the K layout, scores against the fp16 query
+                 * (O1mx); 2 = MXFP4 with E8M0 scales (O1mx8, group 32) in the
+                 * 32-channel-chunk layout, scores against the MXFP4 query */
 } orc_shape;
 
 /* ---- fp16 <-> fp32 (own implementation; pinned against numpy) ---- */
@@ -70,10 +76,14 @@ uint64_t orc_v_bitpos(int t, int c, int D, int bits);
 uint32_t orc_get_bits(const uint8_t* buf, uint64_t bitpos, int nbits);
 void orc_set_bits(uint8_t* buf, uint64_t bitpos, int nbits, uint32_t value);
 
+/* Key format 2: bit address of channel c of token t (orc_k_bitpos's role). */
+uint64_t orc_k_bitpos_mx8(int t, int c, int D);
+
 /* Buffer sizes in bytes for one whole cache. */
 size_t orc_k_codes_bytes(const orc_shape* s);
 size_t orc_v_codes_bytes(const orc_shape* s);
-size_t orc_meta_bytes(const orc_shape* s);   /* each of K and V */
+size_t orc_meta_bytes(const orc_shape* s);   /* V, and K in formats 0, 1 */
+size_t orc_k_meta_bytes(const orc_shape* s); /* K in every format */
 size_t orc_shadow_bytes(const orc_shape* s); /* each of K and V */
 
 /* ---- O1+O2: append n_new tokens per sequence at positions pos[b] ----
@@ -121,6 +131,10 @@ void orc_decode_q(const orc_shape* s, const uint8_t* k_codes,
  * scale (0 for an all-zero block). */
 void orc_quantize_group_mx(const uint16_t* x, int g, uint8_t* codes,
                            uint16_t* scale16);
+/* O1mx8: the same elements with the scale as an E8M0 byte X + 127 (no clamp;
+ * an all-zero block gets 127).  Key format 2 and its query use it. */
+void orc_quantize_block_mx8(const uint16_t* x, int g, uint8_t* codes,
+                            uint8_t* e8);
 /* the value of an E2M1 code (sign << 3 | magnitude index) */
 double orc_e2m1_value(uint32_t code);
 
