@@ -41,10 +41,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32) -> int:
-    """Codes plus fp16 scale and zero of K and V, per token and KV head."""
+def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32, key_format: int = 0) -> int:
+    """Codes plus fp16 scale and zero of K and V, per token and KV head (key
+    format 2: one E8M0 byte per 32 key channels in place of the key meta)."""
     meta = (D // group) * 4
-    return D * kbits // 8 + meta + D * vbits // 8 + meta
+    kmeta = D // 32 if key_format == 2 else meta
+    return D * kbits // 8 + kmeta + D * vbits // 8 + meta
 
 
 def num_splits(units: int, L: int) -> int:
@@ -133,7 +135,7 @@ class Workbench:
         self.lay = lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group,
                                         query_bits=w.query_bits, key_format=w.key_format)
         self.units = w.B * w.Hkv
-        self.ppt = packed_bytes_per_token(w.kbits, w.vbits, group=w.group)
+        self.ppt = packed_bytes_per_token(w.kbits, w.vbits, group=w.group, key_format=w.key_format)
         self.packed = self.units * L * self.ppt
         self.copies = args.copies or max(1, min(8, -(-600_000_000 // self.packed)))
         self.host_shadow = shadow == "host" or args.exact == "host"
@@ -334,7 +336,8 @@ def bench_one(w, args, torch, shadow="hbm", line=True):
         "config": {"workload": w.name, "batch": w.B, "n_q_heads": w.Hq, "n_kv_heads": w.Hkv,
                    "head_dim": w.D, "context": L, "k_bits": w.kbits, "v_bits": w.vbits,
                    "group": w.group, "query_bits": w.query_bits,
-                   "key_format": {0: "affine", 1: "mxfp4"}.get(w.key_format, str(w.key_format)),
+                   "key_format": {0: "affine", 1: "mxfp4_fp16_query", 2: "mxfp4_fp4_query"}.get(
+                       w.key_format, str(w.key_format)),
                    "top_k": 0 if wb.NB else w.k, "recent_window": wb.W,
                    "blocks": wb.NB, "block": args.block if wb.NB else 0,
                    "shadow": "host" if wb.host_shadow else "hbm", "exact": args.exact,

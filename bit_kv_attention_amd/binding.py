@@ -57,6 +57,7 @@ _lib.bkv_status_string.argtypes = [C.c_int]
 _lib.bkv_status_string.restype = C.c_char_p
 _lib.bkv_cache_bytes.argtypes = [_LP, _SZ, _SZ, _SZ, _SZ]
 _lib.bkv_workspace_bytes.argtypes = [_LP, C.c_int32, C.c_int32, _SZ]
+_lib.bkv_k_meta_bytes.argtypes = [_LP, _SZ]
 _lib.kv_pack_append.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P]
 _lib.qattn_decode_approx.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.topk_select.argtypes = [_LP, _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
@@ -73,12 +74,12 @@ _lib.qattn_correct_hybrid.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, _P, C
 _lib.qattn_exact_host.argtypes = [_LP, _P, _P, _P, _P, _P, C.c_int32, _P, C.c_int32]
 _lib.qattn_decode_fused.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.bkv_fused_supported.argtypes = [_LP, C.c_int32, C.c_int32, _P]
-for _f in ("bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append", "qattn_decode_approx",
-           "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
+for _f in ("bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
+           "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
 
-EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
-            "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
+EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_workspace_bytes", "bkv_select_in_scan",
+            "kv_pack_append", "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
             "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step", "qattn_decode_fused",
             "bkv_fused_supported")
@@ -123,6 +124,12 @@ def bkv_cache_bytes(layout: Layout):
     return a.value, b.value, c.value, d.value
 
 
+def bkv_k_meta_bytes(layout: Layout) -> int:
+    out = C.c_size_t()
+    _check("bkv_k_meta_bytes", _lib.bkv_k_meta_bytes(C.byref(layout), C.byref(out)))
+    return out.value
+
+
 def bkv_workspace_bytes(layout: Layout, max_len: int, k: int) -> int:
     out = C.c_size_t()
     _check("bkv_workspace_bytes", _lib.bkv_workspace_bytes(C.byref(layout), int(max_len), int(k), C.byref(out)))
@@ -156,7 +163,7 @@ def allocate_cache(layout: Layout, device="cuda", shadow_on_host: bool = False) 
         sh = lambda n: torch.zeros(n // 2, dtype=torch.float16, pin_memory=True)
     else:
         sh = lambda n: torch.zeros(n // 2, dtype=torch.float16, device=device)
-    return Cache(layout, z8(kb), z8(vb), z32(mb), z32(mb), sh(sb), sh(sb))
+    return Cache(layout, z8(kb), z8(vb), z32(bkv_k_meta_bytes(layout)), z32(mb), sh(sb), sh(sb))
 
 
 def kv_pack_append(layout: Layout, cache: Cache, k_new, v_new, n_new: int, pos_host, stream=None) -> None:

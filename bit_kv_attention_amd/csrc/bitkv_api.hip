@@ -134,8 +134,8 @@ static bkv_status check_layout(const bkv_layout* L) {
   if (G != 4 && G != 8) return BKV_E_UNSUPPORTED;
   if (L->batch > kMaxBatch) return BKV_E_UNSUPPORTED;
   if (L->query_bits != 0 && L->query_bits != 8) return BKV_E_UNSUPPORTED;
-  if (L->key_format != 0 && L->key_format != 1) return BKV_E_UNSUPPORTED;
-  if (L->key_format == 1 && (L->k_bits != 4 || L->group != kGroup || L->query_bits != 0)) return BKV_E_UNSUPPORTED;
+  if (L->key_format < 0 || L->key_format > 2) return BKV_E_UNSUPPORTED;
+  if (L->key_format != 0 && (L->k_bits != 4 || L->group != kGroup || L->query_bits != 0)) return BKV_E_UNSUPPORTED;
   return BKV_OK;
 }
 
@@ -184,6 +184,16 @@ bkv_status bkv_cache_bytes(const bkv_layout* L, size_t* k_codes_bytes, size_t* v
   *v_codes_bytes = units * v_unit_bytes(L->v_bits, L->capacity);
   *meta_bytes_each = units * (size_t)(kHeadDim / L->group) * (size_t)L->capacity * sizeof(uint32_t);
   *shadow_bytes_each = units * (size_t)L->capacity * kHeadDim * sizeof(uint16_t);
+  return BKV_OK;
+}
+
+bkv_status bkv_k_meta_bytes(const bkv_layout* L, size_t* bytes) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if (!bytes) return BKV_E_NULL;
+  const size_t units = (size_t)L->batch * L->n_kv_heads;
+  *bytes = (L->key_format == 2) ? units * (size_t)L->capacity * sizeof(uint32_t)
+                                : units * (size_t)(kHeadDim / L->group) * (size_t)L->capacity * sizeof(uint32_t);
   return BKV_OK;
 }
 

@@ -56,6 +56,18 @@ __host__ __device__ inline size_t v_unit_bytes(int vbits, int cap) { return (siz
 __host__ __device__ inline size_t k_chunk_offset(int kbits, int t, int e) {
   return (size_t)(t / kKBlock) * k_block_bytes(kbits) + (size_t)(e * kKBlock + t % kKBlock) * k_chunk_bytes(kbits);
 }
+// Key format 2 (MXFP4 keys scored against an MXFP4 query): a block of 16
+// tokens is 64 chunks of 16 bytes; chunk 16g + (t mod 16) holds the 32 codes
+// of channels 32g .. 32g+31 of token t, channel 32g + j in nibble j (low
+// nibble first).  Lane l of a wave reading a block's 1 KB (16 bytes a lane)
+// then holds the A operand (row = token l mod 16, K = 32(l/16) .. +31) of a
+// 16x16x128 FP4 MFMA.  The scales are E8M0 bytes (2^(byte - 127)), one per
+// (token, 32-channel block): word t of the unit's [capacity] uint32 plane
+// holds block g's byte at bits 8g.
+__host__ __device__ inline size_t k_chunk_offset_e8(int t, int g) {
+  return (size_t)(t / kKBlock) * k_block_bytes(4) + (size_t)(16 * g + t % kKBlock) * 16;
+}
+
 // Dword index inside a value tile, and bit inside that dword, of the code of
 // (token r of the tile, channel c).
 __host__ __device__ inline void v_code_pos(int vbits, int r, int c, int& dw, int& bit) {
@@ -185,6 +197,12 @@ hipError_t launch_decode_approx_mx(const bkv_layout& L, const bkv_cache& c, cons
                                    const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                    int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                    const uint16_t* v_new, hipStream_t s);
+// Key format 2: the scores on the scaled FP4 MFMA (decode_approx.hip built
+// with BKV_KEY_FP4=1).
+hipError_t launch_decode_approx_fp4(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
+                                    const SeqArg& len, float* sigma, const Workspace& w, int chunk,
+                                    int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
+                                    const uint16_t* v_new, hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 // bkeys: kstride block keys per unit; counter: one arrival counter per unit.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int nb,

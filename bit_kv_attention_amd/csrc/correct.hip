@@ -182,9 +182,10 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
 // selected tokens out, see qattn_decode_unselected); the packed cache is not
 // read.
 // Q8: the approximate logits take the INT8 query of the scan (quant_lane.h).
-// MX: the key codes are MXFP4 (E2M1 numbers, one power-of-two scale per group
-// of 32, no zero point).
-template <int KB, int VB, int G, bool EX, bool AP = true, bool Q8 = false, bool MX = false>
+// KF: the key format -- 1: MXFP4 codes (E2M1 numbers, one power-of-two scale
+// per group of 32, no zero point) against the fp16 query; 2: MXFP4 codes
+// with E8M0 scales against the MXFP4 query (the scan's FP4 product).
+template <int KB, int VB, int G, bool EX, bool AP = true, bool Q8 = false, int KF = 0>
 __global__ __launch_bounds__(256) void chunk_kernel(
     const uint8_t* __restrict__ k_codes, const uint8_t* __restrict__ v_codes,
     const uint32_t* __restrict__ k_meta, const uint32_t* __restrict__ v_meta,
@@ -208,6 +209,11 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   __shared__ uint4 s_q8h[Q8 ? G : 1][kHeadDim / 8];   // Q8: the codes q' as fp16 pairs
   __shared__ float s_q8s[Q8 ? G : 1][kHeadDim / 16];  // Q8: s * (sum of q' over a 16-channel run)
   __shared__ float s_q8c[Q8 ? G : 1][kHeadDim / 16];  // Q8: the scale s of the run's group
+  // key format 2: the query's E2M1 codes as fp16 patterns (value * 2^-14), and
+  // 2^(Xq + 28) per 16-channel run
+  constexpr bool kF2 = KF == 2;
+  __shared__ uint4 s_q4h[kF2 ? G : 1][kHeadDim / 8];
+  __shared__ float s_q4c[kF2 ? G : 1][kHeadDim / 16];
   __shared__ int s_t[kCorrChunk];
   __shared__ float s_lg[2][kCorrChunk][G];  // logits, log2 units: [exact/approx]
   __shared__ float s_w[2][kCorrChunk][G];   // weights
@@ -253,6 +259,21 @@ __global__ __launch_bounds__(256) void chunk_kernel(
           (&s_q8c[0][0])[tid >> 1] = sc;
         }
       }
+      if constexpr (kF2) {
+        // 8 channels per thread, a quad per 32-channel quarter (whole waves)
+        float x[8];
+        halves8(w, x);
+        uint32_t code[8];
+        const int X = (int)quantise_lane_e8(x, code) - 127;
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t c0 = code[2 * j], c1 = code[2 * j + 1];
+          pk[j] = ((c0 & 7u) << 9) | ((c0 & 8u) << 12) | ((c1 & 7u) << 25) | ((c1 & 8u) << 28);
+        }
+        (&s_q4h[0][0])[tid] = (uint4){pk[0], pk[1], pk[2], pk[3]};
+        if ((tid & 1) == 0) (&s_q4c[0][0])[tid >> 1] = __builtin_amdgcn_ldexpf(1.0f, X + 28);
+      }
     }
     if (tid < kCorrChunk) s_t[tid] = (ii < kk && tv >= 0 && tv < n) ? tv : -1;
   }
@@ -260,7 +281,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 
   const uint8_t* kbase = k_codes + (size_t)u * k_unit_bytes(KB, cap);
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
-  const uint32_t* kmeta = k_meta + (size_t)u * meta_planes(mshift) * cap;
+  const uint32_t* kmeta = k_meta + (size_t)u * (kF2 ? 1 : meta_planes(mshift)) * cap;
   const uint32_t* vmeta = v_meta + (size_t)u * meta_planes(mshift) * cap;
   const uint16_t* ksh = k_shadow + (size_t)u * cap * kHeadDim;
   const uint16_t* vsh = v_shadow + (size_t)u * cap * kHeadDim;
@@ -271,7 +292,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   const int tl = tid >> 3;
   const int part = tid & 7;
   const int t_sel = s_t[tl];
-  KeyRun<KB, EX, AP> kr;
+  KeyRun<KB, EX, AP, KF> kr;
   kr.load(ksh, kbase, kmeta, cap, max(t_sel, 0), part, mshift);
   // value loads: one thread per (channel, half of the chunk)
   const int c = tid & (kHeadDim - 1);
@@ -291,7 +312,10 @@ __global__ __launch_bounds__(256) void chunk_kernel(
   // ---- logits: 8 threads per token, 16 channels each (correct_lane.h) -------
   {
     float ex[G], ap[G];
-    run_logits<KB, G, EX, AP, Q8, MX>(kr, part, s_qh, s_qs, s_q8h, s_q8s, s_q8c, ex, ap);
+    if constexpr (kF2)
+      run_logits<KB, G, EX, AP, false, 2>(kr, part, s_qh, s_qs, s_q4h, nullptr, s_q4c, ex, ap);
+    else
+      run_logits<KB, G, EX, AP, Q8, KF>(kr, part, s_qh, s_qs, s_q8h, s_q8s, s_q8c, ex, ap);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       ex[h] = sum8(ex[h]);
@@ -365,7 +389,7 @@ __global__ __launch_bounds__(256) void chunk_kernel(
 // elsewhere).
 enum ChunkTerms { kBoth, kExactOnly, kApproxOnly };
 
-template <int KB, int VB, int G, bool Q8, bool MX = false>
+template <int KB, int VB, int G, bool Q8, int KF = 0>
 void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const SeqArg& len,
               const int32_t* idx, int k, const Workspace& w, ChunkTerms terms, hipStream_t s) {
   const dim3 grid(w.nchunk, L.batch * L.n_kv_heads);
@@ -373,15 +397,15 @@ void launch_t(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
   const uint8_t* kc = static_cast<const uint8_t*>(cc.k_codes);
   const uint8_t* vc = static_cast<const uint8_t*>(cc.v_codes);
   if (terms == kBoth)
-    chunk_kernel<KB, VB, G, true, true, Q8, MX><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
+    chunk_kernel<KB, VB, G, true, true, Q8, KF><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow, q,
                                                               idx, w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity,
                                                               k, w.nchunk, mshift);
   else if (terms == kExactOnly)
-    chunk_kernel<KB, VB, G, true, false><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow,
+    chunk_kernel<KB, VB, G, true, false, false, KF><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, cc.k_shadow, cc.v_shadow,
                                                                q, idx, w.cs, len, L.n_q_heads, L.n_kv_heads,
                                                                L.capacity, k, w.nchunk, mshift);
   else
-    chunk_kernel<KB, VB, G, false, true, Q8, MX><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
+    chunk_kernel<KB, VB, G, false, true, Q8, KF><<<grid, 256, 0, s>>>(kc, vc, cc.k_meta, cc.v_meta, nullptr, nullptr, q, idx,
                                                                w.cs, len, L.n_q_heads, L.n_kv_heads, L.capacity, k,
                                                                w.nchunk, mshift);
 }
@@ -393,9 +417,16 @@ void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
   if constexpr (KB == 4) {
     if (L.key_format == 1) {  // (fp16 query only)
       if (L.n_q_heads / L.n_kv_heads == 4)
-        launch_t<4, VB, 4, false, true>(L, cc, q, len, idx, k, w, terms, s);
+        launch_t<4, VB, 4, false, 1>(L, cc, q, len, idx, k, w, terms, s);
       else
-        launch_t<4, VB, 8, false, true>(L, cc, q, len, idx, k, w, terms, s);
+        launch_t<4, VB, 8, false, 1>(L, cc, q, len, idx, k, w, terms, s);
+      return;
+    }
+    if (L.key_format == 2) {
+      if (L.n_q_heads / L.n_kv_heads == 4)
+        launch_t<4, VB, 4, false, 2>(L, cc, q, len, idx, k, w, terms, s);
+      else
+        launch_t<4, VB, 8, false, 2>(L, cc, q, len, idx, k, w, terms, s);
       return;
     }
   }

@@ -57,6 +57,21 @@
 // scores run on the same fp16 MFMA with the group's scale applied after it,
 // and the 2^14 is folded into the constants that turn scores into sigma and
 // log2 units.
+//
+// MXFP4 keys and query (key format 2; Jet-QSparse abstract: FP4 keys with a
+// native FP4 query-key product): a fourth build, BKV_KEY_FP4=1.  Each
+// workgroup quantises its G query rows per 32-channel quarter to E2M1 codes
+// with an E8M0 scale (quantise_lane_e8, the keys' own rule), and a 16-token
+// tile's scores are one v_mfma_scale_f32_16x16x128_f8f6f4: A = the tile's
+// 1 KB of key chunks as loaded (lane (kb, n) holds quarter kb of token n, see
+// k_chunk_offset_e8) with the token's E8M0 byte of that quarter as its
+// scale; B = column n holding query head n mod G (the GQA group repeated
+// across the 16 columns) with that head's quarter scale.  Both scales are
+// applied inside the MFMA, so each output element is already the whole
+// logit, in the same lane positions the fp16 path reaches after its
+// reduction over groups; no key is unpacked on the VALU.  The key scale
+// words (one per token) travel through the per-wave meta slot like the
+// other meta.
 #include "bkv_internal.h"
 #include "fused_tail.h"
 #include "quant_lane.h"
@@ -68,12 +83,18 @@
 #ifndef BKV_KEY_MXFP4
 #define BKV_KEY_MXFP4 0
 #endif
+#ifndef BKV_KEY_FP4
+#define BKV_KEY_FP4 0
+#endif
 #if BKV_QUERY_INT8
 #define BKV_SCAN_KERNEL decode_approx_q8_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_q8
 #elif BKV_KEY_MXFP4
 #define BKV_SCAN_KERNEL decode_approx_mx_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_mx
+#elif BKV_KEY_FP4
+#define BKV_SCAN_KERNEL decode_approx_fp4_kernel
+#define BKV_SCAN_LAUNCH launch_decode_approx_fp4
 #else
 #define BKV_SCAN_KERNEL decode_approx_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx
@@ -84,6 +105,7 @@ namespace {
 
 constexpr bool kQ8 = BKV_QUERY_INT8 != 0;
 constexpr bool kMX = BKV_KEY_MXFP4 != 0;
+constexpr bool kFP4 = BKV_KEY_FP4 != 0;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -188,6 +210,14 @@ struct QueryOperand<true> {
 template <int KB>
 using QOp = typename QueryOperand<kQ8 && (KB > 0)>::type;
 typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// Key format 2: this lane's B operand of the FP4 scores (column n = query
+// head n mod G, K-block kb: 32 E2M1 codes in dwords 0..3) and its E8M0 scale.
+struct Fp4Query {
+  intx8 b;
+  uint32_t sc;
+};
 
 // Lane l's value from lane l ^ m of the wave.
 __device__ inline int lane_xor(int v, int m, int lane) { return __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, v); }
@@ -277,7 +307,10 @@ __device__ inline void load_step(Step<KB, VB, G>& S, const uint8_t* __restrict__
 #pragma unroll
     for (int pc = 0; pc < VB / 2; ++pc) S.vd[pc] = *reinterpret_cast<const u32x4*>(vt + 1024 * pc);
   }
-  const uint32_t* mp = (lane < 32 ? kmeta : vmeta) + (size_t)(((lane & 31) >> 3) >> mshift) * cap + t0 + 4 * (lane & 7);
+  // (key format 2: lanes < 32 read the one plane of key scale words, lanes
+  // 8..31 repeating lanes 0..7)
+  const size_t plane = (size_t)(((lane & 31) >> 3) >> mshift) * cap;
+  const uint32_t* mp = (lane < 32 ? kmeta + (kFP4 ? 0 : plane) : vmeta + plane) + t0 + 4 * (lane & 7);
   if (!SIGONLY || lane < 32) S.meta = *reinterpret_cast<const u32x4*>(mp);
 }
 
@@ -314,7 +347,8 @@ constexpr int kZS = (VB == 4) ? 2 : 4;
 // selection scores.
 template <int KB, int VB, int G, bool MASK, bool SKIP = false, bool SIGONLY = false>
 __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x4 (&km)[2][Step<KB, VB, G>::NT],
-                                          const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const QOp<KB> (&bq)[kGroups],
+                                          const u32x4 (&vm)[Step<KB, VB, G>::NT][2], const uint32_t (&ks)[2],
+                                          const Fp4Query& fq, const QOp<KB> (&bq)[kGroups],
                                           const float (&qs)[Step<KB, VB, G>::NT], const float (&qsc)[Step<KB, VB, G>::NT],
                                           WaveState<Step<KB, VB, G>::NT, kZS<VB>>& ws,
                                           floatx4* __restrict__ sig_row, int t0, int len, int n, int kb,
@@ -332,7 +366,12 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) di[T][tt] = (intx4){0, 0, 0, 0};
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < 2 && kFP4; ++tt) {  // key format 2: one scaled FP4 MFMA per token tile
+    const intx8 a = {(int)cur.kc[tt][0], (int)cur.kc[tt][1], (int)cur.kc[tt][2], (int)cur.kc[tt][3], 0, 0, 0, 0};
+    d[0][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, fq.b, d[0][tt], 4, 4, 0, ks[tt], 0, fq.sc);
+  }
+#pragma unroll
+  for (int tt = 0; tt < 2 && !kFP4; ++tt) {
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
       uint32_t y;
@@ -375,16 +414,20 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float part = 0.f;
-#pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        const uint32_t mw = km[tt][T][i];
-        part = fmaf(d[T][tt][i], lo_half(mw), fmaf(hi_half(mw), qs[T], part));
-      }
-      if constexpr (G == 8) {
-        part += dpp<kRowRor8>(part);
+      if constexpr (kFP4) {
+        part = d[0][tt][i];  // the whole logit (both scales applied in the MFMA)
       } else {
-        part += dpp<kRowRor4>(part);
-        part += dpp<kRowRor8>(part);
+#pragma unroll
+        for (int T = 0; T < NT; ++T) {
+          const uint32_t mw = km[tt][T][i];
+          part = fmaf(d[T][tt][i], lo_half(mw), fmaf(hi_half(mw), qs[T], part));
+        }
+        if constexpr (G == 8) {
+          part += dpp<kRowRor8>(part);
+        } else {
+          part += dpp<kRowRor4>(part);
+          part += dpp<kRowRor8>(part);
+        }
       }
       if constexpr (MASK) part = ((t0 + 16 * tt + 4 * kb + i) < len) ? part : -INFINITY;
       if constexpr (SKIP) part = ((skipw >> (16 * tt + 4 * kb + i)) & 1u) ? -INFINITY : part;
@@ -507,7 +550,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
 
   const uint8_t* kbase = k_codes + (size_t)u * k_unit_bytes(KB, cap);
   const uint8_t* vbase = v_codes + (size_t)u * v_unit_bytes(VB, cap);
-  const uint32_t* kmeta = k_meta + (size_t)u * meta_planes(mshift) * cap;
+  // (key format 2: one plane of scale words per unit)
+  const uint32_t* kmeta = k_meta + (size_t)u * (kFP4 ? 1 : meta_planes(mshift)) * cap;
   const uint32_t* vmeta = v_meta + (size_t)u * meta_planes(mshift) * cap;
 
   // FUSE: the split's histogram of selection scores (fused_tail.h)
@@ -519,6 +563,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   __shared__ float s_qsum[G][kGroups];   // per quarter: sum of q (INT8: s * sum of q')
   __shared__ int8_t s_q8[kQ8 ? G : 1][kHeadDim];  // INT8: the codes q'
   __shared__ float s_qsc[kQ8 ? G : 1][kGroups];   // INT8: the scale s of each quarter's group
+  __shared__ __attribute__((aligned(16))) uint32_t s_q4[kFP4 ? G : 1][kGroups][4];  // FP4: codes per quarter
+  __shared__ uint32_t s_qe[kFP4 ? G : 1][kGroups];  // FP4: the quarter's E8M0 scale byte
   {
     const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
     if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
@@ -545,6 +591,21 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
           s_qsc[hh][c / kGroup] = sc;
         }
       }
+    } else if constexpr (kFP4) {
+      // a quad of threads per (head, quarter), 8 channels each: the same
+      // rule as the keys' (whole waves: G * 16 is 64 or 128)
+      if (tid < G * 16) {
+        const int hh = tid >> 4, grp = (tid >> 2) & 3, sub = tid & 3;
+        float x[8];
+        halves8(*reinterpret_cast<const uint4*>(&s_q[hh][grp * kGroup + 8 * sub]), x);
+        uint32_t code[8];
+        const uint32_t e8 = quantise_lane_e8(x, code);
+        uint32_t f = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f |= code[j] << (4 * j);
+        s_q4[hh][grp][sub] = f;
+        if (sub == 0) s_qe[hh][grp] = e8;
+      }
     } else if (tid < G * kGroups) {
       const int hh = tid / kGroups, g = tid % kGroups;
       float s = 0.f;
@@ -568,14 +629,22 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
         float x[8];
         halves8(w4, x);
         uint32_t code[8];
-        const uint32_t mw = (kMX && kv == 0) ? quantise_lane_mx(x, code)
-                                             : quantise_lane(x, sub, grp, mshift, (float)((1 << (kv ? VB : KB)) - 1), code);
-        if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
+        const uint32_t mw = (kMX && kv == 0)    ? quantise_lane_mx(x, code)
+                            : (kFP4 && kv == 0) ? quantise_lane_e8(x, code)
+                                                : quantise_lane(x, sub, grp, mshift, (float)((1 << (kv ? VB : KB)) - 1), code);
+        if (kFP4 && kv == 0) {
+          if (sub == 0)
+            reinterpret_cast<uint8_t*>(const_cast<uint32_t*>(k_meta))[((size_t)u * cap + p) * kGroups + grp] = (uint8_t)mw;
+        } else if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0) {
           const_cast<uint32_t*>(kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + p] =
               mw;
+        }
         *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + p) * kHeadDim + c0) = w4;
         if (kv == 0) {
-          store_key_codes<KB>(const_cast<uint8_t*>(k_codes) + (size_t)u * k_unit_bytes(KB, cap), p, sub, grp, code);
+          if constexpr (kFP4)
+            store_key_codes_e8(const_cast<uint8_t*>(k_codes) + (size_t)u * k_unit_bytes(KB, cap), p, sub, grp, code);
+          else
+            store_key_codes<KB>(const_cast<uint8_t*>(k_codes) + (size_t)u * k_unit_bytes(KB, cap), p, sub, grp, code);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) s_newv[c0 + j] = (uint8_t)code[j];
@@ -631,8 +700,16 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     else
       qsc[T] = 1.0f;
   }
+  Fp4Query fq;  // key format 2: column n = head h, K-block kb
+  fq.b = (intx8){0, 0, 0, 0, 0, 0, 0, 0};
+  fq.sc = 127u;
+  if constexpr (kFP4) {
+    const uint4 w = *reinterpret_cast<const uint4*>(&s_q4[h][kb][0]);
+    fq.b = (intx8){(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    fq.sc = s_qe[h][kb];
+  }
 #pragma unroll
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < kGroups && !kFP4; ++g) {
     const int gq = (G == 8) ? (2 * (g >> 1) + (n >> 3)) : (n >> 2);
     if constexpr (kQ8) {  // the codes of channels 32g + 8kb + key_byte_channel(i), in column (g, h) only
       uint64_t v = 0;
@@ -709,7 +786,10 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
 
   // Meta of the step -> this lane's cells: lane (n, kb) needs its column's
   // group for tokens 16tt + 4kb + i.
-  auto meta_cells = [&](const u32x4& meta, u32x4 (&km)[2][NT], u32x4 (&vm)[NT][2]) {
+  // Key format 2: lane (n, kb) takes the scale word of token 16tt + n (cell
+  // (K, tt, n/4, 0), entry n mod 4) and its byte kb (the MFMA reads the low
+  // byte of its scale operand).
+  auto meta_cells = [&](const u32x4& meta, u32x4 (&km)[2][NT], u32x4 (&vm)[NT][2], uint32_t (&ks)[2]) {
     wave_lds_order();  // the previous step's reads of the slot come first
     slot[wcell] = meta;
     wave_lds_order();
@@ -718,10 +798,14 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
       const int gq = (G == 8) ? (2 * T + (n >> 3)) : (n >> 2);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        km[tt][T] = slot[meta_cell(0, tt, kb, gq)];
+        if constexpr (!kFP4) km[tt][T] = slot[meta_cell(0, tt, kb, gq)];
         vm[T][tt] = slot[meta_cell(1, tt, kb, gq)];
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+      ks[tt] = kFP4 ? reinterpret_cast<const uint32_t*>(slot)[4 * meta_cell(0, tt, n >> 2, 0) + (n & 3)] >> (8 * kb)
+                    : 0u;
   };
 
   // One whole step: prefetch the wave's step kAhead steps on into `nxt`
@@ -736,18 +820,20 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     const int tn = (t0 + kAhead * kScanWaves * kTile) < t_end ? t0 + kAhead * kScanWaves * kTile : t0;
     load_step<KB, VB, G, SIGONLY>(nxt, kbase, vbase, kmeta, vmeta, cap, tn, lane, mshift);
     u32x4 km[2][NT], vm[NT][2];
-    meta_cells(cur.meta, km, vm);
+    uint32_t ks[2];
+    meta_cells(cur.meta, km, vm, ks);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, false, SKIP, SIGONLY>(cur, km, vm, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
+    scan_step<KB, VB, G, false, SKIP, SIGONLY>(cur, km, vm, ks, fq, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, len, n, kb, c_s2,
                                       SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     if (++sig_count == kSigBatch) flush_sig();
   };
   // The step that straddles the end of the split (at most one per wave).
   auto last_step = [&](Step<KB, VB, G>& cur, int t0) {
     u32x4 km[2][NT], vm[NT][2];
-    meta_cells(cur.meta, km, vm);
+    uint32_t ks[2];
+    meta_cells(cur.meta, km, vm, ks);
     if (sig_count == 0) sig_first = t0;
-    scan_step<KB, VB, G, true, SKIP, SIGONLY>(cur, km, vm, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
+    scan_step<KB, VB, G, true, SKIP, SIGONLY>(cur, km, vm, ks, fq, bq, qs, qsc, ws, s_sig[wv][sig_count], t0, t_end, n, kb, c_s2,
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
@@ -1055,7 +1141,7 @@ hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 
 }  // namespace
 
-#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4
+#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4 && !BKV_KEY_FP4
 hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                                float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
                                const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s) {
@@ -1079,13 +1165,15 @@ hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                 int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                 const uint16_t* v_new, hipStream_t s) {
-#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4
+#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4 && !BKV_KEY_FP4
   if (L.query_bits == 8)
     return launch_decode_approx_q8(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
   if (L.key_format == 1)
     return launch_decode_approx_mx(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
+  if (L.key_format == 2)
+    return launch_decode_approx_fp4(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
 #endif
-#if BKV_KEY_MXFP4  // (4-bit keys only)
+#if BKV_KEY_MXFP4 || BKV_KEY_FP4  // (4-bit keys only)
   return L.v_bits == 4 ? launch_g<4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s)
                        : launch_g<4, 2>(L, c, q, len, sigma, w, chunk, idx, ksel, skip, sigonly, k_new, v_new, s);
 #else

@@ -484,7 +484,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       __builtin_amdgcn_sched_barrier(0);
       {
         float ex[G], ap[G];
-        run_logits<KB, G, true, true, false, false>(kr, part, qh, s_qrun, nullptr, nullptr, nullptr, ex, ap);
+        run_logits<KB, G, true, true, false, 0>(kr, part, qh, s_qrun, nullptr, nullptr, nullptr, ex, ap);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           ex[h] = sum8(ex[h]);

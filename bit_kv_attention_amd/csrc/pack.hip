@@ -19,8 +19,10 @@
 namespace bkv {
 namespace {
 
-// MXK: MXFP4 keys (quantise_lane_mx) instead of affine codes.
-template <int KB, int VB, bool MXK = false>
+// KF: the key format -- 0 affine codes (quantise_lane), 1 MXFP4 with fp16
+// scales (quantise_lane_mx), 2 MXFP4 with E8M0 scales in the 32-channel chunk
+// layout (quantise_lane_e8, one scale byte per token and quarter).
+template <int KB, int VB, int KF = 0>
 __global__ __launch_bounds__(256) void pack_append_kernel(
     uint8_t* __restrict__ k_codes, uint8_t* __restrict__ v_codes, uint32_t* __restrict__ k_meta,
     uint32_t* __restrict__ v_meta, uint16_t* __restrict__ k_shadow, uint16_t* __restrict__ v_shadow,
@@ -59,13 +61,20 @@ __global__ __launch_bounds__(256) void pack_append_kernel(
     float x[8];
     halves8(w4, x);
     uint32_t code[8];
-    const uint32_t meta =
-        (MXK && kv == 0) ? quantise_lane_mx(x, code) : quantise_lane(x, sub, grp, mshift, qmax, code);
-    if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0)
+    const uint32_t meta = (KF == 1 && kv == 0)   ? quantise_lane_mx(x, code)
+                          : (KF == 2 && kv == 0) ? quantise_lane_e8(x, code)
+                                                 : quantise_lane(x, sub, grp, mshift, qmax, code);
+    if (KF == 2 && kv == 0) {
+      if (sub == 0) reinterpret_cast<uint8_t*>(k_meta)[((size_t)u * cap + t) * kGroups + grp] = (uint8_t)meta;
+    } else if (sub == 0 && (grp & ((1 << mshift) - 1)) == 0) {
       (kv ? v_meta : k_meta)[((size_t)u * meta_planes(mshift) + (grp >> mshift)) * cap + t] = meta;
+    }
     *reinterpret_cast<uint4*>((kv ? v_shadow : k_shadow) + ((size_t)u * cap + t) * kHeadDim + c0) = w4;
     if (kv == 0) {
-      store_key_codes<KB>(k_codes + (size_t)u * k_unit_bytes(KB, cap), t, sub, grp, code);
+      if constexpr (KF == 2)
+        store_key_codes_e8(k_codes + (size_t)u * k_unit_bytes(KB, cap), t, sub, grp, code);
+      else
+        store_key_codes<KB>(k_codes + (size_t)u * k_unit_bytes(KB, cap), t, sub, grp, code);
     } else {
       uint2 cw;
       cw.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
@@ -109,7 +118,11 @@ hipError_t launch_kv(const bkv_layout& L, const bkv_cache& c, const uint16_t* k_
   dim3 grid(tiles, L.batch * L.n_kv_heads);
   (void)hipGetLastError();  // report only this launch's status
   if (KB == 4 && L.key_format == 1)
-    pack_append_kernel<KB, VB, true><<<grid, 256, 0, s>>>(
+    pack_append_kernel<KB, VB, 1><<<grid, 256, 0, s>>>(
+        static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
+        c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, 0);
+  else if (KB == 4 && L.key_format == 2)
+    pack_append_kernel<KB, VB, 2><<<grid, 256, 0, s>>>(
         static_cast<uint8_t*>(c.k_codes), static_cast<uint8_t*>(c.v_codes), c.k_meta, c.v_meta,
         c.k_shadow, c.v_shadow, k_new, v_new, n_new, pos, L.n_kv_heads, L.capacity, 0);
   else

@@ -90,6 +90,44 @@ __device__ inline uint32_t quantise_lane_mx(const float (&x)[8], uint32_t (&code
   return s16;
 }
 
+// Key format 2 and its query (OCP Microscaling block format with the scale
+// kept as E8M0; the Jet-QSparse abstract's FP4 query-key product): the same
+// rounding as quantise_lane_mx, but X = floor(log2(amax)) - 2 is not clamped
+// (fp16 inputs put it in [-26, 13]) and the result is the E8M0 byte X + 127
+// (127 for an all-zero quarter, whose codes are all 0).  Same lane set.
+__device__ inline uint32_t quantise_lane_e8(const float (&x)[8], uint32_t (&code)[8]) {
+#pragma clang fp contract(off)
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, true)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, true)));
+  if (a == 0.0f) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) code[j] = 0u;
+    return 127u;
+  }
+  // a >= 2^-24 is a normal fp32 number: its exponent field is floor(log2 a)
+  const int X = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127 - 2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = __builtin_amdgcn_ldexpf(fabsf(x[j]), -X);  // exact
+    const int idx = (r > 0.25f) + (r >= 0.75f) + (r > 1.25f) + (r >= 1.75f) + (r > 2.5f) + (r >= 3.5f) + (r > 5.0f);
+    code[j] = (uint32_t)(idx | ((x[j] < 0.0f && idx != 0) ? 8 : 0));
+  }
+  return (uint32_t)(X + 127);
+}
+
+// The 8 codes of a lane (channels 32grp + 8sub + j) into their key chunk of
+// key format 2: nibbles 8sub .. 8sub+7, i.e. the chunk's dword sub.
+__device__ inline void store_key_codes_e8(uint8_t* __restrict__ unit_codes, int t, int sub, int grp,
+                                          const uint32_t (&code)[8]) {
+  uint32_t f = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f |= code[j] << (4 * j);
+  *reinterpret_cast<uint32_t*>(unit_codes + k_chunk_offset_e8(t, grp) + 4 * sub) = f;
+}
+
 // The 8 fp16 values of a 16-byte piece as floats (exact).
 __device__ inline void halves8(const uint4& w4, float (&x)[8]) {
   const uint32_t ww[4] = {w4.x, w4.y, w4.z, w4.w};

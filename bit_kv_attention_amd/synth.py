@@ -41,7 +41,7 @@ class Workload:
     n_outlier: int = 4
     outlier_scale: float = 8.0
     query_bits: int = 0  # 8: approximate scores against the INT8 query (HACK's Eq. (4))
-    key_format: int = 0  # 1: MXFP4 keys (E2M1 codes, power-of-two scale per group of 32)
+    key_format: int = 0  # 1: MXFP4 keys, fp16 query; 2: MXFP4 keys (E8M0 scales) and MXFP4 query
 
     @property
     def G(self) -> int:
@@ -66,8 +66,10 @@ CODEC_WORKLOADS = [
     Workload("llama8b_k1v2g64_L32768", 4, 32, 8, 128, 32768, 1, 2, 64, 256, 64, 1006),
     # HACK's INT8-query scores on the 8B K4V4 cache
     Workload("llama8b_k4v4_q8_L32768", 4, 32, 8, 128, 32768, 4, 4, 32, 256, 64, 1007, query_bits=8),
-    # MXFP4 keys, 4-bit values
-    Workload("llama8b_mxfp4v4_L32768", 4, 32, 8, 128, 32768, 4, 4, 32, 256, 64, 1008, key_format=1),
+    # MXFP4 keys scored against the MXFP4 query (the FP4 query-key product), 4-bit values
+    Workload("llama8b_mxfp4v4_L32768", 4, 32, 8, 128, 32768, 4, 4, 32, 256, 64, 1008, key_format=2),
+    # the variant: MXFP4 keys scored against the fp16 query
+    Workload("llama8b_mxfp4v4_f16q_L32768", 4, 32, 8, 128, 32768, 4, 4, 32, 256, 64, 1009, key_format=1),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + CODEC_WORKLOADS}
 

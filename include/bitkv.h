@@ -47,8 +47,8 @@
  *    a failed launch (hipGetLastError) of one of the call's kernels.
  *  - Supported shapes: head_dim 128, group 32 or 64, k_bits in {1, 2, 3, 4},
  *    v_bits in {2, 4}, n_q_heads / n_kv_heads in {4, 8}, capacity a positive
- *    multiple of 32, batch in [1, 256], query_bits 0 or 8, key_format 0 or 1
- *    (MXFP4: k_bits 4, group 32, query_bits 0).  Others return
+ *    multiple of 32, batch in [1, 256], query_bits 0 or 8, key_format 0, 1
+ *    or 2 (1 and 2: k_bits 4, group 32, query_bits 0).  Others return
  *    BKV_E_UNSUPPORTED or BKV_E_SHAPE.
  *  - Query head h attends with KV head h / (n_q_heads / n_kv_heads).
  *  - Softmax scale 1/sqrt(head_dim); no mask inside the cached tokens.
@@ -102,7 +102,19 @@ typedef struct {
                        * sign << 3 | the E2M1 magnitude index (0, 0.5, 1,
                        * 1.5, 2, 3, 4, 6) of x / 2^X, nearest, ties to the
                        * even index, clamped at 6.  Needs k_bits 4, group 32,
-                       * query_bits 0; the key bit layout is that of K4.    */
+                       * query_bits 0; the key bit layout is that of K4.  The
+                       * approximate scores take the fp16 query (a variant
+                       * kept beside format 2).
+                       * 2 = MXFP4 keys scored against an MXFP4 query
+                       * (Jet-QSparse abstract: FP4 keys and a native FP4
+                       * query-key product): keys and, inside the scan, each
+                       * 32-channel block of each query head get the same
+                       * rule as format 1 with the scale kept as the E8M0
+                       * byte X + 127 (X unclamped; 127 for an all-zero
+                       * block), and the scores are the FP4 x FP4 products
+                       * on gfx950's scaled FP4 MFMA.  Layouts below.  The
+                       * exact logits of the correction keep the fp16 query.
+                       * Needs k_bits 4, group 32, query_bits 0.            */
 } bkv_layout;
 
 /*
@@ -126,6 +138,14 @@ typedef struct {
  *           tile.  16-byte aligned.
  *  k_meta,  [B][Hkv][D/group][capacity] uint32: fp16 scale in the low half,
  *  v_meta   fp16 zero point (group minimum) in the high half.
+ *  Key format 2 instead:
+ *  k_codes  [B][Hkv][capacity/16][64][16] bytes: chunk 16g + r of a block
+ *           holds the 32 codes of channels 32g..32g+31 of token r of the
+ *           block, channel 32g + j in nibble j (low nibble first).
+ *  k_meta   [B][Hkv][capacity] uint32: byte g (bits 8g..8g+7) of token t's
+ *           word is the E8M0 scale of its channels 32g..32g+31 (only these
+ *           B*Hkv*capacity words are used: bkv_k_meta_bytes gives the size;
+ *           a buffer of meta_bytes_each is also large enough).
  *  k_shadow,[B][Hkv][capacity][D] fp16: the exact input rows.  Device memory,
  *  v_shadow or pinned host memory the device can address (e.g. hipHostMalloc
  *           with default flags): qattn_correct then gathers the selected
@@ -144,6 +164,11 @@ typedef struct {
 bkv_status bkv_cache_bytes(const bkv_layout* layout, size_t* k_codes_bytes,
                            size_t* v_codes_bytes, size_t* meta_bytes_each,
                            size_t* shadow_bytes_each);
+
+/* Bytes k_meta needs for `layout`: meta_bytes_each for key formats 0 and 1,
+ * B*Hkv*capacity*4 (one word of four E8M0 bytes per token) for key format 2.
+ * Host only. */
+bkv_status bkv_k_meta_bytes(const bkv_layout* layout, size_t* bytes);
 
 /* Workspace bytes that cover qattn_decode_approx, topk_select and
  * qattn_correct (and every variant below) for every step whose longest

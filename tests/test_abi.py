@@ -51,6 +51,10 @@ def test_cache_and_workspace_sizes(bk):
     assert sb == units * 1024 * 128 * 2
     kb2, _, mb64, _ = bk.bkv_cache_bytes(L(bk, k_bits=2, group=64))  # 2-bit keys; one meta word per 64 channels
     assert kb2 == units * 1024 * 128 * 2 // 8 and mb64 == units * 2 * 1024 * 4
+    # key meta: the planes for key formats 0 and 1, one word of four E8M0 bytes per token for format 2
+    assert bk.bkv_k_meta_bytes(L(bk, k_bits=3, v_bits=2)) == mb
+    assert bk.bkv_k_meta_bytes(L(bk, k_bits=4, key_format=1)) == mb
+    assert bk.bkv_k_meta_bytes(L(bk, k_bits=4, key_format=2)) == units * 1024 * 4
     w1 = bk.bkv_workspace_bytes(L(bk), 1024, 64)
     w0 = bk.bkv_workspace_bytes(L(bk), 0, 0)
     assert w1 >= 4 * 32 * 130 * 4 + 4 * 32 * 2 * 260 * 4 and w0 > 0
@@ -84,9 +88,10 @@ def test_unsupported_head_dim_and_group(bk):
     for qb, want in ((8, 0), (4, 3), (16, 3), (-1, 3)):  # query of the approximate scores: fp16 or INT8
         lay = bk.Layout(4, 32, 8, 128, 4, 4, 32, 1024, qb)
         assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == want, qb
-    # key format: MXFP4 needs 4-bit keys, groups of 32 and the fp16 query
+    # key formats 1 and 2 (MXFP4) need 4-bit keys, groups of 32 and query_bits 0
     for args, want in (((4, 32, 0, 1), 0), ((3, 32, 0, 1), 3), ((4, 64, 0, 1), 3), ((4, 32, 8, 1), 3),
-                       ((4, 32, 0, 2), 3)):
+                       ((4, 32, 0, 2), 0), ((3, 32, 0, 2), 3), ((4, 64, 0, 2), 3), ((4, 32, 8, 2), 3),
+                       ((4, 32, 0, 3), 3), ((4, 32, 0, -1), 3)):
         kb, g, qb, kf = args
         lay = bk.Layout(4, 32, 8, 128, kb, 4, g, 1024, qb, kf)
         assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, 4, C.byref(out)) == want, args

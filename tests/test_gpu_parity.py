@@ -347,7 +347,7 @@ def test_step_parity_window(P, kb, vb, G, W, fmt):
     selection on the GPU's scores (exact), the output against the oracle on
     the GPU's rows and on its own."""
     banner(f"step window kb={kb} vb={vb} G={G} W={W} {fmt}")
-    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
+    qb, kf = (8 if fmt == "q8" else 0), {"mx": 2, "mx1": 1}.get(fmt, 0)
     import torch
     import oracle
     from bit_kv_attention_amd.step import DecodeStep
@@ -427,7 +427,7 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs, fmt):
     may differ only by near-ties of the block score), the output against the
     oracle on both rows."""
     banner(f"step blocks kb={kb} vb={vb} G={G} nb={nb} bs={bs} {fmt}")
-    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
+    qb, kf = (8 if fmt == "q8" else 0), {"mx": 2, "mx1": 1}.get(fmt, 0)
     import torch
     import oracle
     from bit_kv_attention_amd import binding as bk
@@ -466,7 +466,7 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs, fmt):
 
 @pytest.mark.parametrize("kb,vb,G,g,fmt", [c + (32, "") for c in COMBOS] + [(2, 2, 4, 64, ""), (1, 2, 8, 64, ""),
                                             (4, 4, 4, 32, "q8"), (2, 2, 8, 64, "q8"),
-                                            (4, 2, 4, 32, "mx"), (4, 4, 8, 32, "mx")])
+                                            (4, 2, 4, 32, "mx"), (4, 4, 8, 32, "mx1")])
 def test_decode_select_equals_two_calls(P, kb, vb, G, g, fmt):
     """qattn_decode_select (selection inside the scan's launch) against
     qattn_decode_approx + topk_select on the same inputs: identical sigma, rows
@@ -474,7 +474,7 @@ def test_decode_select_equals_two_calls(P, kb, vb, G, g, fmt):
     empty sequences, k = 1, k >= len, and a budget past the in-launch limit
     (two launches)."""
     banner(f"decode_select kb={kb} vb={vb} G={G} g={g} {fmt}")
-    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
+    qb, kf = (8 if fmt == "q8" else 0), {"mx": 2, "mx1": 1}.get(fmt, 0)
     import torch
     import oracle
     from bit_kv_attention_amd.step import DecodeStep
@@ -517,7 +517,7 @@ def test_hybrid_host_correction(P, kb, vb, G, fmt):
     against the oracle on the GPU's rows, and against the all-GPU correction;
     ragged and empty sequences, k >= len, k = 0."""
     banner(f"hybrid host correction kb={kb} vb={vb} G={G} {fmt}")
-    qb, kf = (8 if fmt == "q8" else 0), (1 if fmt == "mx" else 0)
+    qb, kf = (8 if fmt == "q8" else 0), {"mx": 2, "mx1": 1}.get(fmt, 0)
     import torch
     from bit_kv_attention_amd import binding as bk
     from bit_kv_attention_amd.step import DecodeStep
@@ -727,17 +727,19 @@ def test_query_int8_decode_step_and_ends(P, kb, vb, G, g):
 
 
 # MXFP4 keys (E2M1 codes, one power-of-two scale per group of 32): both value
-# widths and both GQA group sizes.
-MX_CASES = [(4, 4), (2, 8), (4, 8), (2, 4)]
+# widths and both GQA group sizes, for key format 2 (E8M0 scales, scores
+# against the MXFP4 query on the scaled FP4 MFMA) and key format 1 (fp16
+# scales, scores against the fp16 query).
+MX_CASES = [(4, 4, 2), (2, 8, 2), (4, 8, 2), (2, 4, 2), (4, 4, 1), (2, 8, 1), (4, 8, 1), (2, 4, 1)]
 
 
-@pytest.mark.parametrize("vb,G", MX_CASES)
-def test_mxfp4_keys_step_parity(P, vb, G):
+@pytest.mark.parametrize("vb,G,kf", MX_CASES)
+def test_mxfp4_keys_step_parity(P, vb, G, kf):
     """Pack bit-exact, then scores, selection and output against the oracle
     with MXFP4 keys."""
-    banner(f"mxfp4 keys vb={vb} G={G}")
+    banner(f"mxfp4 keys vb={vb} G={G} key format {kf}")
     import oracle
-    w = P.Workload("mx", 2, 2 * G, 2, 128, 1000, 4, vb, 32, 24, 6, 500 + vb + G, key_format=1)
+    w = P.Workload("mx", 2, 2 * G, 2, 128, 1000, 4, vb, 32, 24, 6, 500 + vb + G, key_format=kf)
     pair = P.build_pair(w, L=1000, cap=1024)
     lens = np.array([1000, 651])
     k = 24
@@ -758,14 +760,14 @@ def test_mxfp4_keys_step_parity(P, vb, G):
     P.assert_close(r["out"], orc["out"], "out vs oracle(S_oracle)")
 
 
-@pytest.mark.parametrize("vb,G", [(4, 4), (2, 8)])
-def test_mxfp4_keys_decode_step_and_ends(P, vb, G):
+@pytest.mark.parametrize("vb,G,kf", [(4, 4, 2), (2, 8, 2), (4, 8, 1), (2, 4, 1)])
+def test_mxfp4_keys_decode_step_and_ends(P, vb, G, kf):
     """The one-launch step (MXFP4 append inside the scan), then k = 0 (the
     approximate output over the MXFP4 keys) and k = len (exact)."""
     import torch
     from bit_kv_attention_amd.step import DecodeStep
-    banner(f"mxfp4 keys step/ends vb={vb} G={G}")
-    w = P.Workload("mxs", 2, 2 * G, 2, 128, 900, 4, vb, 32, 16, 4, 600 + vb + G, key_format=1)
+    banner(f"mxfp4 keys step/ends vb={vb} G={G} key format {kf}")
+    w = P.Workload("mxs", 2, 2 * G, 2, 128, 900, 4, vb, 32, 16, 4, 600 + vb + G, key_format=kf)
     pair = P.build_pair(w, L=900, cap=928)
     lens = np.array([900, 517])
     pos = [int(x) - 1 for x in lens]
