@@ -74,6 +74,7 @@ _lib.qattn_correct_hybrid.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, _P, C
 _lib.qattn_exact_host.argtypes = [_LP, _P, _P, _P, _P, _P, C.c_int32, _P, C.c_int32]
 _lib.qattn_decode_fused.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, _P, C.c_size_t, _P]
 _lib.bkv_fused_supported.argtypes = [_LP, C.c_int32, C.c_int32, _P]
+_lib.qattn_decode_fused_noalloc.argtypes = [_LP, _CP, _P, _P, _P, _P, C.c_int32, _P, _P, _P, _P]
 for _f in ("bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_workspace_bytes", "bkv_select_in_scan", "kv_pack_append",
            "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks", "qattn_correct"):
     getattr(_lib, _f).restype = C.c_int
@@ -82,7 +83,7 @@ EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_wor
             "kv_pack_append", "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
             "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step", "qattn_decode_fused",
-            "bkv_fused_supported")
+            "bkv_fused_supported", "qattn_decode_fused_noalloc")
 
 
 def _check(fn: str, st: int) -> None:
@@ -324,3 +325,15 @@ def raw_status(fn: str, *args) -> int:
     """Call an entry point with raw ctypes arguments and return its status
     (used to exercise the host-side error paths)."""
     return int(getattr(_lib, fn)(*args))
+
+
+def qattn_decode_fused_noalloc(layout: Layout, cache: Cache, k_new, v_new, q, len_host, k: int, sigma, idx, out,
+                               stream=None) -> None:
+    """qattn_decode_fused on the library's own per-device workspace (no
+    workspace argument; the call allocates nothing)."""
+    lens = _host_i32(len_host)
+    view = cache.view()
+    _check("qattn_decode_fused_noalloc",
+           _lib.qattn_decode_fused_noalloc(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                           lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx), _ptr(out),
+                                           _stream(stream)))

@@ -4,9 +4,47 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bkv_internal.h"
 
 namespace bkv {
+
+// ---- the library-held workspace of qattn_decode_fused_noalloc -----------------
+// One array per device, held from the library's load until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): it uses the address hipGetSymbolAddress
+// returned on that device, kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with it current).
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+// Zero n words (a kernel, not a memset: callers may capture the launch into
+// a graph).
+__global__ void zero_words_kernel(uint32_t* __restrict__ p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
 
 int split_tokens(int units, int max_len) {
   // Work per workgroup: a multiple of kScanWaves waves x 32 tokens, sized so
@@ -434,6 +472,42 @@ bkv_status qattn_decode_fused(const bkv_layout* L, const bkv_cache* c, const uin
   if (!fused_shape_ok(L, w, chunk, k)) return BKV_E_UNSUPPORTED;
   const hipError_t e = launch_decode_fused(*L, *c, q, len, sigma, w, chunk, idx, k, k_new, v_new, out,
                                            (hipStream_t)stream);
+  if (e == hipErrorNotSupported) return BKV_E_UNSUPPORTED;
+  return e == hipSuccess ? BKV_OK : BKV_E_HIP;
+}
+
+bkv_status qattn_decode_fused_noalloc(const bkv_layout* L, const bkv_cache* c, const uint16_t* k_new,
+                                      const uint16_t* v_new, const uint16_t* q, const int32_t* len_host, int32_t k,
+                                      float* sigma, int32_t* idx, float* out, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (k < 0) return BKV_E_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return BKV_E_NULL;
+  if (!q || !sigma || !out || (!idx && k > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  if (k_new)
+    for (int b = 0; b < L->batch; ++b)
+      if (len.v[b] < 1) return BKV_E_CAPACITY;  // the new token goes to len - 1
+  const int units = L->batch * L->n_kv_heads;
+  const int chunk = split_tokens(units, max_len);
+  const Workspace need = workspace_layout(nullptr, *L, max_len, k, false);
+  if (need.bytes > kScratchBytes) return BKV_E_WORKSPACE;
+  if (!fused_shape_ok(L, need, chunk, k)) return BKV_E_UNSUPPORTED;
+  if (!decode_fused_fits(*L, need, k_new != nullptr)) return BKV_E_UNSUPPORTED;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return BKV_E_HIP;
+  const Workspace w = workspace_layout(ws, *L, max_len, k, false);
+  const hipStream_t s = (hipStream_t)stream;
+  // the counters and the flag word, which lead the workspace, start at zero
+  // (the array keeps whatever the last call on this device left)
+  const size_t nz = (size_t)(reinterpret_cast<char*>(w.part.acc) - static_cast<char*>(ws)) / 4;
+  (void)hipGetLastError();
+  zero_words_kernel<<<dim3((unsigned)((nz + 255) / 256)), 256, 0, s>>>(static_cast<uint32_t*>(ws), nz);
+  if (hipGetLastError() != hipSuccess) return BKV_E_HIP;
+  const hipError_t e = launch_decode_fused(*L, *c, q, len, sigma, w, chunk, idx, k, k_new, v_new, out, s);
   if (e == hipErrorNotSupported) return BKV_E_UNSUPPORTED;
   return e == hipSuccess ? BKV_OK : BKV_E_HIP;
 }

@@ -184,6 +184,9 @@ hipError_t launch_decode_approx(const bkv_layout& L, const bkv_cache& c, const u
 // launch whose workgroups of a unit meet at barriers.  hipErrorNotSupported
 // when the layout has no fused kernel or the grid does not fit the device at
 // once (nothing launched).
+// Whether launch_decode_fused can run this layout and grid on the current
+// device (the same test it makes before launching).
+bool decode_fused_fits(const bkv_layout& L, const Workspace& w, bool append);
 hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                                float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
                                const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s);

@@ -1102,6 +1102,17 @@ static int resident_workgroups(const void* fn, int& cache) {
   return per * cus;
 }
 
+// Whether the fused grid (nsplit x units workgroups) is resident on the
+// current device at once, as the unit barriers need.
+template <int KB, int VB, int G>
+bool fused_fits_t(const bkv_layout& L, const Workspace& w, bool append) {
+  static int occ_append = 0, occ_plain = 0;  // (per kernel; the same on every device of this build)
+  const void* fn = append ? reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true>)
+                          : reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, true>);
+  return (long long)resident_workgroups(fn, append ? occ_append : occ_plain) >=
+         (long long)w.nsplit * L.batch * L.n_kv_heads;
+}
+
 template <int KB, int VB, int G>
 hipError_t launch_fused_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                           float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel, const uint16_t* k_new,
@@ -1113,11 +1124,7 @@ hipError_t launch_fused_t(const bkv_layout& L, const bkv_cache& c, const uint16_
   FusedArgs fa = w.fused;
   fa.out = out;
   // the unit barriers need every workgroup resident at once
-  static int occ_append = 0, occ_plain = 0;  // (per kernel; the same on every device of this build)
-  const void* fn = k_new ? reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true>)
-                         : reinterpret_cast<const void*>(&BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, true>);
-  if ((long long)resident_workgroups(fn, k_new ? occ_append : occ_plain) < (long long)grid.x * grid.y)
-    return hipErrorNotSupported;
+  if (!fused_fits_t<KB, VB, G>(L, w, k_new != nullptr)) return hipErrorNotSupported;
   (void)hipGetLastError();  // report only this launch's status
   if (k_new)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true><<<grid, 64 * kScanWaves, 0, s>>>(
@@ -1142,6 +1149,18 @@ hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 }  // namespace
 
 #if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4 && !BKV_KEY_FP4
+bool decode_fused_fits(const bkv_layout& L, const Workspace& w, bool append) {
+  if (L.query_bits != 0 || L.key_format != 0 || L.k_bits < 3) return false;
+  const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
+  const bool v4 = L.v_bits == 4;
+  if (L.k_bits == 4) {
+    if (v4) return g4 ? fused_fits_t<4, 4, 4>(L, w, append) : fused_fits_t<4, 4, 8>(L, w, append);
+    return g4 ? fused_fits_t<4, 2, 4>(L, w, append) : fused_fits_t<4, 2, 8>(L, w, append);
+  }
+  if (v4) return g4 ? fused_fits_t<3, 4, 4>(L, w, append) : fused_fits_t<3, 4, 8>(L, w, append);
+  return g4 ? fused_fits_t<3, 2, 4>(L, w, append) : fused_fits_t<3, 2, 8>(L, w, append);
+}
+
 hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                                float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
                                const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s) {

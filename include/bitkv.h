@@ -458,6 +458,26 @@ bkv_status qattn_decode_fused(const bkv_layout* layout, const bkv_cache* cache,
                               float* sigma, int32_t* idx, float* out, void* ws,
                               size_t ws_bytes, void* stream);
 
+/*
+ * qattn_decode_fused_noalloc -- qattn_decode_fused without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a 64 MiB array inside the library, one per device, held from
+ * the library's load until the process ends; the call allocates and frees
+ * nothing.  Each call first clears the array's counters with a small kernel
+ * on `stream` (no memset), then runs the same kernel as qattn_decode_fused;
+ * results are the same.  Every call on a device shares that device's array:
+ * calls that may overlap on one device (other streams, other threads) race
+ * and must be serialised by the caller.
+ * Errors: BKV_E_WORKSPACE if this step needs more than 64 MiB of workspace
+ * (bkv_workspace_bytes with the call's max length and k; the 32K and 128K
+ * headline shapes need about 12 and 46 MiB); otherwise as qattn_decode_fused.
+ */
+bkv_status qattn_decode_fused_noalloc(const bkv_layout* layout, const bkv_cache* cache,
+                                      const uint16_t* k_new, const uint16_t* v_new,
+                                      const uint16_t* q, const int32_t* len_host, int32_t k,
+                                      float* sigma, int32_t* idx, float* out, void* stream);
+
 /* Host only: *supported = 1 if the shape of a qattn_decode_fused call with
  * this layout, longest length max_len and k qualifies (the call can still
  * return BKV_E_UNSUPPORTED when the device cannot hold its grid at once). */
