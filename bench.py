@@ -49,6 +49,46 @@ def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32
     return D * kbits // 8 + kmeta + D * vbits // 8 + meta
 
 
+def read_ceiling(nbytes: int, torch, copies: int = 1) -> int:
+    """The plain streaming read (probe/read_ceiling.hip) of nbytes, 20 timed
+    launches per grid size after 3 untimed ones, rotating over `copies`
+    buffers (several copies whose total exceeds the 256 MB last-level cache
+    keep a buffer of the scan's size from being served by it); prints one
+    JSON line with GB/s per grid and the best."""
+    import ctypes as C
+    lib = C.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_kv_attention_amd",
+                              "libbkvprobe.so"))
+    lib.bkv_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    nbytes -= nbytes % 16
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+    out = torch.zeros(1 << 16, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    res = {}
+    turn = [0]
+    for grid in (256, 512, 1024, 2048, 4096, 8192):
+        def go():
+            buf = bufs[turn[0] % copies]
+            turn[0] += 1
+            st = lib.bkv_probe_read(buf.data_ptr(), nbytes, out.data_ptr(), grid, stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"bkv_probe_read: hipError {st}")
+        for _ in range(3):
+            go()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(20):
+            go()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        res[str(grid)] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+        log(f"read ceiling: {nbytes} B, grid {grid}: {us:.2f} µs, {nbytes / us / 1e3:.1f} GB/s")
+    best = max(v["GBps"] for v in res.values())
+    print(json.dumps({"read_ceiling_bytes": nbytes, "copies": copies, "grids": res, "best_GBps": best,
+                      "best_frac_of_8000": round(best / 8000.0, 4)}), flush=True)
+    return 0
+
+
 def num_splits(units: int, L: int) -> int:
     """The library's split count (about 256 workgroups, 256-token multiples)."""
     per = -(-units * L // 256)
@@ -82,6 +122,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=HOST_THREADS)
+    ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
+                    help="only time a plain streaming read of BYTES bytes (bit_kv_attention_amd/probe), "
+                         "the practical HBM read ceiling, over several grid sizes")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -104,6 +147,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n}), flush=True)
         return 0
+
+    if args.read_ceiling:
+        return read_ceiling(args.read_ceiling, torch, max(args.copies, 1))
 
     from bit_kv_attention_amd.synth import BY_NAME
     res = bench_one(BY_NAME[args.config], args, torch, shadow=args.shadow)

@@ -14,7 +14,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbitkv.so")
+# BKV_SANITIZE=1: the sanitizer build of the same sources (host-side checks
+# on the CPU; built by `python bit_kv_attention_amd/build.py --sanitize`)
+LIB_PATH = os.path.join(_HERE, "libbitkv_san.so" if os.environ.get("BKV_SANITIZE") == "1" else "libbitkv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

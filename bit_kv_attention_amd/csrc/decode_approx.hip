@@ -565,9 +565,25 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   __shared__ float s_qsc[kQ8 ? G : 1][kGroups];   // INT8: the scale s of each quarter's group
   __shared__ __attribute__((aligned(16))) uint32_t s_q4[kFP4 ? G : 1][kGroups][4];  // FP4: codes per quarter
   __shared__ uint32_t s_qe[kFP4 ? G : 1][kGroups];  // FP4: the quarter's E8M0 scale byte
+  // Each wave's first step is loaded right after the query row, so that its
+  // latency overlaps the prologue below.  The load is unconditional (a
+  // clamped, in-range address) so the prologue's wait for the query covers
+  // only the query; a wave that has no step, or that appends the new token
+  // (its stores must come first), loads again before its first step.
+  Step<KB, VB, G> sa, sb, sc;
+  int t0 = t_begin + kTile * wv;
+  constexpr bool kEarly = !SIGONLY;  // (the scores-only scan keeps two steps in flight: not here)
+  bool early = kEarly && t0 < t_end;
+  if constexpr (APPEND) {
+    const int p = len - 1;
+    if (p >= t_begin && p < t_end && wv == (((p - t_begin) >> 5) & (kScanWaves - 1))) early = false;
+  }
   {
     const uint4* qg = reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + (size_t)kvh * G) * kHeadDim);
-    if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qg[tid];
+    const uint4 qv = qg[tid % (G * kHeadDim / 8)];
+    if constexpr (kEarly)
+      load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, min(t0, cap - kTile), lane, mshift);
+    if (tid < G * kHeadDim / 8) reinterpret_cast<uint4*>(&s_q[0][0])[tid] = qv;
     if constexpr (FUSE) {  // the split's score histogram starts empty
       for (int i = tid; i < kFBins; i += 64 * kScanWaves) s_fh[i] = 0u;
       if (tid == 0) s_top = 0u;
@@ -837,10 +853,8 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
-  Step<KB, VB, G> sa, sb, sc;
-  int t0 = t_begin + kTile * wv;
   if constexpr (kAhead == 1) {
-    if (t0 < t_end) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
+    if (t0 < t_end && !early) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
     for (;;) {
       if (t0 + kTile > t_end) {
         if (t0 < t_end) last_step(sa, t0);

@@ -19,15 +19,24 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bitkv_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# BKV_SANITIZE=1: the same source under clang's AddressSanitizer and
+# UndefinedBehaviorSanitizer (CPU checks; the sanitizer runtime must be
+# preloaded, e.g. LD_PRELOAD=$(/opt/rocm/llvm/bin/clang -print-file-name=libclang_rt.asan-x86_64.so))
+_SANITIZE = os.environ.get("BKV_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (IEEE fp32: no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        if _SANITIZE:
+            cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp=libgomp", "-ffp-contract=off",
+                   "-fno-fast-math", "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-shared-libsan",
+                   "-fPIC", "-shared", _SRC, "-o", tmp, "-lm", "-lgomp"]
+        else:
+            cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off",
+                   "-fno-fast-math", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
