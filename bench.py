@@ -237,10 +237,16 @@ class Workbench:
                     bk.topk_select_blocks(lay, st.sigma, lens, self.NB, self.args.block, st.idx, st.ws)
                 else:
                     bk.topk_select_window(lay, st.sigma, lens, w.k, self.W, st.idx, st.ws)
+            if self.NB:  # block rows: the correction over contiguous tiles
+                correct = ("qattn_correct_blocks",
+                           lambda c: bk.qattn_correct_blocks(lay, c, q, lens, st.idx, self.NB, self.args.block, st.ws,
+                                                             st.out))
+            else:
+                correct = ("qattn_correct",
+                           lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))
             return [("kv_pack_append", lambda c: bk.kv_pack_append(lay, c, kn, vn, 1, self.pos)),
                     ("qattn_decode_approx", lambda c: bk.qattn_decode_approx(lay, c, q, lens, st.sigma, st.ws)),
-                    ("topk_select_blocks" if self.NB else "topk_select_window", select),
-                    ("qattn_correct", lambda c: bk.qattn_correct(lay, c, q, lens, st.idx, st.row, st.ws, st.out))]
+                    ("topk_select_blocks" if self.NB else "topk_select_window", select), correct]
         out = [("qattn_decode_step",
                 lambda c: bk.qattn_decode_step(lay, c, kn, vn, q, lens, w.k if self.in_scan else 0, st.sigma,
                                                st.idx, st.ws))]

@@ -69,6 +69,7 @@ _lib.bkv_select_in_scan.argtypes = [_LP, C.c_int32, C.c_int32, C.c_int32, _P]
 _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
+_lib.qattn_correct_blocks.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, C.c_int32, _P, C.c_size_t, _P, _P]
 _lib.qattn_score_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
 _lib.qattn_decode_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P]
 _lib.qattn_correct_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
@@ -85,7 +86,7 @@ EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_wor
             "kv_pack_append", "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
             "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step", "qattn_decode_fused",
-            "bkv_fused_supported", "qattn_decode_fused_noalloc")
+            "bkv_fused_supported", "qattn_decode_fused_noalloc", "qattn_correct_blocks")
 
 
 def _check(fn: str, st: int) -> None:
@@ -339,3 +340,13 @@ def qattn_decode_fused_noalloc(layout: Layout, cache: Cache, k_new, v_new, q, le
            _lib.qattn_decode_fused_noalloc(C.byref(layout), C.byref(view), _ptr(k_new), _ptr(v_new), _ptr(q),
                                            lens.ctypes.data, int(k), _ptr(sigma), _ptr(idx), _ptr(out),
                                            _stream(stream)))
+
+
+def qattn_correct_blocks(layout: Layout, cache: Cache, q, len_host, idx, n_blocks: int, block: int, ws, out,
+                         stream=None) -> None:
+    lens = _host_i32(len_host)
+    view = cache.view()
+    ws_bytes = ws.numel() * ws.element_size()
+    _check("qattn_correct_blocks", _lib.qattn_correct_blocks(C.byref(layout), C.byref(view), _ptr(q),
+                                                             lens.ctypes.data, _ptr(idx), int(n_blocks), int(block),
+                                                             _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))

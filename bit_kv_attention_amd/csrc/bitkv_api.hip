@@ -399,6 +399,27 @@ bkv_status qattn_correct(const bkv_layout* L, const bkv_cache* c, const uint16_t
                                                                                                    : BKV_E_HIP;
 }
 
+bkv_status qattn_correct_blocks(const bkv_layout* L, const bkv_cache* c, const uint16_t* q,
+                                const int32_t* len_host, const int32_t* idx, int32_t n_blocks, int32_t block, void* ws,
+                                size_t ws_bytes, float* out, void* stream) {
+  bkv_status st = check_layout(L);
+  if (st != BKV_OK) return st;
+  if ((st = check_cache(c)) != BKV_OK) return st;
+  if (n_blocks < 0 || block < 32 || block > 1024 || (block & (block - 1)) != 0 ||
+      (long long)n_blocks * block > 0x7FFFFFFF)
+    return BKV_E_ARG;
+  const int row = n_blocks * block;
+  if (!q || !ws || !out || (!idx && row > 0)) return BKV_E_NULL;
+  SeqArg len;
+  int max_len = 0;
+  if ((st = read_lens(L, len_host, &len, &max_len)) != BKV_OK) return st;
+  const Workspace w = workspace_layout(ws, *L, max_len, row, false);
+  if (ws_bytes < w.bytes) return BKV_E_WORKSPACE;
+  return launch_correct_rows(*L, *c, q, len, max_len, idx, row, w, out, (hipStream_t)stream) == hipSuccess
+             ? BKV_OK
+             : BKV_E_HIP;
+}
+
 bkv_status qattn_decode_step(const bkv_layout* L, const bkv_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                              const uint16_t* q, const int32_t* len_host, int32_t k, float* sigma, int32_t* idx,
                              void* ws, size_t ws_bytes, int32_t mode, void* stream) {

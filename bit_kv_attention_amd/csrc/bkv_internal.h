@@ -101,6 +101,10 @@ struct Partials {
 };
 
 constexpr int kCorrChunk = 32;  // selected tokens per correction workgroup
+// The correction of long rows of whole blocks (qattn_correct_blocks): one
+// record per kRowRec row entries, its exact part from the shadow rows
+// (correct.hip) and its approximate part from the scan's rows mode.
+constexpr int kRowRec = 512;
 // Per (b, h, chunk): m_exact, l_exact, m_approx, l_approx, then the exact and
 // the approximate value sums (D each), 16-byte aligned.
 constexpr int kCsStride = 4 + 2 * kHeadDim;
@@ -206,6 +210,21 @@ hipError_t launch_decode_approx_fp4(const bkv_layout& L, const bkv_cache& c, con
                                     const SeqArg& len, float* sigma, const Workspace& w, int chunk,
                                     int32_t* idx, int ksel, bool skip, bool sigonly, const uint16_t* k_new,
                                     const uint16_t* v_new, hipStream_t s);
+// The approximate parts of the correction records of long block rows (row
+// entries per unit; nrec records of kRowRec entries), one per build.
+hipError_t launch_rows_approx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                              const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s);
+hipError_t launch_rows_approx_q8(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                                 const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s);
+hipError_t launch_rows_approx_mx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                                 const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s);
+hipError_t launch_rows_approx_fp4(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                                  const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s);
+// qattn_correct on rows of whole blocks: the records' exact parts, their
+// approximate parts (launch_rows_approx) and the merge into out.
+hipError_t launch_correct_rows(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                               int max_len, const int32_t* idx, int row, const Workspace& w, float* out,
+                               hipStream_t s);
 // Rows of nb << lgb entries per unit: the nb best blocks of 1 << lgb tokens.
 // bkeys: kstride block keys per unit; counter: one arrival counter per unit.
 hipError_t launch_topk_blocks(const bkv_layout& L, const float* sigma, const SeqArg& len, int max_len, int nb,

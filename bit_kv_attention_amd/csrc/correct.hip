@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
                                                            const float* __restrict__ pacc, const float* __restrict__ cs,
                                                            const float* __restrict__ hx, float* __restrict__ out,
                                                            SeqArg lens, int Hq, int nsplit, int nchunk, int k,
-                                                           int rest) {
+                                                           int rest, int rec_tokens) {
   const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x & (kHeadDim - 1);
   // the group is the same in a whole wave: kept scalar, so the record loop and
   // the loads of each record's max and denominator stay scalar too
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
     return;
   }
   const int kk = min(k, n);
-  const int nc = (kk + kCorrChunk - 1) / kCorrChunk;
+  const int nc = (kk + rec_tokens - 1) / rec_tokens;  // records (each of rec_tokens row entries)
   const float* ps = cs + rec * (size_t)nchunk * kCsStride;
   // exact state of the selected tokens, approximate state of every token and
   // approximate terms of the selected tokens; a batch's loads of all three
@@ -174,6 +174,220 @@ __global__ __launch_bounds__(kHeadDim * kCombineGroups) void combine_kernel(cons
   const float mp = fmaxf(M, ex.m);
   const float fa = __builtin_amdgcn_exp2f(M - mp), fe = __builtin_amdgcn_exp2f(ex.m - mp);
   o[c] = (fa * A + fe * ex.a) / (fa * L + fe * ex.l);
+}
+
+// ---- exact terms of long rows (whole blocks of tokens) --------------------------
+// One workgroup per (unit, record of kRowRec row entries), four waves, each
+// taking 16-entry tiles of the record in turn with a softmax state of its own:
+//  * logits on v_mfma_f32_16x16x32_f16: A = the tile's fp16 shadow key rows,
+//    K-step ks taking channels 32ks .. 32ks+31, lane (r, kb) channels
+//    32ks + 8kb .. +7 of entry r's token (each of the four loads covers 64
+//    contiguous bytes of 16 rows); B = column n holding query head n mod G
+//    on the same channels.  D leaves entry 4kb+i's logit of head n mod G in
+//    lane (n, kb).
+//  * weights and the running max per head go through a per-wave LDS slot;
+//  * P.V on the VALU in fp32: lane (p, q) reads channels 8p .. 8p+7 of the
+//    shadow value rows of entries 4j + q (16 bytes each) and accumulates all
+//    G heads.
+// Entries < 0 or >= len are left out.  The record's exact part (m, l and the
+// value sums, log2 units) is written; its approximate part comes from the
+// scan's launch over the same rows.
+constexpr int kRowWaves = 4;
+
+__device__ inline float wmax16(float x) {  // max over the lanes n, n+16, n+32, n+48
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float wsum16(float x) {  // sum over the lanes n, n+16, n+32, n+48
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int G>
+__global__ __launch_bounds__(64 * kRowWaves) void exact_rows_kernel(
+    const uint16_t* __restrict__ k_shadow, const uint16_t* __restrict__ v_shadow, const uint16_t* __restrict__ q,
+    const int32_t* __restrict__ idx, float* __restrict__ cs, SeqArg lens, int Hq, int Hkv, int cap, int row,
+    int nchunk) {
+  const int u = blockIdx.y, rec_i = blockIdx.x;
+  const int b = u / Hkv, kvh = u - b * Hkv;
+  const int n_len = lens.v[b];
+  const int kk = min(row, n_len);
+  const int r_begin = rec_i * kRowRec;
+  if (r_begin >= kk) return;  // the combine reads only the records below kk
+  const int r_end = min(kk, r_begin + kRowRec);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, kb = lane >> 4;
+  const size_t head0 = (size_t)b * Hq + (size_t)kvh * G;
+  const int32_t* rowp = idx + (size_t)u * row;
+  const uint16_t* ksh = k_shadow + (size_t)u * cap * kHeadDim;
+  const uint16_t* vsh = v_shadow + (size_t)u * cap * kHeadDim;
+  const float sm2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2e;
+
+  // B operands: column n = head n mod G, K-step ks = channels 32ks + 8kb .. +7
+  half8 bq[4];
+  {
+    const uint16_t* qr = q + (head0 + (size_t)(n % G)) * kHeadDim + 8 * kb;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) bq[ks] = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(qr + 32 * ks));
+  }
+
+  __shared__ int s_row[kRowRec];           // the record's tokens (-1: left out)
+  __shared__ float s_p[kRowWaves][16][G];  // a tile's weights, per wave
+  __shared__ float s_f[kRowWaves][G];      // the factor of the running sums, per wave
+  __shared__ float s_ml[kRowWaves][2][G];  // each wave's final max and denominator
+  __shared__ float s_acc[kRowWaves][G][kHeadDim];
+
+  const int pc = lane & 15, qs = lane >> 4;  // P.V: channels 8pc .. 8pc+7, entries 4j + qs of a tile
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // of head n mod G (the same in the four lanes of a column)
+
+  // The record's tokens, once, into LDS: a tile's addresses then depend on
+  // no global load (a wait for one would also wait for the loads of the tile
+  // in flight before it).
+  for (int i = tid; i < kRowRec; i += 64 * kRowWaves) {
+    const int e = r_begin + i;
+    const int t = (e < r_end) ? rowp[e] : -1;
+    s_row[i] = (t >= 0 && t < n_len) ? t : -1;
+  }
+  __syncthreads();
+  // A tile's loads (masked entries read token 0's rows, in range; they get
+  // weight 0): the key rows of entries e0 + r for the logits, the value rows
+  // of entries e0 + 4j + qs for P.V.
+  struct Tile {
+    int tr;
+    uint4 ka[4];
+    int tv[4];
+    uint4 va[4];
+  };
+  auto load = [&](Tile& T, int e0) {
+    T.tr = s_row[e0 - r_begin + n];  // (entries past r_end are -1)
+    const uint16_t* kr = ksh + (size_t)max(T.tr, 0) * kHeadDim + 8 * kb;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) T.ka[ks] = *reinterpret_cast<const uint4*>(kr + 32 * ks);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      T.tv[j] = s_row[e0 - r_begin + 4 * j + qs];
+      T.va[j] = *reinterpret_cast<const uint4*>(vsh + (size_t)max(T.tv[j], 0) * kHeadDim + 8 * pc);
+    }
+  };
+  auto tile = [&](const Tile& T) {
+    floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, T.ka[ks]), bq[ks], d, 0, 0, 0);
+    // entry 4kb+i's logit of head n mod G is d[i] (masked entries: -inf)
+    float lg[4], mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = __shfl(T.tr, 4 * kb + i);  // (lane 4kb+i holds entry 4kb+i's token)
+      lg[i] = (t >= 0) ? d[i] * sm2 : -INFINITY;
+      mt = fmaxf(mt, lg[i]);
+    }
+    mt = wmax16(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float ref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - ref);
+    float ls = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(lg[i] - ref);
+      ls += p;
+      if (n < G) s_p[wv][4 * kb + i][n] = p;
+    }
+    l_run = fmaf(l_run, f, wsum16(ls));
+    m_run = m_new;
+    if (n < G && kb == 0) s_f[wv][n] = f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float fh = s_f[wv][h];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[h][c] *= fh;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t vw[4] = {T.va[j].x, T.va[j].y, T.va[j].z, T.va[j].w};
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[2 * c] = h2f((uint16_t)(vw[c] & 0xFFFFu));
+        v[2 * c + 1] = h2f((uint16_t)(vw[c] >> 16));
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = s_p[wv][4 * j + qs][h];  // (0 for a masked entry)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[h][c] = fmaf(p, v[c], acc[h][c]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // the wave's tiles e0 = r_begin + 16 (wv + 4i), one tile's loads ahead (two
+  // register sets taken in turn: no copies of registers with loads in flight)
+  constexpr int kStride = 16 * kRowWaves;
+  int e0 = r_begin + 16 * wv;
+  Tile ta, tb;
+  if (e0 < r_end) load(ta, e0);
+  while (e0 < r_end) {
+    if (e0 + kStride < r_end) load(tb, e0 + kStride);
+    tile(ta);
+    e0 += kStride;
+    if (e0 >= r_end) break;
+    if (e0 + kStride < r_end) load(ta, e0 + kStride);
+    tile(tb);
+    e0 += kStride;
+  }
+
+  // the wave's state: sums over its four entry slots, then into LDS
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[h][c] = wsum16(acc[h][c]);
+  if (qs == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s_acc[wv][h][8 * pc + c] = acc[h][c];
+  }
+  if (n < G && kb == 0) {
+    s_ml[wv][0][n] = m_run;
+    s_ml[wv][1][n] = l_run;
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kHeadDim; e += 64 * kRowWaves) {
+    const int h = e / kHeadDim, c = e - h * kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < kRowWaves; ++x) M = fmaxf(M, s_ml[x][0][h]);
+    float a = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int x = 0; x < kRowWaves; ++x) {
+        const float fx = (s_ml[x][0][h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_ml[x][0][h] - M);
+        a = fmaf(fx, s_acc[x][h][c], a);
+        l = fmaf(fx, s_ml[x][1][h], l);
+      }
+    }
+    float* rec = cs + ((head0 + h) * nchunk + rec_i) * kCsStride;
+    rec[4 + c] = a;
+    if (c == 0) {
+      rec[0] = M;
+      rec[1] = l;
+    }
+  }
 }
 
 // EX = false: only the approximate terms (the exact state comes from
@@ -440,6 +654,39 @@ void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
 
 }  // namespace
 
+hipError_t launch_correct_rows(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                               int max_len, const int32_t* idx, int row, const Workspace& w, float* out,
+                               hipStream_t s) {
+  (void)hipGetLastError();  // report only this call's launches
+  // records per query head: at most w.nchunk (records of kCorrChunk entries over min(row, max_len))
+  const int nrec = (min(row, max_len) + kRowRec - 1) / kRowRec;
+  if (nrec > 0) {
+    const dim3 grid(nrec, L.batch * L.n_kv_heads);
+    if (L.n_q_heads / L.n_kv_heads == 4)
+      exact_rows_kernel<4><<<grid, 64 * kRowWaves, 0, s>>>(c.k_shadow, c.v_shadow, q, idx, w.cs, len, L.n_q_heads,
+                                                          L.n_kv_heads, L.capacity, row, w.nchunk);
+    else
+      exact_rows_kernel<8><<<grid, 64 * kRowWaves, 0, s>>>(c.k_shadow, c.v_shadow, q, idx, w.cs, len, L.n_q_heads,
+                                                          L.n_kv_heads, L.capacity, row, w.nchunk);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const hipError_t e = launch_rows_approx(L, c, q, len, w, idx, row, nrec, s);
+    if (e != hipSuccess) return e;
+  }
+  if (nrec <= 8 && w.nsplit <= 8)
+    combine_kernel<1, 8><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, nullptr,
+                                                                        out, len, L.n_q_heads, w.nsplit, w.nchunk,
+                                                                        row, 0, kRowRec);
+  else if (nrec <= kRecBatchMax && w.nsplit <= kRecBatchMax)
+    combine_kernel<1><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, nullptr,
+                                                                     out, len, L.n_q_heads, w.nsplit, w.nchunk, row,
+                                                                     0, kRowRec);
+  else
+    combine_kernel<4><<<dim3(L.n_q_heads, L.batch), kHeadDim * 4, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs,
+                                                                         nullptr, out, len, L.n_q_heads, w.nsplit,
+                                                                         w.nchunk, row, 0, kRowRec);
+  return hipGetLastError();
+}
+
 hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                           const SeqArg& len, const int32_t* idx, int k, const Workspace& w,
                           const float* hx, bool rest, float* out, hipStream_t s) {
@@ -457,15 +704,15 @@ hipError_t launch_correct(const bkv_layout& L, const bkv_cache& c, const uint16_
   if (w.nchunk <= 8 && w.nsplit <= 8)  // every record list fits one batch of 8
     combine_kernel<1, 8><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
                                                                         len, L.n_q_heads, w.nsplit, w.nchunk, k,
-                                                                        rest ? 1 : 0);
+                                                                        rest ? 1 : 0, kCorrChunk);
   else if (w.nchunk <= kRecBatchMax && w.nsplit <= kRecBatchMax)  // every record list fits one batch
     combine_kernel<1><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx, out,
                                                                      len, L.n_q_heads, w.nsplit, w.nchunk, k,
-                                                                     rest ? 1 : 0);
+                                                                     rest ? 1 : 0, kCorrChunk);
   else
     combine_kernel<4><<<dim3(L.n_q_heads, L.batch), kHeadDim * 4, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, hx,
                                                                          out, len, L.n_q_heads, w.nsplit, w.nchunk,
-                                                                         k, rest ? 1 : 0);
+                                                                         k, rest ? 1 : 0, kCorrChunk);
   return hipGetLastError();
 }
 

@@ -89,15 +89,19 @@
 #if BKV_QUERY_INT8
 #define BKV_SCAN_KERNEL decode_approx_q8_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_q8
+#define BKV_ROWS_LAUNCH launch_rows_approx_q8
 #elif BKV_KEY_MXFP4
 #define BKV_SCAN_KERNEL decode_approx_mx_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_mx
+#define BKV_ROWS_LAUNCH launch_rows_approx_mx
 #elif BKV_KEY_FP4
 #define BKV_SCAN_KERNEL decode_approx_fp4_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx_fp4
+#define BKV_ROWS_LAUNCH launch_rows_approx_fp4
 #else
 #define BKV_SCAN_KERNEL decode_approx_kernel
 #define BKV_SCAN_LAUNCH launch_decode_approx
+#define BKV_ROWS_LAUNCH launch_rows_approx
 #endif
 
 namespace bkv {
@@ -523,15 +527,23 @@ __device__ __forceinline__ void scan_step(const Step<KB, VB, G>& cur, const u32x
 // FUSE: the fused step -- after the scan the same launch selects the unit's
 // top-ksel tokens and corrects them into fa.out (fused_tail.h); every
 // workgroup of the grid must be resident at once.
+// ROWS: the approximate terms of long rows of whole blocks (the rows
+// topk_select_blocks writes, ksel entries per unit): workgroup `split` takes
+// row entries [split * kRowRec, split * kRowRec + kRowRec), each 32-entry step
+// of which is the consecutive tokens t0 .. t0 + nv - 1 of one block (t0 a
+// multiple of 32, the entries past the sequence -1), and writes the
+// approximate part (max, denominator, value sums) of correction record
+// `split` (rcs, records of kCsStride floats, nsplit of them per query head);
+// nothing else is written.
 template <int KB, int VB, int G, bool SEL, bool SKIP = false, bool SIGONLY = false, bool APPEND = false,
-          bool FUSE = false>
+          bool FUSE = false, bool ROWS = false>
 __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERNEL(
     const uint8_t* k_codes, const uint8_t* v_codes, const uint32_t* k_meta, const uint32_t* v_meta,
     const uint16_t* __restrict__ q, float* __restrict__ sigma, float* __restrict__ pm,
     float* __restrict__ pl, float* __restrict__ pacc, SeqArg lens, int Hq, int Hkv, int cap, int nsplit, int chunk,
     uint64_t* __restrict__ cand, uint32_t* __restrict__ counter, int32_t* __restrict__ idx, int ksel, int mshift,
     uint16_t* k_shadow, uint16_t* v_shadow, const uint16_t* __restrict__ k_new,
-    const uint16_t* __restrict__ v_new, FusedArgs fa) {
+    const uint16_t* __restrict__ v_new, FusedArgs fa, float* __restrict__ rcs) {
   constexpr int NT = Step<KB, VB, G>::NT;
   // (workgroup and lane ids via the builtins: this file is built without IEEE
   // mode, so the device library's id functions would not be inlined)
@@ -572,7 +584,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
   // (its stores must come first), loads again before its first step.
   Step<KB, VB, G> sa, sb, sc;
   int t0 = t_begin + kTile * wv;
-  constexpr bool kEarly = !SIGONLY;  // (the scores-only scan keeps two steps in flight: not here)
+  constexpr bool kEarly = !SIGONLY && !ROWS;  // (the scores-only scan keeps two steps in flight: not here)
   bool early = kEarly && t0 < t_end;
   if constexpr (APPEND) {
     const int p = len - 1;
@@ -853,7 +865,39 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
                                      SKIP ? s_skip[(t0 - t_begin) >> 5] : 0u);
     ++sig_count;
   };
-  if constexpr (kAhead == 1) {
+  if constexpr (ROWS) {
+    // the wave's two steps of the record (kRowRec = 16 steps of 32 entries):
+    // first token and count of each, then both loads in flight at once (a
+    // step with no token loads token 0's step and is not scanned)
+    static_assert(kRowRec == 2 * kScanWaves * kTile, "two steps per wave");
+    const int32_t* rowp = idx + (size_t)u * ksel;
+    const int kk = min(ksel, len);
+    const int r_begin = split * kRowRec, r_end = min(kk, r_begin + kRowRec);
+    if (r_begin >= kk) return;  // (the whole workgroup: the combine reads only the records below kk)
+    int rt0[2], rnv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e0 = r_begin + kTile * (wv + kScanWaves * i);
+      const int e = e0 + (lane & 31);
+      const int v = (e < r_end) ? rowp[e] : -1;
+      const uint64_t okm = __ballot(v >= 0 && v < len) & 0xFFFFFFFFull;
+      rnv[i] = __builtin_amdgcn_readfirstlane(__popcll(okm));
+      rt0[i] = __builtin_amdgcn_readfirstlane((v >= 0 && v < len) ? v : 0) & ~(kTile - 1);
+    }
+    load_step<KB, VB, G, false>(sa, kbase, vbase, kmeta, vmeta, cap, rt0[0], lane, mshift);
+    load_step<KB, VB, G, false>(sb, kbase, vbase, kmeta, vmeta, cap, rt0[1], lane, mshift);
+    auto rows_step = [&](const Step<KB, VB, G>& cur, int ts, int nv) {
+      u32x4 km[2][NT], vm[NT][2];
+      uint32_t ks[2];
+      meta_cells(cur.meta, km, vm, ks);
+      if (nv == kTile)
+        scan_step<KB, VB, G, false>(cur, km, vm, ks, fq, bq, qs, qsc, ws, s_sig[wv][0], ts, ts + nv, n, kb, c_s2);
+      else if (nv > 0)
+        scan_step<KB, VB, G, true>(cur, km, vm, ks, fq, bq, qs, qsc, ws, s_sig[wv][0], ts, ts + nv, n, kb, c_s2);
+    };
+    rows_step(sa, rt0[0], rnv[0]);
+    rows_step(sb, rt0[1], rnv[1]);
+  } else if constexpr (kAhead == 1) {
     if (t0 < t_end && !early) load_step<KB, VB, G, SIGONLY>(sa, kbase, vbase, kmeta, vmeta, cap, t0, lane, mshift);
     for (;;) {
       if (t0 + kTile > t_end) {
@@ -961,6 +1005,13 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
       rm[r] = M;
       rl[r] = l;
       ra[r] = a;
+    } else if constexpr (ROWS) {  // the record's approximate part
+      float* rr = rcs + (((size_t)b * Hq + (size_t)kvh * G + hh) * nsplit + split) * kCsStride;
+      rr[4 + kHeadDim + c] = a;
+      if (c == 0) {
+        rr[2] = M;
+        rr[3] = l;
+      }
     } else {
       const size_t rec = ((size_t)b * Hq + (size_t)kvh * G + hh) * nsplit + split;
       pacc[rec * kHeadDim + c] = a;
@@ -1073,31 +1124,31 @@ hipError_t launch_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
   if (k_new && ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{});
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{}, nullptr);
   else if (k_new)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{});
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, c.k_shadow, c.v_shadow, k_new, v_new, FusedArgs{}, nullptr);
   else if (sigonly && ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, nullptr);
   else if (sigonly)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, nullptr);
   else if (skip)
     BKV_SCAN_KERNEL<KB, VB, G, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, nullptr, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, nullptr);
   else if (ksel > 0)
     BKV_SCAN_KERNEL<KB, VB, G, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+        L.capacity, w.nsplit, chunk, w.tkc, w.tkctr, idx, ksel, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, nullptr);
   else
     BKV_SCAN_KERNEL<KB, VB, G, false><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{});
+        L.capacity, w.nsplit, chunk, nullptr, nullptr, nullptr, 0, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, nullptr);
   return hipGetLastError();
 }
 
@@ -1143,12 +1194,33 @@ hipError_t launch_fused_t(const bkv_layout& L, const bkv_cache& c, const uint16_
   if (k_new)
     BKV_SCAN_KERNEL<KB, VB, G, false, false, false, true, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, fa);
+        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, k_new, v_new, fa, nullptr);
   else
     BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
         kc, vc, c.k_meta, c.v_meta, q, sigma, w.part.m, w.part.l, w.part.acc, len, L.n_q_heads, L.n_kv_heads,
-        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, nullptr, nullptr, fa);
+        L.capacity, w.nsplit, chunk, w.tkc, nullptr, idx, ksel, mshift, c.k_shadow, c.v_shadow, nullptr, nullptr, fa, nullptr);
   return hipGetLastError();
+}
+
+// ROWS: the approximate parts of the nrec correction records of long rows.
+template <int KB, int VB, int G>
+hipError_t launch_rows_t(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                         const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s) {
+  const dim3 grid(nrec, L.batch * L.n_kv_heads);
+  const int mshift = L.group == 64 ? 1 : 0;
+  (void)hipGetLastError();  // report only this launch's status
+  BKV_SCAN_KERNEL<KB, VB, G, false, false, false, false, false, true><<<grid, 64 * kScanWaves, 0, s>>>(
+      static_cast<const uint8_t*>(c.k_codes), static_cast<const uint8_t*>(c.v_codes), c.k_meta, c.v_meta, q, nullptr,
+      nullptr, nullptr, nullptr, len, L.n_q_heads, L.n_kv_heads, L.capacity, w.nchunk, kRowRec, nullptr, nullptr,
+      const_cast<int32_t*>(idx), row, mshift, nullptr, nullptr, nullptr, nullptr, FusedArgs{}, w.cs);
+  return hipGetLastError();
+}
+
+template <int KB, int VB>
+hipError_t launch_rows_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                         const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s) {
+  if (L.n_q_heads / L.n_kv_heads == 4) return launch_rows_t<KB, VB, 4>(L, c, q, len, w, idx, row, nrec, s);
+  return launch_rows_t<KB, VB, 8>(L, c, q, len, w, idx, row, nrec, s);
 }
 
 template <int KB, int VB>
@@ -1193,6 +1265,27 @@ hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const ui
             : launch_fused_t<3, 2, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
 }
 #endif
+
+hipError_t BKV_ROWS_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                           const Workspace& w, const int32_t* idx, int row, int nrec, hipStream_t s) {
+#if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4 && !BKV_KEY_FP4
+  if (L.query_bits == 8) return launch_rows_approx_q8(L, c, q, len, w, idx, row, nrec, s);
+  if (L.key_format == 1) return launch_rows_approx_mx(L, c, q, len, w, idx, row, nrec, s);
+  if (L.key_format == 2) return launch_rows_approx_fp4(L, c, q, len, w, idx, row, nrec, s);
+#endif
+#if BKV_KEY_MXFP4 || BKV_KEY_FP4  // (4-bit keys only)
+  return L.v_bits == 4 ? launch_rows_g<4, 4>(L, c, q, len, w, idx, row, nrec, s)
+                       : launch_rows_g<4, 2>(L, c, q, len, w, idx, row, nrec, s);
+#else
+  const bool v4 = L.v_bits == 4;
+  switch (L.k_bits) {
+    case 4: return v4 ? launch_rows_g<4, 4>(L, c, q, len, w, idx, row, nrec, s) : launch_rows_g<4, 2>(L, c, q, len, w, idx, row, nrec, s);
+    case 3: return v4 ? launch_rows_g<3, 4>(L, c, q, len, w, idx, row, nrec, s) : launch_rows_g<3, 2>(L, c, q, len, w, idx, row, nrec, s);
+    case 2: return v4 ? launch_rows_g<2, 4>(L, c, q, len, w, idx, row, nrec, s) : launch_rows_g<2, 2>(L, c, q, len, w, idx, row, nrec, s);
+    default: return v4 ? launch_rows_g<1, 4>(L, c, q, len, w, idx, row, nrec, s) : launch_rows_g<1, 2>(L, c, q, len, w, idx, row, nrec, s);
+  }
+#endif
+}
 
 hipError_t BKV_SCAN_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,
                                 const SeqArg& len, float* sigma, const Workspace& w, int chunk,

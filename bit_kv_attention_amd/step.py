@@ -66,6 +66,9 @@ class DecodeStep:
         if self.block > 0:
             if self.k > 0:
                 bk.topk_select_blocks(self.layout, self.sigma, lens, self.k, self.block, self.idx, self.ws, stream)
+            bk.qattn_correct_blocks(self.layout, cache, q, lens, self.idx if self.k > 0 else None, self.k, self.block,
+                                    self.ws, self.out, stream)
+            return self.out
         elif self.window > 0:
             bk.topk_select_window(self.layout, self.sigma, lens, self.k, self.window, self.idx, self.ws, stream)
         elif self.k > 0:

@@ -24,6 +24,7 @@
  *   topk_select_blocks   or whole blocks of tokens by their best score
  *   qattn_correct        merge the splits, replace the top-k tokens' logits
  *                        and values by exact ones, renormalise
+ *   qattn_correct_blocks the same for block rows, over contiguous tiles
  *   qattn_score_select   sigma and the top-k rows only (no softmax state)
  *   qattn_decode_unselected, qattn_correct_unselected
  *                        the approximate pass over the unselected tokens only,
@@ -320,6 +321,28 @@ bkv_status topk_select_blocks(const bkv_layout* layout, const float* sigma,
                               const int32_t* len_host, int32_t n_blocks,
                               int32_t block, int32_t* idx, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * qattn_correct_blocks -- qattn_correct for the rows topk_select_blocks wrote
+ * (same arguments as that call: n_blocks, block, and the same lengths), read
+ * as whole blocks: the selected tokens' exact logits and fp16 values stream as
+ * contiguous tiles of shadow rows (Jet-QSparse abstract: the chosen 128-token
+ * blocks feed dense fp16 value aggregation with fp32 accumulation through
+ * contiguous tile loads), logits on MFMA, the value sums in fp32, and their
+ * approximate terms are recomputed by the scan's code over the same blocks.
+ * out [B][Hq][D] fp32 as qattn_correct on these rows with n_blocks * block as
+ * its k.  Needs qattn_decode_approx (or qattn_decode_select) of the same step
+ * before it on ws, like qattn_correct.  Rows not written by
+ * topk_select_blocks with these arguments give undefined results (every
+ * access stays inside the cache).
+ * Errors: as topk_select_blocks's BKV_E_ARG; BKV_E_NULL, BKV_E_CAPACITY and
+ * BKV_E_WORKSPACE (bkv_workspace_bytes(layout, max_len, n_blocks * block)) as
+ * qattn_correct.
+ */
+bkv_status qattn_correct_blocks(const bkv_layout* layout, const bkv_cache* cache,
+                                const uint16_t* q, const int32_t* len_host,
+                                const int32_t* idx, int32_t n_blocks, int32_t block,
+                                void* ws, size_t ws_bytes, float* out, void* stream);
 
 /*
  * qattn_correct -- merge the splits written by qattn_decode_approx and apply

@@ -464,6 +464,40 @@ def test_step_parity_blocks(P, kb, vb, G, nb, bs, fmt):
     P.assert_close(out, orc_o["out"], "out vs oracle(rows_oracle)")
 
 
+@pytest.mark.parametrize("kb,vb,G,nb,bs", [(4, 4, 4, 24, 128), (3, 2, 8, 40, 64)])
+def test_step_parity_blocks_long_rows(P, kb, vb, G, nb, bs):
+    """Block rows long enough that each correction workgroup walks several
+    consecutive chunks (32 units, thousands of selected tokens per unit), with
+    ragged lengths: a short sequence whose row ends in -1 entries mid-record,
+    and one shorter than a single block.  Output against the oracle on the
+    GPU's rows."""
+    banner(f"step blocks long rows kb={kb} vb={vb} G={G} nb={nb} bs={bs}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    w = P.Workload("blkl", 4, 8 * G, 8, 128, 6000, kb, vb, 32, 32, 6, 900 + G + nb)
+    pair = P.build_pair(w, L=6000, cap=6016)
+    lens = np.array([6000, 4321, 1000, 50])
+    pos = [int(x) - 1 for x in lens]
+    bk.kv_pack_append(pair["lay"], pair["gc"], P.to_dev(pair["k1"]), P.to_dev(pair["v1"]), 1, pos)
+    pair["oc"].append(pair["k1"], pair["v1"], np.array(pos, np.int32))
+    st = DecodeStep(pair["lay"], nb, 6000, block=bs)
+    out = st.attend(pair["gc"], P.to_dev(pair["q"]), lens)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().reshape(w.B, w.Hq, 128)
+    idx = st.idx.cpu().numpy().reshape(w.B, w.Hkv, nb * bs)
+    assert (nb * bs // 32) * w.B * w.Hkv > 1024  # several chunks per correction workgroup
+    orc_s = pair["oc"].decode(pair["q"], lens, nb * bs, sel=idx)
+    P.assert_close(out, orc_s["out"], "out vs oracle(rows_gpu)")
+    # and the plain top-k with the same long rows (k well past 32 chunks)
+    st2 = DecodeStep(pair["lay"], nb * bs, 6000)
+    out2 = st2.attend(pair["gc"], P.to_dev(pair["q"]), lens)
+    torch.cuda.synchronize()
+    idx2 = st2.idx.cpu().numpy().reshape(w.B, w.Hkv, nb * bs)
+    orc2 = pair["oc"].decode(pair["q"], lens, nb * bs, sel=idx2)
+    P.assert_close(out2.cpu().numpy().reshape(w.B, w.Hq, 128), orc2["out"], "top-k long rows vs oracle(S_gpu)")
+
+
 @pytest.mark.parametrize("kb,vb,G,g,fmt", [c + (32, "") for c in COMBOS] + [(2, 2, 4, 64, ""), (1, 2, 8, 64, ""),
                                             (4, 4, 4, 32, "q8"), (2, 2, 8, 64, "q8"),
                                             (4, 2, 4, 32, "mx"), (4, 4, 8, 32, "mx1")])
