@@ -49,6 +49,84 @@ def packed_bytes_per_token(kbits: int, vbits: int, D: int = 128, group: int = 32
     return D * kbits // 8 + kmeta + D * vbits // 8 + meta
 
 
+def bench_layers(w, args, torch) -> int:
+    """N layers per step, each with a cache of its own (the same tokens):
+    per-layer time of (a) the all-GPU step (the fused launch where it runs),
+    (b) the hybrid step run layer after layer (attend_hybrid: one wait per
+    layer for the rows, host pass, merge), and (c) the hybrid step pipelined
+    over two micro-batches (HybridPipeline: the host pass of one micro-batch
+    overlaps the other's GPU work).  Wall clock around `steps` steps after
+    `warmup`; one JSON line."""
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep, HybridPipeline
+    from bit_kv_attention_amd.synth import make_inputs, make_new_tokens
+    dev = torch.device("cuda:0")
+    nl, L = args.layers, w.L
+    cap = ((L + 31) // 32) * 32
+    lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits,
+                         key_format=w.key_format)
+    log(f"{w.name}: {nl} layers: generating inputs")
+    inp = make_inputs(w, L=L - 1)
+    knew, vnew = make_new_tokens(w, 1, inp.outlier_ch)
+    Kd, Vd = torch.from_numpy(inp.K).to(dev), torch.from_numpy(inp.V).to(dev)
+    q = torch.from_numpy(inp.q).to(dev)
+    kn, vn = torch.from_numpy(knew[0]).to(dev), torch.from_numpy(vnew[0]).to(dev)
+    pos = [L - 1] * w.B
+    dev_caches, host_caches = [], []
+    for _ in range(nl):
+        for lst, on_host in ((dev_caches, False), (host_caches, True)):
+            c = bk.allocate_cache(lay, device=dev, shadow_on_host=on_host)
+            bk.kv_pack_append(lay, c, Kd, Vd, L - 1, [0] * w.B)
+            lst.append(c)
+    del Kd, Vd
+    torch.cuda.synchronize()
+    gpu_steps = [DecodeStep(lay, w.k, L, device=dev, one_launch=True) for _ in range(nl)]
+    hyb_steps = [DecodeStep(lay, w.k, L, device=dev, one_launch=False) for _ in range(nl)]
+    pipe = HybridPipeline(lay, w.k, L, micro=2, device=dev, n_threads=args.cpu_threads)
+    lens = [L] * w.B
+
+    def gpu_step():
+        for i in range(nl):
+            gpu_steps[i].step(dev_caches[i], q, kn, vn, pos)
+
+    def serial_step():
+        for i in range(nl):
+            st = hyb_steps[i]
+            bk.qattn_decode_step(lay, host_caches[i], kn, vn, q, lens, w.k, st.sigma, st.idx, st.ws)
+            st.attend_hybrid(host_caches[i], q, lens, args.cpu_threads, select=False)
+
+    def pipe_step():
+        pipe.run(host_caches, [q] * nl, [kn] * nl, [vn] * nl, pos)
+
+    res = {}
+    for name, fn in (("exact_gpu", gpu_step), ("exact_host_serial", serial_step), ("exact_host_pipelined", pipe_step)):
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t) * 1e6 / args.steps / nl
+        res[name + "_us_per_layer"] = round(us, 2)
+        log(f"{w.name}: {name}: {us:.2f} µs per layer")
+    units = w.B * w.Hkv
+    kk = min(w.k, L)
+    pcie = units * w.k * 4 + w.B * w.Hq * w.D * 2 + w.B * w.Hq * (w.D + 2) * 4 + units * 2 * w.D * 2
+    host_read = units * kk * 2 * w.D * 2
+    t_pipe = res["exact_host_pipelined_us_per_layer"]
+    print(json.dumps({"mode": "layers", "config": {"workload": w.name, "layers": nl, "micro_batches": 2,
+                                                   "host_threads": args.cpu_threads},
+                      **res,
+                      "pcie_bytes_per_layer": pcie,
+                      "pcie_GBps_at_pipelined_rate": round(pcie / t_pipe / 1e3, 2),
+                      "pcie_peak_GBps": 64.0,
+                      "host_shadow_read_bytes_per_layer": host_read,
+                      "host_read_GBps_at_pipelined_rate": round(host_read / t_pipe / 1e3, 2),
+                      "host_cores": os.cpu_count()}), flush=True)
+    return 0
+
+
 def read_ceiling(nbytes: int, torch, copies: int = 1) -> int:
     """The plain streaming read (probe/read_ceiling.hip) of nbytes, 20 timed
     launches per grid size after 3 untimed ones, rotating over `copies`
@@ -122,6 +200,9 @@ def main(argv=None) -> int:
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=HOST_THREADS)
+    ap.add_argument("--layers", type=int, default=0, metavar="N",
+                    help="only time N layers per step (each its own cache): the all-GPU step, the hybrid "
+                         "step per layer, and the hybrid step pipelined over two micro-batches")
     ap.add_argument("--read-ceiling", type=int, default=0, metavar="BYTES",
                     help="only time a plain streaming read of BYTES bytes (bit_kv_attention_amd/probe), "
                          "the practical HBM read ceiling, over several grid sizes")
@@ -150,6 +231,9 @@ def main(argv=None) -> int:
 
     if args.read_ceiling:
         return read_ceiling(args.read_ceiling, torch, max(args.copies, 1))
+    if args.layers:
+        from bit_kv_attention_amd.synth import BY_NAME
+        return bench_layers(BY_NAME[args.config], args, torch)
 
     from bit_kv_attention_amd.synth import BY_NAME
     res = bench_one(BY_NAME[args.config], args, torch, shadow=args.shadow)

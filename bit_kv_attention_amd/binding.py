@@ -156,6 +156,20 @@ class Cache:
                                                             "k_shadow", "v_shadow")))
 
 
+def cache_rows(cache: Cache, b0: int, nb: int):
+    """(layout, cache) of batch rows b0 .. b0 + nb - 1 of a cache: views of its
+    buffers (every buffer is unit-major, unit = b * n_kv_heads + kvh), so
+    calls on the slice read and write the same memory."""
+    L = cache.layout
+    units = L.batch * L.n_kv_heads
+    lo, hi = b0 * L.n_kv_heads, (b0 + nb) * L.n_kv_heads
+    part = lambda t: t[t.numel() // units * lo:t.numel() // units * hi]
+    lay = make_layout(nb, L.n_q_heads, L.n_kv_heads, L.capacity, L.k_bits, L.v_bits, head_dim=L.head_dim,
+                      group=L.group, query_bits=L.query_bits, key_format=L.key_format)
+    return lay, Cache(lay, *(part(getattr(cache, n)) for n in ("k_codes", "v_codes", "k_meta", "v_meta",
+                                                                 "k_shadow", "v_shadow")))
+
+
 def allocate_cache(layout: Layout, device="cuda", shadow_on_host: bool = False) -> Cache:
     """Zero-filled cache buffers (torch).  With shadow_on_host the fp16 shadow
     rows live in pinned host memory that the GPU reads across PCIe."""

@@ -151,3 +151,91 @@ class DecodeStep:
             return self.out
         bk.kv_pack_append(self.layout, cache, k_new, v_new, 1, pos, stream)
         return self.attend(cache, q, lens, stream)
+
+
+class HybridPipeline:
+    """The hybrid step (JetFire README, introduction: a low-bit cache on the
+    GPU, the high-precision correction of the top-k tokens on the host) over
+    several layers, the host's exact pass overlapped with GPU work.
+
+    A layer's query depends on the previous layer's output, so the host pass
+    of a layer cannot overlap the next layer's scan of the same sequences.
+    The batch is split into `micro` micro-batches (contiguous batch rows)
+    instead: while the host computes micro-batch m's exact states of layer i
+    (qattn_exact_host), the GPU runs the other micro-batches' work -- their
+    scans, and their merges and next-layer scans.  Per micro-batch and layer:
+    qattn_decode_step (append of the new token, scan, top-k) and the copies of
+    the rows and the query to pinned host memory, then an event; the host
+    waits for that event only (no stream-wide synchronise), computes, and
+    enqueues the copy of the states and qattn_correct_hybrid, then the
+    micro-batch's next layer.  Every enqueue is on the current stream, so a
+    micro-batch's buffers are reused only after its previous merge.
+    caches[i] must keep its shadow in pinned host memory."""
+
+    def __init__(self, layout: bk.Layout, k: int, max_len: int, micro: int = 2, device="cuda",
+                 n_threads: int = 0):
+        import torch
+        if layout.batch % micro:
+            raise ValueError("the batch must split into equal micro-batches")
+        self.layout, self.k, self.micro, self.n_threads = layout, int(k), int(micro), int(n_threads)
+        self.nb = layout.batch // micro
+        self.steps = []
+        for m in range(micro):
+            lay_m = bk.make_layout(self.nb, layout.n_q_heads, layout.n_kv_heads, layout.capacity, layout.k_bits,
+                                   layout.v_bits, head_dim=layout.head_dim, group=layout.group,
+                                   query_bits=layout.query_bits, key_format=layout.key_format)
+            st = DecodeStep(lay_m, k, max_len, device=device)
+            L = lay_m
+            st.h_idx = torch.empty(st.idx.numel(), dtype=torch.int32, pin_memory=True)
+            st.h_q = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float16, pin_memory=True)
+            st.h_state = torch.empty(L.batch * L.n_q_heads * (L.head_dim + 2), dtype=torch.float32,
+                                     pin_memory=True)
+            st.d_state = torch.empty_like(st.h_state, device=st.out.device)
+            self.steps.append(st)
+
+    def run(self, caches, qs, k_news, v_news, pos, outs=None):
+        """Layer i appends (k_news[i], v_news[i]) at pos[b] and attends over
+        pos[b] + 1 tokens of caches[i] with qs[i] ([B][Hq][D] fp16, device).
+        outs: None, or one [B*Hq*D] fp32 device tensor per layer that receives
+        that layer's output; returns the list."""
+        import torch
+        nl, M, nb = len(caches), self.micro, self.nb
+        lens = [int(p) + 1 for p in pos]
+        L = self.layout
+        per_q = nb * L.n_q_heads * L.head_dim
+        per_kv = nb * L.n_kv_heads * L.head_dim
+        stream = torch.cuda.current_stream()
+
+        def view(i, m):
+            lay_m, c = bk.cache_rows(caches[i], m * nb, nb)
+            return (lay_m, c, qs[i].reshape(-1)[m * per_q:(m + 1) * per_q],
+                    k_news[i].reshape(-1)[m * per_kv:(m + 1) * per_kv],
+                    v_news[i].reshape(-1)[m * per_kv:(m + 1) * per_kv], lens[m * nb:(m + 1) * nb])
+
+        def select(i, m):
+            st = self.steps[m]
+            lay_m, c, q, kn, vn, ln = view(i, m)
+            bk.qattn_decode_step(lay_m, c, kn, vn, q, ln, self.k, st.sigma, st.idx, st.ws)
+            st.h_idx.copy_(st.idx, non_blocking=True)
+            st.h_q.copy_(q, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            return ev
+
+        events = [select(0, m) for m in range(M)]
+        for i in range(nl):
+            for m in range(M):
+                st = self.steps[m]
+                lay_m, c, q, _, _, ln = view(i, m)
+                events[m].synchronize()  # this micro-batch's rows and appended token are in place
+                bk.qattn_exact_host(lay_m, c.k_shadow, c.v_shadow, st.h_q, ln, st.h_idx, self.k, st.h_state,
+                                    self.n_threads)
+                st.d_state.copy_(st.h_state, non_blocking=True)
+                bk.qattn_correct_hybrid(lay_m, c, q, ln, st.idx if self.k > 0 else None, self.k, st.d_state,
+                                        st.ws, st.out)
+                if outs is not None:
+                    outs[i].reshape(-1)[m * per_q:(m + 1) * per_q].copy_(st.out, non_blocking=True)
+                if i + 1 < nl:
+                    events[m] = select(i + 1, m)
+        return outs
+

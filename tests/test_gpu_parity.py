@@ -579,6 +579,54 @@ def test_hybrid_host_correction(P, kb, vb, G, fmt):
         np.testing.assert_allclose(oh, og, rtol=1e-4, atol=1e-5)
 
 
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
+def test_hybrid_pipeline_layers(P, kb, vb, G):
+    """HybridPipeline: three layers of the hybrid step over two micro-batches,
+    each micro-batch's host pass overlapping the other's GPU work: every
+    layer's output against the all-GPU step on a copy of that layer's cache
+    and against the oracle end to end (the appended token included, ragged
+    lengths)."""
+    banner(f"hybrid pipeline kb={kb} vb={vb} G={G}")
+    import torch
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep, HybridPipeline
+    import oracle
+    nl, L, cap, k = 3, 1500, 1504, 40
+    pos = [1499, 1100, 640, 3]
+    lens = np.array(pos) + 1
+    caches, refs, orcs, qs, kns, vns, outs, ins = [], [], [], [], [], [], [], []
+    for i in range(nl):
+        w = P.Workload("hypipe", 4, 2 * G, 2, 128, L, kb, vb, 32, k, 4, 1300 + 10 * i + G)
+        inp = P.make_inputs(w, L=L - 1)
+        kn, vn = P.make_new_tokens(w, 1, inp.outlier_ch)
+        lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, kb, vb)
+        hc = bk.allocate_cache(lay, shadow_on_host=True)
+        bk.kv_pack_append(lay, hc, P.to_dev(inp.K), P.to_dev(inp.V), L - 1, [0] * w.B)
+        gc = bk.allocate_cache(lay)
+        for name in ("k_codes", "v_codes", "k_meta", "v_meta", "k_shadow", "v_shadow"):
+            getattr(gc, name).copy_(getattr(hc, name))
+        oc = oracle.Cache(oracle.Shape(w.B, w.Hq, w.Hkv, 128, kb, vb, 32, cap))
+        oc.append(inp.K, inp.V, np.zeros(w.B, np.int32))
+        oc.append(kn[0], vn[0], np.array(pos, np.int32))
+        caches.append(hc), refs.append(gc), orcs.append(oc), ins.append(inp)
+        qs.append(P.to_dev(inp.q)), kns.append(P.to_dev(kn[0])), vns.append(P.to_dev(vn[0]))
+        outs.append(torch.full((w.B * w.Hq * 128,), float("nan"), dtype=torch.float32, device="cuda"))
+    pipe = HybridPipeline(lay, k, L, micro=2, n_threads=4)
+    pipe.run(caches, qs, kns, vns, pos, outs)
+    torch.cuda.synchronize()
+    for i in range(nl):
+        st = DecodeStep(lay, k, L, one_launch=False)
+        og = st.step(refs[i], qs[i], kns[i], vns[i], pos)
+        torch.cuda.synchronize()
+        oh = outs[i].cpu().numpy().reshape(4, 2 * G, 128)
+        np.testing.assert_allclose(oh, og.cpu().numpy().reshape(4, 2 * G, 128), rtol=1e-4, atol=1e-5)
+        # the appended token reached the host shadow of both micro-batches
+        for name in ("k_shadow", "v_shadow"):
+            assert torch.equal(getattr(caches[i], name), getattr(refs[i], name).cpu()), (i, name)
+        orc = orcs[i].decode(ins[i].q, lens, k)
+        P.assert_close(oh, orc["out"], f"layer {i} vs oracle(S_oracle)")
+
+
 @pytest.mark.parametrize("kb,vb,G,g", [(4, 4, 4, 32), (3, 2, 8, 32), (2, 2, 8, 64), (1, 2, 4, 64), (1, 4, 8, 32)])
 def test_exclude_path(P, kb, vb, G, g):
     """qattn_decode_unselected + qattn_correct_unselected (the unselected
