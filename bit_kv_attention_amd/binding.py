@@ -51,6 +51,12 @@ class CacheView(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("k_codes", "v_codes", "k_meta", "v_meta", "k_shadow", "v_shadow")]
 
 
+class HybridSlot(C.Structure):
+    _fields_ = [("sigma", C.c_void_p), ("idx", C.c_void_p), ("ws", C.c_void_p), ("ws_bytes", C.c_size_t),
+                ("state_dev", C.c_void_p), ("idx_host", C.c_void_p), ("q_host", C.c_void_p),
+                ("state_host", C.c_void_p)]
+
+
 _P = C.c_void_p
 _LP = C.POINTER(Layout)
 _CP = C.POINTER(CacheView)
@@ -70,6 +76,8 @@ _lib.topk_select_window.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C
 _lib.topk_select_blocks.argtypes = [_LP, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
 _lib.qattn_correct.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
 _lib.qattn_correct_blocks.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, C.c_int32, _P, C.c_size_t, _P, _P]
+_lib.qattn_hybrid_layers.argtypes = [_LP, C.c_int32, _P, _P, _P, _P, _P, C.c_int32, C.c_int32, _P, _P, C.c_int32,
+                                     _P]
 _lib.qattn_score_select.argtypes = [_LP, _CP, _P, _P, C.c_int32, _P, _P, _P, C.c_size_t, C.c_int32, _P]
 _lib.qattn_decode_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P]
 _lib.qattn_correct_unselected.argtypes = [_LP, _CP, _P, _P, _P, C.c_int32, _P, C.c_size_t, _P, _P]
@@ -86,7 +94,7 @@ EXPORTED = ("bkv_status_string", "bkv_cache_bytes", "bkv_k_meta_bytes", "bkv_wor
             "kv_pack_append", "qattn_decode_approx", "qattn_decode_select", "topk_select", "topk_select_window", "topk_select_blocks",
             "qattn_correct", "qattn_correct_hybrid", "qattn_exact_host", "qattn_decode_unselected",
             "qattn_correct_unselected", "qattn_score_select", "qattn_decode_step", "qattn_decode_fused",
-            "bkv_fused_supported", "qattn_decode_fused_noalloc", "qattn_correct_blocks")
+            "bkv_fused_supported", "qattn_decode_fused_noalloc", "qattn_correct_blocks", "qattn_hybrid_layers")
 
 
 def _check(fn: str, st: int) -> None:
@@ -364,3 +372,22 @@ def qattn_correct_blocks(layout: Layout, cache: Cache, q, len_host, idx, n_block
     _check("qattn_correct_blocks", _lib.qattn_correct_blocks(C.byref(layout), C.byref(view), _ptr(q),
                                                              lens.ctypes.data, _ptr(idx), int(n_blocks), int(block),
                                                              _ptr(ws), ws_bytes, _ptr(out), _stream(stream)))
+
+
+def qattn_hybrid_layers(layout: Layout, caches, qs, k_news, v_news, pos_host, k: int, micro: int, slots, outs,
+                        n_threads: int = 0, stream=None) -> None:
+    """caches, qs, k_news, v_news, outs: one per layer; slots: one dict per
+    micro-batch with the HybridSlot fields (torch tensors; ws_bytes taken
+    from ws)."""
+    n = len(caches)
+    views = (CacheView * n)(*(c.view() for c in caches))
+    arr = lambda ts: (C.c_void_p * n)(*(_ptr(t) for t in ts))
+    sl = (HybridSlot * len(slots))(*(HybridSlot(_ptr(d["sigma"]), _ptr(d["idx"]), _ptr(d["ws"]),
+                                                d["ws"].numel() * d["ws"].element_size(), _ptr(d["state_dev"]),
+                                                _ptr(d["idx_host"]), _ptr(d["q_host"]), _ptr(d["state_host"]))
+                                     for d in slots))
+    pos = _host_i32(pos_host)
+    _check("qattn_hybrid_layers", _lib.qattn_hybrid_layers(C.byref(layout), n, views, arr(qs), arr(k_news),
+                                                           arr(v_news), pos.ctypes.data, int(k), int(micro), sl,
+                                                           arr(outs), int(n_threads), _stream(stream)))
+

@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["bitkv_api.hip", "pack.hip", "decode_approx.hip", "decode_approx.hip:q8", "decode_approx.hip:mx",
-           "decode_approx.hip:fp4", "topk.hip", "correct.hip", "host_correct.cpp"]
+           "decode_approx.hip:fp4", "topk.hip", "correct.hip", "hybrid_layers.hip", "host_correct.cpp"]
 # "file:variant" builds the file again into its own object with extra defines
 VARIANT_DEFINES = {"q8": ["-DBKV_QUERY_INT8=1"], "mx": ["-DBKV_KEY_MXFP4=1"], "fp4": ["-DBKV_KEY_FP4=1"]}
 # host-only source (the host-side exact correction), OpenMP over host threads

@@ -195,47 +195,20 @@ class HybridPipeline:
 
     def run(self, caches, qs, k_news, v_news, pos, outs=None):
         """Layer i appends (k_news[i], v_news[i]) at pos[b] and attends over
-        pos[b] + 1 tokens of caches[i] with qs[i] ([B][Hq][D] fp16, device).
-        outs: None, or one [B*Hq*D] fp32 device tensor per layer that receives
-        that layer's output; returns the list."""
+        pos[b] + 1 tokens of caches[i] with qs[i] ([B][Hq][D] fp16, device),
+        its output into outs[i] ([B*Hq*D] fp32, device; one buffer reused
+        for every layer when outs is None).  The schedule runs natively
+        (qattn_hybrid_layers); returns outs."""
         import torch
-        nl, M, nb = len(caches), self.micro, self.nb
-        lens = [int(p) + 1 for p in pos]
-        L = self.layout
-        per_q = nb * L.n_q_heads * L.head_dim
-        per_kv = nb * L.n_kv_heads * L.head_dim
-        stream = torch.cuda.current_stream()
-
-        def view(i, m):
-            lay_m, c = bk.cache_rows(caches[i], m * nb, nb)
-            return (lay_m, c, qs[i].reshape(-1)[m * per_q:(m + 1) * per_q],
-                    k_news[i].reshape(-1)[m * per_kv:(m + 1) * per_kv],
-                    v_news[i].reshape(-1)[m * per_kv:(m + 1) * per_kv], lens[m * nb:(m + 1) * nb])
-
-        def select(i, m):
-            st = self.steps[m]
-            lay_m, c, q, kn, vn, ln = view(i, m)
-            bk.qattn_decode_step(lay_m, c, kn, vn, q, ln, self.k, st.sigma, st.idx, st.ws)
-            st.h_idx.copy_(st.idx, non_blocking=True)
-            st.h_q.copy_(q, non_blocking=True)
-            ev = torch.cuda.Event()
-            ev.record(stream)
-            return ev
-
-        events = [select(0, m) for m in range(M)]
-        for i in range(nl):
-            for m in range(M):
-                st = self.steps[m]
-                lay_m, c, q, _, _, ln = view(i, m)
-                events[m].synchronize()  # this micro-batch's rows and appended token are in place
-                bk.qattn_exact_host(lay_m, c.k_shadow, c.v_shadow, st.h_q, ln, st.h_idx, self.k, st.h_state,
-                                    self.n_threads)
-                st.d_state.copy_(st.h_state, non_blocking=True)
-                bk.qattn_correct_hybrid(lay_m, c, q, ln, st.idx if self.k > 0 else None, self.k, st.d_state,
-                                        st.ws, st.out)
-                if outs is not None:
-                    outs[i].reshape(-1)[m * per_q:(m + 1) * per_q].copy_(st.out, non_blocking=True)
-                if i + 1 < nl:
-                    events[m] = select(i + 1, m)
+        nl = len(caches)
+        if outs is None:
+            L = self.layout
+            if not hasattr(self, "_out"):
+                self._out = torch.empty(L.batch * L.n_q_heads * L.head_dim, dtype=torch.float32,
+                                        device=self.steps[0].out.device)
+            outs = [self._out] * nl
+        slots = [dict(sigma=st.sigma, idx=st.idx, ws=st.ws, state_dev=st.d_state, idx_host=st.h_idx,
+                      q_host=st.h_q, state_host=st.h_state) for st in self.steps]
+        bk.qattn_hybrid_layers(self.layout, list(caches), list(qs), list(k_news), list(v_news), pos, self.k,
+                               self.micro, slots, list(outs), self.n_threads)
         return outs
-

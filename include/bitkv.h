@@ -32,6 +32,8 @@
  *   qattn_exact_host     (host) exact states of the selected tokens from a
  *                        host copy of the shadow rows, for
  *   qattn_correct_hybrid qattn_correct with those exact states
+ *   qattn_hybrid_layers  (host schedule) the hybrid step over several layers,
+ *                        host passes overlapping GPU work
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -39,7 +41,9 @@
  *    Shadow pointers may also be device-visible pinned host memory (see
  *    bkv_cache).  The caller owns every buffer; the library never allocates,
  *    frees or synchronises, and keeps no state between calls (the one
- *    host-only computation, qattn_exact_host, uses OpenMP's thread pool).
+ *    host-only computation, qattn_exact_host, uses OpenMP's thread pool;
+ *    qattn_hybrid_layers waits on events of its own; qattn_decode_fused_noalloc
+ *    uses an array the library holds).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work; results are ready when the stream is.
  *  - Errors: every call validates its arguments on the host before any launch
@@ -429,6 +433,51 @@ bkv_status qattn_correct_hybrid(const bkv_layout* layout, const bkv_cache* cache
                                 const int32_t* idx, int32_t k,
                                 const float* exact_state, void* ws,
                                 size_t ws_bytes, float* out, void* stream);
+
+/*
+ * qattn_hybrid_layers -- the hybrid step (qattn_decode_step, qattn_exact_host,
+ * qattn_correct_hybrid; JetFire README, introduction: the correction of the
+ * top-k tokens from the high-precision copy in host memory) over n_layers
+ * layers, scheduled on the calling thread so that the host's exact passes
+ * overlap GPU work.  The batch is split into `micro` micro-batches of
+ * batch / micro consecutive rows (a layer's query depends on the previous
+ * layer's output, so overlap comes from the other micro-batches): while the
+ * host computes micro-batch m's states of layer i, the GPU runs the other
+ * micro-batches' queued scans and merges.  Layer i appends (k_new[i],
+ * v_new[i], [B][Hkv][D] fp16, device) at pos_host[b] and attends over
+ * pos_host[b] + 1 tokens of caches[i] with q[i] ([B][Hq][D] fp16, device);
+ * its output goes to out[i] ([B][Hq][D] fp32, device).  caches[i] must keep
+ * its shadow rows in pinned host memory (bkv_cache).  slots[m]: micro-batch
+ * m's buffers (layout with batch / micro rows): sigma, idx, a workspace of
+ * bkv_workspace_bytes(that layout, max length, k) zero-filled once, state_dev
+ * [B/micro][Hq][2 + D] fp32 (device), and pinned host idx_host, q_host,
+ * state_host of the matching sizes.  The one call of the library that waits:
+ * for each micro-batch's event (never for the whole stream); it creates and
+ * destroys `micro` events.  Returns once every host pass is done and the
+ * last merges are enqueued on `stream`.
+ * Errors: BKV_E_NULL, BKV_E_ARG (n_layers, k, n_threads < 0, micro < 1 or
+ * not dividing the batch), BKV_E_WORKSPACE, BKV_E_CAPACITY (a position
+ * outside [0, capacity)) before anything is enqueued; later failures of
+ * the calls it makes are returned as they come (work already enqueued
+ * stays enqueued).
+ */
+typedef struct {
+  float* sigma;        /* device [B/micro][Hkv][capacity]                   */
+  int32_t* idx;        /* device [B/micro][Hkv][k]                          */
+  void* ws;            /* device workspace                                  */
+  size_t ws_bytes;
+  float* state_dev;    /* device [B/micro][Hq][2 + D]                       */
+  int32_t* idx_host;   /* pinned host [B/micro][Hkv][k]                     */
+  uint16_t* q_host;    /* pinned host [B/micro][Hq][D]                      */
+  float* state_host;   /* pinned host [B/micro][Hq][2 + D]                  */
+} bkv_hybrid_slot;
+
+bkv_status qattn_hybrid_layers(const bkv_layout* layout, int32_t n_layers,
+                               const bkv_cache* caches, const uint16_t* const* q,
+                               const uint16_t* const* k_new, const uint16_t* const* v_new,
+                               const int32_t* pos_host, int32_t k, int32_t micro,
+                               const bkv_hybrid_slot* slots, float* const* out,
+                               int32_t n_threads, void* stream);
 
 /*
  * qattn_exact_host -- HOST computation (runs on the calling thread and

@@ -187,6 +187,38 @@ def test_host_error_paths(bk):
     assert bk.raw_status(tb, C.byref(big), FAKE, P(lens), 4, 32, FAKE, FAKE, need, None) == 3
 
 
+def test_hybrid_layers_host_errors(bk):
+    """qattn_hybrid_layers validates everything before enqueueing anything
+    (the pointers here are fake and never dereferenced)."""
+    import numpy as np
+    fn = "qattn_hybrid_layers"
+    lay = L(bk)  # batch 4
+    cv = (bk.CacheView * 2)(fake_cache(bk), fake_cache(bk))
+    ptrs = (C.c_void_p * 2)(FAKE, FAKE)
+    pos = np.full(4, 100, np.int32)
+    need = bk.bkv_workspace_bytes(bk.make_layout(2, 32, 8, 1024, 4, 4), 101, 8)
+    slot = lambda ws_bytes: bk.HybridSlot(FAKE, FAKE, FAKE, ws_bytes, FAKE, FAKE, FAKE, FAKE)
+    slots = (bk.HybridSlot * 2)(slot(need), slot(need))
+    P = pos.ctypes.data
+    args = lambda **kw: [kw.get("lay", C.byref(lay)), kw.get("n", 2), kw.get("cv", cv), ptrs, ptrs, ptrs,
+                         kw.get("pos", P), kw.get("k", 8), kw.get("micro", 2), kw.get("slots", slots), ptrs,
+                         kw.get("threads", 0), None]
+    assert bk.raw_status(fn, *args(micro=3)) == 7      # 4 rows do not split in 3
+    assert bk.raw_status(fn, *args(micro=0)) == 7
+    assert bk.raw_status(fn, *args(k=-1)) == 7
+    assert bk.raw_status(fn, *args(threads=-1)) == 7
+    assert bk.raw_status(fn, *args(n=0)) == 0           # nothing to do
+    assert bk.raw_status(fn, *args(lay=None)) == 1
+    bad = np.array([100, 1024, 5, 5], np.int32)        # a position at the capacity
+    assert bk.raw_status(fn, *args(pos=bad.ctypes.data)) == 4
+    small = (bk.HybridSlot * 2)(slot(need), slot(64))
+    assert bk.raw_status(fn, *args(slots=small)) == 5
+    nulls = (bk.HybridSlot * 2)(slot(need), bk.HybridSlot(FAKE, None, FAKE, need, FAKE, FAKE, FAKE, FAKE))
+    assert bk.raw_status(fn, *args(slots=nulls)) == 1   # no idx with k > 0
+    cv2 = (bk.CacheView * 2)(fake_cache(bk), bk.CacheView(FAKE, FAKE, FAKE, FAKE, None, FAKE))
+    assert bk.raw_status(fn, *args(cv=cv2)) == 1
+
+
 def test_status_strings(bk):
     for s in range(8):
         assert bk._lib.bkv_status_string(s)
