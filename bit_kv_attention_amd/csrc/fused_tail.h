@@ -12,14 +12,16 @@
 //     of its own kk-th largest score, lists its entries of bins >= D_s in
 //     index order (composites) in the workspace with the list's size and
 //     D_s, and meets the unit's other workgroups at a barrier.
-//  2. Threshold.  Each loads every list into LDS.  A split's kk-th largest
-//     score is never above the unit's, so the bin D of the unit's kk-th
-//     largest is >= Dmax = max D_s, and in the bins >= Dmax the lists hold
-//     every entry of the unit: their histogram there is the unit's.  It gives
-//     D and how many of D's entries are taken; those are ranked exactly and
-//     T = the needD-th largest.  The selected set {t : composite(t) >= T} is
-//     the set topk_select finds.  (Lists too long for LDS -- many equal
-//     scores -- take a radix select over the lists in the workspace.)
+//  2. Threshold.  Each loads every list into LDS (the list sizes and the
+//     first entries of every list in one round trip).  A split's kk-th
+//     largest score is never above the unit's, so the bin D of the unit's
+//     kk-th largest is >= Dmax = max D_s, and in the bins >= Dmax the lists
+//     hold every entry of the unit: their histogram there is the unit's.  It
+//     gives D and how many of D's entries are taken; those are ranked
+//     exactly and T = the needD-th largest.  The selected set
+//     {t : composite(t) >= T} is the set topk_select finds.  (Lists too long
+//     for LDS -- many equal scores -- take a radix select over the lists in
+//     the workspace.)
 //  3. Correction.  The split's own selected tokens in passes of kFPass:
 //     exact logits from the fp16 shadow rows, approximate logits recomputed
 //     from the codes (correct_lane.h), the exact state online over the
@@ -118,9 +120,50 @@ struct FusedCtx {
 };
 
 constexpr int kFUnion = kSelStage / 2;  // list entries (composites) the LDS takes: the scores' room
-constexpr int kFBinD = kFBins / 2;      // bin-D entries the LDS takes: the histogram's room
+constexpr int kFSubBits = 8;            // the second level inside bin D: the next bits of the composites
 constexpr int kFWin = 512;              // bins of the window histogram above Dmax
 constexpr int kFStage = 512;            // list entries a wave stages in LDS (the correction partials' room)
+
+// The loads of one correction pass of up to kFPass tokens (toks[j]; an empty
+// slot, -1, reads token 0, present whenever a token is selected): thread tid
+// takes the key run of token tid / 8 (channels 16 (tid % 8) ..), and lane l
+// of wave w the values of channels 2l, 2l + 1 of tokens 8w .. 8w + 7 (one
+// coalesced 256-byte row per token and wave).
+template <int KB, int VB>
+struct FPass {
+  KeyRun<KB, true, true> kr;
+  uint32_t vx[8];     // the fp16 shadow pair
+  uint32_t vd[8][2];  // the two channels' code dwords
+  uint32_t vm[8];     // their group's meta word
+
+  __device__ inline void load(const uint16_t* __restrict__ ksh, const uint8_t* __restrict__ kbase,
+                              const uint32_t* __restrict__ kmeta, const uint16_t* __restrict__ vsh,
+                              const uint8_t* __restrict__ vbase, const uint32_t* __restrict__ vmeta, int cap,
+                              int mshift, const int* toks) {
+    const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+    kr.load(ksh, kbase, kmeta, cap, max(toks[tid >> 3], 0), tid & 7, mshift);
+    const int c0 = 2 * lane;
+    const size_t mrow = (size_t)((c0 / kGroup) >> mshift) * cap;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = max(toks[8 * wv + j], 0);
+      vx[j] = *reinterpret_cast<const uint32_t*>(vsh + (size_t)t * kHeadDim + c0);
+      const uint32_t* tile = reinterpret_cast<const uint32_t*>(vbase + (size_t)(t / kTile) * v_tile_bytes(VB));
+      int d0, d1, bit;
+      v_code_pos(VB, t % kTile, c0, d0, bit);
+      v_code_pos(VB, t % kTile, c0 + 1, d1, bit);
+      vd[j][0] = tile[d0];
+      vd[j][1] = tile[d1];
+      vm[j] = vmeta[mrow + t];
+    }
+  }
+  __device__ inline void zero() {
+    kr.k0 = kr.k1 = (uint4){0u, 0u, 0u, 0u};
+    kr.kraw[0][0] = kr.kraw[0][1] = kr.kraw[1][0] = kr.kraw[1][1] = kr.kmw = 0u;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vx[j] = vd[j][0] = vd[j][1] = vm[j] = 0u;
+  }
+};
 
 // rm, rl, ra: this thread's (head, channel) pairs e = tid + 512 r of the
 // split's approximate state (max in log2 units, denominator, value sum).
@@ -141,22 +184,150 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
   uint32_t* dsv = x.fa.dsv + (size_t)x.u * x.nsplit;    // the splits' D_s
   uint64_t* s_union = reinterpret_cast<uint64_t*>(x.s_split);
   uint64_t* s_dl = reinterpret_cast<uint64_t*>(x.s_fh);
-  uint32_t* s_sel = x.s_fh;  // the split's own selected tokens (offsets), once the threshold is known
   __shared__ int s_res[8];
   __shared__ int s_wsum[NW];
-  __shared__ float s_mm[2 * NW];
-  __shared__ uint64_t s_small[65];
   __shared__ uint64_t s_T;
   __shared__ int s_dc[kFMaxSplits + 1];  // list offsets (prefix sums of the sizes)
   __shared__ int s_flag;
   __shared__ int s_n;
+  __shared__ int s_more;
   __shared__ uint32_t s_dmax;
 
-  int n_sel = 0;   // own selected tokens in s_sel
+  int n_sel = 0;   // own selected tokens (offsets in s_sel)
   uint64_t T = 0;  // partial: the threshold composite
   bool in_lds = false;
   int32_t* row = x.idx + (size_t)x.u * x.ksel;  // the unit's row of idx
-  const uint64_t below = (1ull << lane) - 1;
+  uint32_t* s_sel = x.s_fh;  // (the histogram's room, once the threshold is known)
+  __shared__ int s_tok[kFPass];  // a pass's tokens (-1: empty slot)
+  __shared__ int s_okl[kFPass];  // its occupied slots
+
+  // ---- the correction's pieces -------------------------------------------------------
+  const float sm2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2eF;
+  __shared__ float s_qrun[G][kHeadDim / 16];  // sums of 16-channel runs of the query rows
+  __shared__ float s_rmh[G];                   // the split's approximate maximum per head
+  __shared__ float s_mx[G];
+  __shared__ float s_ls[2][G];
+  if (tid < G * (kHeadDim / 16)) {
+    const int h = tid / (kHeadDim / 16), p = tid % (kHeadDim / 16);
+    float r = 0.f;
+    for (int c = 0; c < 16; ++c) r += h2f(x.s_q[h][16 * p + c]);
+    s_qrun[h][p] = r;
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int e = tid + NTH * r;
+    if ((e & (kHeadDim - 1)) == 0) s_rmh[e / kHeadDim] = rm[r];
+  }
+  const uint4(*qh)[kHeadDim / 8] = reinterpret_cast<const uint4(*)[kHeadDim / 8]>(&x.s_q[0][0]);
+  float(*s_lg)[kFPass][G] = reinterpret_cast<float(*)[kFPass][G]>(x.s_lg);
+  float(*s_w)[kFPass][G] = reinterpret_cast<float(*)[kFPass][G]>(x.s_w);
+  // the value partial sums of the NW waves: exact in the correction scratch,
+  // approximate in the scores' room (both free once the own tokens are known)
+  float(*s_pe)[G][kHeadDim] = reinterpret_cast<float(*)[G][kHeadDim]>(x.s_acc);
+  float(*s_pa)[G][kHeadDim] = reinterpret_cast<float(*)[G][kHeadDim]>(x.s_split);
+  const int tl = tid >> 3, part = tid & 7;  // logits: 8 threads per token
+  float ex_m[NR], ex_l[NR], ex_a[NR], ap_l[NR], ap_a[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    ex_m[r] = -INFINITY;
+    ex_l[r] = ex_a[r] = ap_l[r] = ap_a[r] = 0.f;
+  }
+  // One pass over the loads of FPass (tokens toks[j], slot j counted where
+  // okv[j] != 0): exact logits and weights (relative to the pass maximum),
+  // approximate ones (relative to the split's maximum), the value sums, then
+  // the exact state online over the passes and the approximate sums.
+  auto pass_run = [&](const FPass<KB, VB>& pd, const int* toks, const int* okv) {
+    {
+      float ex[G], ap[G];
+      run_logits<KB, G, true, true, false, 0>(pd.kr, part, qh, s_qrun, nullptr, nullptr, nullptr, ex, ap);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        ex[h] = sum8(ex[h]);
+        ap[h] = sum8(ap[h]);
+      }
+      if (part == 0) {
+        const bool ok = okv[tl] != 0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          s_lg[0][tl][h] = ok ? ex[h] * sm2 : -INFINITY;
+          s_lg[1][tl][h] = ok ? ap[h] * sm2 : -INFINITY;
+        }
+      }
+    }
+    __syncthreads();
+    // per (exact/approximate, head): lane t of a wave takes slot t -- the
+    // weights, their sum and the pass maximum by wave reductions
+    for (int cb = wv; cb < 2 * G; cb += NW) {
+      const int ty = cb / G, h = cb % G;
+      const bool ok = okv[lane] != 0;
+      const float lg = s_lg[ty][lane][h];
+      const float ref = (ty == 0) ? wave_minmax<true>(lg) : s_rmh[h];
+      const float wgt = ok ? __builtin_amdgcn_exp2f(lg - ref) : 0.f;
+      s_w[ty][lane][h] = wgt;
+      const float l = wave_sum(wgt);
+      if (lane == 0) {
+        s_ls[ty][h] = l;
+        if (ty == 0) s_mx[h] = ref;
+      }
+    }
+    __syncthreads();
+    {  // lane: channels 2 lane, 2 lane + 1 of the wave's slots 8 wv .. 8 wv + 7
+      float pe[G][2], pa[G][2];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pe[h][0] = pe[h][1] = pa[h][0] = pa[h][1] = 0.f;
+      constexpr uint32_t VM = (1u << VB) - 1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int slot = 8 * wv + j, t = max(toks[slot], 0);
+        int d, bit;
+        v_code_pos(VB, t % kTile, 2 * lane, d, bit);
+        const half2v_t vh = __builtin_bit_cast(half2v_t, pd.vx[j]);
+        const float v0 = (float)vh[0], v1 = (float)vh[1];
+        const float sc = h2f((uint16_t)(pd.vm[j] & 0xFFFFu)), zp = h2f((uint16_t)(pd.vm[j] >> 16));
+        const float q0 = fmaf(sc, (float)((pd.vd[j][0] >> bit) & VM), zp);
+        const float q1 = fmaf(sc, (float)((pd.vd[j][1] >> bit) & VM), zp);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float we = s_w[0][slot][h], wa = s_w[1][slot][h];
+          pe[h][0] = fmaf(we, v0, pe[h][0]);
+          pe[h][1] = fmaf(we, v1, pe[h][1]);
+          pa[h][0] = fmaf(wa, q0, pa[h][0]);
+          pa[h][1] = fmaf(wa, q1, pa[h][1]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        *reinterpret_cast<float2*>(&s_pe[wv][h][2 * lane]) = make_float2(pe[h][0], pe[h][1]);
+        *reinterpret_cast<float2*>(&s_pa[wv][h][2 * lane]) = make_float2(pa[h][0], pa[h][1]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int e = tid + NTH * r, hh = e / kHeadDim, cc = e & (kHeadDim - 1);
+      float pe = 0.f, pa = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        pe += s_pe[w][hh][cc];
+        pa += s_pa[w][hh][cc];
+      }
+      const float mp = s_mx[hh];  // -inf: no counted slot in the pass
+      if (mp != -INFINITY) {
+        const float mn = fmaxf(ex_m[r], mp);
+        const float f0 = __builtin_amdgcn_exp2f(ex_m[r] - mn), f1 = __builtin_amdgcn_exp2f(mp - mn);
+        ex_a[r] = fmaf(ex_a[r], f0, pe * f1);
+        ex_l[r] = fmaf(ex_l[r], f0, s_ls[0][hh] * f1);
+        ex_m[r] = mn;
+        ap_a[r] += pa;
+        ap_l[r] += s_ls[1][hh];
+      }
+    }
+  };
+  auto load_pass = [&](FPass<KB, VB>& pd, const int* toks) {
+    pd.load(x.ksh, x.kbase, x.kmeta, x.vsh, x.vbase, x.vmeta, x.cap, x.mshift, toks);
+  };
+
+  bool ident = false;  // the selected tokens are the split's offsets 0 .. n_sel - 1
   if (partial) {
     // ---- 1. publish ------------------------------------------------------------------
     const int kks = min(kk, len_s);
@@ -250,19 +421,33 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
     unit_barrier(&ctr[0], (uint32_t)x.nsplit, x.fa.flag);
 
     // ---- 2. threshold ---------------------------------------------------------------
+    // in flight together: the list sizes and bins and the first kBat * 64
+    // entries of each wave's first list (whatever its size)
+    constexpr int kBat = 8;
+    const int q = min(tid, x.nsplit - 1);  // (unconditional loads: a branch around a load waits for it)
+    const int lc = (int)ld_dev32(&cnts[q]);
+    const uint32_t ld = ld_dev32(&dsv[q]);
+    uint64_t lv[kBat];
+    {
+      const uint64_t* src = lists + (size_t)min(wv, x.nsplit - 1) * x.chunk;
+#pragma unroll
+      for (int r = 0; r < kBat; ++r) lv[r] = ld_dev64(&src[min(64 * r + lane, x.chunk - 1)]);
+    }
     {  // list sizes (prefix sums) and Dmax
-      const int q = min(tid, x.nsplit - 1);  // (unconditional loads: a branch around a load waits for it)
-      const int c = (int)ld_dev32(&cnts[q]);
-      const uint32_t d = ld_dev32(&dsv[q]);
       if (tid < x.nsplit) {
-        s_dc[tid + 1] = c;
-        atomicMax(&s_dmax, d);
+        s_dc[tid + 1] = lc;
+        atomicMax(&s_dmax, ld);
       }
       __syncthreads();
       if (tid == 0) {
+        bool more = x.nsplit > NW;  // entries the first batches do not hold
         s_dc[0] = 0;
-        for (int s = 0; s < x.nsplit; ++s) s_dc[s + 1] += s_dc[s];
+        for (int s = 0; s < x.nsplit; ++s) {
+          more = more || s_dc[s + 1] > 64 * kBat;
+          s_dc[s + 1] += s_dc[s];
+        }
         s_n = 0;
+        s_more = more ? 1 : 0;
       }
       __syncthreads();
     }
@@ -270,31 +455,49 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
     const int total = s_dc[x.nsplit];
     in_lds = total <= kFUnion;
     if (in_lds) {
-      // the lists to LDS: wave w loads the lists of splits w, w + NW, ..., 8
-      // unconditional loads per lane in flight together
+      // the lists to LDS: the first batches from the loads above, the rest
+      // (longer lists; splits beyond the first NW) 8 unconditional loads per
+      // lane in flight together
       for (int i = tid; i < kFWin; i += NTH) x.s_fh[i] = 0u;
-      for (int s = wv; s < x.nsplit; s += NW) {
-        const int o = s_dc[s], c = s_dc[s + 1] - o;
-        const uint64_t* src = lists + (size_t)s * x.chunk;
-        constexpr int kBat = 8;
-        for (int p0 = 0; p0 < c; p0 += 64 * kBat) {
-          uint64_t v[kBat];
+      if (wv < x.nsplit) {
+        const int o = s_dc[wv], c = s_dc[wv + 1] - o;
 #pragma unroll
-          for (int r = 0; r < kBat; ++r) v[r] = ld_dev64(&src[min(p0 + 64 * r + lane, c - 1)]);
+        for (int r = 0; r < kBat; ++r) {
+          const int p = 64 * r + lane;
+          if (p < c) s_union[o + p] = lv[r];
+        }
+      }
+      if (s_more) {
+        for (int s = wv; s < x.nsplit; s += NW) {
+          const int o = s_dc[s], c = s_dc[s + 1] - o;
+          const uint64_t* src = lists + (size_t)s * x.chunk;
+          for (int p0 = (s == wv) ? 64 * kBat : 0; p0 < c; p0 += 64 * kBat) {
+            uint64_t v[kBat];
 #pragma unroll
-          for (int r = 0; r < kBat; ++r) {
-            const int p = p0 + 64 * r + lane;
-            if (p < c) s_union[o + p] = v[r];
+            for (int r = 0; r < kBat; ++r) v[r] = ld_dev64(&src[min(p0 + 64 * r + lane, c - 1)]);
+#pragma unroll
+            for (int r = 0; r < kBat; ++r) {
+              const int p = p0 + 64 * r + lane;
+              if (p < c) s_union[o + p] = v[r];
+            }
           }
         }
       }
       __syncthreads();
+      // every thread keeps its union entries tid + NTH r in registers for
+      // the passes below
+      constexpr int PU = kFUnion / NTH;
+      uint64_t ue[PU];
+#pragma unroll
+      for (int r = 0; r < PU; ++r) ue[r] = s_union[min(tid + NTH * r, total - 1)];
+      auto valid = [&](int r) { return tid + NTH * r < total; };
       // their histogram in the bins Dmax .. Dmax + kFWin - 2 (the unit's
       // there; the last counter takes every bin above), then D: thread tid
       // owns counter kFWin - 1 - tid
-      for (int i = tid; i < total; i += NTH) {
-        const uint32_t b = fbin_c(s_union[i]);
-        if (b >= Dmax) atomicAdd(&x.s_fh[min(b - Dmax, (uint32_t)kFWin - 1)], 1u);
+#pragma unroll
+      for (int r = 0; r < PU; ++r) {
+        const uint32_t b = fbin_c(ue[r]);
+        if (valid(r) && b >= Dmax) atomicAdd(&x.s_fh[min(b - Dmax, (uint32_t)kFWin - 1)], 1u);
       }
       __syncthreads();
       {
@@ -307,14 +510,15 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
           s_res[2] = mine;
           s_res[3] = (tid == 0);  // the top counter: bins merged
         }
-        __syncthreads();  // (every read of the counters is done: their room takes bin D's entries)
+        __syncthreads();
       }
       if (s_res[3]) {  // the kk-th largest lies kFWin - 1 or more bins above Dmax: the full histogram
         for (int i = tid; i < kFBins; i += NTH) x.s_fh[i] = 0u;
         __syncthreads();
-        for (int i = tid; i < total; i += NTH) {
-          const uint32_t b = fbin_c(s_union[i]);
-          if (b >= Dmax) atomicAdd(&x.s_fh[b], 1u);
+#pragma unroll
+        for (int r = 0; r < PU; ++r) {
+          const uint32_t b = fbin_c(ue[r]);
+          if (valid(r) && b >= Dmax) atomicAdd(&x.s_fh[b], 1u);
         }
         __syncthreads();
         constexpr int PB = kFBins / NTH;
@@ -341,42 +545,65 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       const int needD = kk - s_res[1], inD = s_res[2];
       if (needD == inD) {  // all of bin D
         if (tid == 0) s_T = (uint64_t)D << (64 - kFBinBits);
-      } else if (inD <= kFBinD) {
-        for (int i = tid; i < total; i += NTH) {
-          const uint64_t e = s_union[i];
-          if (fbin_c(e) == D) s_dl[atomicAdd(&s_n, 1)] = e;
-        }
+      } else {
+        // a second level inside bin D: the next kFSubBits bits of its
+        // entries' composites, histogrammed from the registers; the sub-bin
+        // S holding the needD-th largest, then only S's entries are ranked
+        constexpr int kSh = 64 - kFBinBits - kFSubBits;
+        constexpr int NS = 1 << kFSubBits;
+        uint32_t* s_sub = reinterpret_cast<uint32_t*>(x.s_acc);
+        for (int i = tid; i < NS; i += NTH) s_sub[i] = 0u;
         __syncthreads();
-        const int m = inD;
-        if (m <= NTH) {  // rank every entry against all (distinct composites), 8 reads in flight
-          if (tid < m) {
-            const uint64_t c = s_dl[tid];
-            int r = 0, j = 0;
-            for (; j + 8 <= m; j += 8) {
 #pragma unroll
-              for (int z = 0; z < 8; ++z) r += (s_dl[j + z] > c) ? 1 : 0;
-            }
-            for (; j < m; ++j) r += (s_dl[j] > c) ? 1 : 0;
-            if (r == needD - 1) s_T = c;
+        for (int r = 0; r < PU; ++r)
+          if (valid(r) && fbin_c(ue[r]) == D) atomicAdd(&s_sub[(uint32_t)(ue[r] >> kSh) & (NS - 1)], 1u);
+        __syncthreads();
+        {
+          const int mine = (tid < NS) ? (int)s_sub[NS - 1 - tid] : 0;
+          int tot;
+          const int above = block_excl_scan<NW>(mine, s_wsum, tot);
+          if (above < needD && above + mine >= needD) {
+            s_res[4] = NS - 1 - tid;
+            s_res[5] = above;
+            s_res[6] = mine;
           }
-        } else {
-          constexpr int PER = kFBinD / NTH;
-          uint64_t c[PER];
+          __syncthreads();
+        }
+        const uint64_t P = ((uint64_t)D << kFSubBits) | (uint64_t)s_res[4];  // the top kFBinBits + kFSubBits bits
+        const int needS = needD - s_res[5], inS = s_res[6];
+        if (needS == inS) {  // all of sub-bin S
+          if (tid == 0) s_T = P << kSh;
+        } else if (inS <= NTH) {
+          // S's entries to LDS (one atomic per wave and register), then each
+          // ranked against all (distinct composites)
+          const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
-          for (int j = 0; j < PER; ++j) c[j] = (j * NTH + tid < m) ? s_dl[j * NTH + tid] : 0ull;
-          auto get = [&](int i) { return s_dl[i]; };
-          auto fill = [] {};  // (the entries are in LDS already)
-          const uint64_t t = hist_select<NTH>(c, m, needD, get, fill, reinterpret_cast<uint32_t*>(x.s_acc),
-                                              s_wsum, s_res, s_mm, s_small);
+          for (int r = 0; r < PU; ++r) {
+            const bool p = valid(r) && (ue[r] >> kSh) == P;
+            const uint64_t m = __ballot(p);
+            if (m) {
+              int base = 0;
+              if (lane == 0) base = atomicAdd(&s_n, __popcll(m));
+              base = __shfl(base, 0);
+              if (p) s_dl[base + __popcll(m & below)] = ue[r];
+            }
+          }
+          __syncthreads();
+          if (tid < inS) {
+            const uint64_t c = s_dl[tid];
+            int rk = 0;
+            for (int j = 0; j < inS; ++j) rk += (s_dl[j] > c) ? 1 : 0;
+            if (rk == needS - 1) s_T = c;
+          }
+        } else {  // many entries share the top bits (equal scores): radix select among them in LDS
+          auto get = [&](int i) -> uint64_t {
+            const uint64_t e = s_union[i];
+            return (e >> kSh) == P ? e : 0ull;
+          };
+          const uint64_t t =
+              lds_threshold<NTH>(get, total, needS, reinterpret_cast<uint32_t*>(x.s_acc), s_wsum, s_res);
           if (tid == 0) s_T = t;
         }
-      } else {  // a crowded bin D: radix select among its entries in LDS
-        auto get = [&](int i) -> uint64_t {
-          const uint64_t e = s_union[i];
-          return fbin_c(e) == D ? e : 0ull;
-        };
-        const uint64_t t = lds_threshold<NTH>(get, total, needD, reinterpret_cast<uint32_t*>(x.s_acc), s_wsum, s_res);
-        if (tid == 0) s_T = t;
       }
     } else {  // many equal scores: a radix select over the lists in the workspace (bins >= Dmax)
       auto get = [&](int i) -> uint64_t {
@@ -403,7 +630,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
           c, [&](int i) { return s_union[o + i] >= T; },
           [&](int q, int i) {
             const int t = (int)~(uint32_t)(s_union[o + i] & 0xFFFFFFFFu);
-            s_sel[q] = (uint32_t)(t - x.t_begin);
+            if (q < kFBins) s_sel[q] = (uint32_t)(t - x.t_begin);
             if (before + q < x.ksel) row[before + q] = t;
           },
           s_wsum);
@@ -413,146 +640,41 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       if (tid == 0) s_n = 0;
       __syncthreads();
       for (int i = tid; i < len_s; i += NTH)
-        if (composite(x.s_split[i], x.t_begin + i) >= T) s_sel[atomicAdd(&s_n, 1)] = (uint32_t)i;
+        if (composite(x.s_split[i], x.t_begin + i) >= T) {
+          const int p = atomicAdd(&s_n, 1);
+          if (p < kFBins) s_sel[p] = (uint32_t)i;
+        }
       __syncthreads();
       n_sel = s_n;
     }
     __syncthreads();
-    n_sel = min(n_sel, x.ksel);  // (<= min(kk, len_s); the clamp only guards the lists)
+    n_sel = min(min(n_sel, x.ksel), kFBins);  // (<= min(kk, len_s); the clamp only guards the lists)
   } else {
     if (kk > 0) {  // every token is selected
-      for (int i = tid; i < len_s; i += NTH) {
-        s_sel[i] = (uint32_t)i;
-        row[x.t_begin + i] = x.t_begin + i;
-      }
+      for (int i = tid; i < len_s; i += NTH) row[x.t_begin + i] = x.t_begin + i;
       n_sel = len_s;
+      ident = true;
     }
     if (x.split == 0)
       for (int j = kk + tid; j < x.ksel; j += NTH) row[j] = -1;
     __syncthreads();
   }
-
   // ---- 3. correction of this split's state ------------------------------------------
-  float ex_m[NR], ex_l[NR], ex_a[NR], ap_l[NR], ap_a[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    ex_m[r] = -INFINITY;
-    ex_l[r] = ex_a[r] = ap_l[r] = ap_a[r] = 0.f;
-  }
-  if (n_sel > 0) {
-    const float sm2 = (1.0f / sqrtf((float)kHeadDim)) * kLog2eF;
-    __shared__ float s_qrun[G][kHeadDim / 16];  // sums of 16-channel runs of the query rows
-    __shared__ float s_rmh[G];                   // the split's approximate maximum per head
-    __shared__ int s_tok[kFPass];
-    __shared__ float s_mx[G];
-    __shared__ float s_ls[2][G];
-    if (tid < G * (kHeadDim / 16)) {
-      const int h = tid / (kHeadDim / 16), p = tid % (kHeadDim / 16);
-      float r = 0.f;
-      for (int c = 0; c < 16; ++c) r += h2f(x.s_q[h][16 * p + c]);
-      s_qrun[h][p] = r;
+  // the selected tokens in passes of kFPass
+  for (int p0 = 0; p0 < n_sel; p0 += kFPass) {
+    const int np = min(kFPass, n_sel - p0);
+    if (tid < kFPass) {
+      s_tok[tid] = (tid < np) ? x.t_begin + (ident ? p0 + tid : (int)s_sel[p0 + tid]) : -1;
+      s_okl[tid] = (tid < np) ? 1 : 0;
     }
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int e = tid + NTH * r;
-      if ((e & (kHeadDim - 1)) == 0) s_rmh[e / kHeadDim] = rm[r];
-    }
-    const uint4(*qh)[kHeadDim / 8] = reinterpret_cast<const uint4(*)[kHeadDim / 8]>(&x.s_q[0][0]);
-    float(*s_lg)[kFPass][G] = reinterpret_cast<float(*)[kFPass][G]>(x.s_lg);
-    float(*s_w)[kFPass][G] = reinterpret_cast<float(*)[kFPass][G]>(x.s_w);
-    float(*s_part)[4][G][kHeadDim] = reinterpret_cast<float(*)[4][G][kHeadDim]>(x.s_acc);
-    const int tl = tid >> 3, part = tid & 7;             // logits: 8 threads per token
-    const int c = tid & (kHeadDim - 1), qtr = tid >> 7;  // values: (channel, quarter of the pass)
-    for (int p0 = 0; p0 < n_sel; p0 += kFPass) {
-      const int np = min(kFPass, n_sel - p0);
-      if (tid < kFPass) s_tok[tid] = (tid < np) ? x.t_begin + (int)s_sel[p0 + tid] : -1;
-      __syncthreads();
-      // loads: every one unconditional (an empty slot reads token 0, present
-      // whenever a token is selected) and in flight before the first is used
-      const int tsel = s_tok[tl];
-      KeyRun<KB, true, true> kr;
-      kr.load(x.ksh, x.kbase, x.kmeta, x.cap, max(tsel, 0), part, x.mshift);
-      constexpr int kQ = kFPass / 4;
-      uint16_t vx16[kQ];
-      ValueCode<VB> vcd[kQ];
-#pragma unroll
-      for (int j = 0; j < kQ; ++j) {
-        const int t = max(s_tok[qtr * kQ + j], 0);
-        vcd[j].load(x.vbase, x.vmeta, x.cap, t, c, x.mshift);
-        vx16[j] = x.vsh[(size_t)t * kHeadDim + c];
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        float ex[G], ap[G];
-        run_logits<KB, G, true, true, false, 0>(kr, part, qh, s_qrun, nullptr, nullptr, nullptr, ex, ap);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          ex[h] = sum8(ex[h]);
-          ap[h] = sum8(ap[h]);
-        }
-        if (part == 0) {
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            s_lg[0][tl][h] = (tsel >= 0) ? ex[h] * sm2 : -INFINITY;
-            s_lg[1][tl][h] = (tsel >= 0) ? ap[h] * sm2 : -INFINITY;
-          }
-        }
-      }
-      __syncthreads();
-      // per (exact/approximate, head): lane t of a wave takes token t -- the
-      // weights (exact: relative to the pass maximum; approximate: to the
-      // split's), their sum and the pass maximum by wave reductions
-      for (int cb = wv; cb < 2 * G; cb += NW) {
-        const int ty = cb / G, h = cb % G;
-        const bool ok = s_tok[lane] >= 0;
-        const float lg = s_lg[ty][lane][h];
-        const float ref = (ty == 0) ? wave_minmax<true>(lg) : s_rmh[h];
-        const float wgt = ok ? __builtin_amdgcn_exp2f(lg - ref) : 0.f;
-        s_w[ty][lane][h] = wgt;
-        const float l = wave_sum(wgt);
-        if (lane == 0) {
-          s_ls[ty][h] = l;
-          if (ty == 0) s_mx[h] = ref;
-        }
-      }
-      __syncthreads();
-      {
-        float ea[G], aa[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) ea[h] = aa[h] = 0.f;
-#pragma unroll
-        for (int j = 0; j < kQ; ++j) {
-          const int t2 = qtr * kQ + j;
-          const float vx = h2f(vx16[j]);
-          const float vq = vcd[j].value(max(s_tok[t2], 0), c);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-            ea[h] = fmaf(s_w[0][t2][h], vx, ea[h]);
-            aa[h] = fmaf(s_w[1][t2][h], vq, aa[h]);
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          s_part[0][qtr][h][c] = ea[h];
-          s_part[1][qtr][h][c] = aa[h];
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const int e = tid + NTH * r, hh = e / kHeadDim, cc = e & (kHeadDim - 1);
-        const float pe = s_part[0][0][hh][cc] + s_part[0][1][hh][cc] + s_part[0][2][hh][cc] + s_part[0][3][hh][cc];
-        const float pa = s_part[1][0][hh][cc] + s_part[1][1][hh][cc] + s_part[1][2][hh][cc] + s_part[1][3][hh][cc];
-        const float mp = s_mx[hh];  // finite: the pass has a token
-        const float mn = fmaxf(ex_m[r], mp);
-        const float f0 = __builtin_amdgcn_exp2f(ex_m[r] - mn), f1 = __builtin_amdgcn_exp2f(mp - mn);
-        ex_a[r] = fmaf(ex_a[r], f0, pe * f1);
-        ex_l[r] = fmaf(ex_l[r], f0, s_ls[0][hh] * f1);
-        ex_m[r] = mn;
-        ap_a[r] += pa;
-        ap_l[r] += s_ls[1][hh];
-      }
-    }
+    __syncthreads();
+    // (a wave whose 8 slots are all empty loads nothing)
+    FPass<KB, VB> pd;
+    if (8 * wv < np)
+      load_pass(pd, s_tok);
+    else
+      pd.zero();
+    pass_run(pd, s_tok, s_okl);
   }
 
   // ---- 4. the corrected record; the unit's last workgroup writes the output ----------

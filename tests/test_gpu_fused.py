@@ -116,6 +116,20 @@ def test_fused_step_parity(P, kb, vb, G):
 
 
 @pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
+def test_fused_many_selected_per_split(P, kb, vb, G):
+    """k far above 64 per split (about 128 selected tokens in each split of
+    512): most selected tokens lie outside each split's likely set and take
+    passes of their own after the threshold."""
+    banner(f"fused many per split kb={kb} vb={vb} G={G}")
+    w = P.Workload("fmany", 4, 8 * G, 8, 128, 4096, kb, vb, 32, 1024, 8, 500 + kb + G)
+    pair = P.build_pair(w, L=4096, cap=4096)
+    lens = np.array([4096, 4000, 3001, 2048])
+    ra, rb = run_both(P, pair, lens, w.k)
+    assert_same_selection(ra, rb, lens)
+    check_against_oracle(P, pair, ra, lens, w.k)
+
+
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
 def test_fused_attend_without_append(P, kb, vb, G):
     banner(f"fused attend kb={kb} vb={vb} G={G}")
     w = P.Workload("fattend", 2, 4 * G, 4, 128, 3000, kb, vb, 32, 64, 10, 400 + kb + G)
@@ -205,6 +219,45 @@ def test_fused_ties_overflow(P, L, k):
     oc.append(K, V, np.zeros(1, np.int32))
     ref = oc.decode(q, np.array([L], np.int32), k, sel=idx.reshape(1, 1, -1))
     P.assert_close(out.cpu().numpy().reshape(1, 4, 128), ref["out"], "ties out")
+    assert flag_word(st, lay) == 0
+
+
+def test_fused_tie_group_at_threshold(P):
+    """A few equal scores straddle the threshold in different splits: the
+    threshold lies inside a group whose composites share every score bit, so
+    it is found by ranking the group's entries (the lower indices win)."""
+    banner("fused tie group at the threshold")
+    import torch
+    import oracle
+    from bit_kv_attention_amd import binding as bk
+    from bit_kv_attention_amd.step import DecodeStep
+    rng = np.random.default_rng(21)
+    L, k = 4000, 5
+    cap = ((L + 31) // 32) * 32
+    q = rng.standard_normal((1, 4, 128)).astype(np.float16)
+    K = rng.standard_normal((1, 1, L, 128)).astype(np.float16)
+    d = q[0, 0].astype(np.float32) / np.linalg.norm(q[0, 0].astype(np.float32))
+    for t, s in ((50, 2.5), (2000, 2.0), (3500, 1.5)):  # three clear winners
+        K[0, 0, t] = (d * 12 * s).astype(np.float16)
+    for t in (3900, 100, 2500, 1500, 3000):  # the tied group: two of them are taken
+        K[0, 0, t] = (d * 12).astype(np.float16)
+    V = rng.standard_normal((1, 1, L, 128)).astype(np.float16)
+    lay = bk.make_layout(1, 4, 1, cap, 4, 4)
+    gc = bk.allocate_cache(lay)
+    bk.kv_pack_append(lay, gc, P.to_dev(K), P.to_dev(V), L, [0])
+    st = DecodeStep(lay, k, L, one_launch=True)
+    assert st.one_launch
+    out = st.attend(gc, P.to_dev(q), [L])
+    torch.cuda.synchronize()
+    sig = st.sigma.cpu().numpy()[:L].astype(np.float64)
+    idx = st.idx.cpu().numpy()[:k]
+    assert sig[100] == sig[1500] == sig[2500] == sig[3000] == sig[3900]
+    assert np.array_equal(idx, oracle.topk(sig, k))
+    assert set(idx.tolist()) == {50, 100, 1500, 2000, 3500}
+    oc = oracle.Cache(oracle.Shape(1, 4, 1, 128, 4, 4, 32, cap))
+    oc.append(K, V, np.zeros(1, np.int32))
+    ref = oc.decode(q, np.array([L], np.int32), k, sel=idx.reshape(1, 1, -1))
+    P.assert_close(out.cpu().numpy().reshape(1, 4, 128), ref["out"], "tie group out")
     assert flag_word(st, lay) == 0
 
 
