@@ -497,14 +497,11 @@ def bench_one(w, args, torch, shadow="hbm", line=True):
     }
     if path == "fused" and "separate" in paths:
         # the fused launch holds the whole step (scan, selection, correction,
-        # merge); beside it, the scan kernel of the separate launches on the
-        # same packed bytes, which is what the scan alone reaches
+        # merge); beside it, the separate launches' calls on the same step
+        # (events around each call; a call may hold several launches)
         sk = wb.per_call_us(wb.calls("separate"), max(args.steps, 20))
-        sname = "qattn_decode_step" if "qattn_decode_step" in sk else "qattn_decode_approx"
-        if sname in sk:
-            s_ach = wb.packed / (sk[sname] / 1e6) / 1e9
-            res["roofline"]["scan_kernel"] = {"kernel": sname, "kernel_us_per_launch": round(sk[sname], 2),
-                                              "achieved": round(s_ach, 1), "frac": round(s_ach / HBM_PEAK_GBPS, 4)}
+        res["separate_path"] = {"ms_per_step": round(paths["separate"] / 1000.0, 5),
+                                "us_per_call": {n: round(v, 2) for n, v in sk.items()}}
     if prof and "rocprof_median_us" in prof:  # the committed kernel-trace figure beside the live one
         r_us = float(prof["rocprof_median_us"])
         res["roofline"]["rocprof_kernel_us_median"] = r_us
