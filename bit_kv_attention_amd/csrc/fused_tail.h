@@ -69,9 +69,11 @@ __device__ inline int ordered_compact(int n, Pred pred, Emit emit, int* s_wc) {
   const int R = ((n + NW * 64 - 1) / (NW * 64)) * 64;
   const int lo = wv * R, hi = min(n, lo + R);
   int cnt = 0;
+  // (pred is evaluated at a clamped index and combined bitwise: no branch
+  // per entry)
   for (int b = lo; b < hi; b += 64) {
     const int i = b + lane;
-    cnt += __popcll(__ballot(i < hi && pred(i)));
+    cnt += __popcll(__ballot((int)(i < hi) & (int)pred(min(i, hi - 1))));
   }
   __syncthreads();  // (s_wc may still be read by a previous call)
   if (lane == 0) s_wc[wv] = cnt;
@@ -86,7 +88,7 @@ __device__ inline int ordered_compact(int n, Pred pred, Emit emit, int* s_wc) {
   const uint64_t below = (1ull << lane) - 1;
   for (int b = lo; b < hi; b += 64) {
     const int i = b + lane;
-    const bool p = i < hi && pred(i);
+    const bool p = (int)(i < hi) & (int)pred(min(i, hi - 1));
     const uint64_t m = __ballot(p);
     if (p) emit(base + __popcll(m & below), i);
     base += __popcll(m);
@@ -191,6 +193,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
   __shared__ int s_flag;
   __shared__ int s_n;
   __shared__ int s_more;
+  __shared__ uint32_t s_junk[64];  // a lane's target for writes and counts that do not count
   __shared__ uint32_t s_dmax;
 
   int n_sel = 0;   // own selected tokens (offsets in s_sel)
@@ -364,6 +367,9 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       // kSelStage scores)
       const int R = ((len_s + NW * 256 - 1) / (NW * 256)) * 256;
       const int lo = wv * R, hi = min(len_s, lo + R);
+      // (branch-free: the predicates are combined bitwise and a lane with
+      // nothing to stage writes its own scratch word -- per-entry branches
+      // made this loop several times slower)
       int cnt = 0;
       for (int b0 = lo; b0 < hi; b0 += 512) {
         floatx4 v[2];
@@ -372,23 +378,21 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int i0 = b0 + 256 * r + 4 * lane;
-          bool p[4];
-          int c = 0;
+          int pj[4], c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            p[j] = i0 + j < hi && fbin(v[r][j]) >= Ds;
-            c += p[j] ? 1 : 0;
+            pj[j] = (int)(i0 + j < hi) & (int)(fbin(v[r][j]) >= Ds);
+            c += pj[j];
           }
           const int inc = wave_incl_scan(c);
           int q = cnt + inc - c;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            if (p[j]) {
-              if (q < kFStage) stage[q] = (uint32_t)(i0 + j);
-              ++q;
-            }
+            uint32_t* dst = (pj[j] & (int)(q < kFStage)) ? &stage[min(q, kFStage - 1)] : &s_junk[lane];
+            *dst = (uint32_t)(i0 + j);
+            q += pj[j];
           }
-          cnt += __shfl(inc, 63);
+          cnt += __builtin_amdgcn_readlane(inc, 63);
         }
       }
       if (lane == 0) s_wsum[wv] = cnt;
@@ -489,15 +493,19 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       constexpr int PU = kFUnion / NTH;
       uint64_t ue[PU];
 #pragma unroll
-      for (int r = 0; r < PU; ++r) ue[r] = s_union[min(tid + NTH * r, total - 1)];
+      for (int r = 0; r < PU; ++r) ue[r] = (r < (total + NTH - 1) / NTH) ? s_union[min(tid + NTH * r, total - 1)] : 0ull;
       auto valid = [&](int r) { return tid + NTH * r < total; };
       // their histogram in the bins Dmax .. Dmax + kFWin - 2 (the unit's
       // there; the last counter takes every bin above), then D: thread tid
       // owns counter kFWin - 1 - tid
+      const int ru = (total + NTH - 1) / NTH;  // (registers in use: a uniform bound)
 #pragma unroll
       for (int r = 0; r < PU; ++r) {
-        const uint32_t b = fbin_c(ue[r]);
-        if (valid(r) && b >= Dmax) atomicAdd(&x.s_fh[min(b - Dmax, (uint32_t)kFWin - 1)], 1u);
+        if (r < ru) {
+          const uint32_t b = fbin_c(ue[r]);
+          uint32_t* dst = ((int)valid(r) & (int)(b >= Dmax)) ? &x.s_fh[min(b - Dmax, (uint32_t)kFWin - 1)] : &s_junk[lane];
+          atomicAdd(dst, 1u);
+        }
       }
       __syncthreads();
       {
@@ -555,8 +563,13 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
         for (int i = tid; i < NS; i += NTH) s_sub[i] = 0u;
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < PU; ++r)
-          if (valid(r) && fbin_c(ue[r]) == D) atomicAdd(&s_sub[(uint32_t)(ue[r] >> kSh) & (NS - 1)], 1u);
+        for (int r = 0; r < PU; ++r) {
+          if (r < ru) {
+            uint32_t* dst = ((int)valid(r) & (int)(fbin_c(ue[r]) == D)) ? &s_sub[(uint32_t)(ue[r] >> kSh) & (NS - 1)]
+                                                                        : &s_junk[lane];
+            atomicAdd(dst, 1u);
+          }
+        }
         __syncthreads();
         {
           const int mine = (tid < NS) ? (int)s_sub[NS - 1 - tid] : 0;
