@@ -449,12 +449,13 @@ bkv_status qattn_decode_step(const bkv_layout* L, const bkv_cache* c, const uint
   return launch_topk(*L, sigma, len, max_len, k, 0, idx, w.tkc, w.tkctr, s) == hipSuccess ? BKV_OK : BKV_E_HIP;
 }
 
-// Whether the fused step can run this call: a plain layout (fp16 query,
-// affine keys of 3 or 4 bits), splits that fit the LDS stage, the per-split
-// lists and the unit barriers' limits.
+// Whether the fused step can run this call: an fp16 query with affine keys
+// of 3 or 4 bits or MXFP4 keys (key formats 1 and 2), splits that fit the LDS
+// stage, the per-split lists and the unit barriers' limits.
 static bool fused_shape_ok(const bkv_layout* L, const Workspace& w, int chunk, int k) {
   const int units = L->batch * L->n_kv_heads;
-  if (L->query_bits != 0 || L->key_format != 0 || L->k_bits < 3) return false;
+  if (L->query_bits != 0 || L->k_bits < 3) return false;
+  if (L->key_format != 0 && L->k_bits != 4) return false;
   if (units > kFMaxUnits || w.nsplit > kFMaxSplits || chunk > kSelStage) return false;
   return (long long)w.nsplit * k <= kSelSlots;
 }

@@ -194,6 +194,15 @@ bool decode_fused_fits(const bkv_layout& L, const Workspace& w, bool append);
 hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                                float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
                                const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s);
+// (the MXFP4 key formats' builds of the same: 1 fp16 query, 2 MXFP4 query)
+bool decode_fused_fits_mx(const bkv_layout& L, const Workspace& w, bool append);
+bool decode_fused_fits_fp4(const bkv_layout& L, const Workspace& w, bool append);
+hipError_t launch_decode_fused_mx(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                                  float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
+                                  const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s);
+hipError_t launch_decode_fused_fp4(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                                   float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
+                                   const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s);
 // The same with the INT8 query (layouts with query_bits = 8) and with MXFP4
 // keys (key_format = 1); launch_decode_approx forwards those layouts here.
 hipError_t launch_decode_approx_q8(const bkv_layout& L, const bkv_cache& c, const uint16_t* q,

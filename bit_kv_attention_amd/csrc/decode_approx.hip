@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(64 * kScanWaves, 8 / kScanWaves) void BKV_SCAN_KERN
     x.s_acc = &s_acc[0][0][0];
     x.s_lg = reinterpret_cast<float*>(&s_meta[0][0]);
     x.s_w = reinterpret_cast<float*>(&s_sig[0][0][0]);
-    fused_tail<KB, VB, G>(x, rm, rl, ra);
+    fused_tail<KB, VB, G, kFP4 ? 2 : (kMX ? 1 : 0)>(x, rm, rl, ra);
     return;
   }
   }  // !SIGONLY
@@ -1234,9 +1234,38 @@ hipError_t launch_g(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, 
 
 }  // namespace
 
+#if BKV_KEY_MXFP4 || BKV_KEY_FP4
+// The fused step of the MXFP4 key formats (4-bit keys), this build's.
+#if BKV_KEY_FP4
+#define BKV_FUSED_FITS decode_fused_fits_fp4
+#define BKV_FUSED_LAUNCH launch_decode_fused_fp4
+#else
+#define BKV_FUSED_FITS decode_fused_fits_mx
+#define BKV_FUSED_LAUNCH launch_decode_fused_mx
+#endif
+bool BKV_FUSED_FITS(const bkv_layout& L, const Workspace& w, bool append) {
+  const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
+  if (L.v_bits == 4) return g4 ? fused_fits_t<4, 4, 4>(L, w, append) : fused_fits_t<4, 4, 8>(L, w, append);
+  return g4 ? fused_fits_t<4, 2, 4>(L, w, append) : fused_fits_t<4, 2, 8>(L, w, append);
+}
+hipError_t BKV_FUSED_LAUNCH(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
+                            float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
+                            const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s) {
+  const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
+  if (L.v_bits == 4)
+    return g4 ? launch_fused_t<4, 4, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+              : launch_fused_t<4, 4, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+  return g4 ? launch_fused_t<4, 2, 4>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+            : launch_fused_t<4, 2, 8>(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+}
+#endif
+
 #if !BKV_QUERY_INT8 && !BKV_KEY_MXFP4 && !BKV_KEY_FP4
+// (dispatch to the build of the layout's key format)
 bool decode_fused_fits(const bkv_layout& L, const Workspace& w, bool append) {
-  if (L.query_bits != 0 || L.key_format != 0 || L.k_bits < 3) return false;
+  if (L.query_bits != 0 || L.k_bits < 3) return false;
+  if (L.key_format == 1) return L.k_bits == 4 && decode_fused_fits_mx(L, w, append);
+  if (L.key_format == 2) return L.k_bits == 4 && decode_fused_fits_fp4(L, w, append);
   const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
   const bool v4 = L.v_bits == 4;
   if (L.k_bits == 4) {
@@ -1250,7 +1279,12 @@ bool decode_fused_fits(const bkv_layout& L, const Workspace& w, bool append) {
 hipError_t launch_decode_fused(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
                                float* sigma, const Workspace& w, int chunk, int32_t* idx, int ksel,
                                const uint16_t* k_new, const uint16_t* v_new, float* out, hipStream_t s) {
-  if (L.query_bits != 0 || L.key_format != 0 || L.k_bits < 3) return hipErrorNotSupported;
+  if (L.query_bits != 0 || L.k_bits < 3) return hipErrorNotSupported;
+  if (L.key_format == 1 || L.key_format == 2) {
+    if (L.k_bits != 4) return hipErrorNotSupported;
+    return L.key_format == 1 ? launch_decode_fused_mx(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s)
+                             : launch_decode_fused_fp4(L, c, q, len, sigma, w, chunk, idx, ksel, k_new, v_new, out, s);
+  }
   const bool g4 = L.n_q_heads / L.n_kv_heads == 4;
   const bool v4 = L.v_bits == 4;
   if (L.k_bits == 4) {

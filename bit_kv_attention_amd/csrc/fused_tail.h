@@ -39,6 +39,7 @@
 
 #include "bkv_internal.h"
 #include "correct_lane.h"
+#include "quant_lane.h"
 #include "select_lds.h"
 
 namespace bkv {
@@ -131,9 +132,9 @@ constexpr int kFStage = 512;            // list entries a wave stages in LDS (th
 // takes the key run of token tid / 8 (channels 16 (tid % 8) ..), and lane l
 // of wave w the values of channels 2l, 2l + 1 of tokens 8w .. 8w + 7 (one
 // coalesced 256-byte row per token and wave).
-template <int KB, int VB>
+template <int KB, int VB, int KF>
 struct FPass {
-  KeyRun<KB, true, true> kr;
+  KeyRun<KB, true, true, KF> kr;
   uint32_t vx[8];     // the fp16 shadow pair
   uint32_t vd[8][2];  // the two channels' code dwords
   uint32_t vm[8];     // their group's meta word
@@ -169,7 +170,11 @@ struct FPass {
 
 // rm, rl, ra: this thread's (head, channel) pairs e = tid + 512 r of the
 // split's approximate state (max in log2 units, denominator, value sum).
-template <int KB, int VB, int G>
+// KF: the key format (0 affine keys; 1 MXFP4 keys against the fp16 query; 2
+// MXFP4 keys against the MXFP4 query, whose E2M1 codes and scales the tail
+// derives from the query rows by the keys' own rule, as the correction
+// kernel does).
+template <int KB, int VB, int G, int KF = 0>
 __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&rm)[G / 4],
                                            const float (&rl)[G / 4], const float (&ra)[G / 4]) {
   constexpr int NTH = 64 * kScanWaves;
@@ -216,6 +221,28 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
     for (int c = 0; c < 16; ++c) r += h2f(x.s_q[h][16 * p + c]);
     s_qrun[h][p] = r;
   }
+  // key format 2: the query's E2M1 codes as fp16 patterns (value * 2^-14) and
+  // 2^(Xq + 28) per 16-channel run; 8 channels per thread, a quad per
+  // 32-channel quarter (whole waves)
+  constexpr bool kF2 = KF == 2;
+  __shared__ uint4 s_q4h[kF2 ? G : 1][kHeadDim / 8];
+  __shared__ float s_q4c[kF2 ? G : 1][kHeadDim / 16];
+  if constexpr (kF2) {
+    if (tid < G * kHeadDim / 8) {
+      float xq[8];
+      halves8(reinterpret_cast<const uint4*>(&x.s_q[0][0])[tid], xq);
+      uint32_t code[8];
+      const int X = (int)quantise_lane_e8(xq, code) - 127;
+      uint32_t pk[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t c0 = code[2 * j], c1 = code[2 * j + 1];
+        pk[j] = ((c0 & 7u) << 9) | ((c0 & 8u) << 12) | ((c1 & 7u) << 25) | ((c1 & 8u) << 28);
+      }
+      (&s_q4h[0][0])[tid] = (uint4){pk[0], pk[1], pk[2], pk[3]};
+      if ((tid & 1) == 0) (&s_q4c[0][0])[tid >> 1] = __builtin_amdgcn_ldexpf(1.0f, X + 28);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int e = tid + NTH * r;
@@ -239,10 +266,11 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
   // okv[j] != 0): exact logits and weights (relative to the pass maximum),
   // approximate ones (relative to the split's maximum), the value sums, then
   // the exact state online over the passes and the approximate sums.
-  auto pass_run = [&](const FPass<KB, VB>& pd, const int* toks, const int* okv) {
+  auto pass_run = [&](const FPass<KB, VB, KF>& pd, const int* toks, const int* okv) {
     {
       float ex[G], ap[G];
-      run_logits<KB, G, true, true, false, 0>(pd.kr, part, qh, s_qrun, nullptr, nullptr, nullptr, ex, ap);
+      run_logits<KB, G, true, true, false, KF>(pd.kr, part, qh, s_qrun, kF2 ? &s_q4h[0] : nullptr, nullptr,
+                                               kF2 ? &s_q4c[0] : nullptr, ex, ap);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         ex[h] = sum8(ex[h]);
@@ -326,7 +354,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
       }
     }
   };
-  auto load_pass = [&](FPass<KB, VB>& pd, const int* toks) {
+  auto load_pass = [&](FPass<KB, VB, KF>& pd, const int* toks) {
     pd.load(x.ksh, x.kbase, x.kmeta, x.vsh, x.vbase, x.vmeta, x.cap, x.mshift, toks);
   };
 
@@ -682,7 +710,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
     }
     __syncthreads();
     // (a wave whose 8 slots are all empty loads nothing)
-    FPass<KB, VB> pd;
+    FPass<KB, VB, KF> pd;
     if (8 * wv < np)
       load_pass(pd, s_tok);
     else

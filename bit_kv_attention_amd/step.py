@@ -49,6 +49,7 @@ class DecodeStep:
         elif one_launch and not plain:
             raise ValueError("one_launch runs the plain top-k step only")
         self.one_launch = bool(one_launch)
+        self.ran_fused = False  # whether the last call ran as one launch
 
     def attend(self, cache: bk.Cache, q, lens, stream=None):
         """Approximate pass, top-k, exact correction over the first lens[b] tokens."""
@@ -80,6 +81,7 @@ class DecodeStep:
     def _fused(self, cache, k_new, v_new, q, lens, stream) -> bool:
         """qattn_decode_fused; False (nothing enqueued) when the library cannot
         run this call in one launch (e.g. the device cannot hold its grid)."""
+        self.ran_fused = False
         try:
             bk.qattn_decode_fused(self.layout, cache, k_new, v_new, q, lens, self.k, self.sigma,
                                   self.idx if self.k > 0 else None, self.out, self.ws, stream)
@@ -87,6 +89,7 @@ class DecodeStep:
             if e.status != 3:  # BKV_E_UNSUPPORTED
                 raise
             return False
+        self.ran_fused = True
         return True
 
     def _attend_exclude(self, cache: bk.Cache, q, lens, stream=None):

@@ -514,12 +514,16 @@ bkv_status qattn_exact_host(const bkv_layout* layout, const uint16_t* k_shadow_h
  * approximate output; k >= len: exact attention).  The scan's workgroups of
  * a (b, kvh) pair meet at barriers inside the launch, so the grid must be
  * resident on the device at once; the call checks that and the shape.
+ * Layouts: the fp16 query (query_bits 0) with affine keys of 3 or 4 bits, or
+ * with MXFP4 keys (key_format 1 and 2, whose scores and correction follow
+ * qattn_decode_approx and qattn_correct for that format).
  * Workspace: bkv_workspace_bytes(layout, max_len, k), zero-filled once
  * (the call keeps its counters and histograms at zero between calls).
  * Errors: BKV_E_UNSUPPORTED when the fused step cannot run this call (query
- * bits, key format, k_bits < 3, more than 256 (b, kvh) pairs, more than 64
- * scan ranges per pair, ranges over 16384 tokens, ranges per pair times k
- * over 8192, or a grid larger than the device holds at once -- nothing is
+ * bits 8, k_bits < 3, MXFP4 keys of other than 4 bits, more than 256 (b, kvh)
+ * pairs, more than 64 scan ranges per pair, ranges over 16384 tokens, ranges
+ * per pair times k over 8192, or a grid larger than the device holds at once
+ * -- nothing is
  * enqueued; bkv_fused_supported says which shapes qualify); BKV_E_NULL if
  * only one of k_new, v_new is NULL; otherwise as qattn_decode_step and
  * qattn_correct.

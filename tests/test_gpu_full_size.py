@@ -55,6 +55,7 @@ def test_full_size_sampled_units(P, name, shadow):
         st = DecodeStep(lay, w.k, L, one_launch=one)
         out = st.step(gc, P.to_dev(inp.q), P.to_dev(kn[0]), P.to_dev(vn[0]), [L - 1] * w.B)
         torch.cuda.synchronize()
+        assert st.ran_fused == one, "the fused step fell back to the separate launches"
         results[one] = dict(
             out=out.cpu().numpy().reshape(w.B, w.Hq, 128),
             sig=st.sigma.cpu().numpy().reshape(units, cap),

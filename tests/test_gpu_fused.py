@@ -81,6 +81,7 @@ def run_both(P, pair, lens, k, append=True):
         a.attend(pair["gc"], q, lens)
         b.attend(gc2, q, lens)
     torch.cuda.synchronize()
+    assert a.ran_fused, "the fused step fell back to the separate launches"
     cap = pair["cap"]
     res = []
     for st in (a, b):
@@ -107,6 +108,21 @@ def test_fused_step_parity(P, kb, vb, G):
     """Ragged lengths over several splits; the append inside the launch."""
     banner(f"fused step kb={kb} vb={vb} G={G}")
     w = P.Workload("fused", 3, 2 * G, 2, 128, 5000, kb, vb, 32, 40, 8, 300 + 10 * kb + vb + G)
+    pair = P.build_pair(w, L=5000, cap=5024)
+    lens = np.array([5000, 2311, 777])
+    ra, rb = run_both(P, pair, lens, w.k)
+    assert_same_selection(ra, rb, lens)
+    check_against_oracle(P, pair, ra, lens, w.k)
+    check_against_oracle(P, pair, rb, lens, w.k)
+
+
+@pytest.mark.parametrize("kf,vb,G", [(2, 4, 4), (2, 2, 8), (1, 4, 4), (1, 2, 8)])
+def test_fused_step_parity_mxfp4(P, kf, vb, G):
+    """MXFP4 keys in the fused launch: key format 2 (scores FP4 x FP4 on the
+    scaled MFMA, the correction's approximate logits from the same FP4 query)
+    and key format 1 (fp16 query); ragged lengths, the append inside."""
+    banner(f"fused step mxfp4 kf={kf} vb={vb} G={G}")
+    w = P.Workload("fusedmx", 3, 2 * G, 2, 128, 5000, 4, vb, 32, 40, 8, 600 + 10 * kf + vb + G, key_format=kf)
     pair = P.build_pair(w, L=5000, cap=5024)
     lens = np.array([5000, 2311, 777])
     ra, rb = run_both(P, pair, lens, w.k)
