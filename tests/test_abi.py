@@ -100,6 +100,26 @@ def test_unsupported_head_dim_and_group(bk):
     assert bk.raw_status("bkv_workspace_bytes", C.byref(lay), 10, -1, C.byref(out)) == 7
 
 
+def test_fused_supported_shapes(bk):
+    """Which calls the one-launch step takes (host logic only): the fp16 query
+    with 3- or 4-bit affine keys or 4-bit MXFP4 keys of both formats; not the
+    INT8 query nor 1- and 2-bit keys; not more than 256 (b, kvh) pairs; not
+    more splits times k than the lists hold."""
+    def sup(*args, max_len=32768, k=256):
+        return bk.bkv_fused_supported(bk.Layout(*args), max_len, k)
+    assert sup(4, 32, 8, 128, 4, 4, 32, 32768)
+    assert sup(4, 32, 8, 128, 3, 2, 32, 32768)
+    assert sup(4, 64, 8, 128, 3, 2, 32, 131072, max_len=131072, k=512)
+    assert sup(4, 32, 8, 128, 4, 4, 32, 32768, 0, 1)  # MXFP4 keys, fp16 query
+    assert sup(4, 32, 8, 128, 4, 2, 32, 32768, 0, 2)  # MXFP4 keys and query
+    assert not sup(4, 32, 8, 128, 4, 4, 32, 32768, 8)  # INT8 query
+    assert not sup(4, 32, 8, 128, 2, 2, 64, 32768)
+    assert not sup(4, 32, 8, 128, 1, 2, 64, 32768)
+    assert not sup(64, 32, 8, 128, 4, 4, 32, 4096, max_len=4096)  # 512 (b, kvh) pairs
+    assert sup(1, 4, 1, 128, 4, 4, 32, 4096, max_len=4096, k=100)
+    assert not sup(1, 4, 1, 128, 4, 4, 32, 4096, max_len=4096, k=4096)  # splits x k over the lists' room
+
+
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
