@@ -23,6 +23,8 @@
 //           scan's split states and of the chunk states (every load of a
 //           record independent of the others, batched), then the formula
 //           above.
+#include <mutex>
+
 #include "bkv_internal.h"
 #include "correct_lane.h"
 #include "quant_lane.h"
@@ -652,6 +654,40 @@ void launch_g(const bkv_layout& L, const bkv_cache& cc, const uint16_t* q, const
        : launch_t<KB, VB, 8, false>(L, cc, q, len, idx, k, w, terms, s);
 }
 
+// A second stream per device, at the default priority, with a fork and a join
+// event: the block correction runs the approximate rows on it while the exact
+// rows run on the caller's stream (independent parts of the same records).
+// Created on the first call on a device and kept until the process ends; the
+// fork-join of one call is enqueued under a lock, so calls from several host
+// threads do not interleave their events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxSideDevices];
+
+// (under g_side_mu) The current device's side stream, or null where none can
+// be made: the caller then enqueues everything on its own stream.
+SideStream* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.failed) return nullptr;
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      ss.failed = true;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+  }
+  return &ss;
+}
+
 }  // namespace
 
 hipError_t launch_correct_rows(const bkv_layout& L, const bkv_cache& c, const uint16_t* q, const SeqArg& len,
@@ -662,6 +698,16 @@ hipError_t launch_correct_rows(const bkv_layout& L, const bkv_cache& c, const ui
   const int nrec = (min(row, max_len) + kRowRec - 1) / kRowRec;
   if (nrec > 0) {
     const dim3 grid(nrec, L.batch * L.n_kv_heads);
+    // the approximate rows on the side stream, forked from and joined back
+    // into the caller's stream around the exact rows
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = side_stream();
+    hipStream_t sa = s;
+    if (ss && hipEventRecord(ss->fork, s) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess)
+      sa = ss->s;
+    const hipError_t ea = launch_rows_approx(L, c, q, len, w, idx, row, nrec, sa);
+    if (ea != hipSuccess) return ea;
+    if (sa != s && hipEventRecord(ss->join, sa) != hipSuccess) return hipErrorLaunchFailure;
     if (L.n_q_heads / L.n_kv_heads == 4)
       exact_rows_kernel<4><<<grid, 64 * kRowWaves, 0, s>>>(c.k_shadow, c.v_shadow, q, idx, w.cs, len, L.n_q_heads,
                                                           L.n_kv_heads, L.capacity, row, w.nchunk);
@@ -669,8 +715,8 @@ hipError_t launch_correct_rows(const bkv_layout& L, const bkv_cache& c, const ui
       exact_rows_kernel<8><<<grid, 64 * kRowWaves, 0, s>>>(c.k_shadow, c.v_shadow, q, idx, w.cs, len, L.n_q_heads,
                                                           L.n_kv_heads, L.capacity, row, w.nchunk);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    const hipError_t e = launch_rows_approx(L, c, q, len, w, idx, row, nrec, s);
-    if (e != hipSuccess) return e;
+    // the combine after both parts
+    if (sa != s && hipStreamWaitEvent(s, ss->join, 0) != hipSuccess) return hipErrorLaunchFailure;
   }
   if (nrec <= 8 && w.nsplit <= 8)
     combine_kernel<1, 8><<<dim3(L.n_q_heads, L.batch), kHeadDim, 0, s>>>(w.part.m, w.part.l, w.part.acc, w.cs, nullptr,

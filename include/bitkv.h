@@ -43,7 +43,8 @@
  *    frees or synchronises, and keeps no state between calls (the one
  *    host-only computation, qattn_exact_host, uses OpenMP's thread pool;
  *    qattn_hybrid_layers waits on events of its own; qattn_decode_fused_noalloc
- *    uses an array the library holds).
+ *    uses an array the library holds; qattn_correct_blocks forks onto a
+ *    stream of the library's and joins back).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work; results are ready when the stream is.
  *  - Errors: every call validates its arguments on the host before any launch
@@ -338,7 +339,11 @@ bkv_status topk_select_blocks(const bkv_layout* layout, const float* sigma,
  * its k.  Needs qattn_decode_approx (or qattn_decode_select) of the same step
  * before it on ws, like qattn_correct.  Rows not written by
  * topk_select_blocks with these arguments give undefined results (every
- * access stays inside the cache).
+ * access stays inside the cache).  The approximate terms run on a second
+ * stream of the library's (one per device, default priority, made on the
+ * first call and kept until the process ends), forked from and joined back
+ * into `stream` with events; everything after the call on `stream` sees both
+ * parts.
  * Errors: as topk_select_blocks's BKV_E_ARG; BKV_E_NULL, BKV_E_CAPACITY and
  * BKV_E_WORKSPACE (bkv_workspace_bytes(layout, max_len, n_blocks * block)) as
  * qattn_correct.
