@@ -373,14 +373,22 @@ class Workbench:
                 for j, (name, _) in enumerate(calls)}
 
 
+# The sources the scan kernel (and the fused step, which is its FUSE build) is
+# compiled from: decode_approx.hip and every header it includes.
+SCAN_SOURCES = ("decode_approx.hip", "bkv_internal.h", "fused_tail.h", "correct_lane.h", "quant_lane.h",
+                "select_lds.h")
+
+
 def kernel_sources_sha256() -> str:
-    """One hash over every kernel source file: a counter summary holds for the
-    kernels built from exactly these sources."""
+    """One hash over the scan kernel's sources (and the public header): a
+    counter summary of the scan or the fused step holds for the kernels built
+    from exactly these sources."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in SCAN_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "bitkv.h"), "rb") as f:
+        h.update(b"bitkv.h\0" + f.read())
     return h.hexdigest()
 
 
