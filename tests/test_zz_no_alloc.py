@@ -34,9 +34,12 @@ def test_noalloc_host_errors():
     assert bk.bkv_workspace_bytes(big, 1 << 20, 100000) > 64 << 20
     assert bk.raw_status(fn, C.byref(big), C.byref(cv), FAKE, FAKE, FAKE, bl.ctypes.data, 100000, FAKE, FAKE,
                          FAKE, None) == 5
-    # layouts the fused step does not take
-    mx = bk.make_layout(4, 32, 8, 1024, 4, 4, key_format=2)
-    assert bk.raw_status(fn, C.byref(mx), C.byref(cv), FAKE, FAKE, FAKE, P, 8, FAKE, FAKE, FAKE, None) == 3
+    # a layout the fused step does not take (the INT8 query): refused by the
+    # host-side shape check, before any device call -- every call here must
+    # fail on the host, since the pointers are fake (key format 2, taken by
+    # the fused step, would launch on them where a GPU is present)
+    q8 = bk.make_layout(4, 32, 8, 1024, 4, 4, query_bits=8)
+    assert bk.raw_status(fn, C.byref(q8), C.byref(cv), FAKE, FAKE, FAKE, P, 8, FAKE, FAKE, FAKE, None) == 3
 
 
 @pytest.mark.gpu
