@@ -59,11 +59,14 @@ def to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(torch_dev())
 
 
-def build_pair(w: Workload, L: int, cap: int | None = None):
+def build_pair(w: Workload, L: int, cap: int | None = None, tweak=None):
     """Both caches holding the same L-1 prefill tokens, plus the step's new
-    token, q and the layout.  Returns dict."""
+    token, q and the layout.  tweak(inp), if given, may change the seeded
+    inputs in place before they are packed.  Returns dict."""
     cap = cap or ((L + 31) // 32) * 32
     inp = make_inputs(w, L=L - 1) if L > 1 else None
+    if tweak is not None and inp is not None:
+        tweak(inp)
     k1, v1 = make_new_tokens(w, 1, inp.outlier_ch if inp else make_inputs(w, L=1).outlier_ch)
     lay = bk.make_layout(w.B, w.Hq, w.Hkv, cap, w.kbits, w.vbits, group=w.group, query_bits=w.query_bits,
                          key_format=w.key_format)

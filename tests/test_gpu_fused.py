@@ -116,6 +116,31 @@ def test_fused_step_parity(P, kb, vb, G):
     check_against_oracle(P, pair, rb, lens, w.k)
 
 
+@pytest.mark.parametrize("kb,vb,G", [(4, 4, 4), (3, 2, 8)])
+def test_fused_step_crowded_selection(P, kb, vb, G):
+    """Selected tokens crowded into the first split (their keys follow the
+    query), so that one workgroup corrects several passes of them while
+    others correct few or none.  Ragged lengths; every sequence appends."""
+    banner(f"fused step, crowded selection kb={kb} vb={vb} G={G}")
+    w = P.Workload("crowded", 3, 2 * G, 2, 128, 5000, kb, vb, 32, 300, 8, 500 + 10 * kb + vb + G)
+
+    def crowd(inp):  # tokens 0..399 of each (b, kvh): keys along the group's first query head, plus noise
+        rng = np.random.default_rng(7)
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                qd = inp.q[b, h * G].astype(np.float32)
+                noise = rng.standard_normal((400, 128)).astype(np.float32)
+                inp.K[b, h, :400] = (0.5 * qd[None, :] + 0.3 * noise).astype(np.float16)
+
+    pair = P.build_pair(w, L=5000, cap=5024, tweak=crowd)
+    lens = np.array([5000, 2311, 777])
+    ra, rb = run_both(P, pair, lens, w.k)
+    # the crowding worked: more than a pass of selected tokens in the first split
+    assert all(int((ra["idx"][b, h] < 256).sum()) > 64 for b in range(w.B) for h in range(w.Hkv))
+    assert_same_selection(ra, rb, lens)
+    check_against_oracle(P, pair, ra, lens, w.k)
+
+
 @pytest.mark.parametrize("kf,vb,G", [(2, 4, 4), (2, 2, 8), (1, 4, 4), (1, 2, 8)])
 def test_fused_step_parity_mxfp4(P, kf, vb, G):
     """MXFP4 keys in the fused launch: key format 2 (scores FP4 x FP4 on the
