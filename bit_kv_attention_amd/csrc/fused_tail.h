@@ -388,6 +388,13 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
     // many equal scores -- sends the workgroup to the two-pass compaction)
     uint64_t* mylist = lists + (size_t)x.split * x.chunk;
     int nlist = 0;
+    // bin(s) >= Ds  <=>  s >= the least value of bin Ds (the key is monotone
+    // in s, -0 and +0 alike): one compare per score instead of its key.
+    // Scores are finite or -inf (bin 15); bins 0..14 and above 8176 (+inf)
+    // hold only NaN keys, so those Ds take -inf and the least value of 8176.
+    constexpr uint32_t kBinNegInf = 15u, kBinPosInf = 8176u;
+    const float sth =
+        (Ds <= kBinNegInf) ? -INFINITY : key_value(min(Ds, kBinPosInf) << (32 - kFBinBits));
     {
       uint32_t* stage = reinterpret_cast<uint32_t*>(x.s_acc) + wv * kFStage;
       // wave range: a multiple of 256 entries (lane l reads entries 4l..4l+3
@@ -409,7 +416,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
           int pj[4], c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            pj[j] = (int)(i0 + j < hi) & (int)(fbin(v[r][j]) >= Ds);
+            pj[j] = (int)(i0 + j < hi) & (int)(v[r][j] >= sth);
             c += pj[j];
           }
           const int inc = wave_incl_scan(c);
@@ -441,7 +448,7 @@ __device__ __forceinline__ void fused_tail(const FusedCtx<G>& x, const float (&r
         }
       } else {
         ordered_compact<NW>(
-            len_s, [&](int i) { return fbin(x.s_split[i]) >= Ds; },
+            len_s, [&](int i) { return x.s_split[i] >= sth; },
             [&](int q, int i) { st_dev64(&mylist[q], composite(x.s_split[i], x.t_begin + i)); }, s_wsum);
       }
     }
